@@ -1,0 +1,18 @@
+"""Float64 CPU oracle for the causal softmax attention hot path.
+
+TEST INFRASTRUCTURE ONLY: imported by the tests, the smoke check and the
+CPU-baseline leg of the benchmark, never by the product package.  It shares no
+code with the HIP library and the HIP library never calls it.
+
+Every function is pinned by CPU tests against something other than itself
+(torch float64 library attention and autograd, finite differences, closed
+forms, invariants, brute force, torch's own fp8 decoding).
+"""
+from .prefill import (gate_prefix, visible_mask, forward, backward, row_stats,
+                      forward_rows)
+from .decode import (fp8_e4m3fn_to_f64, gather_request_kv, decode_paged,
+                     decode_partials, splitk_reduce)
+
+__all__ = ["gate_prefix", "visible_mask", "forward", "backward", "row_stats",
+           "forward_rows", "fp8_e4m3fn_to_f64", "gather_request_kv",
+           "decode_paged", "decode_partials", "splitk_reduce"]
