@@ -1,0 +1,364 @@
+// C ABI of the attention library: argument validation, workspace layout and
+// launch of the gfx950 kernels.  Every check runs before the first launch,
+// so a call that returns an error has enqueued nothing.
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "../../include/attn.h"
+#include "common.h"
+#include "kernels.h"
+
+namespace {
+
+thread_local char g_last_error[512] = "";
+
+int fail(int code, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_last_error, sizeof(g_last_error), fmt, ap);
+  va_end(ap);
+  return code;
+}
+
+int ok() {
+  g_last_error[0] = '\0';
+  return ATTN_OK;
+}
+
+int hip_fail(hipError_t e, const char* where) {
+  return fail(ATTN_ERR_HIP, "%s: %s", where, hipGetErrorString(e));
+}
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+size_t round_up(size_t x) { return (x + 255) & ~size_t(255); }
+
+#define REQUIRE(cond, code, ...) \
+  do {                           \
+    if (!(cond)) return fail(code, __VA_ARGS__); \
+  } while (0)
+#define REQ_PTR(p, align)                                                               \
+  do {                                                                                  \
+    if ((p) == nullptr) return fail(ATTN_ERR_INVALID, "%s is NULL", #p);                \
+    if (!aligned((p), (align)))                                                         \
+      return fail(ATTN_ERR_INVALID, "%s is not %d-byte aligned", #p, (int)(align));     \
+  } while (0)
+
+bool fwd_dims_supported(int dqk, int dv) {
+  return (dqk == 64 && dv == 64) || (dqk == 128 && dv == 128) || (dqk == 256 && dv == 256) ||
+         (dqk == 256 && dv == 512);
+}
+
+int check_prefill_common(const void* q, const void* k, const void* v, const int32_t* cu, int num_seqs,
+                         int max_seqlen, int T, int Hq, int Hkv, int dqk, int dv, float scale) {
+  REQUIRE(num_seqs >= 0 && T >= 0 && max_seqlen >= 0, ATTN_ERR_INVALID,
+          "negative size (num_seqs=%d total_tokens=%d max_seqlen=%d)", num_seqs, T, max_seqlen);
+  REQUIRE(Hq >= 1 && Hkv >= 1, ATTN_ERR_INVALID, "head counts must be positive (Hq=%d Hkv=%d)", Hq, Hkv);
+  REQUIRE(Hq % Hkv == 0, ATTN_ERR_INVALID, "num_q_heads (%d) must be a multiple of num_kv_heads (%d)", Hq, Hkv);
+  REQUIRE(fwd_dims_supported(dqk, dv), ATTN_ERR_UNSUPPORTED,
+          "head dims (d_qk=%d, d_v=%d) not supported; supported: (64,64) (128,128) (256,256) (256,512)",
+          dqk, dv);
+  REQUIRE(std::isfinite(scale), ATTN_ERR_INVALID, "softmax_scale is not finite");
+  REQUIRE(num_seqs <= 65535, ATTN_ERR_UNSUPPORTED, "num_seqs %d exceeds 65535", num_seqs);
+  REQUIRE(Hq <= 65535, ATTN_ERR_UNSUPPORTED, "num_q_heads %d exceeds 65535", Hq);
+  if (num_seqs > 0 && T > 0) {
+    REQUIRE(max_seqlen >= 1 && max_seqlen <= T, ATTN_ERR_INVALID,
+            "max_seqlen %d must be in [1, total_tokens=%d]", max_seqlen, T);
+    REQUIRE(max_seqlen <= 65535 * 16, ATTN_ERR_UNSUPPORTED, "max_seqlen %d too large", max_seqlen);
+    REQ_PTR(q, 16);
+    REQ_PTR(k, 16);
+    REQ_PTR(v, 16);
+    REQ_PTR(cu, 4);
+  }
+  return ATTN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* attn_status_string(int status) {
+  switch (status) {
+    case ATTN_OK: return "ok";
+    case ATTN_ERR_INVALID: return "invalid argument";
+    case ATTN_ERR_UNSUPPORTED: return "unsupported configuration";
+    case ATTN_ERR_HIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+const char* attn_last_error(void) { return g_last_error; }
+
+const char* attn_version(void) { return "attn-mi355x 0.1 (gfx950)"; }
+
+// ---------------------------------------------------------------------------
+size_t attn_fwd_workspace_size(int total_tokens, int num_q_heads, int has_gate) {
+  if (!has_gate || total_tokens <= 0 || num_q_heads <= 0) return 0;
+  return round_up((size_t)total_tokens * num_q_heads * sizeof(float));
+}
+
+int attn_fwd_varlen(const void* q, const void* k, const void* v, const int32_t* cu_seqlens,
+                    int num_seqs, int max_seqlen, int total_tokens, int num_q_heads,
+                    int num_kv_heads, int head_dim_qk, int head_dim_v, float softmax_scale,
+                    int window, const float* sink, const float* g, void* o, float* lse,
+                    void* workspace, size_t workspace_bytes, void* stream) {
+  int st = check_prefill_common(q, k, v, cu_seqlens, num_seqs, max_seqlen, total_tokens, num_q_heads,
+                                num_kv_heads, head_dim_qk, head_dim_v, softmax_scale);
+  if (st != ATTN_OK) return st;
+  if (num_seqs == 0 || total_tokens == 0) return ok();
+  REQ_PTR(o, 16);
+  REQ_PTR(lse, 4);
+  if (sink) REQ_PTR(sink, 4);
+  if (g) REQ_PTR(g, 4);
+  const size_t need = attn_fwd_workspace_size(total_tokens, num_q_heads, g != nullptr);
+  REQUIRE(workspace_bytes >= need, ATTN_ERR_INVALID, "workspace too small: %zu < %zu bytes",
+          workspace_bytes, need);
+  if (need) REQ_PTR(workspace, 256);
+
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  attn::FwdParams p{};
+  p.q = q; p.k = k; p.v = v; p.cu = cu_seqlens; p.sink = sink; p.g = g;
+  p.G2 = g ? reinterpret_cast<float*>(workspace) : nullptr;
+  p.o = o; p.lse = lse;
+  p.num_seqs = num_seqs; p.max_seqlen = max_seqlen; p.T = total_tokens;
+  p.Hq = num_q_heads; p.Hkv = num_kv_heads; p.window = window;
+  p.scale_log2 = softmax_scale * attn::kLog2e;
+  hipError_t e;
+  if (g) {
+    e = attn::launch_gate_prefix(g, cu_seqlens, p.G2, num_seqs, total_tokens, num_q_heads, s);
+    if (e != hipSuccess) return hip_fail(e, "gate prefix launch");
+  }
+  e = attn::launch_fwd(p, head_dim_qk, head_dim_v, s);
+  if (e != hipSuccess) return hip_fail(e, "forward launch");
+  return ok();
+}
+
+// ---------------------------------------------------------------------------
+namespace {
+struct BwdLayout {
+  size_t delta, dq_acc, dG, G2, total;
+};
+BwdLayout bwd_layout(int T, int Hq, int dqk, int has_gate) {
+  BwdLayout L{};
+  const size_t rows = (size_t)(T > 0 ? T : 0) * (Hq > 0 ? Hq : 0);
+  size_t off = 0;
+  L.delta = off; off += round_up(rows * sizeof(float));
+  L.dq_acc = off; off += round_up(rows * (size_t)(dqk > 0 ? dqk : 0) * sizeof(float));
+  L.dG = off; if (has_gate) off += round_up(rows * sizeof(float));
+  L.G2 = off; if (has_gate) off += round_up(rows * sizeof(float));
+  L.total = off;
+  return L;
+}
+}  // namespace
+
+size_t attn_bwd_workspace_size(int total_tokens, int num_q_heads, int head_dim_qk, int has_gate) {
+  if (total_tokens <= 0 || num_q_heads <= 0) return 0;
+  return bwd_layout(total_tokens, num_q_heads, head_dim_qk, has_gate).total;
+}
+
+int attn_bwd_varlen(const void* q, const void* k, const void* v, const void* o, const void* dO,
+                    const float* lse, const int32_t* cu_seqlens, int num_seqs, int max_seqlen,
+                    int total_tokens, int num_q_heads, int num_kv_heads, int head_dim_qk,
+                    int head_dim_v, float softmax_scale, int window, const float* sink,
+                    const float* g, void* dq, void* dk, void* dv, float* dsink, float* dg,
+                    void* workspace, size_t workspace_bytes, void* stream) {
+  int st = check_prefill_common(q, k, v, cu_seqlens, num_seqs, max_seqlen, total_tokens, num_q_heads,
+                                num_kv_heads, head_dim_qk, head_dim_v, softmax_scale);
+  if (st != ATTN_OK) return st;
+  REQUIRE((sink == nullptr) == (dsink == nullptr), ATTN_ERR_INVALID,
+          "dsink must be given exactly when sink is given");
+  REQUIRE((g == nullptr) == (dg == nullptr), ATTN_ERR_INVALID, "dg must be given exactly when g is given");
+  if (num_seqs == 0 || total_tokens == 0) {
+    // Nothing to differentiate; a sink gradient over no tokens is zero.
+    if (dsink != nullptr && num_q_heads > 0) {
+      REQ_PTR(dsink, 4);
+      hipError_t e = attn::launch_fill_zero(dsink, num_q_heads, reinterpret_cast<hipStream_t>(stream));
+      if (e != hipSuccess) return hip_fail(e, "dsink clear");
+    }
+    return ok();
+  }
+  REQ_PTR(o, 16);
+  REQ_PTR(dO, 16);
+  REQ_PTR(lse, 4);
+  REQ_PTR(dq, 16);
+  REQ_PTR(dk, 16);
+  REQ_PTR(dv, 16);
+  if (sink) { REQ_PTR(sink, 4); REQ_PTR(dsink, 4); }
+  if (g) { REQ_PTR(g, 4); REQ_PTR(dg, 4); }
+  const BwdLayout lay = bwd_layout(total_tokens, num_q_heads, head_dim_qk, g != nullptr);
+  REQUIRE(workspace_bytes >= lay.total, ATTN_ERR_INVALID, "workspace too small: %zu < %zu bytes",
+          workspace_bytes, lay.total);
+  REQ_PTR(workspace, 256);
+
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  char* ws = reinterpret_cast<char*>(workspace);
+  attn::BwdParams p{};
+  float* G2 = g ? reinterpret_cast<float*>(ws + lay.G2) : nullptr;
+  p.q = q; p.k = k; p.v = v; p.o = o; p.dO = dO; p.lse = lse; p.cu = cu_seqlens; p.sink = sink;
+  p.G2 = G2;
+  p.delta = reinterpret_cast<float*>(ws + lay.delta);
+  p.dq_acc = reinterpret_cast<float*>(ws + lay.dq_acc);
+  p.dG = g ? reinterpret_cast<float*>(ws + lay.dG) : nullptr;
+  p.dsink_acc = dsink;
+  p.dq = dq; p.dk = dk; p.dv = dv; p.dg = dg;
+  p.num_seqs = num_seqs; p.max_seqlen = max_seqlen; p.T = total_tokens;
+  p.Hq = num_q_heads; p.Hkv = num_kv_heads; p.window = window;
+  p.scale = softmax_scale;
+  p.scale_log2 = softmax_scale * attn::kLog2e;
+  hipError_t e;
+  if (g) {
+    e = attn::launch_gate_prefix(g, cu_seqlens, G2, num_seqs, total_tokens, num_q_heads, s);
+    if (e != hipSuccess) return hip_fail(e, "gate prefix launch");
+  }
+  e = attn::launch_bwd(p, head_dim_qk, head_dim_v, s);
+  if (e != hipSuccess) return hip_fail(e, "backward launch");
+  return ok();
+}
+
+// ---------------------------------------------------------------------------
+namespace {
+int choose_split_len(int R, int Hkv, int max_seq_len, int B) {
+  // Aim at ~2048 wavefront work items: long enough segments to amortise the
+  // partial traffic, enough of them to keep every SIMD streaming.
+  const double est_tokens = (double)R * max_seq_len * 0.5;
+  const double want = est_tokens * Hkv / 2048.0;
+  int sl = 256;
+  while (sl < want && sl < 8192) sl *= 2;
+  const int unit = B > 32 ? B : 32;
+  if (sl < unit) sl = unit;
+  return sl;
+}
+
+struct DecLayout {
+  size_t acc, m, l, total;
+  int split_len, num_splits;
+};
+DecLayout dec_layout(int R, int max_q, int max_seq_len, int Hq, int Hkv, int D, int B, int split_len) {
+  DecLayout L{};
+  L.split_len = split_len > 0 ? split_len : choose_split_len(R, Hkv, max_seq_len, B);
+  L.num_splits = (max_seq_len + L.split_len - 1) / L.split_len;
+  const size_t rows = (size_t)R * max_q * Hq;
+  size_t off = 0;
+  L.acc = off; off += round_up(rows * L.num_splits * (size_t)D * sizeof(float));
+  L.m = off; off += round_up(rows * L.num_splits * sizeof(float));
+  L.l = off; off += round_up(rows * L.num_splits * sizeof(float));
+  L.total = off;
+  return L;
+}
+}  // namespace
+
+size_t attn_decode_workspace_size(int num_requests, int max_seqlen_q, int max_seq_len, int num_q_heads,
+                                  int num_kv_heads, int head_dim, int block_size, int kv_split_len) {
+  if (num_requests <= 0 || max_seqlen_q <= 0 || max_seq_len <= 0 || num_q_heads <= 0 ||
+      num_kv_heads <= 0 || head_dim <= 0 || block_size <= 0 || kv_split_len < 0)
+    return 0;
+  return dec_layout(num_requests, max_seqlen_q, max_seq_len, num_q_heads, num_kv_heads, head_dim,
+                    block_size, kv_split_len).total;
+}
+
+int attn_decode_paged(const void* q, const int32_t* cu_seqlens_q, int num_requests, int max_seqlen_q,
+                      const void* k_cache, const void* v_cache, int kv_dtype, const float* k_scale,
+                      const float* v_scale, const int32_t* block_table, int max_pages,
+                      const int32_t* seq_lens, int max_seq_len, int num_blocks, int block_size,
+                      int num_q_heads, int num_kv_heads, int head_dim, float softmax_scale,
+                      int kv_split_len, void* out, float* lse, void* workspace,
+                      size_t workspace_bytes, void* stream) {
+  REQUIRE(num_requests >= 0, ATTN_ERR_INVALID, "num_requests %d is negative", num_requests);
+  REQUIRE(max_seqlen_q >= 1, ATTN_ERR_INVALID, "max_seqlen_q %d must be >= 1", max_seqlen_q);
+  REQUIRE(max_seqlen_q <= 4, ATTN_ERR_UNSUPPORTED,
+          "max_seqlen_q %d > 4: prefill is not supported by the split-K decode path", max_seqlen_q);
+  REQUIRE(kv_dtype == ATTN_DTYPE_BF16 || kv_dtype == ATTN_DTYPE_FP8_E4M3FN, ATTN_ERR_UNSUPPORTED,
+          "kv_dtype %d not supported (bf16 or fp8 e4m3fn)", kv_dtype);
+  const bool fp8 = kv_dtype == ATTN_DTYPE_FP8_E4M3FN;
+  REQUIRE(!fp8 || (k_scale != nullptr && v_scale != nullptr), ATTN_ERR_UNSUPPORTED,
+          "fp8 KV cache needs per-token k_scale and v_scale");
+  REQUIRE(fp8 || (k_scale == nullptr && v_scale == nullptr), ATTN_ERR_UNSUPPORTED,
+          "scales are only read with an fp8 KV cache");
+  REQUIRE(head_dim == 64 || head_dim == 128, ATTN_ERR_UNSUPPORTED, "head_dim %d not supported (64, 128)",
+          head_dim);
+  REQUIRE(block_size == 16 || block_size == 32 || block_size == 64 || block_size == 128,
+          ATTN_ERR_UNSUPPORTED, "block_size %d not supported (16, 32, 64, 128)", block_size);
+  REQUIRE(num_q_heads >= 1 && num_kv_heads >= 1, ATTN_ERR_INVALID, "head counts must be positive");
+  REQUIRE(num_q_heads % num_kv_heads == 0, ATTN_ERR_INVALID,
+          "num_q_heads (%d) must be a multiple of num_kv_heads (%d)", num_q_heads, num_kv_heads);
+  REQUIRE(max_seqlen_q * (num_q_heads / num_kv_heads) <= 64, ATTN_ERR_UNSUPPORTED,
+          "max_seqlen_q * (Hq/Hkv) = %d exceeds 64 query rows per KV head",
+          max_seqlen_q * (num_q_heads / num_kv_heads));
+  REQUIRE(std::isfinite(softmax_scale), ATTN_ERR_INVALID, "softmax_scale is not finite");
+  REQUIRE(kv_split_len >= 0, ATTN_ERR_INVALID, "kv_split_len %d is negative", kv_split_len);
+  if (kv_split_len > 0) {
+    const int unit = block_size > 32 ? block_size : 32;
+    REQUIRE(kv_split_len % unit == 0, ATTN_ERR_INVALID,
+            "kv_split_len %d must be a multiple of %d", kv_split_len, unit);
+  }
+  if (num_requests == 0) return ok();
+  REQUIRE(max_seq_len >= 1, ATTN_ERR_INVALID, "max_seq_len %d must be >= 1", max_seq_len);
+  REQUIRE(num_blocks >= 1, ATTN_ERR_INVALID, "num_blocks %d must be >= 1", num_blocks);
+  REQUIRE((long)max_pages * block_size >= max_seq_len, ATTN_ERR_INVALID,
+          "max_pages %d * block_size %d cannot hold max_seq_len %d", max_pages, block_size, max_seq_len);
+  REQ_PTR(q, 16);
+  REQ_PTR(cu_seqlens_q, 4);
+  REQ_PTR(k_cache, 16);
+  REQ_PTR(v_cache, 16);
+  if (fp8) { REQ_PTR(k_scale, 16); REQ_PTR(v_scale, 16); }
+  REQ_PTR(block_table, 4);
+  REQ_PTR(seq_lens, 4);
+  REQ_PTR(out, 16);
+  if (lse) REQ_PTR(lse, 4);
+  const DecLayout lay = dec_layout(num_requests, max_seqlen_q, max_seq_len, num_q_heads, num_kv_heads,
+                                   head_dim, block_size, kv_split_len);
+  REQUIRE(workspace_bytes >= lay.total, ATTN_ERR_INVALID, "workspace too small: %zu < %zu bytes",
+          workspace_bytes, lay.total);
+  REQ_PTR(workspace, 256);
+
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  char* ws = reinterpret_cast<char*>(workspace);
+  attn::DecodeParams p{};
+  p.q = q; p.cu_q = cu_seqlens_q; p.k_cache = k_cache; p.v_cache = v_cache;
+  p.k_scale = k_scale; p.v_scale = v_scale; p.block_table = block_table; p.seq_lens = seq_lens;
+  p.acc = reinterpret_cast<float*>(ws + lay.acc);
+  p.m = reinterpret_cast<float*>(ws + lay.m);
+  p.l = reinterpret_cast<float*>(ws + lay.l);
+  p.R = num_requests; p.max_pages = max_pages; p.Hq = num_q_heads; p.Hkv = num_kv_heads;
+  p.B = block_size; p.split_len = lay.split_len; p.num_splits = lay.num_splits;
+  p.scale_log2 = softmax_scale * attn::kLog2e;
+  hipError_t e = attn::launch_decode_splitk(p, head_dim, fp8, max_seqlen_q, s);
+  if (e != hipSuccess) return hip_fail(e, "decode launch");
+
+  attn::ReduceParams r{};
+  r.acc = p.acc; r.m = p.m; r.l = p.l; r.out = out; r.lse = lse;
+  r.rows = (long)num_requests * max_seqlen_q * num_q_heads;
+  r.num_splits = lay.num_splits; r.dv = head_dim; r.out_fp32 = 0;
+  r.seq_lens = seq_lens; r.cu_seqlens_q = cu_seqlens_q; r.num_requests = num_requests;
+  r.heads = num_q_heads; r.split_len = lay.split_len;
+  e = attn::launch_splitk_reduce(r, s);
+  if (e != hipSuccess) return hip_fail(e, "reduce launch");
+  return ok();
+}
+
+// ---------------------------------------------------------------------------
+int attn_splitk_reduce(const float* acc, const float* m, const float* l, int rows, int num_splits,
+                       int head_dim_v, void* out, int out_dtype, float* lse, void* stream) {
+  REQUIRE(rows >= 0, ATTN_ERR_INVALID, "rows %d is negative", rows);
+  REQUIRE(num_splits >= 1, ATTN_ERR_INVALID, "num_splits %d must be >= 1", num_splits);
+  REQUIRE(head_dim_v == 64 || head_dim_v == 128 || head_dim_v == 256 || head_dim_v == 512,
+          ATTN_ERR_UNSUPPORTED, "head_dim_v %d not supported (64, 128, 256, 512)", head_dim_v);
+  REQUIRE(out_dtype == ATTN_DTYPE_BF16 || out_dtype == ATTN_DTYPE_FP32, ATTN_ERR_UNSUPPORTED,
+          "out_dtype %d not supported (bf16 or fp32)", out_dtype);
+  if (rows == 0) return ok();
+  REQ_PTR(acc, 16);
+  REQ_PTR(m, 4);
+  REQ_PTR(l, 4);
+  REQ_PTR(out, 16);
+  if (lse) REQ_PTR(lse, 4);
+  attn::ReduceParams r{};
+  r.acc = acc; r.m = m; r.l = l; r.out = out; r.lse = lse; r.rows = rows;
+  r.num_splits = num_splits; r.dv = head_dim_v; r.out_fp32 = out_dtype == ATTN_DTYPE_FP32;
+  hipError_t e = attn::launch_splitk_reduce(r, reinterpret_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "reduce launch");
+  return ok();
+}
+
+}  // extern "C"

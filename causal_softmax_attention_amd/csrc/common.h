@@ -1,0 +1,94 @@
+// Device helpers shared by the gfx950 attention kernels.
+//
+// Matrix-core lane layouts used throughout (checked on gfx950 with an
+// in-bounds probe; l = lane 0..63):
+//   v_mfma_f32_16x16x32_bf16: A[m][k]: m = l%16, k = 8*(l/16)+e (e = 0..7)
+//                             B[k][n]: n = l%16, k = 8*(l/16)+e
+//                             C[m][n]: n = l%16, m = 4*(l/16)+i (i = 0..3)
+//   v_mfma_f32_16x16x16_bf16: as above with k = 4*(l/16)+e (e = 0..3)
+//   ds_read_b64_tr_b16: within each group of 16 lanes, result lane i,
+//                       element j (0..3) is element i%4 of the 8 bytes
+//                       addressed by lane 4*j + i/4 of the same group.
+//   ds_read_b64_tr_b8:  result lane i, byte j (0..7) is byte i%8 of the
+//                       8 bytes addressed by lane 2*j + i/8 of its group.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace attn {
+
+typedef __bf16 bf16;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef int i32x2 __attribute__((ext_vector_type(2)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+
+#define LDS_AS __attribute__((address_space(3)))
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+// Finite stand-in for -inf in running maxima: exp2(x - kNegBig) is 0 for
+// every finite score, and kNegBig - kNegBig = 0 avoids inf - inf.
+constexpr float kNegBig = -1.0e30f;
+
+__device__ __forceinline__ f32x4 mfma16x16x32(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mfma16x16x16(bf16x4 a, bf16x4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(
+      __builtin_bit_cast(i16x4, a), __builtin_bit_cast(i16x4, b), c, 0, 0, 0);
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
+
+// 8 contiguous bf16 read from LDS as one 16-byte access.
+__device__ __forceinline__ bf16x8 lds_read8(const bf16* p) {
+  return *reinterpret_cast<const bf16x8*>(p);
+}
+// Transposed 4 x bf16 read (see the layout note at the top).
+__device__ __forceinline__ bf16x4 lds_read_tr16(const bf16* p) {
+  i16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (LDS_AS i16x4*)(LDS_AS void*)(const_cast<bf16*>(p)));
+  return __builtin_bit_cast(bf16x4, v);
+}
+// Transposed 8 x byte read.
+__device__ __forceinline__ i32x2 lds_read_tr8(const uint8_t* p) {
+  return __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+      (LDS_AS i32x2*)(LDS_AS void*)(const_cast<uint8_t*>(p)));
+}
+
+__device__ __forceinline__ bf16x8 concat(bf16x4 a, bf16x4 b) {
+  return bf16x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+}
+
+// Round-to-nearest-even float -> bf16 (the compiler emits the gfx950
+// hardware conversion for this cast).
+__device__ __forceinline__ bf16 to_bf16(float x) { return (bf16)x; }
+
+__device__ __forceinline__ bf16x4 to_bf16x4(f32x4 x) {
+  return bf16x4{(bf16)x[0], (bf16)x[1], (bf16)x[2], (bf16)x[3]};
+}
+
+// Max / sum across the four 16-lane groups that hold the same column n.
+__device__ __forceinline__ float xgroup_max(float x) {
+  x = fmaxf(x, __shfl_xor(x, 16));
+  x = fmaxf(x, __shfl_xor(x, 32));
+  return x;
+}
+__device__ __forceinline__ float xgroup_sum(float x) {
+  x += __shfl_xor(x, 16);
+  x += __shfl_xor(x, 32);
+  return x;
+}
+
+// Two OCP e4m3fn bytes (low or high half of a 32-bit word) -> two floats.
+template <bool HI>
+__device__ __forceinline__ f32x2 fp8x2_to_f32(int word) {
+  return __builtin_amdgcn_cvt_pk_f32_fp8(word, HI);
+}
+
+}  // namespace attn

@@ -1,0 +1,90 @@
+// Parameter blocks and launchers of the gfx950 kernels (internal to the
+// library; the public interface is include/attn.h).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace attn {
+
+struct ReduceParams {
+  const float* acc;   // [rows, num_splits, dv]
+  const float* m;     // [rows, num_splits]
+  const float* l;     // [rows, num_splits]
+  void* out;          // [rows, dv] bf16 or fp32
+  float* lse;         // [rows] or nullptr
+  long rows;
+  int num_splits;
+  int dv;
+  int out_fp32;
+  // Decode rows only (else nullptr): bound the splits of each row by its
+  // request's KV length.  row = token * heads + head.
+  const int32_t* seq_lens;
+  const int32_t* cu_seqlens_q;
+  int num_requests;
+  int heads;
+  int split_len;
+};
+hipError_t launch_splitk_reduce(const ReduceParams& p, hipStream_t st);
+
+struct DecodeParams {
+  const void* q;            // bf16 [Tq, Hq, D]
+  const int32_t* cu_q;      // [R+1]
+  const void* k_cache;      // [NB, Hkv, B, D]
+  const void* v_cache;
+  const float* k_scale;     // [NB, Hkv, B] (fp8 only)
+  const float* v_scale;
+  const int32_t* block_table;  // [R, max_pages]
+  const int32_t* seq_lens;     // [R]
+  float* acc;               // [Tq_max * Hq, S, D]
+  float* m;                 // [Tq_max * Hq, S]
+  float* l;
+  int R, max_pages, Hq, Hkv, B, split_len, num_splits;
+  float scale_log2;         // softmax_scale * log2(e)
+};
+hipError_t launch_decode_splitk(const DecodeParams& p, int head_dim, bool fp8,
+                                int max_seqlen_q, hipStream_t st);
+
+struct FwdParams {
+  const void* q;            // bf16 [T, Hq, DQK]
+  const void* k;            // bf16 [T, Hkv, DQK]
+  const void* v;            // bf16 [T, Hkv, DV]
+  const int32_t* cu;        // [N+1]
+  const float* sink;        // [Hq] or nullptr
+  const float* g;           // [T, Hq] log gates or nullptr
+  float* G2;                // [T, Hq] workspace: gate prefix * log2(e)
+  void* o;                  // bf16 [T, Hq, DV]
+  float* lse;               // [T, Hq]
+  int num_seqs, max_seqlen, T, Hq, Hkv, window;
+  float scale_log2;         // softmax_scale * log2(e)
+};
+hipError_t launch_gate_prefix(const float* g, const int32_t* cu, float* G2,
+                              int num_seqs, int T, int Hq, hipStream_t st);
+hipError_t launch_fwd(const FwdParams& p, int dqk, int dv, hipStream_t st);
+
+struct BwdParams {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* o;
+  const void* dO;
+  const float* lse;         // [T, Hq]
+  const int32_t* cu;
+  const float* sink;
+  const float* G2;          // [T, Hq] gate prefix * log2(e) or nullptr
+  float* delta;             // [T, Hq] workspace
+  float* dq_acc;            // [T, Hq, DQK] fp32 workspace
+  float* dG;                // [T, Hq] fp32 workspace (row minus column sums)
+  float* dsink_acc;         // [Hq] fp32 (the dsink output itself)
+  void* dq;
+  void* dk;
+  void* dv;
+  float* dg;
+  int num_seqs, max_seqlen, T, Hq, Hkv, window;
+  float scale;              // softmax_scale
+  float scale_log2;
+};
+hipError_t launch_bwd(const BwdParams& p, int dqk, int dv, hipStream_t st);
+// Zero n floats with a kernel (no memset node, so it is safe under capture).
+hipError_t launch_fill_zero(float* x, long n, hipStream_t st);
+
+}  // namespace attn
