@@ -1,0 +1,282 @@
+#!/usr/bin/env python3
+"""Benchmark of the causal softmax attention hot path on one MI355X.
+
+One step = one pass over every hot-path step on synthetic inputs already
+resident in HBM:
+  * prefill: attn_fwd_varlen + attn_bwd_varlen on the packed varlen workload
+    (8 sequences of seeded lengths in [256, 4096], 32 query / 8 KV heads,
+    head dim 128, window 1024, sink and log gates) -- tile schedule, gate
+    prefix, forward tile loop, backward pre / fused / post;
+  * decode: attn_decode_paged on 64 requests with contexts in [1, 32768],
+    64 query / 4 KV heads, head dim 128, page 16, per-token fp8 KV, one query
+    token each -- split-K partials and the LSE reduce (one layer).
+
+Prints ONE JSON line.  `value` is the prefill fwd+bwd throughput in TFLOP/s
+(algorithmic flops: visible (query, key) pairs only); the decode figures
+(us per layer, GB/s of algorithmic bytes) sit in `decode`.  Every API call is
+bracketed by HIP events on the stream it runs on.  `roofline` describes the
+call with the largest share of the step; `cpu_baseline` is the float64 CPU
+oracle timed on a bounded sample of the same prefill workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+MFMA_BF16_PEAK_TFLOPS = 256 * 2.4e9 * 4096 / 1e12   # 2516.6 dense bf16
+HBM_PEAK_GBPS = 8000.0
+
+
+def visible_pairs(seqlens, window):
+    tot = 0
+    for L in seqlens:
+        if window > 0 and L > window:
+            tot += window * (window + 1) // 2 + (L - window) * window
+        else:
+            tot += L * (L + 1) // 2
+    return tot
+
+
+def prefill_flops(x):
+    Hq, dqk = x.q.shape[1], x.q.shape[2]
+    dv = x.v.shape[2]
+    pairs = visible_pairs(x.seqlens, x.window)
+    return 2 * pairs * Hq * (dqk + dv), 2 * pairs * Hq * (3 * dqk + 2 * dv), pairs
+
+
+def decode_bytes(d):
+    L = d.seq_lens.to(torch.int64).sum().item()
+    Hkv, D = d.k_cache.shape[1], d.k_cache.shape[3]
+    elem = 1 if d.kv_dtype == 1 else 2
+    b = L * Hkv * 2 * D * elem
+    if d.kv_dtype == 1:
+        b += L * Hkv * 8
+    b += d.q.numel() * 2 * 2                       # q in, o out (bf16)
+    pages = sum(math.ceil(int(x) / d.block_size) for x in d.seq_lens.tolist())
+    b += pages * 4                                 # block-table entries read
+    return b
+
+
+class Timer:
+    """HIP events on the current stream around each API call."""
+
+    def __init__(self):
+        self.t = {}
+
+    def run(self, name, fn):
+        s = torch.cuda.Event(enable_timing=True)
+        e = torch.cuda.Event(enable_timing=True)
+        s.record()
+        r = fn()
+        e.record()
+        self.t.setdefault(name, []).append((s, e))
+        return r
+
+    def mean_us(self, name):
+        ev = self.t.get(name, [])
+        return 1e3 * sum(s.elapsed_time(e) for s, e in ev) / max(1, len(ev))
+
+
+def cpu_oracle_baseline(x, budget_s=12.0):
+    """The float64 oracle, as it stands, on a bounded sample of the prefill
+    workload: whole KV-head groups of the first sequences, until ~budget_s."""
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        threads = os.cpu_count() or 1
+    cu = x.cu_seqlens.cpu().numpy()
+    Hq, Hkv = x.q.shape[1], x.k.shape[1]
+    grp = Hq // Hkv
+    q, k, v, do = (t.cpu() for t in (x.q, x.k, x.v, x.do))
+    sink = x.sink.cpu() if x.sink is not None else None
+    g = x.g.cpu() if x.g is not None else None
+    flops, spent, done = 0, 0.0, []
+    for n in range(len(cu) - 1):
+        a, b = int(cu[n]), int(cu[n + 1])
+        c1 = np.array([0, b - a])
+        for kv in range(Hkv):
+            hs = slice(kv * grp, (kv + 1) * grp)
+            t0 = time.perf_counter()
+            oracle.forward(q[a:b, hs], k[a:b, kv:kv + 1], v[a:b, kv:kv + 1], c1, x.scale, x.window,
+                           None if sink is None else sink[hs], None if g is None else g[a:b, hs])
+            oracle.backward(q[a:b, hs], k[a:b, kv:kv + 1], v[a:b, kv:kv + 1], do[a:b, hs], c1,
+                            x.scale, x.window, None if sink is None else sink[hs],
+                            None if g is None else g[a:b, hs])
+            spent += time.perf_counter() - t0
+            pairs = visible_pairs([b - a], x.window)
+            dqk, dv = x.q.shape[2], x.v.shape[2]
+            flops += 2 * pairs * grp * ((dqk + dv) + (3 * dqk + 2 * dv))
+            done.append(f"seq{n}(L={b - a})/kv{kv}")
+            if spent >= budget_s:
+                break
+        if spent >= budget_s:
+            break
+    return {"value": flops / spent / 1e12, "unit": "TFLOP/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"float64 oracle forward+backward on {len(done)} (sequence, KV-head group) "
+                      f"slices of the prefill workload ({done[0]} .. {done[-1]}), "
+                      f"{flops / 1e9:.1f} GFLOP in {spent:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--extra", action="store_true",
+                    help="also time the 227K-context verify and the large-head prefill")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on exactly one GPU (asked for {args.gpus}): the hot path here is the "
+              "one-GPU kernel; multi-GPU sharding is not built.", file=sys.stderr)
+        sys.exit(2)
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+
+    import causal_softmax_attention_amd as A
+    import synth
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    x = synth.config2(device=dev)
+    d = synth.config3(device=dev)
+    f_fwd, f_bwd, pairs = prefill_flops(x)
+    dec_bytes = decode_bytes(d)
+    print(f"[bench] prefill T={x.total_tokens} pairs={pairs} fwd={f_fwd:.3e} bwd={f_bwd:.3e} flop; "
+          f"decode tokens={int(d.seq_lens.sum())} bytes={dec_bytes:.3e}", file=sys.stderr, flush=True)
+
+    def fwd():
+        return A.attn_fwd_varlen(x.q, x.k, x.v, x.cu_seqlens, x.max_seqlen, x.scale, x.window,
+                                 x.sink, x.g)
+
+    o, lse = fwd()
+
+    def bwd():
+        return A.attn_bwd_varlen(x.q, x.k, x.v, o, x.do, lse, x.cu_seqlens, x.max_seqlen, x.scale,
+                                 x.window, x.sink, x.g)
+
+    def dec():
+        return A.attn_decode_paged(d.q, d.cu_seqlens_q, d.max_seqlen_q, d.k_cache, d.v_cache,
+                                   d.kv_dtype, d.k_scale, d.v_scale, d.block_table, d.seq_lens,
+                                   d.max_seq_len, d.scale)
+
+    tm = Timer()
+    for _ in range(args.warmup):
+        fwd(); bwd(); dec()
+    torch.cuda.synchronize()
+    tm = Timer()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        tm.run("fwd", fwd)
+        tm.run("bwd", bwd)
+        tm.run("decode", dec)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_step = 1e3 * wall / args.steps
+    us = {k: tm.mean_us(k) for k in ("fwd", "bwd", "decode")}
+    tf_fwd = f_fwd / (us["fwd"] * 1e-6) / 1e12
+    tf_bwd = f_bwd / (us["bwd"] * 1e-6) / 1e12
+    tf_fb = (f_fwd + f_bwd) / ((us["fwd"] + us["bwd"]) * 1e-6) / 1e12
+    gbps = dec_bytes / (us["decode"] * 1e-6) / 1e9
+
+    phases = {
+        "fwd": dict(kernel="attn_fwd_varlen (gate prefix + forward tile loop)", bound="mfma",
+                    achieved=tf_fwd, peak=MFMA_BF16_PEAK_TFLOPS, unit="TFLOP/s"),
+        "bwd": dict(kernel="attn_bwd_varlen (gate prefix + pre + fused dK/dV/dQ + post)",
+                    bound="mfma", achieved=tf_bwd, peak=MFMA_BF16_PEAK_TFLOPS, unit="TFLOP/s"),
+        "decode": dict(kernel="attn_decode_paged (split-K partials + LSE reduce)", bound="hbm",
+                       achieved=gbps, peak=HBM_PEAK_GBPS, unit="GB/s"),
+    }
+    dom = max(us, key=us.get)
+    roof = dict(phases[dom])
+    roof["frac"] = roof["achieved"] / roof["peak"]
+    roof["us_per_launch"] = us[dom]
+    roof["traffic"] = None
+    for ph in phases.values():
+        ph["frac"] = ph["achieved"] / ph["peak"]
+
+    out = {
+        "metric": "decode µs/layer + HBM GB/s; prefill fwd+bwd TFLOP/s vs MFMA peak",
+        "value": tf_fb,
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded; no dataset)",
+        "config": {
+            "workload": "prefill fwd+bwd: 8 packed seqs (lengths U[256,4096], seed 2, T=%d), "
+                        "32q/8kv heads, d 128, window 1024, sink, log gates; decode: 64 requests "
+                        "(contexts U[1,32768], seed 3), 64q/4kv heads, d 128, page 16, "
+                        "per-token fp8 e4m3fn KV, split-K + LSE reduce" % x.total_tokens,
+            "global_batch": len(x.seqlens), "seq_len": x.max_seqlen, "parallelism": "single-gpu",
+        },
+        "prefill": {"fwd_us": us["fwd"], "bwd_us": us["bwd"], "fwd_tflops": tf_fwd,
+                    "bwd_tflops": tf_bwd, "fwdbwd_tflops": tf_fb,
+                    "fwd_frac_of_mfma_peak": tf_fwd / MFMA_BF16_PEAK_TFLOPS,
+                    "fwdbwd_frac_of_mfma_peak": tf_fb / MFMA_BF16_PEAK_TFLOPS,
+                    "flops_fwd": f_fwd, "flops_bwd": f_bwd},
+        "decode": {"us_per_layer": us["decode"], "GBps": gbps, "frac_of_hbm_peak": gbps / HBM_PEAK_GBPS,
+                   "algorithmic_bytes": dec_bytes},
+        "roofline": roof,
+        "phases": phases,
+    }
+
+    if args.extra:
+        extra = {}
+        for kvd, tag in ((synth.KV_BF16, "bf16"), (synth.KV_FP8_E4M3FN, "fp8")):
+            d4 = synth.config4(kv_dtype=kvd, device=dev)
+            f = lambda: A.attn_decode_paged(d4.q, d4.cu_seqlens_q, 4, d4.k_cache, d4.v_cache, kvd,
+                                            d4.k_scale, d4.v_scale, d4.block_table, d4.seq_lens,
+                                            d4.max_seq_len, d4.scale)
+            for _ in range(3):
+                f()
+            t4 = Timer()
+            for _ in range(20):
+                t4.run("v", f)
+            torch.cuda.synchronize()
+            u = t4.mean_us("v")
+            extra[f"verify_{tag}"] = {"us_per_layer": u, "GBps": decode_bytes(d4) / (u * 1e-6) / 1e9}
+            del d4
+        x5 = synth.config5(device=dev)
+        f5f, f5b, _ = prefill_flops(x5)
+        o5, l5 = A.attn_fwd_varlen(x5.q, x5.k, x5.v, x5.cu_seqlens, x5.max_seqlen, x5.scale, 0,
+                                   x5.sink, x5.g)
+        t5 = Timer()
+        for _ in range(3):
+            t5.run("f", lambda: A.attn_fwd_varlen(x5.q, x5.k, x5.v, x5.cu_seqlens, x5.max_seqlen,
+                                                  x5.scale, 0, x5.sink, x5.g))
+            t5.run("b", lambda: A.attn_bwd_varlen(x5.q, x5.k, x5.v, o5, x5.do, l5, x5.cu_seqlens,
+                                                  x5.max_seqlen, x5.scale, 0, x5.sink, x5.g))
+        torch.cuda.synchronize()
+        extra["prefill_large_heads"] = {
+            "fwd_us": t5.mean_us("f"), "bwd_us": t5.mean_us("b"),
+            "fwd_tflops": f5f / (t5.mean_us("f") * 1e-6) / 1e12,
+            "bwd_tflops": f5b / (t5.mean_us("b") * 1e-6) / 1e12}
+        out["extra_workloads"] = extra
+
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_oracle_baseline(x)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()
