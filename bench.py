@@ -169,6 +169,10 @@ def main():
         return A.attn_bwd_varlen(x.q, x.k, x.v, o, x.do, lse, x.cu_seqlens, x.max_seqlen, x.scale,
                                  x.window, x.sink, x.g)
 
+    def bwd_fused():
+        return A.attn_bwd_varlen(x.q, x.k, x.v, o, x.do, lse, x.cu_seqlens, x.max_seqlen, x.scale,
+                                 x.window, x.sink, x.g, flags=A.ATTN_BWD_FUSED_DQ)
+
     def dec():
         return A.attn_decode_paged(d.q, d.cu_seqlens_q, d.max_seqlen_q, d.k_cache, d.v_cache,
                                    d.kv_dtype, d.k_scale, d.v_scale, d.block_table, d.seq_lens,
@@ -187,6 +191,12 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_step = 1e3 * wall / args.steps
+    # the fused-dQ variant of the backward, timed outside the step
+    tf = Timer()
+    bwd_fused()
+    for _ in range(max(3, args.steps // 4)):
+        tf.run("bwd_fused", bwd_fused)
+    torch.cuda.synchronize()
     us = {k: tm.mean_us(k) for k in ("fwd", "bwd", "decode")}
     tf_fwd = f_fwd / (us["fwd"] * 1e-6) / 1e12
     tf_bwd = f_bwd / (us["bwd"] * 1e-6) / 1e12
@@ -196,7 +206,7 @@ def main():
     phases = {
         "fwd": dict(kernel="attn_fwd_varlen (gate prefix + forward tile loop)", bound="mfma",
                     achieved=tf_fwd, peak=MFMA_BF16_PEAK_TFLOPS, unit="TFLOP/s"),
-        "bwd": dict(kernel="attn_bwd_varlen (gate prefix + pre + fused dK/dV/dQ + post)",
+        "bwd": dict(kernel="attn_bwd_varlen (gate prefix + pre + dK/dV pass + dQ pass + post)",
                     bound="mfma", achieved=tf_bwd, peak=MFMA_BF16_PEAK_TFLOPS, unit="TFLOP/s"),
         "decode": dict(kernel="attn_decode_paged (split-K partials + LSE reduce)", bound="hbm",
                        achieved=gbps, peak=HBM_PEAK_GBPS, unit="GB/s"),
@@ -229,7 +239,11 @@ def main():
                         "per-token fp8 e4m3fn KV, split-K + LSE reduce" % x.total_tokens,
             "global_batch": len(x.seqlens), "seq_len": x.max_seqlen, "parallelism": "single-gpu",
         },
-        "prefill": {"fwd_us": us["fwd"], "bwd_us": us["bwd"], "fwd_tflops": tf_fwd,
+        "prefill": {"fwd_us": us["fwd"], "bwd_us": us["bwd"],
+                    "bwd_path": "two-pass (deterministic)",
+                    "bwd_fused_dq_us": tf.mean_us("bwd_fused"),
+                    "bwd_fused_dq_tflops": f_bwd / (tf.mean_us("bwd_fused") * 1e-6) / 1e12,
+                    "fwd_tflops": tf_fwd,
                     "bwd_tflops": tf_bwd, "fwdbwd_tflops": tf_fb,
                     "fwd_frac_of_mfma_peak": tf_fwd / MFMA_BF16_PEAK_TFLOPS,
                     "fwdbwd_frac_of_mfma_peak": tf_fb / MFMA_BF16_PEAK_TFLOPS,

@@ -138,31 +138,47 @@ int attn_fwd_varlen(const void* q, const void* k, const void* v, const int32_t* 
 // ---------------------------------------------------------------------------
 namespace {
 struct BwdLayout {
-  size_t delta, dq_acc, dG, G2, total;
+  size_t delta, G2, dq_acc, dG, dGrow, dGcol, sink_rows, total;
+  bool fused;
 };
-BwdLayout bwd_layout(int T, int Hq, int dqk, int has_gate) {
+// Which backward runs: the fused-dQ kernel (fp32 atomics; the pages keep it
+// to head dims up to 128) only when asked for, the two-pass kernels
+// otherwise (faster on this GPU, and deterministic).
+bool bwd_uses_fused(int dqk, int flags) {
+  return (flags & ATTN_BWD_FUSED_DQ) && !(flags & ATTN_BWD_DETERMINISTIC) && dqk <= 128;
+}
+BwdLayout bwd_layout(int T, int Hq, int dqk, int has_gate, int has_sink, int flags) {
   BwdLayout L{};
   const size_t rows = (size_t)(T > 0 ? T : 0) * (Hq > 0 ? Hq : 0);
+  const size_t r4 = round_up(rows * sizeof(float));
+  L.fused = bwd_uses_fused(dqk, flags);
   size_t off = 0;
-  L.delta = off; off += round_up(rows * sizeof(float));
-  L.dq_acc = off; off += round_up(rows * (size_t)(dqk > 0 ? dqk : 0) * sizeof(float));
-  L.dG = off; if (has_gate) off += round_up(rows * sizeof(float));
-  L.G2 = off; if (has_gate) off += round_up(rows * sizeof(float));
+  L.delta = off; off += r4;
+  L.G2 = off; if (has_gate) off += r4;
+  if (L.fused) {
+    L.dq_acc = off; off += round_up(rows * (size_t)(dqk > 0 ? dqk : 0) * sizeof(float));
+    L.dG = off; if (has_gate) off += r4;
+  } else {
+    L.dGrow = off; if (has_gate) off += r4;
+    L.dGcol = off; if (has_gate) off += r4;
+    L.sink_rows = off; if (has_sink) off += r4;
+  }
   L.total = off;
   return L;
 }
 }  // namespace
 
-size_t attn_bwd_workspace_size(int total_tokens, int num_q_heads, int head_dim_qk, int has_gate) {
+size_t attn_bwd_workspace_size(int total_tokens, int num_q_heads, int head_dim_qk, int has_gate,
+                               int has_sink, int flags) {
   if (total_tokens <= 0 || num_q_heads <= 0) return 0;
-  return bwd_layout(total_tokens, num_q_heads, head_dim_qk, has_gate).total;
+  return bwd_layout(total_tokens, num_q_heads, head_dim_qk, has_gate, has_sink, flags).total;
 }
 
 int attn_bwd_varlen(const void* q, const void* k, const void* v, const void* o, const void* dO,
                     const float* lse, const int32_t* cu_seqlens, int num_seqs, int max_seqlen,
                     int total_tokens, int num_q_heads, int num_kv_heads, int head_dim_qk,
                     int head_dim_v, float softmax_scale, int window, const float* sink,
-                    const float* g, void* dq, void* dk, void* dv, float* dsink, float* dg,
+                    const float* g, void* dq, void* dk, void* dv, float* dsink, float* dg, int flags,
                     void* workspace, size_t workspace_bytes, void* stream) {
   int st = check_prefill_common(q, k, v, cu_seqlens, num_seqs, max_seqlen, total_tokens, num_q_heads,
                                 num_kv_heads, head_dim_qk, head_dim_v, softmax_scale);
@@ -170,6 +186,12 @@ int attn_bwd_varlen(const void* q, const void* k, const void* v, const void* o, 
   REQUIRE((sink == nullptr) == (dsink == nullptr), ATTN_ERR_INVALID,
           "dsink must be given exactly when sink is given");
   REQUIRE((g == nullptr) == (dg == nullptr), ATTN_ERR_INVALID, "dg must be given exactly when g is given");
+  REQUIRE((flags & ~(ATTN_BWD_DETERMINISTIC | ATTN_BWD_FUSED_DQ)) == 0, ATTN_ERR_INVALID,
+          "unknown flags 0x%x", flags);
+  REQUIRE(!((flags & ATTN_BWD_FUSED_DQ) && (flags & ATTN_BWD_DETERMINISTIC)), ATTN_ERR_INVALID,
+          "ATTN_BWD_FUSED_DQ and ATTN_BWD_DETERMINISTIC exclude each other");
+  REQUIRE(!((flags & ATTN_BWD_FUSED_DQ) && head_dim_qk > 128), ATTN_ERR_UNSUPPORTED,
+          "the fused-dQ backward covers head_dim_qk <= 128 (got %d)", head_dim_qk);
   if (num_seqs == 0 || total_tokens == 0) {
     // Nothing to differentiate; a sink gradient over no tokens is zero.
     if (dsink != nullptr && num_q_heads > 0) {
@@ -187,7 +209,7 @@ int attn_bwd_varlen(const void* q, const void* k, const void* v, const void* o, 
   REQ_PTR(dv, 16);
   if (sink) { REQ_PTR(sink, 4); REQ_PTR(dsink, 4); }
   if (g) { REQ_PTR(g, 4); REQ_PTR(dg, 4); }
-  const BwdLayout lay = bwd_layout(total_tokens, num_q_heads, head_dim_qk, g != nullptr);
+  const BwdLayout lay = bwd_layout(total_tokens, num_q_heads, head_dim_qk, g != nullptr, sink != nullptr, flags);
   REQUIRE(workspace_bytes >= lay.total, ATTN_ERR_INVALID, "workspace too small: %zu < %zu bytes",
           workspace_bytes, lay.total);
   REQ_PTR(workspace, 256);
@@ -199,8 +221,14 @@ int attn_bwd_varlen(const void* q, const void* k, const void* v, const void* o, 
   p.q = q; p.k = k; p.v = v; p.o = o; p.dO = dO; p.lse = lse; p.cu = cu_seqlens; p.sink = sink;
   p.G2 = G2;
   p.delta = reinterpret_cast<float*>(ws + lay.delta);
-  p.dq_acc = reinterpret_cast<float*>(ws + lay.dq_acc);
-  p.dG = g ? reinterpret_cast<float*>(ws + lay.dG) : nullptr;
+  if (lay.fused) {
+    p.dq_acc = reinterpret_cast<float*>(ws + lay.dq_acc);
+    p.dG = g ? reinterpret_cast<float*>(ws + lay.dG) : nullptr;
+  } else {
+    p.dGrow = g ? reinterpret_cast<float*>(ws + lay.dGrow) : nullptr;
+    p.dGcol = g ? reinterpret_cast<float*>(ws + lay.dGcol) : nullptr;
+    p.sink_rows = sink ? reinterpret_cast<float*>(ws + lay.sink_rows) : nullptr;
+  }
   p.dsink_acc = dsink;
   p.dq = dq; p.dk = dk; p.dv = dv; p.dg = dg;
   p.num_seqs = num_seqs; p.max_seqlen = max_seqlen; p.T = total_tokens;
@@ -212,7 +240,7 @@ int attn_bwd_varlen(const void* q, const void* k, const void* v, const void* o, 
     e = attn::launch_gate_prefix(g, cu_seqlens, G2, num_seqs, total_tokens, num_q_heads, s);
     if (e != hipSuccess) return hip_fail(e, "gate prefix launch");
   }
-  e = attn::launch_bwd(p, head_dim_qk, head_dim_v, s);
+  e = attn::launch_bwd(p, head_dim_qk, head_dim_v, lay.fused, s);
   if (e != hipSuccess) return hip_fail(e, "backward launch");
   return ok();
 }
@@ -225,7 +253,7 @@ int choose_split_len(int R, int Hkv, int max_seq_len, int B) {
   const double est_tokens = (double)R * max_seq_len * 0.5;
   const double want = est_tokens * Hkv / 2048.0;
   int sl = 256;
-  while (sl < want && sl < 8192) sl *= 2;
+  while (sl < want && sl < attn::kDecodeMaxSplit) sl *= 2;
   const int unit = B > 32 ? B : 32;
   if (sl < unit) sl = unit;
   return sl;
@@ -292,6 +320,8 @@ int attn_decode_paged(const void* q, const int32_t* cu_seqlens_q, int num_reques
     const int unit = block_size > 32 ? block_size : 32;
     REQUIRE(kv_split_len % unit == 0, ATTN_ERR_INVALID,
             "kv_split_len %d must be a multiple of %d", kv_split_len, unit);
+    REQUIRE(kv_split_len <= attn::kDecodeMaxSplit, ATTN_ERR_UNSUPPORTED,
+            "kv_split_len %d exceeds %d", kv_split_len, attn::kDecodeMaxSplit);
   }
   if (num_requests == 0) return ok();
   REQUIRE(max_seq_len >= 1, ATTN_ERR_INVALID, "max_seq_len %d must be >= 1", max_seq_len);
@@ -322,7 +352,7 @@ int attn_decode_paged(const void* q, const int32_t* cu_seqlens_q, int num_reques
   p.m = reinterpret_cast<float*>(ws + lay.m);
   p.l = reinterpret_cast<float*>(ws + lay.l);
   p.R = num_requests; p.max_pages = max_pages; p.Hq = num_q_heads; p.Hkv = num_kv_heads;
-  p.B = block_size; p.split_len = lay.split_len; p.num_splits = lay.num_splits;
+  p.B = block_size; p.B_shift = __builtin_ctz((unsigned)block_size); p.split_len = lay.split_len; p.num_splits = lay.num_splits;
   p.scale_log2 = softmax_scale * attn::kLog2e;
   hipError_t e = attn::launch_decode_splitk(p, head_dim, fp8, max_seqlen_q, s);
   if (e != hipSuccess) return hip_fail(e, "decode launch");

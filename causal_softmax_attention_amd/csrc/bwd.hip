@@ -44,8 +44,10 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(BwdParams p) {
     p.delta[row] = s;
     if (p.dG != nullptr) p.dG[row] = 0.f;
   }
-  float* dqa = p.dq_acc + row * DQK;
-  for (int j = lane * 4; j < DQK; j += 256) *reinterpret_cast<f32x4*>(dqa + j) = f32x4{0.f, 0.f, 0.f, 0.f};
+  if (p.dq_acc != nullptr) {
+    float* dqa = p.dq_acc + row * DQK;
+    for (int j = lane * 4; j < DQK; j += 256) *reinterpret_cast<f32x4*>(dqa + j) = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -277,7 +279,9 @@ __global__ __launch_bounds__(256) void bwd_dq_convert_kernel(const float* __rest
 
 // dg[t, h] = sum over s >= t within t's sequence of dG[s, h]: one workgroup
 // per (sequence, head), chunked reverse scan.
-__global__ __launch_bounds__(256) void gate_grad_kernel(const float* __restrict__ dG,
+// dG[t, h] = a[t, h] - b[t, h] (b may be null).
+__global__ __launch_bounds__(256) void gate_grad_kernel(const float* __restrict__ a_,
+                                                        const float* __restrict__ b_,
                                                         const int32_t* __restrict__ cu,
                                                         float* __restrict__ dg, int Hq) {
   const int h = blockIdx.x, n = blockIdx.y;
@@ -286,8 +290,12 @@ __global__ __launch_bounds__(256) void gate_grad_kernel(const float* __restrict_
   const int chunk = (L + 255) / 256;
   const int t0 = threadIdx.x * chunk;
   const int t1 = min(L, t0 + chunk);
+  auto dG = [&](int t) {
+    const long i = (long)(a + t) * Hq + h;
+    return b_ ? a_[i] - b_[i] : a_[i];
+  };
   float s = 0.f;
-  for (int t = t0; t < t1; ++t) s += dG[(long)(a + t) * Hq + h];
+  for (int t = t0; t < t1; ++t) s += dG(t);
   __shared__ float part[256];
   part[threadIdx.x] = s;
   __syncthreads();
@@ -300,7 +308,7 @@ __global__ __launch_bounds__(256) void gate_grad_kernel(const float* __restrict_
   }
   float run = threadIdx.x < 255 ? part[threadIdx.x + 1] : 0.f;
   for (int t = t1 - 1; t >= t0; --t) {
-    run += dG[(long)(a + t) * Hq + h];
+    run += dG(t);
     dg[(long)(a + t) * Hq + h] = run;
   }
 }
@@ -317,35 +325,44 @@ hipError_t launch_fill_zero(float* x, long n, hipStream_t st) {
 }
 
 template <int DQK, int DV>
-static hipError_t launch_bwd_t(const BwdParams& p, hipStream_t st) {
+static hipError_t launch_bwd_t(const BwdParams& p, bool fused, hipStream_t st) {
   const long rows = (long)p.T * p.Hq;
   bwd_pre_kernel<DQK, DV><<<dim3((unsigned)((rows + 3) / 4)), 256, 0, st>>>(p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const int ktiles = (p.max_seqlen + 63) / 64;
-  bwd_fused_kernel<DQK, DV><<<dim3(p.Hkv, p.num_seqs, ktiles), 256, 0, st>>>(p);
-  e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  const long n4 = rows * DQK / 4;
-  bwd_dq_convert_kernel<DQK><<<dim3((unsigned)((n4 + 255) / 256)), 256, 0, st>>>(
-      p.dq_acc, reinterpret_cast<bf16*>(p.dq), n4);
-  e = hipGetLastError();
+  if (fused) {
+    const int ktiles = (p.max_seqlen + 63) / 64;
+    bwd_fused_kernel<DQK, DV><<<dim3(p.Hkv, p.num_seqs, ktiles), 256, 0, st>>>(p);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const long n4 = rows * DQK / 4;
+    bwd_dq_convert_kernel<DQK><<<dim3((unsigned)((n4 + 255) / 256)), 256, 0, st>>>(
+        p.dq_acc, reinterpret_cast<bf16*>(p.dq), n4);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    if (p.dg != nullptr) {
+      gate_grad_kernel<<<dim3(p.Hq, p.num_seqs), 256, 0, st>>>(p.dG, nullptr, p.cu, p.dg, p.Hq);
+      e = hipGetLastError();
+    }
+    return e;
+  }
+  e = launch_bwd_two_pass(p, DQK, DV, st);
   if (e != hipSuccess) return e;
   if (p.dg != nullptr) {
-    gate_grad_kernel<<<dim3(p.Hq, p.num_seqs), 256, 0, st>>>(p.dG, p.cu, p.dg, p.Hq);
+    gate_grad_kernel<<<dim3(p.Hq, p.num_seqs), 256, 0, st>>>(p.dGrow, p.dGcol, p.cu, p.dg, p.Hq);
     e = hipGetLastError();
   }
   return e;
 }
 
-hipError_t launch_bwd(const BwdParams& p, int dqk, int dv, hipStream_t st) {
+hipError_t launch_bwd(const BwdParams& p, int dqk, int dv, bool fused, hipStream_t st) {
   if (p.num_seqs == 0 || p.T == 0 || p.max_seqlen == 0) {
     return hipSuccess;
   }
-  if (dqk == 64 && dv == 64) return launch_bwd_t<64, 64>(p, st);
-  if (dqk == 128 && dv == 128) return launch_bwd_t<128, 128>(p, st);
-  if (dqk == 256 && dv == 256) return launch_bwd_t<256, 256>(p, st);
-  if (dqk == 256 && dv == 512) return launch_bwd_t<256, 512>(p, st);
+  if (dqk == 64 && dv == 64) return launch_bwd_t<64, 64>(p, fused, st);
+  if (dqk == 128 && dv == 128) return launch_bwd_t<128, 128>(p, fused, st);
+  if (dqk == 256 && dv == 256) return launch_bwd_t<256, 256>(p, fused, st);
+  if (dqk == 256 && dv == 512) return launch_bwd_t<256, 512>(p, fused, st);
   return hipErrorInvalidValue;
 }
 

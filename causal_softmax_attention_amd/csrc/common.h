@@ -33,6 +33,11 @@ constexpr float kLn2 = 0.6931471805599453f;
 // Finite stand-in for -inf in running maxima: exp2(x - kNegBig) is 0 for
 // every finite score, and kNegBig - kNegBig = 0 avoids inf - inf.
 constexpr float kNegBig = -1.0e30f;
+// Lazy-rescale slack (log2 units): a running max is raised only when a new
+// score exceeds it by more than this, so probabilities stay below 2^8 and
+// the accumulators are rescaled rarely.  Numerator and denominator share the
+// same stale max, so the result is unchanged.
+constexpr float kRescaleSlack = 8.0f;
 
 __device__ __forceinline__ f32x4 mfma16x16x32(bf16x8 a, bf16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);

@@ -43,19 +43,30 @@ __device__ __forceinline__ void lds_wave_sync() {
   asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
 }
 
+// Raw bytes of one 32-key step, fetched one step ahead of their use.
+template <int D, bool FP8>
+struct StepRaw {
+  static constexpr int ES = FP8 ? 1 : 2;
+  static constexpr int KCH = (D / 4) * ES / 16;      // 16-byte K chunks per lane per key block
+  static constexpr int NCH = 32 * D * ES / 16 / 64;  // 16-byte V chunks per lane
+  i32x4 k[2][KCH];
+  i32x4 v[NCH];
+  f32x4 ks[2], vs[2];
+};
+
 template <int D, bool FP8, int RB>
 __global__ __launch_bounds__(256) void decode_splitk_kernel(DecodeParams p) {
+  using Raw = StepRaw<D, FP8>;
   constexpr int KS = D / 32;          // k-steps of 32 over the head dim
   constexpr int DPG = 8 * KS;         // head-dim elements per 16-lane group
-  constexpr int ES = FP8 ? 1 : 2;     // bytes per cache element
+  constexpr int ES = Raw::ES;         // bytes per cache element
   constexpr int ROWB = D * ES;        // bytes per cached token row
   constexpr int VROW = ROWB + 16;     // padded LDS row stride
   constexpr int CPR = ROWB / 16;      // 16-byte chunks per row
-  constexpr int NCH = 32 * CPR / 64;  // chunks per lane for a 32-key step
   constexpr int DB = D / 16;          // 16-wide output column blocks
   __shared__ __attribute__((aligned(16))) uint8_t v_lds_all[4][32 * VROW];
 
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int li = lane & 15, g = lane >> 4;
   uint8_t* v_lds = v_lds_all[wave];
 
@@ -72,9 +83,52 @@ __global__ __launch_bounds__(256) void decode_splitk_kernel(DecodeParams p) {
   const int qs = p.cu_q[r];
   const int qlen = p.cu_q[r + 1] - qs;
   const int G = p.Hq / p.Hkv;
-  const int32_t* bt = p.block_table + (long)r * p.max_pages;
   const long head_stride = (long)p.B * D;              // elements per (page, kv head)
   const long page_stride = (long)p.Hkv * head_stride;
+  const uint8_t* kc = reinterpret_cast<const uint8_t*>(p.k_cache) + kvh * head_stride * ES;
+  const uint8_t* vc = reinterpret_cast<const uint8_t*>(p.v_cache) + kvh * head_stride * ES;
+
+  // Page ids are wave-uniform per 32-key step (a step spans at most two
+  // pages, and one when pages hold 32 or more keys), so they come through
+  // scalar loads, one step ahead of the vector loads that use them.  Keys
+  // past seq_len read the request's last page and are masked later: every
+  // load stays unconditional and in range, so several steps can be in flight.
+  const int bsh = p.B_shift, bmask = p.B - 1;   // page size is a power of two
+  const int last_page = (L - 1) >> bsh;
+  const int32_t* bt = p.block_table + (long)r * p.max_pages;
+  struct Pages { int a, b; };                    // pages of keys kk and kk+16
+  auto pages_of = [&](int kk) {
+    Pages pp;
+    pp.a = __builtin_amdgcn_readfirstlane(bt[min(kk >> bsh, last_page)]);
+    pp.b = __builtin_amdgcn_readfirstlane(bt[min((kk + 16) >> bsh, last_page)]);
+    return pp;
+  };
+
+  auto fetch = [&](int kk, Pages pp, Raw& raw) {
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      const int key = kk + kb * 16 + li;
+      const long pid = kb ? pp.b : pp.a;
+      const long off = (pid * page_stride + (long)(key & bmask) * D + g * DPG) * ES;
+#pragma unroll
+      for (int c = 0; c < Raw::KCH; ++c) raw.k[kb][c] = *reinterpret_cast<const i32x4*>(kc + off + 16 * c);
+      if constexpr (FP8) {
+        const int k4 = kk + kb * 16 + 4 * g;
+        const long so = ((pid * p.Hkv + kvh) << bsh) + (k4 & bmask);
+        raw.ks[kb] = *reinterpret_cast<const f32x4*>(p.k_scale + so);
+        raw.vs[kb] = *reinterpret_cast<const f32x4*>(p.v_scale + so);
+      }
+    }
+#pragma unroll
+    for (int c = 0; c < Raw::NCH; ++c) {
+      const int ch = lane + 64 * c;
+      const int kr = ch / CPR, col = (ch % CPR) * 16;
+      const int key = kk + kr;
+      const long pid = kr < 16 ? pp.a : pp.b;
+      const long off = (pid * page_stride + (long)(key & bmask) * D) * ES + col;
+      raw.v[c] = *reinterpret_cast<const i32x4*>(vc + off);
+    }
+  };
 
   // Q rows as the B operand: lane (row li, group g) holds the head-dim
   // elements [g*DPG, g*DPG + DPG) in k-step order.
@@ -108,117 +162,89 @@ __global__ __launch_bounds__(256) void decode_splitk_kernel(DecodeParams p) {
     for (int db = 0; db < DB; ++db) oacc[rb][db] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
 
-  for (int kk = k_begin; kk < k_end; kk += 32) {
-    // ---- K operand (A): lane (key li of block kb, group g) ----
-    bf16x8 kop[2][KS];
+  auto compute = [&](int kk, const Raw& raw) {
+    // ---- V of the 32 keys into LDS, zeros past seq_len (NaN-safe select) ----
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      const int key = kk + kb * 16 + li;
-      if (key < L) {
-        const int page = bt[key / p.B];
-        const long off = page * page_stride + kvh * head_stride + (long)(key % p.B) * D + g * DPG;
-        if constexpr (FP8) {
-          const uint8_t* kp = reinterpret_cast<const uint8_t*>(p.k_cache) + off;
-#pragma unroll
-          for (int ks = 0; ks < KS; ++ks)
-            kop[kb][ks] = fp8x8_to_bf16x8(*reinterpret_cast<const i32x2*>(kp + 8 * ks));
-        } else {
-          const bf16* kp = reinterpret_cast<const bf16*>(p.k_cache) + off;
-#pragma unroll
-          for (int ks = 0; ks < KS; ++ks) kop[kb][ks] = *reinterpret_cast<const bf16x8*>(kp + 8 * ks);
-        }
-      } else {
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) kop[kb][ks] = bf16x8{};
-      }
-    }
-    // ---- per-token scales for this lane's score columns: keys kk+kb*16+4g+i ----
-    float ksc[2][4], vsc[2][4];
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      const int k4 = kk + kb * 16 + 4 * g;
-      if constexpr (FP8) {
-        f32x4 kv4 = {0.f, 0.f, 0.f, 0.f}, vv4 = {0.f, 0.f, 0.f, 0.f};
-        if (k4 < L) {
-          const int page = bt[k4 / p.B];
-          const long so = ((long)page * p.Hkv + kvh) * p.B + (k4 % p.B);
-          kv4 = *reinterpret_cast<const f32x4*>(p.k_scale + so);
-          vv4 = *reinterpret_cast<const f32x4*>(p.v_scale + so);
-        }
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const bool ok = (k4 + i) < L;           // select: unused slots may hold NaN
-          ksc[kb][i] = ok ? kv4[i] : 0.f;
-          vsc[kb][i] = ok ? vv4[i] : 0.f;
-        }
-      } else {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          ksc[kb][i] = 1.f;
-          vsc[kb][i] = 1.f;
-        }
-      }
-    }
-    // ---- stage V of the 32 keys into LDS (zeros past seq_len) ----
-#pragma unroll
-    for (int c = 0; c < NCH; ++c) {
+    for (int c = 0; c < Raw::NCH; ++c) {
       const int ch = lane + 64 * c;
       const int kr = ch / CPR, col = (ch % CPR) * 16;
-      const int key = kk + kr;
-      i32x4 val = {0, 0, 0, 0};
-      if (key < L) {
-        const int page = bt[key / p.B];
-        const long off = (page * page_stride + kvh * head_stride + (long)(key % p.B) * D) * ES + col;
-        val = *reinterpret_cast<const i32x4*>(reinterpret_cast<const uint8_t*>(p.v_cache) + off);
-      }
-      *reinterpret_cast<i32x4*>(v_lds + kr * VROW + col) = val;
+      const i32x4 z = {0, 0, 0, 0};
+      *reinterpret_cast<i32x4*>(v_lds + kr * VROW + col) = (kk + kr < L) ? raw.v[c] : z;
     }
-
-    // ---- scores S^T = K Q^T, masked, base-2 ----
+    // ---- scores S^T = K Q^T ----
     f32x4 sc[2][RB];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+    for (int kb = 0; kb < 2; ++kb) {
+      bf16x8 kop[KS];
+      if constexpr (FP8) {
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+          const i32x4 w = raw.k[kb][ks / 2];
+          kop[ks] = fp8x8_to_bf16x8((ks & 1) ? i32x2{w[2], w[3]} : i32x2{w[0], w[1]});
+        }
+      } else {
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) kop[ks] = __builtin_bit_cast(bf16x8, raw.k[kb][ks]);
+      }
 #pragma unroll
       for (int rb = 0; rb < RB; ++rb) {
         f32x4 a = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) a = mfma16x16x32(kop[kb][ks], qop[rb][ks], a);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int key = kk + kb * 16 + 4 * g + i;
-          const bool vis = key < L && key <= pos[rb];
-          sc[kb][rb][i] = vis ? a[i] * p.scale_log2 * ksc[kb][i] : -INFINITY;
-        }
+        for (int ks = 0; ks < KS; ++ks) a = mfma16x16x32(kop[ks], qop[rb][ks], a);
+        sc[kb][rb] = a;
       }
-
+    }
+    // ---- K scales on the score columns; mask (select: slots past seq_len may be NaN) ----
+    float ksc[2][4], vsc[2][4];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const bool ok = kk + kb * 16 + 4 * g + i < L;
+        ksc[kb][i] = FP8 ? (ok ? raw.ks[kb][i] : 0.f) * p.scale_log2 : p.scale_log2;
+        vsc[kb][i] = FP8 ? (ok ? raw.vs[kb][i] : 0.f) : 1.f;
+      }
     // ---- online softmax; P' = P * v_scale split into bf16 hi + lo ----
     bf16x8 phi[RB], plo[RB];
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
-      float mx = fmaxf(fmaxf(fmaxf(sc[0][rb][0], sc[0][rb][1]), fmaxf(sc[0][rb][2], sc[0][rb][3])),
-                       fmaxf(fmaxf(sc[1][rb][0], sc[1][rb][1]), fmaxf(sc[1][rb][2], sc[1][rb][3])));
+      float x[2][4];
+      float mx = -INFINITY;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int key = kk + kb * 16 + 4 * g + i;
+          const bool vis = key < L && key <= pos[rb];
+          x[kb][i] = vis ? sc[kb][rb][i] * ksc[kb][i] : -INFINITY;
+          mx = fmaxf(mx, x[kb][i]);
+        }
       mx = xgroup_max(mx);
-      const float m_new = fmaxf(m_run[rb], mx);
-      const float alpha = fast_exp2(m_run[rb] - m_new);
+      if (__any(mx > m_run[rb] + kRescaleSlack)) {
+        // raise the running max only when a score passes it by more than
+        // the slack, so exp2(score - max) stays below 2^8 in between
+        const float m_new = fmaxf(m_run[rb], mx);
+        const float alpha = fast_exp2(m_run[rb] - m_new);
+        l_run[rb] *= alpha;
+#pragma unroll
+        for (int db = 0; db < DB; ++db) oacc[rb][db] *= alpha;
+        m_run[rb] = m_new;
+      }
+      const float m_new = m_run[rb];
       float rs = 0.f;
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const float pv = fast_exp2(sc[kb][rb][i] - m_new);
+          const float pv = fast_exp2(x[kb][i] - m_new);
           rs += pv;
           const float pp = pv * vsc[kb][i];
           const bf16 h = (bf16)pp;
           phi[rb][kb * 4 + i] = h;
           plo[rb][kb * 4 + i] = (bf16)(pp - (float)h);
         }
-      rs = xgroup_sum(rs);
-      l_run[rb] = l_run[rb] * alpha + rs;
-      m_run[rb] = m_new;
-#pragma unroll
-      for (int db = 0; db < DB; ++db) oacc[rb][db] *= alpha;
+      l_run[rb] += xgroup_sum(rs);
     }
-
     lds_wave_sync();
     // ---- O^T += V^T P'^T (hi and lo) ----
 #pragma unroll
@@ -241,6 +267,33 @@ __global__ __launch_bounds__(256) void decode_splitk_kernel(DecodeParams p) {
       }
     }
     lds_wave_sync();
+  };
+
+  if constexpr (RB <= 2) {
+    // ---- two-deep software pipeline over 32-key steps ----
+    // The prefetch is unconditional (its addresses are clamped in range):
+    // a conditional one would make the compiler drain every outstanding
+    // load at the branch join, serialising the pipeline.
+    Raw ra, rb_;
+    fetch(k_begin, pages_of(k_begin), ra);
+    Pages nxt = pages_of(k_begin + 32);
+    for (int kk = k_begin; kk < k_end; kk += 64) {
+      fetch(kk + 32, nxt, rb_);
+      nxt = pages_of(kk + 64);
+      compute(kk, ra);
+      if (kk + 32 >= k_end) break;
+      fetch(kk + 64, nxt, ra);
+      nxt = pages_of(kk + 96);
+      compute(kk + 32, rb_);
+    }
+  } else {
+    // Many query rows: more math per byte and no registers left for a
+    // second buffer; fetch and compute one step at a time.
+    Raw ra;
+    for (int kk = k_begin; kk < k_end; kk += 32) {
+      fetch(kk, pages_of(kk), ra);
+      compute(kk, ra);
+    }
   }
 
   // ---- store the partial ----

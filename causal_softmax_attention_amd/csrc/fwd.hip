@@ -28,6 +28,13 @@
 #include "common.h"
 #include "kernels.h"
 
+#ifndef FWD_RW_SMALL
+#define FWD_RW_SMALL 16
+#endif
+#ifndef FWD_BN_SMALL
+#define FWD_BN_SMALL 64
+#endif
+
 namespace attn {
 
 // ---------------------------------------------------------------------------
@@ -73,6 +80,13 @@ hipError_t launch_gate_prefix(const float* g, const int32_t* cu, float* G2, int 
 // ---------------------------------------------------------------------------
 // Forward kernel
 // ---------------------------------------------------------------------------
+// Blocks are dispatched round-robin over the 8 XCDs (each with its own L2);
+// map block x so that the query heads of one KV group land on one XCD.
+__device__ __forceinline__ int xcd_head(int x, int Hq) {
+  if (Hq % 8 != 0) return x;
+  return (x % 8) * (Hq / 8) + x / 8;
+}
+
 template <int DQK, int DV, int RW, int BN>
 __global__ __launch_bounds__(256) void fwd_kernel(FwdParams p) {
   constexpr int BM = 4 * RW;
@@ -82,12 +96,15 @@ __global__ __launch_bounds__(256) void fwd_kernel(FwdParams p) {
   constexpr int DB = DV / 16;        // 16-wide output column blocks
   constexpr int KROW = DQK + 8;      // LDS row strides (elements)
   constexpr int VROW = DV + 16;
+  constexpr int KCH = BN * DQK / 8 / 256;   // 16-byte chunks per thread per tile
+  constexpr int VCH = BN * DV / 8 / 256;
   static_assert(KB % 2 == 0, "PV consumes keys in pairs of 16-key blocks");
-  __shared__ __attribute__((aligned(16))) bf16 k_lds[BN * KROW];
-  __shared__ __attribute__((aligned(16))) bf16 v_lds[BN * VROW];
-  __shared__ float gk_lds[BN];
+  static_assert(KCH * 256 * 8 == BN * DQK && VCH * 256 * 8 == BN * DV, "tile must split evenly");
+  __shared__ __attribute__((aligned(16))) bf16 k_lds[2][BN * KROW];
+  __shared__ __attribute__((aligned(16))) bf16 v_lds[2][BN * VROW];
+  __shared__ float gk_lds[2][BN];
 
-  const int h = blockIdx.x, n = blockIdx.y;
+  const int h = xcd_head(blockIdx.x, p.Hq), n = blockIdx.y;
   const int tile = gridDim.z - 1 - blockIdx.z;
   const int seq0 = p.cu[n];
   const int L = p.cu[n + 1] - seq0;
@@ -95,15 +112,17 @@ __global__ __launch_bounds__(256) void fwd_kernel(FwdParams p) {
   if (i0 >= L) return;
   const int grp = p.Hq / p.Hkv;
   const int kvh = h / grp;
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int li = lane & 15, g = lane >> 4;
   const int W = p.window;
   const bool gated = p.G2 != nullptr;
+  const float c = p.scale_log2;
 
   const int r0 = i0 + wave * RW;                 // first row of this wave
   const int r_last = min(r0 + RW, L) - 1;        // last real row (may be < r0)
 
-  // ---- Q operand and per-row state ----
+  // ---- Q operand and per-row state (running max m is kept without the
+  //      row's own gate term gq, which is constant along the row) ----
   bf16x8 qop[RBW][KS];
   float gq[RBW], m_run[RBW], l_run[RBW];
   f32x4 oacc[RBW][DB];
@@ -121,7 +140,7 @@ __global__ __launch_bounds__(256) void fwd_kernel(FwdParams p) {
       for (int ks = 0; ks < KS; ++ks) qop[rb][ks] = bf16x8{};
       gq[rb] = 0.f;
     }
-    m_run[rb] = sink2;
+    m_run[rb] = p.sink ? sink2 - gq[rb] : kNegBig;
     l_run[rb] = p.sink ? 1.f : 0.f;
 #pragma unroll
     for (int db = 0; db < DB; ++db) oacc[rb][db] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -135,114 +154,145 @@ __global__ __launch_bounds__(256) void fwd_kernel(FwdParams p) {
   const bf16* vbase = reinterpret_cast<const bf16*>(p.v) + ((long)seq0 * p.Hkv + kvh) * DV;
   const long kstride = (long)p.Hkv * DQK, vstride = (long)p.Hkv * DV;
 
+  // ---- register staging of one K/V tile (global -> regs -> LDS) ----
+  i32x4 kreg[KCH], vreg[VCH];
+  float gkreg = 0.f;
+  auto fetch = [&](int j0) {
+#pragma unroll
+    for (int cc = 0; cc < KCH; ++cc) {
+      const int ch = tid + 256 * cc;
+      const int kr = ch / (DQK / 8), col = (ch % (DQK / 8)) * 8;
+      const int key = min(j0 + kr, L - 1);       // rows past the end: any valid row
+      kreg[cc] = *reinterpret_cast<const i32x4*>(kbase + (long)key * kstride + col);
+    }
+#pragma unroll
+    for (int cc = 0; cc < VCH; ++cc) {
+      const int ch = tid + 256 * cc;
+      const int kr = ch / (DV / 8), col = (ch % (DV / 8)) * 8;
+      const int key = min(j0 + kr, L - 1);
+      vreg[cc] = *reinterpret_cast<const i32x4*>(vbase + (long)key * vstride + col);
+    }
+    if (gated && tid < BN) gkreg = p.G2[(long)(seq0 + min(j0 + tid, L - 1)) * p.Hq + h];
+  };
+  auto stash = [&](int buf, int j0) {
+    const i32x4 z = {0, 0, 0, 0};
+#pragma unroll
+    for (int cc = 0; cc < KCH; ++cc) {
+      const int ch = tid + 256 * cc;
+      const int kr = ch / (DQK / 8), col = (ch % (DQK / 8)) * 8;
+      *reinterpret_cast<i32x4*>(&k_lds[buf][kr * KROW + col]) = (j0 + kr < L) ? kreg[cc] : z;
+    }
+#pragma unroll
+    for (int cc = 0; cc < VCH; ++cc) {
+      const int ch = tid + 256 * cc;
+      const int kr = ch / (DV / 8), col = (ch % (DV / 8)) * 8;
+      *reinterpret_cast<i32x4*>(&v_lds[buf][kr * VROW + col]) = (j0 + kr < L) ? vreg[cc] : z;
+    }
+    if (gated && tid < BN) gk_lds[buf][tid] = gkreg;
+  };
+
+  fetch(t_begin * BN);
+  stash(0, t_begin * BN);
+  __syncthreads();
+
   for (int t = t_begin; t < t_end; ++t) {
     const int j0 = t * BN;
-    __syncthreads();
-    // ---- stage K, V (and the key-side gate prefix) of keys j0..j0+BN-1 ----
-    constexpr int KCH = BN * DQK / 8, VCH = BN * DV / 8;   // 16-byte chunks
-#pragma unroll
-    for (int c = tid; c < KCH; c += 256) {
-      const int kr = c / (DQK / 8), col = (c % (DQK / 8)) * 8;
-      i32x4 val = {0, 0, 0, 0};
-      if (j0 + kr < L) val = *reinterpret_cast<const i32x4*>(kbase + (long)(j0 + kr) * kstride + col);
-      *reinterpret_cast<i32x4*>(k_lds + kr * KROW + col) = val;
-    }
-#pragma unroll
-    for (int c = tid; c < VCH; c += 256) {
-      const int kr = c / (DV / 8), col = (c % (DV / 8)) * 8;
-      i32x4 val = {0, 0, 0, 0};
-      if (j0 + kr < L) val = *reinterpret_cast<const i32x4*>(vbase + (long)(j0 + kr) * vstride + col);
-      *reinterpret_cast<i32x4*>(v_lds + kr * VROW + col) = val;
-    }
-    if (gated && tid < BN)
-      gk_lds[tid] = (j0 + tid < L) ? p.G2[(long)(seq0 + j0 + tid) * p.Hq + h] : 0.f;
-    __syncthreads();
+    const int buf = (t - t_begin) & 1;
+    const bool more = t + 1 < t_end;
+    // Unconditional (addresses are clamped in range) so the compiler does not
+    // drain the loads at a branch join before the math below.
+    fetch(j0 + BN);
 
-    // ---- does this tile matter for this wave's rows? ----
-    if (r_last < r0) continue;                       // wave has no rows
-    if (j0 > r_last) continue;                       // all keys in the future
-    if (W > 0 && r0 - (j0 + BN - 1) >= W) continue;  // all keys out of window
-    const bool need_mask = (j0 + BN - 1 > r0) || (W > 0 && r_last - j0 >= W) || (j0 + BN > L);
-
-    // ---- S^T = K Q^T ----
-    f32x4 sc[KB][RBW];
-#pragma unroll
-    for (int kb = 0; kb < KB; ++kb) {
-#pragma unroll
-      for (int rb = 0; rb < RBW; ++rb) sc[kb][rb] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        const bf16x8 a = lds_read8(k_lds + (kb * 16 + li) * KROW + ks * 32 + 8 * g);
-#pragma unroll
-        for (int rb = 0; rb < RBW; ++rb) sc[kb][rb] = mfma16x16x32(a, qop[rb][ks], sc[kb][rb]);
-      }
-    }
-    // ---- scale, gate bias, mask (base 2) ----
-#pragma unroll
-    for (int kb = 0; kb < KB; ++kb) {
-      float gk[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) gk[i] = gated ? gk_lds[kb * 16 + 4 * g + i] : 0.f;
-#pragma unroll
-      for (int rb = 0; rb < RBW; ++rb) {
-        const int row = r0 + rb * 16 + li;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          float x = sc[kb][rb][i] * p.scale_log2 + (gq[rb] - gk[i]);
-          if (need_mask) {
-            const int key = j0 + kb * 16 + 4 * g + i;
-            const bool vis = key <= row && key < L && (W <= 0 || row - key < W);
-            x = vis ? x : -INFINITY;
-          }
-          sc[kb][rb][i] = x;
-        }
-      }
-    }
-    // ---- online softmax ----
-    bf16x4 pb[KB][RBW];
-#pragma unroll
-    for (int rb = 0; rb < RBW; ++rb) {
-      float mx = -INFINITY;
-#pragma unroll
-      for (int kb = 0; kb < KB; ++kb)
-        mx = fmaxf(mx, fmaxf(fmaxf(sc[kb][rb][0], sc[kb][rb][1]), fmaxf(sc[kb][rb][2], sc[kb][rb][3])));
-      mx = xgroup_max(mx);
-      const float m_new = fmaxf(m_run[rb], mx);
-      const float alpha = fast_exp2(m_run[rb] - m_new);
-      float rs = 0.f;
+    const bool active = !(r_last < r0) && !(j0 > r_last) && !(W > 0 && r0 - (j0 + BN - 1) >= W);
+    if (active) {
+      const bool need_mask = (j0 + BN - 1 > r0) || (W > 0 && r_last - j0 >= W) || (j0 + BN > L);
+      const bf16* kl = k_lds[buf];
+      const bf16* vl = v_lds[buf];
+      // ---- S^T = K Q^T ----
+      f32x4 sc[KB][RBW];
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb) {
-        f32x4 e;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          e[i] = fast_exp2(sc[kb][rb][i] - m_new);
-          rs += e[i];
+        for (int rb = 0; rb < RBW; ++rb) sc[kb][rb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+          const bf16x8 a = lds_read8(kl + (kb * 16 + li) * KROW + ks * 32 + 8 * g);
+#pragma unroll
+          for (int rb = 0; rb < RBW; ++rb) sc[kb][rb] = mfma16x16x32(a, qop[rb][ks], sc[kb][rb]);
         }
-        pb[kb][rb] = to_bf16x4(e);
       }
-      rs = xgroup_sum(rs);
-      l_run[rb] = l_run[rb] * alpha + rs;
-      m_run[rb] = m_new;
+      // ---- y = s*c - gk (base 2, without the row's gate term), masked ----
 #pragma unroll
-      for (int db = 0; db < DB; ++db) oacc[rb][db] *= alpha;
-    }
-    // ---- O^T += V^T P^T, 32 keys per MFMA ----
+      for (int kb = 0; kb < KB; ++kb) {
+        float gk[4];
 #pragma unroll
-    for (int kp = 0; kp < KB / 2; ++kp) {
-      const int mm = li >> 2, c4 = li & 3;
-      const bf16* vr0 = v_lds + (kp * 32 + 4 * g + mm) * VROW + 4 * c4;
-      const bf16* vr1 = v_lds + (kp * 32 + 16 + 4 * g + mm) * VROW + 4 * c4;
+        for (int i = 0; i < 4; ++i) gk[i] = gated ? gk_lds[buf][kb * 16 + 4 * g + i] : 0.f;
 #pragma unroll
-      for (int db = 0; db < DB; ++db) {
-        const bf16x8 a = concat(lds_read_tr16(vr0 + db * 16), lds_read_tr16(vr1 + db * 16));
+        for (int rb = 0; rb < RBW; ++rb) {
+          const int row = r0 + rb * 16 + li;
 #pragma unroll
-        for (int rb = 0; rb < RBW; ++rb)
-          oacc[rb][db] = mfma16x16x32(a, concat(pb[2 * kp][rb], pb[2 * kp + 1][rb]), oacc[rb][db]);
+          for (int i = 0; i < 4; ++i) {
+            float y = gated ? __builtin_fmaf(sc[kb][rb][i], c, -gk[i]) : sc[kb][rb][i] * c;
+            if (need_mask) {
+              const int key = j0 + kb * 16 + 4 * g + i;
+              const bool vis = key <= row && key < L && (W <= 0 || row - key < W);
+              y = vis ? y : -INFINITY;
+            }
+            sc[kb][rb][i] = y;
+          }
+        }
+      }
+      // ---- online softmax with lazy rescale ----
+      bf16x4 pb[KB][RBW];
+#pragma unroll
+      for (int rb = 0; rb < RBW; ++rb) {
+        float mx = -INFINITY;
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb)
+          mx = fmaxf(mx, fmaxf(fmaxf(sc[kb][rb][0], sc[kb][rb][1]), fmaxf(sc[kb][rb][2], sc[kb][rb][3])));
+        mx = xgroup_max(mx);
+        if (__builtin_expect(__any(mx > m_run[rb] + kRescaleSlack), 0)) {
+          const float m_new = fmaxf(m_run[rb], mx);
+          const float alpha = fast_exp2(m_run[rb] - m_new);
+          l_run[rb] *= alpha;
+#pragma unroll
+          for (int db = 0; db < DB; ++db) oacc[rb][db] *= alpha;
+          m_run[rb] = m_new;
+        }
+        const float mr = m_run[rb];
+        float rs = 0.f;
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) {
+          f32x4 e;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            e[i] = fast_exp2(sc[kb][rb][i] - mr);
+            rs += e[i];
+          }
+          pb[kb][rb] = to_bf16x4(e);
+        }
+        l_run[rb] += xgroup_sum(rs);
+      }
+      // ---- O^T += V^T P^T, 32 keys per MFMA ----
+#pragma unroll
+      for (int kp = 0; kp < KB / 2; ++kp) {
+        const int mm = li >> 2, c4 = li & 3;
+        const bf16* vr0 = vl + (kp * 32 + 4 * g + mm) * VROW + 4 * c4;
+        const bf16* vr1 = vl + (kp * 32 + 16 + 4 * g + mm) * VROW + 4 * c4;
+#pragma unroll
+        for (int db = 0; db < DB; ++db) {
+          const bf16x8 a = concat(lds_read_tr16(vr0 + db * 16), lds_read_tr16(vr1 + db * 16));
+#pragma unroll
+          for (int rb = 0; rb < RBW; ++rb)
+            oacc[rb][db] = mfma16x16x32(a, concat(pb[2 * kp][rb], pb[2 * kp + 1][rb]), oacc[rb][db]);
+        }
       }
     }
+    if (more) stash(buf ^ 1, j0 + BN);
+    __syncthreads();
   }
 
-  // ---- finalize: O = acc / l, lse = ln(l) + m ----
+  // ---- finalize: O = acc / l, lse = ln 2 * (m + gq + log2 l) ----
 #pragma unroll
   for (int rb = 0; rb < RBW; ++rb) {
     const int row = r0 + rb * 16 + li;
@@ -254,7 +304,8 @@ __global__ __launch_bounds__(256) void fwd_kernel(FwdParams p) {
       const f32x4 x = oacc[rb][db] * inv;
       *reinterpret_cast<bf16x4*>(op + db * 16) = to_bf16x4(x);
     }
-    if (g == 0) p.lse[(long)(seq0 + row) * p.Hq + h] = (m_run[rb] + fast_log2(l_run[rb])) * kLn2;
+    if (g == 0)
+      p.lse[(long)(seq0 + row) * p.Hq + h] = (m_run[rb] + gq[rb] + fast_log2(l_run[rb])) * kLn2;
   }
 }
 
@@ -269,8 +320,8 @@ static hipError_t launch_cfg(const FwdParams& p, hipStream_t st) {
 
 hipError_t launch_fwd(const FwdParams& p, int dqk, int dv, hipStream_t st) {
   if (p.num_seqs == 0 || p.T == 0 || p.max_seqlen == 0) return hipSuccess;
-  if (dqk == 64 && dv == 64) return launch_cfg<64, 64, 32, 64>(p, st);
-  if (dqk == 128 && dv == 128) return launch_cfg<128, 128, 32, 64>(p, st);
+  if (dqk == 64 && dv == 64) return launch_cfg<64, 64, FWD_RW_SMALL, FWD_BN_SMALL>(p, st);
+  if (dqk == 128 && dv == 128) return launch_cfg<128, 128, FWD_RW_SMALL, FWD_BN_SMALL>(p, st);
   if (dqk == 256 && dv == 256) return launch_cfg<256, 256, 16, 32>(p, st);
   if (dqk == 256 && dv == 512) return launch_cfg<256, 512, 16, 32>(p, st);
   return hipErrorInvalidValue;

@@ -26,6 +26,9 @@ struct ReduceParams {
 };
 hipError_t launch_splitk_reduce(const ReduceParams& p, hipStream_t st);
 
+// Longest KV segment one decode work item walks (sizes its page-id buffer).
+constexpr int kDecodeMaxSplit = 8192;
+
 struct DecodeParams {
   const void* q;            // bf16 [Tq, Hq, D]
   const int32_t* cu_q;      // [R+1]
@@ -38,7 +41,7 @@ struct DecodeParams {
   float* acc;               // [Tq_max * Hq, S, D]
   float* m;                 // [Tq_max * Hq, S]
   float* l;
-  int R, max_pages, Hq, Hkv, B, split_len, num_splits;
+  int R, max_pages, Hq, Hkv, B, B_shift, split_len, num_splits;
   float scale_log2;         // softmax_scale * log2(e)
 };
 hipError_t launch_decode_splitk(const DecodeParams& p, int head_dim, bool fp8,
@@ -72,8 +75,11 @@ struct BwdParams {
   const float* sink;
   const float* G2;          // [T, Hq] gate prefix * log2(e) or nullptr
   float* delta;             // [T, Hq] workspace
-  float* dq_acc;            // [T, Hq, DQK] fp32 workspace
-  float* dG;                // [T, Hq] fp32 workspace (row minus column sums)
+  float* dq_acc;            // [T, Hq, DQK] fp32 workspace (fused dQ only)
+  float* dG;                // [T, Hq] fp32 (fused: row minus column sums, by atomics)
+  float* dGrow;             // [T, Hq] fp32 (two-pass: row sums of dS, stored)
+  float* dGcol;             // [T, Hq] fp32 (two-pass: column sums of dS, stored)
+  float* sink_rows;         // [T, Hq] fp32 (two-pass: psink_i * sum_j P_ij dP_ij)
   float* dsink_acc;         // [Hq] fp32 (the dsink output itself)
   void* dq;
   void* dk;
@@ -83,7 +89,10 @@ struct BwdParams {
   float scale;              // softmax_scale
   float scale_log2;
 };
-hipError_t launch_bwd(const BwdParams& p, int dqk, int dv, hipStream_t st);
+// Fused dQ (fp32 atomics) or deterministic two-pass backward, plus the
+// shared pre/post kernels.
+hipError_t launch_bwd(const BwdParams& p, int dqk, int dv, bool fused, hipStream_t st);
+hipError_t launch_bwd_two_pass(const BwdParams& p, int dqk, int dv, hipStream_t st);
 // Zero n floats with a kernel (no memset node, so it is safe under capture).
 hipError_t launch_fill_zero(float* x, long n, hipStream_t st);
 

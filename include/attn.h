@@ -136,9 +136,16 @@ int attn_fwd_varlen(const void* q, const void* k, const void* v,
  *            comment; psink_i = e^(sink_h - lse_i))
  *   dg_t   = sum over i >= t in t's sequence of
  *            (sum_j dS_ij - sum_i' dS_i'i)         (gate bias G_i - G_j)
- * dq is accumulated in an fp32 workspace inside the fused dK/dV pass and
- * converted to bf16 afterwards (Oct 5 comment); all atomics are fp32, so dq,
- * dsink and dg are not bitwise reproducible run to run.
+ * Two implementations (Oct 5 comment), chosen by `flags`:
+ *   0 or ATTN_BWD_DETERMINISTIC: two passes (dK/dV KV-major, then dQ
+ *     Q-major, S and dP recomputed in each); every sum is complete inside
+ *     one wavefront and stored, so results are bitwise reproducible.
+ *   ATTN_BWD_FUSED_DQ: dQ fused into the dK/dV pass, each S and dP tile
+ *     computed once, dQ partials added with fp32 atomics into a zeroed fp32
+ *     workspace and converted to bf16 after the kernel; gate and sink
+ *     partials also through fp32 atomics, so dq, dsink and dg are not
+ *     bitwise reproducible.  head_dim_qk <= 128 only (as on the page).
+ * Any other flag bit, or both bits, is ATTN_ERR_INVALID.
  *
  *   q, k, v, cu_seqlens, sink, g, sizes: exactly as passed to the forward
  *   o    bf16 [T, Hq, head_dim_v]   the forward's output
@@ -149,10 +156,19 @@ int attn_fwd_varlen(const void* q, const void* k, const void* v,
  *   dv   bf16 [T, Hkv, head_dim_v]   (output)
  *   dsink fp32 [Hq]       output; must be NULL iff sink is NULL
  *   dg    fp32 [T, Hq]    output; must be NULL iff g is NULL
- * workspace: attn_bwd_workspace_size() bytes.
+ * workspace: attn_bwd_workspace_size() bytes for the same gate, sink and
+ * flags.
  * ---------------------------------------------------------------------- */
+enum attn_bwd_flags {
+  ATTN_BWD_DETERMINISTIC = 1,  /* two-pass kernels, no atomics: bitwise
+                                  reproducible (also the default path) */
+  ATTN_BWD_FUSED_DQ = 2        /* dQ fused into the dK/dV pass through fp32
+                                  atomics (head_dim_qk <= 128 only) */
+};
+
 size_t attn_bwd_workspace_size(int total_tokens, int num_q_heads,
-                               int head_dim_qk, int has_gate);
+                               int head_dim_qk, int has_gate, int has_sink,
+                               int flags);
 
 int attn_bwd_varlen(const void* q, const void* k, const void* v,
                     const void* o, const void* dO, const float* lse,
@@ -161,7 +177,8 @@ int attn_bwd_varlen(const void* q, const void* k, const void* v,
                     int head_dim_qk, int head_dim_v, float softmax_scale,
                     int window, const float* sink, const float* g,
                     void* dq, void* dk, void* dv, float* dsink, float* dg,
-                    void* workspace, size_t workspace_bytes, void* stream);
+                    int flags, void* workspace, size_t workspace_bytes,
+                    void* stream);
 
 /* ------------------------------------------------------------------------
  * attn_decode_paged -- paged decode of 1..4 new query tokens per request.
@@ -189,7 +206,8 @@ int attn_bwd_varlen(const void* q, const void* k, const void* v,
  *            must be NULL for bf16
  *   block_table int32 [num_requests, max_pages]; seq_lens int32 [num_requests]
  *   max_seq_len >= every seq_lens[r] (sizes the split grid)
- *   kv_split_len 0 = library's choice, else a positive multiple of block_size
+ *   kv_split_len 0 = library's choice, else a multiple of max(block_size, 32)
+ *            and at most 8192
  *   out      bf16 [Tq, Hq, head_dim] (output)
  *   lse      fp32 [Tq, Hq] (output, natural log) or NULL
  * Supported: head_dim 64 or 128; block_size 16, 32, 64 or 128;

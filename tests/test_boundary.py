@@ -1,0 +1,183 @@
+"""The C ABI without a GPU: the library loads, exports every function the
+header declares, and rejects every malformed or unsupported argument with
+its status code before anything is launched (so these calls never reach the
+GPU).  Pointers here are fake but aligned, non-null addresses: each call is
+built to fail validation, which never dereferences them."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import causal_softmax_attention_amd as A
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+L = A.library
+P = ctypes.c_void_p(0x10000)          # aligned stand-in pointer (never read)
+P_ODD = ctypes.c_void_p(0x10004)      # 4-byte but not 16-byte aligned
+NULL = None
+OK, INVALID, UNSUPPORTED = 0, -1, -2
+
+
+def declared_functions():
+    text = open(os.path.join(ROOT, "include", "attn.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(attn_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_functions_all_exported():
+    names = declared_functions()
+    assert len(names) >= 10
+    lib = ctypes.CDLL(A.lib_path())
+    for n in names:
+        assert hasattr(lib, n), f"{n} declared in attn.h but not exported"
+
+
+def test_status_strings_and_version():
+    assert L.attn_status_string(0) == b"ok"
+    assert L.attn_status_string(-2) == b"unsupported configuration"
+    assert L.attn_status_string(123) == b"unknown status"
+    assert b"gfx950" in L.attn_version()
+
+
+def _decode(**kw):
+    a = dict(q=P, cu=P, R=2, maxq=1, kc=P, vc=P, kvd=A.ATTN_DTYPE_FP8_E4M3FN, ks=P, vs=P, bt=P,
+             maxp=8, sl=P, maxsl=128, nb=16, B=16, Hq=64, Hkv=4, D=128, scale=0.1, split=0,
+             out=P, lse=NULL, ws=P, wsb=1 << 30)
+    a.update(kw)
+    return L.attn_decode_paged(a["q"], a["cu"], a["R"], a["maxq"], a["kc"], a["vc"], a["kvd"], a["ks"],
+                               a["vs"], a["bt"], a["maxp"], a["sl"], a["maxsl"], a["nb"], a["B"], a["Hq"],
+                               a["Hkv"], a["D"], a["scale"], a["split"], a["out"], a["lse"], a["ws"],
+                               a["wsb"], NULL)
+
+
+@pytest.mark.parametrize("kw,code,msg", [
+    (dict(maxq=5), UNSUPPORTED, "prefill"),
+    (dict(maxq=0), INVALID, "max_seqlen_q"),
+    (dict(ks=NULL), UNSUPPORTED, "per-token"),
+    (dict(vs=NULL), UNSUPPORTED, "per-token"),
+    (dict(kvd=A.ATTN_DTYPE_BF16), UNSUPPORTED, "only read with an fp8"),
+    (dict(kvd=7), UNSUPPORTED, "kv_dtype"),
+    (dict(D=96), UNSUPPORTED, "head_dim"),
+    (dict(B=24), UNSUPPORTED, "block_size"),
+    (dict(Hq=60, Hkv=8), INVALID, "multiple"),
+    (dict(Hq=128, Hkv=2, maxq=4), UNSUPPORTED, "exceeds 64"),
+    (dict(split=48), INVALID, "multiple of"),
+    (dict(split=16384), UNSUPPORTED, "exceeds"),
+    (dict(maxp=4), INVALID, "cannot hold"),
+    (dict(q=NULL), INVALID, "q is NULL"),
+    (dict(kc=P_ODD), INVALID, "aligned"),
+    (dict(wsb=16), INVALID, "workspace too small"),
+    (dict(R=-1), INVALID, "negative"),
+    (dict(scale=float("nan")), INVALID, "finite"),
+])
+def test_decode_validation(kw, code, msg):
+    st = _decode(**kw)
+    assert st == code
+    assert msg in L.attn_last_error().decode()
+
+
+def test_decode_empty_batch_is_a_no_op():
+    assert _decode(R=0) == OK
+
+
+def _fwd(**kw):
+    a = dict(q=P, k=P, v=P, cu=P, N=2, maxs=64, T=100, Hq=8, Hkv=2, dqk=128, dv=128, scale=0.1, W=0,
+             sink=NULL, g=NULL, o=P, lse=P, ws=NULL, wsb=0)
+    a.update(kw)
+    return L.attn_fwd_varlen(a["q"], a["k"], a["v"], a["cu"], a["N"], a["maxs"], a["T"], a["Hq"], a["Hkv"],
+                             a["dqk"], a["dv"], a["scale"], a["W"], a["sink"], a["g"], a["o"], a["lse"],
+                             a["ws"], a["wsb"], NULL)
+
+
+@pytest.mark.parametrize("kw,code,msg", [
+    (dict(dqk=96, dv=96), UNSUPPORTED, "head dims"),
+    (dict(dqk=128, dv=256), UNSUPPORTED, "head dims"),
+    (dict(Hq=6, Hkv=4), INVALID, "multiple"),
+    (dict(Hkv=0), INVALID, "positive"),
+    (dict(maxs=0), INVALID, "max_seqlen"),
+    (dict(maxs=101), INVALID, "max_seqlen"),
+    (dict(q=NULL), INVALID, "q is NULL"),
+    (dict(v=P_ODD), INVALID, "aligned"),
+    (dict(o=NULL), INVALID, "o is NULL"),
+    (dict(g=P, wsb=0), INVALID, "workspace too small"),
+    (dict(scale=float("inf")), INVALID, "finite"),
+    (dict(N=70000), UNSUPPORTED, "num_seqs"),
+])
+def test_forward_validation(kw, code, msg):
+    assert _fwd(**kw) == code
+    assert msg in L.attn_last_error().decode()
+
+
+def test_forward_empty_is_a_no_op():
+    assert _fwd(N=0, T=0, maxs=0) == OK
+    assert _fwd(T=0) == OK
+
+
+def _bwd(**kw):
+    a = dict(q=P, k=P, v=P, o=P, do=P, lse=P, cu=P, N=2, maxs=64, T=100, Hq=8, Hkv=2, dqk=128, dv=128,
+             scale=0.1, W=0, sink=NULL, g=NULL, dq=P, dk=P, dv_=P, ds=NULL, dg=NULL, flags=0, ws=P, wsb=0)
+    a.update(kw)
+    return L.attn_bwd_varlen(a["q"], a["k"], a["v"], a["o"], a["do"], a["lse"], a["cu"], a["N"], a["maxs"],
+                             a["T"], a["Hq"], a["Hkv"], a["dqk"], a["dv"], a["scale"], a["W"], a["sink"],
+                             a["g"], a["dq"], a["dk"], a["dv_"], a["ds"], a["dg"], a["flags"], a["ws"],
+                             a["wsb"], NULL)
+
+
+@pytest.mark.parametrize("kw,code,msg", [
+    (dict(sink=P), INVALID, "dsink must be given"),
+    (dict(ds=P), INVALID, "dsink must be given"),
+    (dict(g=P), INVALID, "dg must be given"),
+    (dict(flags=3), INVALID, "exclude each other"),
+    (dict(flags=8), INVALID, "unknown flags"),
+    (dict(flags=2, dqk=256, dv=512), UNSUPPORTED, "fused-dQ"),
+    (dict(do=NULL), INVALID, "dO is NULL"),
+    (dict(wsb=64), INVALID, "workspace too small"),
+    (dict(dqk=64, dv=128), UNSUPPORTED, "head dims"),
+])
+def test_backward_validation(kw, code, msg):
+    assert _bwd(**kw) == code
+    assert msg in L.attn_last_error().decode()
+
+
+@pytest.mark.parametrize("kw,code,msg", [
+    (dict(dv=96), UNSUPPORTED, "head_dim_v"),
+    (dict(S=0), INVALID, "num_splits"),
+    (dict(dt=7), UNSUPPORTED, "out_dtype"),
+    (dict(acc=NULL), INVALID, "acc is NULL"),
+    (dict(rows=-3), INVALID, "negative"),
+])
+def test_reduce_validation(kw, code, msg):
+    a = dict(acc=P, m=P, l=P, rows=10, S=4, dv=128, out=P, dt=A.ATTN_DTYPE_FP32, lse=NULL)
+    a.update(kw)
+    st = L.attn_splitk_reduce(a["acc"], a["m"], a["l"], a["rows"], a["S"], a["dv"], a["out"], a["dt"],
+                              a["lse"], NULL)
+    assert st == code
+    assert msg in L.attn_last_error().decode()
+
+
+def test_workspace_sizes():
+    # forward: gate prefix only
+    assert A.attn_fwd_workspace_size(1000, 8, False) == 0
+    assert A.attn_fwd_workspace_size(1000, 8, True) >= 1000 * 8 * 4
+    # backward: the fused path holds an fp32 dQ accumulator, the two-pass one does not
+    two = A.attn_bwd_workspace_size(1000, 8, 128, True, True, 0)
+    fused = A.attn_bwd_workspace_size(1000, 8, 128, True, True, A.ATTN_BWD_FUSED_DQ)
+    assert fused >= 1000 * 8 * 128 * 4 > two
+    # decode: partials for every (query row, split)
+    ws = A.attn_decode_workspace_size(64, 1, 32768, 64, 4, 128, 16, 1024)
+    assert ws >= 64 * 64 * 32 * 128 * 4
+    assert A.attn_decode_workspace_size(64, 1, 32768, 64, 4, 128, 16, 0) > 0
+
+
+def test_python_wrapper_rejects_strided_and_wrong_dtype():
+    import torch
+    q = torch.zeros(10, 4, 64, dtype=torch.bfloat16)
+    k = torch.zeros(10, 1, 64, dtype=torch.bfloat16)
+    cu = torch.tensor([0, 10], dtype=torch.int32)
+    with pytest.raises(ValueError, match="contiguous"):
+        A.attn_fwd_varlen(q.transpose(0, 1), k, k, cu, 10)
+    with pytest.raises(ValueError, match="bfloat16"):
+        A.attn_fwd_varlen(q.float(), k, k, cu, 10)
+    with pytest.raises(ValueError, match="int32"):
+        A.attn_fwd_varlen(q, k, k, cu.long(), 10)

@@ -188,14 +188,18 @@ def test_forward_matches_oracle(A, case):
     assert np.max(np.abs(_np(lse) - rl)) <= 2e-3
 
 
+@pytest.mark.parametrize("mode", ["two-pass", "fused-dq"])
 @pytest.mark.parametrize("case", PREFILL_CASES, ids=_pf_id)
-def test_backward_matches_oracle(A, case):
-    _say(f"[case] backward {_pf_id(case)}")
+def test_backward_matches_oracle(A, case, mode):
+    if mode == "fused-dq" and case[3] > 128:
+        pytest.skip("the fused-dQ backward covers d_qk <= 128 (rejected with NotImplementedError)")
+    flags = A.ATTN_BWD_FUSED_DQ if mode == "fused-dq" else 0
+    _say(f"[case] backward {mode} {_pf_id(case)}")
     x = _prefill(case, seed=321)
     o, lse = A.attn_fwd_varlen(x.q, x.k, x.v, x.cu_seqlens, x.max_seqlen, x.scale, x.window,
                                x.sink, x.g)
     dq, dk, dv, ds, dg = A.attn_bwd_varlen(x.q, x.k, x.v, o, x.do, lse, x.cu_seqlens, x.max_seqlen,
-                                           x.scale, x.window, x.sink, x.g)
+                                           x.scale, x.window, x.sink, x.g, flags=flags)
     torch.cuda.synchronize()
     ref = oracle.backward(x.q, x.k, x.v, x.do, x.cu_seqlens, x.scale, x.window, x.sink, x.g)
     names = ["dq", "dk", "dv", "dsink", "dg"]
@@ -208,6 +212,26 @@ def test_backward_matches_oracle(A, case):
     _say("    " + " ".join(f"{k}={v:.3e}" for k, v in errs.items()))
     for nm, e in errs.items():
         assert e <= TOL, nm
+
+
+def test_backward_two_pass_is_bitwise_deterministic(A):
+    _say("[case] backward determinism")
+    x = _prefill(PREFILL_CASES[2], seed=9)
+    o, lse = A.attn_fwd_varlen(x.q, x.k, x.v, x.cu_seqlens, x.max_seqlen, x.scale, x.window, x.sink, x.g)
+    runs = [A.attn_bwd_varlen(x.q, x.k, x.v, o, x.do, lse, x.cu_seqlens, x.max_seqlen, x.scale, x.window,
+                              x.sink, x.g, flags=A.ATTN_BWD_DETERMINISTIC) for _ in range(3)]
+    torch.cuda.synchronize()
+    for r in runs[1:]:
+        for a, b in zip(runs[0], r):
+            assert torch.equal(a, b)
+
+
+def test_fused_dq_rejects_large_heads(A):
+    x = _prefill(PREFILL_CASES[-1], seed=1)
+    o, lse = A.attn_fwd_varlen(x.q, x.k, x.v, x.cu_seqlens, x.max_seqlen, x.scale, x.window, x.sink, x.g)
+    with pytest.raises(NotImplementedError, match="fused-dQ"):
+        A.attn_bwd_varlen(x.q, x.k, x.v, o, x.do, lse, x.cu_seqlens, x.max_seqlen, x.scale, x.window,
+                          x.sink, x.g, flags=A.ATTN_BWD_FUSED_DQ)
 
 
 def test_forward_empty_and_zero_length_sequences(A):
