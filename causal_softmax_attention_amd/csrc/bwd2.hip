@@ -20,6 +20,10 @@
 #include "common.h"
 #include "kernels.h"
 
+#ifndef BWD_KW_SMALL
+#define BWD_KW_SMALL 16
+#endif
+
 namespace attn {
 
 __device__ __forceinline__ int xcd_remap(int x, int n) {
@@ -29,7 +33,9 @@ __device__ __forceinline__ int xcd_remap(int x, int n) {
 }
 
 // ---------------------------------------------------------------------------
-template <int DQK, int DV, int KW>
+// PF: fetch the next query tile into registers during the current one
+// (off for the largest heads, where those registers are not available).
+template <int DQK, int DV, int KW, bool PF, bool GATED>
 __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdParams p) {
   constexpr int RQ = 32;              // query rows per tile
   constexpr int KBW = KW / 16;        // 16-key blocks per wave
@@ -37,9 +43,12 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdParams p) {
   constexpr int KSQ = DQK / 32, KSV = DV / 32;
   constexpr int DBQ = DQK / 16, DBV = DV / 16;
   constexpr int QROW = DQK + 8, OROW = DV + 16;
-  __shared__ __attribute__((aligned(16))) bf16 q_lds[RQ * QROW];
-  __shared__ __attribute__((aligned(16))) bf16 do_lds[RQ * OROW];
-  __shared__ float lse_lds[RQ], delta_lds[RQ], gq_lds[RQ];
+  constexpr int QCH = RQ * DQK / 8 / 256, OCH = RQ * DV / 8 / 256;   // 16-byte chunks per thread
+  static_assert(QCH * 256 * 8 == RQ * DQK && OCH * 256 * 8 == RQ * DV, "tile must split evenly");
+  constexpr int NB = PF ? 2 : 1;
+  __shared__ __attribute__((aligned(16))) bf16 q_lds[NB][RQ * QROW];
+  __shared__ __attribute__((aligned(16))) bf16 do_lds[NB][RQ * OROW];
+  __shared__ __attribute__((aligned(16))) float lse_lds[NB][RQ], delta_lds[NB][RQ], gq_lds[NB][RQ];
 
   const int kvh = xcd_remap(blockIdx.x, p.Hkv), n = blockIdx.y, ktile = blockIdx.z;
   const int seq0 = p.cu[n];
@@ -50,7 +59,7 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdParams p) {
   const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int li = lane & 15, g = lane >> 4;
   const int W = p.window;
-  const bool gated = p.G2 != nullptr;
+  constexpr bool gated = GATED;
   const int jw = j0 + wave * KW;
 
   bf16x8 kop[KBW][KSQ], vop[KBW][KSV];
@@ -74,48 +83,122 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdParams p) {
     for (int db = 0; db < DBV; ++db) dv_acc[kb][db] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
 
+  // Flattened iteration over (query head of the group, 32-row query tile);
+  // tile it+1 is fetched into registers while tile it is computed.
   const int i_end = W > 0 ? min(L, j0 + BNW - 1 + W) : L;
+  const int nqt = (i_end - j0 + RQ - 1) / RQ;
+  const int n_it = grp * nqt;
 
-  for (int hg = 0; hg < grp; ++hg) {
-    const int h = kvh * grp + hg;
-    float gk[KBW], colsum[KBW];
+  i32x4 qreg[QCH], oreg[OCH];
+  float sreg[3] = {0.f, 0.f, 0.f};
+  auto fetch = [&](int it) {
+    const int hh = kvh * grp + min(it / nqt, grp - 1);
+    const int i0 = j0 + (it % nqt) * RQ;
 #pragma unroll
-    for (int kb = 0; kb < KBW; ++kb) {
-      const int key = jw + kb * 16 + li;
-      gk[kb] = (gated && key < L) ? p.G2[(long)(seq0 + key) * p.Hq + h] : 0.f;
-      colsum[kb] = 0.f;
+    for (int cc = 0; cc < QCH; ++cc) {
+      const int ch = tid + 256 * cc;
+      const int rr = ch / (DQK / 8), col = (ch % (DQK / 8)) * 8;
+      qreg[cc] = *reinterpret_cast<const i32x4*>(reinterpret_cast<const bf16*>(p.q) +
+                                                 ((long)(seq0 + min(i0 + rr, L - 1)) * p.Hq + hh) * DQK + col);
     }
-    for (int i0 = j0; i0 < i_end; i0 += RQ) {
-      __syncthreads();
+#pragma unroll
+    for (int cc = 0; cc < OCH; ++cc) {
+      const int ch = tid + 256 * cc;
+      const int rr = ch / (DV / 8), col = (ch % (DV / 8)) * 8;
+      oreg[cc] = *reinterpret_cast<const i32x4*>(reinterpret_cast<const bf16*>(p.dO) +
+                                                 ((long)(seq0 + min(i0 + rr, L - 1)) * p.Hq + hh) * DV + col);
+    }
+    if (tid < RQ) {
+      const long ri = (long)(seq0 + min(i0 + tid, L - 1)) * p.Hq + hh;
+      sreg[0] = p.lse[ri];
+      sreg[1] = p.delta[ri];
+      sreg[2] = gated ? p.G2[ri] : 0.f;
+    }
+  };
+  auto stash = [&](int buf, int it) {
+    const int i0 = j0 + (it % nqt) * RQ;
+    const i32x4 z = {0, 0, 0, 0};
+#pragma unroll
+    for (int cc = 0; cc < QCH; ++cc) {
+      const int ch = tid + 256 * cc;
+      const int rr = ch / (DQK / 8), col = (ch % (DQK / 8)) * 8;
+      *reinterpret_cast<i32x4*>(&q_lds[buf][rr * QROW + col]) = (i0 + rr < L) ? qreg[cc] : z;
+    }
+#pragma unroll
+    for (int cc = 0; cc < OCH; ++cc) {
+      const int ch = tid + 256 * cc;
+      const int rr = ch / (DV / 8), col = (ch % (DV / 8)) * 8;
+      *reinterpret_cast<i32x4*>(&do_lds[buf][rr * OROW + col]) = (i0 + rr < L) ? oreg[cc] : z;
+    }
+    if (tid < RQ) {
+      const bool ok = i0 + tid < L;
+      lse_lds[buf][tid] = ok ? sreg[0] * kLog2e : 0.f;
+      delta_lds[buf][tid] = ok ? sreg[1] : 0.f;
+      gq_lds[buf][tid] = ok ? sreg[2] : 0.f;
+    }
+  };
+
+  if constexpr (PF) {
+    fetch(0);
+    stash(0, 0);
+    __syncthreads();
+  }
+
+  float gk[KBW], colsum[KBW];
+  for (int it = 0; it < n_it; ++it) {
+    const int buf = PF ? (it & 1) : 0;
+    if constexpr (!PF) {
+      // chunk by chunk straight into LDS: few live registers
+      const int hh = kvh * grp + it / nqt;
+      const int i0s = j0 + (it % nqt) * RQ;
       for (int c = tid; c < RQ * DQK / 8; c += 256) {
         const int rr = c / (DQK / 8), col = (c % (DQK / 8)) * 8;
         i32x4 val = {0, 0, 0, 0};
-        if (i0 + rr < L)
+        if (i0s + rr < L)
           val = *reinterpret_cast<const i32x4*>(reinterpret_cast<const bf16*>(p.q) +
-                                                ((long)(seq0 + i0 + rr) * p.Hq + h) * DQK + col);
-        *reinterpret_cast<i32x4*>(q_lds + rr * QROW + col) = val;
+                                                ((long)(seq0 + i0s + rr) * p.Hq + hh) * DQK + col);
+        *reinterpret_cast<i32x4*>(&q_lds[0][rr * QROW + col]) = val;
       }
       for (int c = tid; c < RQ * DV / 8; c += 256) {
         const int rr = c / (DV / 8), col = (c % (DV / 8)) * 8;
         i32x4 val = {0, 0, 0, 0};
-        if (i0 + rr < L)
+        if (i0s + rr < L)
           val = *reinterpret_cast<const i32x4*>(reinterpret_cast<const bf16*>(p.dO) +
-                                                ((long)(seq0 + i0 + rr) * p.Hq + h) * DV + col);
-        *reinterpret_cast<i32x4*>(do_lds + rr * OROW + col) = val;
+                                                ((long)(seq0 + i0s + rr) * p.Hq + hh) * DV + col);
+        *reinterpret_cast<i32x4*>(&do_lds[0][rr * OROW + col]) = val;
       }
       if (tid < RQ) {
-        const bool ok = i0 + tid < L;
-        const long ri = (long)(seq0 + i0 + tid) * p.Hq + h;
-        lse_lds[tid] = ok ? p.lse[ri] * kLog2e : 0.f;
-        delta_lds[tid] = ok ? p.delta[ri] : 0.f;
-        gq_lds[tid] = (ok && gated) ? p.G2[ri] : 0.f;
+        const bool ok = i0s + tid < L;
+        const long ri = (long)(seq0 + i0s + tid) * p.Hq + hh;
+        lse_lds[0][tid] = ok ? p.lse[ri] * kLog2e : 0.f;
+        delta_lds[0][tid] = ok ? p.delta[ri] : 0.f;
+        gq_lds[0][tid] = (ok && gated) ? p.G2[ri] : 0.f;
       }
       __syncthreads();
+    }
+    const int hg = it / nqt, qt = it % nqt;
+    const int h = kvh * grp + hg;
+    const int i0 = j0 + qt * RQ;
+    if (qt == 0) {
+#pragma unroll
+      for (int kb = 0; kb < KBW; ++kb) {
+        const int key = jw + kb * 16 + li;
+        gk[kb] = gated ? p.G2[(long)(seq0 + min(key, L - 1)) * p.Hq + h] : 0.f;
+        colsum[kb] = 0.f;
+      }
+    }
+    if constexpr (PF) fetch(it + 1);   // unconditional: indices clamped, no drain at a branch join
 
-      if (jw >= L) continue;
-      if (i0 + RQ - 1 < jw) continue;
-      if (W > 0 && i0 - (jw + KW - 1) >= W) continue;
-
+    // no branch around the math (see the forward kernel): masked pairs give
+    // P = dS = 0; the per-element mask runs only on tiles that need it
+    const bool need_mask = (i0 < jw + KW - 1) || (W > 0 && i0 + RQ - 1 - jw >= W) || (i0 + RQ > L) ||
+                           (jw + KW > L);
+    {
+      const bf16* ql = q_lds[buf];
+      const bf16* ol = do_lds[buf];
+      const float* lsel = lse_lds[buf];
+      const float* dell = delta_lds[buf];
+      const float* gql = gq_lds[buf];
       // ---- S = Q K^T, dP = dO V^T: C lane (key li, rows rb*16+4g+i) ----
       f32x4 s[KBW][2], dp[KBW][2];
 #pragma unroll
@@ -127,60 +210,85 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdParams p) {
         }
 #pragma unroll
         for (int ks = 0; ks < KSQ; ++ks) {
-          const bf16x8 a = lds_read8(q_lds + (rb * 16 + li) * QROW + ks * 32 + 8 * g);
+          const bf16x8 a = lds_read8(ql + (rb * 16 + li) * QROW + ks * 32 + 8 * g);
 #pragma unroll
           for (int kb = 0; kb < KBW; ++kb) s[kb][rb] = mfma16x16x32(a, kop[kb][ks], s[kb][rb]);
         }
 #pragma unroll
         for (int ks = 0; ks < KSV; ++ks) {
-          const bf16x8 a = lds_read8(do_lds + (rb * 16 + li) * OROW + ks * 32 + 8 * g);
+          const bf16x8 a = lds_read8(ol + (rb * 16 + li) * OROW + ks * 32 + 8 * g);
 #pragma unroll
           for (int kb = 0; kb < KBW; ++kb) dp[kb][rb] = mfma16x16x32(a, vop[kb][ks], dp[kb][rb]);
         }
       }
-      // ---- P and dS ----
+      // ---- P (masked only on tiles that need it) and dS ----
+      f32x4 pv[KBW][2];
+#pragma unroll
+      for (int rb = 0; rb < 2; ++rb) {
+        const f32x4 lse4 = *reinterpret_cast<const f32x4*>(lsel + rb * 16 + 4 * g);
+        f32x4 gq4 = {0.f, 0.f, 0.f, 0.f};
+        if constexpr (GATED) gq4 = *reinterpret_cast<const f32x4*>(gql + rb * 16 + 4 * g);
+#pragma unroll
+        for (int kb = 0; kb < KBW; ++kb)
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            pv[kb][rb][i] = fast_exp2(__builtin_fmaf(s[kb][rb][i], p.scale_log2, (gq4[i] - gk[kb]) - lse4[i]));
+      }
+      if (need_mask) {
+#pragma unroll
+        for (int kb = 0; kb < KBW; ++kb) {
+          const int key = jw + kb * 16 + li;
+#pragma unroll
+          for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const int row = i0 + rb * 16 + 4 * g + i;
+              const bool vis = key < L && row < L && key <= row && (W <= 0 || row - key < W);
+              pv[kb][rb][i] = vis ? pv[kb][rb][i] : 0.f;
+            }
+        }
+      }
       bf16x8 pop[KBW], dsop[KBW];
 #pragma unroll
       for (int kb = 0; kb < KBW; ++kb) {
-        const int key = jw + kb * 16 + li;
-        f32x4 pv[2], dsv[2];
+        f32x4 dsv[2];
 #pragma unroll
-        for (int rb = 0; rb < 2; ++rb)
+        for (int rb = 0; rb < 2; ++rb) {
+          const f32x4 del4 = *reinterpret_cast<const f32x4*>(dell + rb * 16 + 4 * g);
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
-            const int rl = rb * 16 + 4 * g + i;
-            const int row = i0 + rl;
-            const bool vis = key < L && row < L && key <= row && (W <= 0 || row - key < W);
-            const float x = s[kb][rb][i] * p.scale_log2 + (gq_lds[rl] - gk[kb]) - lse_lds[rl];
-            const float pr = vis ? fast_exp2(x) : 0.f;
-            const float d = pr * (dp[kb][rb][i] - delta_lds[rl]);
+            const float d = pv[kb][rb][i] * (dp[kb][rb][i] - del4[i]);
             colsum[kb] += d;
-            pv[rb][i] = pr;
             dsv[rb][i] = d;
           }
-        pop[kb] = concat(to_bf16x4(pv[0]), to_bf16x4(pv[1]));
+        }
+        pop[kb] = concat(to_bf16x4(pv[kb][0]), to_bf16x4(pv[kb][1]));
         dsop[kb] = concat(to_bf16x4(dsv[0]), to_bf16x4(dsv[1]));
       }
       // ---- dV^T += dO^T P, dK^T += Q^T dS (32 rows per MFMA) ----
       const int mm = li >> 2, c4 = li & 3;
-      const bf16* o0 = do_lds + (4 * g + mm) * OROW + 4 * c4;
-      const bf16* o1 = do_lds + (16 + 4 * g + mm) * OROW + 4 * c4;
+      const bf16* o0 = ol + (4 * g + mm) * OROW + 4 * c4;
+      const bf16* o1 = ol + (16 + 4 * g + mm) * OROW + 4 * c4;
+      // (compiler barriers every few column blocks keep the scheduler from
+      //  hoisting every transposed read at once and running out of registers)
 #pragma unroll
       for (int db = 0; db < DBV; ++db) {
         const bf16x8 a = concat(lds_read_tr16(o0 + db * 16), lds_read_tr16(o1 + db * 16));
 #pragma unroll
         for (int kb = 0; kb < KBW; ++kb) dv_acc[kb][db] = mfma16x16x32(a, pop[kb], dv_acc[kb][db]);
+        if ((db & 3) == 3) asm volatile("" ::: "memory");
       }
-      const bf16* q0 = q_lds + (4 * g + mm) * QROW + 4 * c4;
-      const bf16* q1 = q_lds + (16 + 4 * g + mm) * QROW + 4 * c4;
+      const bf16* q0 = ql + (4 * g + mm) * QROW + 4 * c4;
+      const bf16* q1 = ql + (16 + 4 * g + mm) * QROW + 4 * c4;
 #pragma unroll
       for (int db = 0; db < DBQ; ++db) {
         const bf16x8 a = concat(lds_read_tr16(q0 + db * 16), lds_read_tr16(q1 + db * 16));
 #pragma unroll
         for (int kb = 0; kb < KBW; ++kb) dk_acc[kb][db] = mfma16x16x32(a, dsop[kb], dk_acc[kb][db]);
+        if ((db & 3) == 3) asm volatile("" ::: "memory");
       }
     }
-    if (gated) {
+    if (gated && qt == nqt - 1) {
 #pragma unroll
       for (int kb = 0; kb < KBW; ++kb) {
         const float cs = xgroup_sum(colsum[kb]);
@@ -188,6 +296,10 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdParams p) {
         if (g == 0 && key < L) p.dGcol[(long)(seq0 + key) * p.Hq + h] = cs;
       }
     }
+    if constexpr (PF) {
+      if (it + 1 < n_it) stash(buf ^ 1, it + 1);
+    }
+    __syncthreads();
   }
 
 #pragma unroll
@@ -204,7 +316,7 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdParams p) {
 }
 
 // ---------------------------------------------------------------------------
-template <int DQK, int DV, int RW, int BN>
+template <int DQK, int DV, int RW, int BN, bool GATED>
 __global__ __launch_bounds__(256) void bwd_dq_kernel(BwdParams p) {
   constexpr int BM = 4 * RW;
   constexpr int RBW = RW / 16;
@@ -216,7 +328,7 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(BwdParams p) {
   static_assert(KB % 2 == 0, "dQ consumes keys in pairs of 16-key blocks");
   __shared__ __attribute__((aligned(16))) bf16 k_lds[2][BN * KROW];
   __shared__ __attribute__((aligned(16))) bf16 v_lds[2][BN * VROW];
-  __shared__ float gk_lds[2][BN];
+  __shared__ __attribute__((aligned(16))) float gk_lds[2][BN];
 
   const int h = xcd_remap(blockIdx.x, p.Hq), n = blockIdx.y;
   const int tile = gridDim.z - 1 - blockIdx.z;
@@ -229,7 +341,7 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(BwdParams p) {
   const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int li = lane & 15, g = lane >> 4;
   const int W = p.window;
-  const bool gated = p.G2 != nullptr;
+  constexpr bool gated = GATED;
   const float c = p.scale_log2;
   const int r0 = i0 + wave * RW;
   const int r_last = min(r0 + RW, L) - 1;
@@ -283,17 +395,18 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(BwdParams p) {
   };
   auto stash = [&](int buf, int j0) {
     const i32x4 z = {0, 0, 0, 0};
+    const bool tail = j0 + BN > L;               // zero-fill rows past the end (last tile only)
 #pragma unroll
     for (int cc = 0; cc < KCH; ++cc) {
       const int ch = tid + 256 * cc;
       const int kr = ch / (DQK / 8), col = (ch % (DQK / 8)) * 8;
-      *reinterpret_cast<i32x4*>(&k_lds[buf][kr * KROW + col]) = (j0 + kr < L) ? kreg[cc] : z;
+      *reinterpret_cast<i32x4*>(&k_lds[buf][kr * KROW + col]) = (tail && j0 + kr >= L) ? z : kreg[cc];
     }
 #pragma unroll
     for (int cc = 0; cc < VCH; ++cc) {
       const int ch = tid + 256 * cc;
       const int kr = ch / (DV / 8), col = (ch % (DV / 8)) * 8;
-      *reinterpret_cast<i32x4*>(&v_lds[buf][kr * VROW + col]) = (j0 + kr < L) ? vreg[cc] : z;
+      *reinterpret_cast<i32x4*>(&v_lds[buf][kr * VROW + col]) = (tail && j0 + kr >= L) ? z : vreg[cc];
     }
     if (gated && tid < BN) gk_lds[buf][tid] = gkreg;
   };
@@ -308,9 +421,10 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(BwdParams p) {
     const bool more = t + 1 < t_end;
     fetch(j0 + BN);   // unconditional: clamped addresses, no drain at a branch join
 
-    const bool active = !(r_last < r0) && !(j0 > r_last) && !(W > 0 && r0 - (j0 + BN - 1) >= W);
-    if (active) {
-      // rows past the end are masked too: their lse is not defined
+    // no branch around the math (see the forward kernel): wholly masked
+    // tiles contribute zeros; rows past the end are masked too, their lse
+    // is not defined
+    {
       const bool need_mask = (j0 + BN - 1 > r0) || (W > 0 && r_last - j0 >= W) || (j0 + BN > L) ||
                              (r_last < r0 + RW - 1);
       const bf16* kl = k_lds[buf];
@@ -336,25 +450,42 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(BwdParams p) {
           for (int rb = 0; rb < RBW; ++rb) dp[kb][rb] = mfma16x16x32(a, doop[rb][ks], dp[kb][rb]);
         }
       }
-      bf16x4 dsb[KB][RBW];
+      // ---- P (masked only on tiles that need it), dS, row sums ----
+      f32x4 pv[KB][RBW];
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb) {
-        float gk[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) gk[i] = gated ? gk_lds[buf][kb * 16 + 4 * g + i] : 0.f;
+        f32x4 gk = {0.f, 0.f, 0.f, 0.f};
+        if constexpr (GATED) gk = *reinterpret_cast<const f32x4*>(&gk_lds[buf][kb * 16 + 4 * g]);
 #pragma unroll
         for (int rb = 0; rb < RBW; ++rb) {
-          const int row = r0 + rb * 16 + li;
           const float base = gq[rb] - lse2[rb];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) pv[kb][rb][i] = fast_exp2(__builtin_fmaf(s[kb][rb][i], c, base - gk[i]));
+        }
+      }
+      if (need_mask) {
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+          for (int rb = 0; rb < RBW; ++rb) {
+            const int row = r0 + rb * 16 + li;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const int key = j0 + kb * 16 + 4 * g + i;
+              const bool vis = key <= row && key < L && row < L && (W <= 0 || row - key < W);
+              pv[kb][rb][i] = vis ? pv[kb][rb][i] : 0.f;
+            }
+          }
+      }
+      bf16x4 dsb[KB][RBW];
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+        for (int rb = 0; rb < RBW; ++rb) {
           f32x4 dsv;
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
-            float pr = fast_exp2(__builtin_fmaf(s[kb][rb][i], c, base - gk[i]));
-            if (need_mask) {
-              const int key = j0 + kb * 16 + 4 * g + i;
-              const bool vis = key <= row && key < L && row < L && (W <= 0 || row - key < W);
-              pr = vis ? pr : 0.f;
-            }
+            const float pr = pv[kb][rb][i];
             const float d = pr * (dp[kb][rb][i] - dlt[rb]);
             pdp[rb] += pr * dp[kb][rb][i];
             rowsum[rb] += d;
@@ -362,7 +493,6 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(BwdParams p) {
           }
           dsb[kb][rb] = to_bf16x4(dsv);
         }
-      }
       // ---- dQ^T += K^T dS^T, 32 keys per MFMA ----
 #pragma unroll
       for (int kp = 0; kp < KB / 2; ++kp) {
@@ -419,11 +549,15 @@ __global__ __launch_bounds__(256) void sink_reduce_kernel(const float* __restric
 template <int DQK, int DV, int KW, int RW, int BN>
 hipError_t launch_bwd_two_pass_t(const BwdParams& p, hipStream_t st) {
   const int ktiles = (p.max_seqlen + 4 * KW - 1) / (4 * KW);
-  bwd_dkdv_kernel<DQK, DV, KW><<<dim3(p.Hkv, p.num_seqs, ktiles), 256, 0, st>>>(p);
+  const dim3 gk(p.Hkv, p.num_seqs, ktiles);
+  if (p.G2) bwd_dkdv_kernel<DQK, DV, KW, (DV <= 256), true><<<gk, 256, 0, st>>>(p);
+  else bwd_dkdv_kernel<DQK, DV, KW, (DV <= 256), false><<<gk, 256, 0, st>>>(p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int qtiles = (p.max_seqlen + 4 * RW - 1) / (4 * RW);
-  bwd_dq_kernel<DQK, DV, RW, BN><<<dim3(p.Hq, p.num_seqs, qtiles), 256, 0, st>>>(p);
+  const dim3 gq(p.Hq, p.num_seqs, qtiles);
+  if (p.G2) bwd_dq_kernel<DQK, DV, RW, BN, true><<<gq, 256, 0, st>>>(p);
+  else bwd_dq_kernel<DQK, DV, RW, BN, false><<<gq, 256, 0, st>>>(p);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (p.sink) {
@@ -434,8 +568,8 @@ hipError_t launch_bwd_two_pass_t(const BwdParams& p, hipStream_t st) {
 }
 
 hipError_t launch_bwd_two_pass(const BwdParams& p, int dqk, int dv, hipStream_t st) {
-  if (dqk == 64 && dv == 64) return launch_bwd_two_pass_t<64, 64, 32, 16, 64>(p, st);
-  if (dqk == 128 && dv == 128) return launch_bwd_two_pass_t<128, 128, 32, 16, 64>(p, st);
+  if (dqk == 64 && dv == 64) return launch_bwd_two_pass_t<64, 64, BWD_KW_SMALL, 16, 64>(p, st);
+  if (dqk == 128 && dv == 128) return launch_bwd_two_pass_t<128, 128, BWD_KW_SMALL, 16, 64>(p, st);
   if (dqk == 256 && dv == 256) return launch_bwd_two_pass_t<256, 256, 16, 16, 32>(p, st);
   if (dqk == 256 && dv == 512) return launch_bwd_two_pass_t<256, 512, 16, 16, 32>(p, st);
   return hipErrorInvalidValue;

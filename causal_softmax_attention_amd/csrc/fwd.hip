@@ -87,7 +87,7 @@ __device__ __forceinline__ int xcd_head(int x, int Hq) {
   return (x % 8) * (Hq / 8) + x / 8;
 }
 
-template <int DQK, int DV, int RW, int BN>
+template <int DQK, int DV, int RW, int BN, bool GATED>
 __global__ __launch_bounds__(256) void fwd_kernel(FwdParams p) {
   constexpr int BM = 4 * RW;
   constexpr int RBW = RW / 16;       // 16-row blocks per wave
@@ -102,7 +102,7 @@ __global__ __launch_bounds__(256) void fwd_kernel(FwdParams p) {
   static_assert(KCH * 256 * 8 == BN * DQK && VCH * 256 * 8 == BN * DV, "tile must split evenly");
   __shared__ __attribute__((aligned(16))) bf16 k_lds[2][BN * KROW];
   __shared__ __attribute__((aligned(16))) bf16 v_lds[2][BN * VROW];
-  __shared__ float gk_lds[2][BN];
+  __shared__ __attribute__((aligned(16))) float gk_lds[2][BN];
 
   const int h = xcd_head(blockIdx.x, p.Hq), n = blockIdx.y;
   const int tile = gridDim.z - 1 - blockIdx.z;
@@ -115,7 +115,7 @@ __global__ __launch_bounds__(256) void fwd_kernel(FwdParams p) {
   const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int li = lane & 15, g = lane >> 4;
   const int W = p.window;
-  const bool gated = p.G2 != nullptr;
+  constexpr bool gated = GATED;
   const float c = p.scale_log2;
 
   const int r0 = i0 + wave * RW;                 // first row of this wave
@@ -176,17 +176,18 @@ __global__ __launch_bounds__(256) void fwd_kernel(FwdParams p) {
   };
   auto stash = [&](int buf, int j0) {
     const i32x4 z = {0, 0, 0, 0};
+    const bool tail = j0 + BN > L;               // zero-fill rows past the end (last tile only)
 #pragma unroll
     for (int cc = 0; cc < KCH; ++cc) {
       const int ch = tid + 256 * cc;
       const int kr = ch / (DQK / 8), col = (ch % (DQK / 8)) * 8;
-      *reinterpret_cast<i32x4*>(&k_lds[buf][kr * KROW + col]) = (j0 + kr < L) ? kreg[cc] : z;
+      *reinterpret_cast<i32x4*>(&k_lds[buf][kr * KROW + col]) = (tail && j0 + kr >= L) ? z : kreg[cc];
     }
 #pragma unroll
     for (int cc = 0; cc < VCH; ++cc) {
       const int ch = tid + 256 * cc;
       const int kr = ch / (DV / 8), col = (ch % (DV / 8)) * 8;
-      *reinterpret_cast<i32x4*>(&v_lds[buf][kr * VROW + col]) = (j0 + kr < L) ? vreg[cc] : z;
+      *reinterpret_cast<i32x4*>(&v_lds[buf][kr * VROW + col]) = (tail && j0 + kr >= L) ? z : vreg[cc];
     }
     if (gated && tid < BN) gk_lds[buf][tid] = gkreg;
   };
@@ -203,9 +204,13 @@ __global__ __launch_bounds__(256) void fwd_kernel(FwdParams p) {
     // drain the loads at a branch join before the math below.
     fetch(j0 + BN);
 
-    const bool active = !(r_last < r0) && !(j0 > r_last) && !(W > 0 && r0 - (j0 + BN - 1) >= W);
-    if (active) {
-      const bool need_mask = (j0 + BN - 1 > r0) || (W > 0 && r_last - j0 >= W) || (j0 + BN > L);
+    // No branch around the math: a tile that is wholly masked for this
+    // wave's rows goes through the masked path and contributes zeros.  (A
+    // branch here makes the compiler shuttle every accumulator between
+    // AGPRs and VGPRs on each iteration.)
+    {
+      const bool need_mask = (j0 + BN - 1 > r0) || (W > 0 && r_last - j0 >= W) || (j0 + BN > L) ||
+                             (r_last < r0 + RW - 1);
       const bf16* kl = k_lds[buf];
       const bf16* vl = v_lds[buf];
       // ---- S^T = K Q^T ----
@@ -221,26 +226,31 @@ __global__ __launch_bounds__(256) void fwd_kernel(FwdParams p) {
           for (int rb = 0; rb < RBW; ++rb) sc[kb][rb] = mfma16x16x32(a, qop[rb][ks], sc[kb][rb]);
         }
       }
-      // ---- y = s*c - gk (base 2, without the row's gate term), masked ----
+      // ---- y = s*c - gk (base 2, without the row's gate term) ----
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb) {
-        float gk[4];
+        f32x4 gk = {0.f, 0.f, 0.f, 0.f};
+        if constexpr (GATED) gk = *reinterpret_cast<const f32x4*>(&gk_lds[buf][kb * 16 + 4 * g]);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) gk[i] = gated ? gk_lds[buf][kb * 16 + 4 * g + i] : 0.f;
+        for (int rb = 0; rb < RBW; ++rb)
 #pragma unroll
-        for (int rb = 0; rb < RBW; ++rb) {
-          const int row = r0 + rb * 16 + li;
+          for (int i = 0; i < 4; ++i)
+            sc[kb][rb][i] = GATED ? __builtin_fmaf(sc[kb][rb][i], c, -gk[i]) : sc[kb][rb][i] * c;
+      }
+      // ---- mask, only on tiles crossing the diagonal, window edge or end ----
+      if (need_mask) {
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            float y = gated ? __builtin_fmaf(sc[kb][rb][i], c, -gk[i]) : sc[kb][rb][i] * c;
-            if (need_mask) {
+        for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+          for (int rb = 0; rb < RBW; ++rb) {
+            const int row = r0 + rb * 16 + li;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
               const int key = j0 + kb * 16 + 4 * g + i;
               const bool vis = key <= row && key < L && (W <= 0 || row - key < W);
-              y = vis ? y : -INFINITY;
+              sc[kb][rb][i] = vis ? sc[kb][rb][i] : -INFINITY;
             }
-            sc[kb][rb][i] = y;
           }
-        }
       }
       // ---- online softmax with lazy rescale ----
       bf16x4 pb[KB][RBW];
@@ -314,7 +324,10 @@ static hipError_t launch_cfg(const FwdParams& p, hipStream_t st) {
   constexpr int BM = 4 * RW;
   const int tiles = (p.max_seqlen + BM - 1) / BM;
   dim3 grid(p.Hq, p.num_seqs, tiles), block(256);
-  fwd_kernel<DQK, DV, RW, BN><<<grid, block, 0, st>>>(p);
+  if (p.G2 != nullptr)
+    fwd_kernel<DQK, DV, RW, BN, true><<<grid, block, 0, st>>>(p);
+  else
+    fwd_kernel<DQK, DV, RW, BN, false><<<grid, block, 0, st>>>(p);
   return hipGetLastError();
 }
 
