@@ -30,6 +30,13 @@ COMMON_FLAGS = [
     "-Wno-unused-result",
 ]
 
+# Per-file extra flags.  decode.hip: keep MFMA accumulators in VGPRs; the
+# default AGPR form makes the compiler copy every accumulator to VGPRs and
+# back around the (rarely taken) rescale branch on each step.
+FILE_FLAGS = {
+    "decode.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+}
+
 
 def hipcc() -> str:
     for cand in (os.environ.get("HIPCC"), shutil.which("hipcc"), "/opt/rocm/bin/hipcc"):
@@ -44,7 +51,7 @@ def sources():
 
 def _compile(src: str, verbose: bool) -> str:
     obj = os.path.join(BUILD, os.path.basename(src) + ".o")
-    cmd = [hipcc(), *COMMON_FLAGS, "-c", src, "-o", obj]
+    cmd = [hipcc(), *COMMON_FLAGS, *FILE_FLAGS.get(os.path.basename(src), []), "-c", src, "-o", obj]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)

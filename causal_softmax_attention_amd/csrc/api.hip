@@ -306,6 +306,7 @@ int attn_decode_paged(const void* q, const int32_t* cu_seqlens_q, int num_reques
           "scales are only read with an fp8 KV cache");
   REQUIRE(head_dim == 64 || head_dim == 128, ATTN_ERR_UNSUPPORTED, "head_dim %d not supported (64, 128)",
           head_dim);
+  REQUIRE(!fp8 || head_dim == 128, ATTN_ERR_UNSUPPORTED, "the fp8 KV cache is supported with head_dim 128");
   REQUIRE(block_size == 16 || block_size == 32 || block_size == 64 || block_size == 128,
           ATTN_ERR_UNSUPPORTED, "block_size %d not supported (16, 32, 64, 128)", block_size);
   REQUIRE(num_q_heads >= 1 && num_kv_heads >= 1, ATTN_ERR_INVALID, "head counts must be positive");
@@ -354,7 +355,8 @@ int attn_decode_paged(const void* q, const int32_t* cu_seqlens_q, int num_reques
   p.R = num_requests; p.max_pages = max_pages; p.Hq = num_q_heads; p.Hkv = num_kv_heads;
   p.B = block_size; p.B_shift = __builtin_ctz((unsigned)block_size); p.split_len = lay.split_len; p.num_splits = lay.num_splits;
   p.scale_log2 = softmax_scale * attn::kLog2e;
-  hipError_t e = attn::launch_decode_splitk(p, head_dim, fp8, max_seqlen_q, s);
+  p.row_blocks = (max_seqlen_q * (num_q_heads / num_kv_heads) + 15) / 16;
+  hipError_t e = attn::launch_decode_splitk(p, head_dim, fp8, s);
   if (e != hipSuccess) return hip_fail(e, "decode launch");
 
   attn::ReduceParams r{};

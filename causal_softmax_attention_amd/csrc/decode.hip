@@ -3,7 +3,7 @@
 //
 // Method (ROCm/aiter PR #6660, commit messages and "Technical details"):
 // the keys of a request are split into segments; each (request, KV head,
-// segment) produces (acc, m, l) partials for all query rows of the request
+// segment) produces (acc, m, l) partials for the query rows of the request
 // that share the KV head.  K scales multiply the QK columns; V scales
 // multiply the probability columns after the row sum; the scaled
 // probabilities are split into a bf16 high and low part so that PV keeps
@@ -12,70 +12,121 @@
 // query whose last visible key precedes the segment stores an empty partial
 // (m = -inf, l = 0).
 //
-// gfx950 mapping: one wavefront per work item, so four independent streams
-// per workgroup and no barriers.  The wave walks its segment 32 keys at a
-// time:
-//   S^T (32 keys x 16 rows per row block) = K Q^T with
-//     v_mfma_f32_16x16x32_bf16; K is fetched straight from the pages into
-//     the A-operand layout (fp8 -> bf16 conversion is exact), Q stays in
-//     registers as the B operand for the whole segment;
-//   online softmax per query row in the base-2 domain;
-//   O^T += V^T (P v_scale)^T, twice (bf16 high and low parts); V is staged
-//     through LDS in page order and read back transposed with
-//     ds_read_b64_tr_b8 (fp8) / ds_read_b64_tr_b16 (bf16).
-// Query rows are (query token, head of the KV group) pairs, so GQA 16 with
-// one token fills one 16-row block and 4 tokens fill four.
+// gfx950 mapping: one workgroup per (segment, request, KV head) with one
+// wavefront per 16-row block of query rows; rows are (query token, head of
+// the KV group) pairs, so GQA 16 with one token is a one-wave workgroup and
+// a 4-token verify is four waves that share every K/V tile.  The segment is
+// walked 32 keys at a time through a ring of NST LDS stages:
+//   * every byte a step needs (K tile, V tile, and for fp8 the per-token
+//     scales) arrives by direct global->LDS copies (global_load_lds) from a
+//     wave-uniform page base in SGPRs plus a fixed per-lane 32-bit offset;
+//     the waves of a workgroup split the copies of a tile evenly;
+//   * the copies are issued through inline asm and awaited with an explicit
+//     vmcnt: the compiler, which does not track them, then neither drains
+//     the ring at each LDS read nor at the barrier;
+//   * page ids come through scalar loads, issued at the end of the step
+//     before the one that uses them.
+// K and V tiles are stored as 32 rows of D * elem bytes with 16-byte chunks
+// permuted per row so that the two read patterns are free of bank conflicts:
+// MFMA operand rows for K (ds_read_b128) and transposed reads for V
+// (ds_read_b64_tr_b8 for fp8, ds_read_b64_tr_b16 for bf16).
+//   fp8 cache: K bytes become bf16 with v_cvt_scalef32_pk_bf16_fp8 (exact:
+//     every e4m3 value is a bf16 value; two bytes per instruction) and
+//     S^T = K Q^T runs on v_mfma_f32_16x16x32_bf16 with the bf16 query as
+//     given.  (The fp8 MFMA could take the bytes directly, but it sums its
+//     128 products with about 2^-13 relative error, far coarser than the
+//     fp32 accumulation of the bf16 MFMA.)  V^T is converted the same way.
+//   PV: O^T += V^T (P v_scale)^T with v_mfma_f32_16x16x32_bf16, once for the
+//     bf16 high part of P v_scale and once for the low part.
 #include "common.h"
 #include "kernels.h"
 
 namespace attn {
 
+namespace {
+
+// LDS byte address of a pointer into __shared__ memory.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const LDS_AS void*)p;
+}
+
+// Direct global->LDS copies in saddr form: lane l reads sbase + voff and
+// writes its 16 (or 4) bytes at LDS address m0 + 16 l (or 4 l).  Only the
+// kernel's explicit vmcnt waits order them against LDS reads.
+__device__ __forceinline__ void dma16(const void* sbase, uint32_t voff, uint32_t m0) {
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1"
+               :: "v"(voff), "s"(sbase), "s"(m0) : "memory");
+}
+__device__ __forceinline__ void dma4(const void* sbase, uint32_t voff, uint32_t m0) {
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dword %0, %1"
+               :: "v"(voff), "s"(sbase), "s"(m0) : "memory");
+}
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  asm volatile("s_waitcnt vmcnt(%0)" :: "n"(N) : "memory");
+}
+__device__ __forceinline__ void wait_lgkm0() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
+
+// 8 e4m3fn bytes -> 8 bf16 (exact), two bytes per instruction.
 __device__ __forceinline__ bf16x8 fp8x8_to_bf16x8(i32x2 w) {
-  f32x2 a = fp8x2_to_f32<false>(w[0]), b = fp8x2_to_f32<true>(w[0]);
-  f32x2 c = fp8x2_to_f32<false>(w[1]), d = fp8x2_to_f32<true>(w[1]);
-  return bf16x8{(bf16)a[0], (bf16)a[1], (bf16)b[0], (bf16)b[1],
-                (bf16)c[0], (bf16)c[1], (bf16)d[0], (bf16)d[1]};
+  const auto a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[0], 1.0f, false);
+  const auto b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[0], 1.0f, true);
+  const auto c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[1], 1.0f, false);
+  const auto d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[1], 1.0f, true);
+  return bf16x8{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
 }
 
-__device__ __forceinline__ void lds_wave_sync() {
-  // LDS operations of one wavefront complete in order; this only stops the
-  // compiler from moving LDS accesses across the point and waits for them.
-  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+// Chunk permutations of the K and V tiles (ROWB bytes per row).
+//   K, read as MFMA rows: 16 lanes read the same logical chunk of 16
+//   consecutive rows.  128-byte rows: rows of equal parity share banks, so
+//   the 8 even (odd) rows must land on 8 different chunk positions.
+//   256-byte rows: all rows share banks, 16 different positions.
+template <int ROWB>
+__device__ __forceinline__ int swz_k(int r) {
+  if constexpr (ROWB == 256) return r & 15;
+  else return (r >> 1) & 7;
+}
+//   V, read transposed: fp8 lane groups read one chunk of rows
+//   {4g..4g+3, 16+4g..16+4g+3}; bf16 groups read two adjacent chunks of
+//   rows 4g..4g+3 (and 16+4g..).
+template <int ROWB, bool FP8>
+__device__ __forceinline__ int swz_v(int r) {
+  if constexpr (FP8) return ((r >> 1) & 3) | ((r >> 2) & 4);
+  else if constexpr (ROWB == 256) return (r & 7) << 1;
+  else return ((r >> 1) & 3) << 1;
 }
 
-// Raw bytes of one 32-key step, fetched one step ahead of their use.
-template <int D, bool FP8>
-struct StepRaw {
-  static constexpr int ES = FP8 ? 1 : 2;
-  static constexpr int KCH = (D / 4) * ES / 16;      // 16-byte K chunks per lane per key block
-  static constexpr int NCH = 32 * D * ES / 16 / 64;  // 16-byte V chunks per lane
-  i32x4 k[2][KCH];
-  i32x4 v[NCH];
-  f32x4 ks[2], vs[2];
-};
+}  // namespace
 
-template <int D, bool FP8, int RB>
-__global__ __launch_bounds__(256) void decode_splitk_kernel(DecodeParams p) {
-  using Raw = StepRaw<D, FP8>;
-  constexpr int KS = D / 32;          // k-steps of 32 over the head dim
-  constexpr int DPG = 8 * KS;         // head-dim elements per 16-lane group
-  constexpr int ES = Raw::ES;         // bytes per cache element
-  constexpr int ROWB = D * ES;        // bytes per cached token row
-  constexpr int VROW = ROWB + 16;     // padded LDS row stride
-  constexpr int CPR = ROWB / 16;      // 16-byte chunks per row
-  constexpr int DB = D / 16;          // 16-wide output column blocks
-  __shared__ __attribute__((aligned(16))) uint8_t v_lds_all[4][32 * VROW];
+template <int D, bool FP8, int W, int NST>
+__global__ __launch_bounds__(64 * W) void decode_splitk_kernel(DecodeParams p) {
+  constexpr int ES = FP8 ? 1 : 2;      // bytes per cache element
+  constexpr int ROWB = D * ES;         // bytes per cached token row
+  constexpr int CPR = ROWB / 16;       // 16-byte chunks per row
+  constexpr int RPI = 1024 / ROWB;     // rows per copy instruction (64 lanes x 16 B)
+  constexpr int NT = 32 * ROWB / 1024; // copy instructions per 32-row tile
+  constexpr int NTW = NT / W;          // ... issued by each wave
+  static_assert(NT % W == 0 && (ROWB == 128 || ROWB == 256), "tile split");
+  constexpr int KS = D / 32;           // bf16 k-steps of 32 over the head dim
+  constexpr int DPG = 8 * KS;          // head-dim elements per 16-lane group
+  constexpr int KCH = DPG * ES / 16;   // 16-byte K chunks per lane and key block
+  constexpr int DB = D / 16;           // 16-wide output column blocks
+  constexpr int TILE = 32 * ROWB;
+  constexpr int SCB = FP8 ? 256 : 0;   // bytes of one scale copy (64 lanes x 4 B)
+  constexpr int STAGE = 2 * TILE + W * 2 * SCB;
+  constexpr int LPS = 2 * NTW + (FP8 ? 2 : 0);   // copies per step and wave
+  static_assert(NST == 2 || NST == 3, "ring depth");
+  static_assert((NST - 2) * LPS <= 63, "vmcnt range");
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[NST * STAGE];
 
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
-  const int li = lane & 15, g = lane >> 4;
-  uint8_t* v_lds = v_lds_all[wave];
+  const int wave = W == 1 ? 0 : __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63, li = lane & 15, g = lane >> 4;
 
-  long item = (long)blockIdx.x * 4 + wave;
-  const int kvh = (int)(item % p.Hkv);
+  int item = blockIdx.x;
+  const int kvh = item % p.Hkv;
   item /= p.Hkv;
-  const int r = (int)(item % p.R);
-  const int s = (int)(item / p.R);
-  if (s >= p.num_splits) return;
+  const int r = item % p.R;
+  const int s = item / p.R;
   const int L = p.seq_lens[r];
   const int k_begin = s * p.split_len;
   if (k_begin >= L) return;            // segment beyond this request: none
@@ -83,169 +134,175 @@ __global__ __launch_bounds__(256) void decode_splitk_kernel(DecodeParams p) {
   const int qs = p.cu_q[r];
   const int qlen = p.cu_q[r + 1] - qs;
   const int G = p.Hq / p.Hkv;
-  const long head_stride = (long)p.B * D;              // elements per (page, kv head)
-  const long page_stride = (long)p.Hkv * head_stride;
-  const uint8_t* kc = reinterpret_cast<const uint8_t*>(p.k_cache) + kvh * head_stride * ES;
-  const uint8_t* vc = reinterpret_cast<const uint8_t*>(p.v_cache) + kvh * head_stride * ES;
+  if (qlen <= 0) return;               // whole workgroup, before any barrier
+  const bool active = wave * 16 < qlen * G;   // wave-uniform; idle waves still copy
 
-  // Page ids are wave-uniform per 32-key step (a step spans at most two
-  // pages, and one when pages hold 32 or more keys), so they come through
-  // scalar loads, one step ahead of the vector loads that use them.  Keys
-  // past seq_len read the request's last page and are masked later: every
-  // load stays unconditional and in range, so several steps can be in flight.
+  // ---- copy set-up: page bases (SGPR) and fixed per-lane offsets ----
   const int bsh = p.B_shift, bmask = p.B - 1;   // page size is a power of two
   const int last_page = (L - 1) >> bsh;
-  const int32_t* bt = p.block_table + (long)r * p.max_pages;
-  struct Pages { int a, b; };                    // pages of keys kk and kk+16
+  // block-table reads are wave-uniform: the constant address space makes
+  // them scalar loads
+  const __attribute__((address_space(4))) int32_t* bt =
+      (const __attribute__((address_space(4))) int32_t*)(p.block_table + (long)r * p.max_pages);
+  const long page_bytes = (long)p.Hkv * p.B * ROWB;
+  const long head_bytes = (long)kvh * p.B * ROWB;
+  const uint8_t* kc = reinterpret_cast<const uint8_t*>(p.k_cache) + head_bytes;
+  const uint8_t* vc = reinterpret_cast<const uint8_t*>(p.v_cache) + head_bytes;
+  uint32_t voff_k[NTW], voff_v[NTW];
+#pragma unroll
+  for (int i = 0; i < NTW; ++i) {
+    const int r0 = (wave + W * i) * RPI;
+    const int row = r0 + lane / CPR;
+    voff_k[i] = (uint32_t)(((r0 & 15) + lane / CPR) * ROWB + 16 * ((lane % CPR) ^ swz_k<ROWB>(row)));
+    voff_v[i] = (uint32_t)(((r0 & 15) + lane / CPR) * ROWB + 16 * ((lane % CPR) ^ swz_v<ROWB, FP8>(row)));
+  }
+  const uint32_t smem_lds = lds_addr(smem);
+
+  struct Pages { int a, b; };          // pages of keys kk .. kk+15 and kk+16 .. kk+31
   auto pages_of = [&](int kk) {
     Pages pp;
-    pp.a = __builtin_amdgcn_readfirstlane(bt[min(kk >> bsh, last_page)]);
-    pp.b = __builtin_amdgcn_readfirstlane(bt[min((kk + 16) >> bsh, last_page)]);
+    pp.a = bt[min(kk >> bsh, last_page)];
+    pp.b = bt[min((kk + 16) >> bsh, last_page)];
     return pp;
   };
-
-  auto fetch = [&](int kk, Pages pp, Raw& raw) {
+  // Copies of the 32-key step at kk into ring stage st.  Keys past seq_len
+  // read rows of the request's last page (in range; masked later).
+  auto fetch = [&](int kk, Pages pg, int st) {
+    const long ra = pg.a * page_bytes + (long)(kk & bmask) * ROWB;
+    const long rb = pg.b * page_bytes + (long)((kk + 16) & bmask) * ROWB;
+    const uint32_t stage = smem_lds + st * STAGE;
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      const int key = kk + kb * 16 + li;
-      const long pid = kb ? pp.b : pp.a;
-      const long off = (pid * page_stride + (long)(key & bmask) * D + g * DPG) * ES;
-#pragma unroll
-      for (int c = 0; c < Raw::KCH; ++c) raw.k[kb][c] = *reinterpret_cast<const i32x4*>(kc + off + 16 * c);
-      if constexpr (FP8) {
-        const int k4 = kk + kb * 16 + 4 * g;
-        const long so = ((pid * p.Hkv + kvh) << bsh) + (k4 & bmask);
-        raw.ks[kb] = *reinterpret_cast<const f32x4*>(p.k_scale + so);
-        raw.vs[kb] = *reinterpret_cast<const f32x4*>(p.v_scale + so);
-      }
+    for (int i = 0; i < NTW; ++i) {
+      const int ci = wave + W * i;
+      const long ro = ci * RPI < 16 ? ra : rb;
+      dma16(kc + ro, voff_k[i], stage + ci * 1024);
+      dma16(vc + ro, voff_v[i], stage + TILE + ci * 1024);
     }
-#pragma unroll
-    for (int c = 0; c < Raw::NCH; ++c) {
-      const int ch = lane + 64 * c;
-      const int kr = ch / CPR, col = (ch % CPR) * 16;
-      const int key = kk + kr;
-      const long pid = kr < 16 ? pp.a : pp.b;
-      const long off = (pid * page_stride + (long)(key & bmask) * D) * ES + col;
-      raw.v[c] = *reinterpret_cast<const i32x4*>(vc + off);
+    if constexpr (FP8) {
+      const int pid = (lane & 16) ? pg.b : pg.a;
+      const int slot = ((kk + (lane & 16)) & bmask) + (lane & 15);
+      const uint32_t so = (uint32_t)((((pid * p.Hkv + kvh) << bsh) + slot) * 4);
+      const uint32_t sc = stage + 2 * TILE + wave * 2 * SCB;
+      dma4(p.k_scale, so, sc);
+      dma4(p.v_scale, so, sc + SCB);
     }
   };
 
-  // Q rows as the B operand: lane (row li, group g) holds the head-dim
-  // elements [g*DPG, g*DPG + DPG) in k-step order.
-  bf16x8 qop[RB][KS];
-  int pos[RB];
-  bool rvalid[RB];
+  // ---- prologue: first NST-1 steps in flight, then the query ----
+  Pages nxt = pages_of(k_begin);
 #pragma unroll
-  for (int rb = 0; rb < RB; ++rb) {
-    const int rho = rb * 16 + li;
-    const int t = rho / G;
-    rvalid[rb] = t < qlen;
-    pos[rb] = L - qlen + t;
-    if (rvalid[rb]) {
-      const bf16* qp = reinterpret_cast<const bf16*>(p.q) +
-                       ((long)(qs + t) * p.Hq + (long)kvh * G + rho % G) * D + g * DPG;
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) qop[rb][ks] = *reinterpret_cast<const bf16x8*>(qp + 8 * ks);
-    } else {
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) qop[rb][ks] = bf16x8{};
-    }
+  for (int j = 0; j < NST - 1; ++j) {
+    const int kk = k_begin + 32 * j;
+    if (kk < k_end) fetch(kk, nxt, j);
+    nxt = pages_of(kk + 32);
   }
 
-  f32x4 oacc[RB][DB];
-  float m_run[RB], l_run[RB];
+  // this lane's query row (li of the wave's block) and its Q operand
+  const int rho = wave * 16 + li;
+  const int t = rho / G;
+  const bool rvalid = active && t < qlen;
+  const int pos = L - qlen + t;                       // last key this row sees
+  bf16x8 qop[KS];
+  {
+    const bf16* qp = reinterpret_cast<const bf16*>(p.q) +
+                     ((long)(qs + min(t, qlen - 1)) * p.Hq + (long)kvh * G + rho % G) * D + g * DPG;
 #pragma unroll
-  for (int rb = 0; rb < RB; ++rb) {
-    m_run[rb] = kNegBig;
-    l_run[rb] = 0.f;
+    for (int ks = 0; ks < KS; ++ks)
+      qop[ks] = rvalid ? *reinterpret_cast<const bf16x8*>(qp + 8 * ks) : bf16x8{};
+    // consume the loads here, while only prologue copies are in flight, so
+    // that the compiler's own wait for them does not land inside the loop
 #pragma unroll
-    for (int db = 0; db < DB; ++db) oacc[rb][db] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int ks = 0; ks < KS; ++ks) asm volatile("" :: "v"(qop[ks]));
   }
 
-  auto compute = [&](int kk, const Raw& raw) {
-    // ---- V of the 32 keys into LDS, zeros past seq_len (NaN-safe select) ----
+  f32x4 oacc[DB];
+  float m_run = kNegBig, l_run = 0.f;
 #pragma unroll
-    for (int c = 0; c < Raw::NCH; ++c) {
-      const int ch = lane + 64 * c;
-      const int kr = ch / CPR, col = (ch % CPR) * 16;
-      const i32x4 z = {0, 0, 0, 0};
-      *reinterpret_cast<i32x4*>(v_lds + kr * VROW + col) = (kk + kr < L) ? raw.v[c] : z;
-    }
-    // ---- scores S^T = K Q^T ----
-    f32x4 sc[2][RB];
+  for (int db = 0; db < DB; ++db) oacc[db] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const int vis_all = L - qlen;        // keys below this are visible to every row
+
+  auto compute = [&](int kk, int st) {
+    const uint8_t* Kt = smem + st * STAGE;
+    const uint8_t* Vt = Kt + TILE;
+    const float* Sc = reinterpret_cast<const float*>(Kt + 2 * TILE + wave * 2 * SCB);
+    const bool need_mask = kk + 31 > vis_all;   // uniform: a key past some row's position
+    // ---- scores S^T = K Q^T (C lane: row li, keys kk+kb*16+4g+i) ----
+    f32x4 sc[2];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
-      bf16x8 kop[KS];
-      if constexpr (FP8) {
+      const int row = kb * 16 + li;
+      i32x4 kraw[KCH];
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-          const i32x4 w = raw.k[kb][ks / 2];
-          kop[ks] = fp8x8_to_bf16x8((ks & 1) ? i32x2{w[2], w[3]} : i32x2{w[0], w[1]});
+      for (int c = 0; c < KCH; ++c)
+        kraw[c] = *reinterpret_cast<const i32x4*>(Kt + row * ROWB + 16 * ((g * KCH + c) ^ swz_k<ROWB>(row)));
+      f32x4 a = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        bf16x8 kop;
+        if constexpr (FP8) {
+          const i32x4 w = kraw[ks / 2];
+          kop = fp8x8_to_bf16x8(i32x2{w[(ks & 1) * 2], w[(ks & 1) * 2 + 1]});
+        } else {
+          kop = __builtin_bit_cast(bf16x8, kraw[ks]);
         }
-      } else {
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) kop[ks] = __builtin_bit_cast(bf16x8, raw.k[kb][ks]);
+        a = mfma16x16x32(kop, qop[ks], a);
       }
-#pragma unroll
-      for (int rb = 0; rb < RB; ++rb) {
-        f32x4 a = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) a = mfma16x16x32(kop[ks], qop[rb][ks], a);
-        sc[kb][rb] = a;
-      }
+      sc[kb] = a;
     }
-    // ---- K scales on the score columns; mask (select: slots past seq_len may be NaN) ----
-    float ksc[2][4], vsc[2][4];
+    // ---- scale (softmax scale x per-token K scale), mask ----
+    float x[2][4], vsc[2][4];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+    for (int kb = 0; kb < 2; ++kb) {
+      f32x4 ks4 = {1.f, 1.f, 1.f, 1.f}, vs4 = {1.f, 1.f, 1.f, 1.f};
+      if constexpr (FP8) {
+        ks4 = *reinterpret_cast<const f32x4*>(Sc + kb * 16 + 4 * g);
+        vs4 = *reinterpret_cast<const f32x4*>(Sc + 64 + kb * 16 + 4 * g);
+      }
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const bool ok = kk + kb * 16 + 4 * g + i < L;
-        ksc[kb][i] = FP8 ? (ok ? raw.ks[kb][i] : 0.f) * p.scale_log2 : p.scale_log2;
-        vsc[kb][i] = FP8 ? (ok ? raw.vs[kb][i] : 0.f) : 1.f;
+        vsc[kb][i] = vs4[i];
+        x[kb][i] = sc[kb][i] * (p.scale_log2 * ks4[i]);
       }
-    // ---- online softmax; P' = P * v_scale split into bf16 hi + lo ----
-    bf16x8 phi[RB], plo[RB];
-#pragma unroll
-    for (int rb = 0; rb < RB; ++rb) {
-      float x[2][4];
-      float mx = -INFINITY;
+    }
+    if (need_mask) {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int key = kk + kb * 16 + 4 * g + i;
-          const bool vis = key < L && key <= pos[rb];
-          x[kb][i] = vis ? sc[kb][rb][i] * ksc[kb][i] : -INFINITY;
-          mx = fmaxf(mx, x[kb][i]);
+          const bool ok = key < L;                    // scale slots past seq_len may be NaN
+          x[kb][i] = (ok && key <= pos) ? x[kb][i] : -INFINITY;
+          vsc[kb][i] = ok ? vsc[kb][i] : 0.f;
         }
-      mx = xgroup_max(mx);
-      if (__any(mx > m_run[rb] + kRescaleSlack)) {
-        // raise the running max only when a score passes it by more than
-        // the slack, so exp2(score - max) stays below 2^8 in between
-        const float m_new = fmaxf(m_run[rb], mx);
-        const float alpha = fast_exp2(m_run[rb] - m_new);
-        l_run[rb] *= alpha;
-#pragma unroll
-        for (int db = 0; db < DB; ++db) oacc[rb][db] *= alpha;
-        m_run[rb] = m_new;
-      }
-      const float m_new = m_run[rb];
-      float rs = 0.f;
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float pv = fast_exp2(x[kb][i] - m_new);
-          rs += pv;
-          const float pp = pv * vsc[kb][i];
-          const bf16 h = (bf16)pp;
-          phi[rb][kb * 4 + i] = h;
-          plo[rb][kb * 4 + i] = (bf16)(pp - (float)h);
-        }
-      l_run[rb] += xgroup_sum(rs);
     }
-    lds_wave_sync();
+    // ---- online softmax (lazy rescale); P' = P * v_scale as bf16 hi + lo ----
+    float mx = fmaxf(fmaxf(fmaxf(x[0][0], x[0][1]), fmaxf(x[0][2], x[0][3])),
+                     fmaxf(fmaxf(x[1][0], x[1][1]), fmaxf(x[1][2], x[1][3])));
+    mx = xgroup_max(mx);
+    if (__any(mx > m_run + kRescaleSlack)) {
+      // raise the running max only when a score passes it by more than
+      // the slack, so exp2(score - max) stays below 2^8 in between
+      const float m_new = fmaxf(m_run, mx);
+      const float alpha = fast_exp2(m_run - m_new);
+      l_run *= alpha;
+#pragma unroll
+      for (int db = 0; db < DB; ++db) oacc[db] *= alpha;
+      m_run = m_new;
+    }
+    bf16x8 phi, plo;
+    float rs = 0.f;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float pv = fast_exp2(x[kb][i] - m_run);
+        rs += pv;
+        const float pp = pv * vsc[kb][i];
+        const bf16 h = (bf16)pp;
+        phi[kb * 4 + i] = h;
+        plo[kb * 4 + i] = (bf16)(pp - (float)h);
+      }
+    l_run += xgroup_sum(rs);
     // ---- O^T += V^T P'^T (hi and lo) ----
 #pragma unroll
     for (int db = 0; db < DB; ++db) {
@@ -253,86 +310,103 @@ __global__ __launch_bounds__(256) void decode_splitk_kernel(DecodeParams p) {
       if constexpr (FP8) {
         const int j = li >> 1, c = li & 1;
         const int row = (j < 4) ? 4 * g + j : 16 + 4 * g + (j - 4);
-        vop = fp8x8_to_bf16x8(lds_read_tr8(v_lds + row * VROW + db * 16 + 8 * c));
+        vop = fp8x8_to_bf16x8(lds_read_tr8(Vt + row * ROWB + 16 * (db ^ swz_v<ROWB, FP8>(row)) + 8 * c));
       } else {
         const int mm = li >> 2, c = li & 3;
-        const bf16* b0 = reinterpret_cast<const bf16*>(v_lds + (4 * g + mm) * VROW) + db * 16 + 4 * c;
-        const bf16* b1 = reinterpret_cast<const bf16*>(v_lds + (16 + 4 * g + mm) * VROW) + db * 16 + 4 * c;
+        const int r0 = 4 * g + mm, r1 = 16 + 4 * g + mm, q = 2 * db + (c >> 1);
+        const bf16* b0 = reinterpret_cast<const bf16*>(Vt + r0 * ROWB + 16 * (q ^ swz_v<ROWB, FP8>(r0)) + 8 * (c & 1));
+        const bf16* b1 = reinterpret_cast<const bf16*>(Vt + r1 * ROWB + 16 * (q ^ swz_v<ROWB, FP8>(r1)) + 8 * (c & 1));
         vop = concat(lds_read_tr16(b0), lds_read_tr16(b1));
       }
-#pragma unroll
-      for (int rb = 0; rb < RB; ++rb) {
-        oacc[rb][db] = mfma16x16x32(vop, phi[rb], oacc[rb][db]);
-        oacc[rb][db] = mfma16x16x32(vop, plo[rb], oacc[rb][db]);
-      }
+      oacc[db] = mfma16x16x32(vop, phi, oacc[db]);
+      oacc[db] = mfma16x16x32(vop, plo, oacc[db]);
     }
-    lds_wave_sync();
   };
 
-  if constexpr (RB <= 2) {
-    // ---- two-deep software pipeline over 32-key steps ----
-    // The prefetch is unconditional (its addresses are clamped in range):
-    // a conditional one would make the compiler drain every outstanding
-    // load at the branch join, serialising the pipeline.
-    Raw ra, rb_;
-    fetch(k_begin, pages_of(k_begin), ra);
-    Pages nxt = pages_of(k_begin + 32);
-    for (int kk = k_begin; kk < k_end; kk += 64) {
-      fetch(kk + 32, nxt, rb_);
-      nxt = pages_of(kk + 64);
-      compute(kk, ra);
-      if (kk + 32 >= k_end) break;
-      fetch(kk + 64, nxt, ra);
-      nxt = pages_of(kk + 96);
-      compute(kk + 32, rb_);
+  // ---- one step of the ring: wait for step kk, release it to the
+  // workgroup, put step kk + 32 (NST-1) in flight, compute step kk ----
+  auto step = [&](int kk, int st) {
+    if constexpr (NST == 3) {
+      if (kk + 32 < k_end) wait_vm<LPS>(); else wait_vm<0>();
+    } else {
+      wait_vm<0>();
     }
-  } else {
-    // Many query rows: more math per byte and no registers left for a
-    // second buffer; fetch and compute one step at a time.
-    Raw ra;
-    for (int kk = k_begin; kk < k_end; kk += 32) {
-      fetch(kk, pages_of(kk), ra);
-      compute(kk, ra);
+    if (kk + 32 > L) {
+      // last step of the request: zero the V rows past seq_len that this
+      // wave copied (their bytes may be NaN; P is 0 there, but 0 * NaN is not)
+      uint8_t* Vt = smem + st * STAGE + TILE;
+#pragma unroll
+      for (int i = 0; i < NTW; ++i) {
+        const int ci = wave + W * i;
+        if (kk + ci * RPI + lane / CPR >= L)
+          *reinterpret_cast<i32x4*>(Vt + ci * 1024 + 16 * lane) = i32x4{0, 0, 0, 0};
+      }
+    }
+    if constexpr (W > 1) {
+      wait_lgkm0();
+      __builtin_amdgcn_s_barrier();
+      asm volatile("" ::: "memory");
+    }
+    const int kn = kk + 32 * (NST - 1);
+    if (kn < k_end) fetch(kn, nxt, (st + NST - 1) % NST);
+    if (active) compute(kk, st);
+    // Page ids of the next copy: issued only now, after this step's LDS
+    // reads, because a scalar load can only be awaited with lgkmcnt(0),
+    // which would also wait for any LDS read issued after it.  The empty
+    // asm keeps the compiler from hoisting these (invariant) loads.
+    int kq = kn + 32;
+    asm volatile("" : "+s"(kq) :: "memory");
+    nxt = pages_of(kq);
+  };
+
+  for (int kk = k_begin;; kk += 32 * NST) {
+    step(kk, 0);
+    if (kk + 32 >= k_end) break;
+    step(kk + 32, 1);
+    if (kk + 64 >= k_end) break;
+    if constexpr (NST == 3) {
+      step(kk + 64, 2);
+      if (kk + 96 >= k_end) break;
     }
   }
+  wait_vm<0>();
 
   // ---- store the partial ----
-#pragma unroll
-  for (int rb = 0; rb < RB; ++rb) {
-    if (!rvalid[rb]) continue;
-    const int rho = rb * 16 + li;
-    const long grow = (long)(qs + rho / G) * p.Hq + (long)kvh * G + rho % G;
+  if (rvalid) {
+    const long grow = (long)(qs + t) * p.Hq + (long)kvh * G + rho % G;
     float* a = p.acc + (grow * p.num_splits + s) * D;
 #pragma unroll
-    for (int db = 0; db < DB; ++db) *reinterpret_cast<f32x4*>(a + db * 16 + 4 * g) = oacc[rb][db];
+    for (int db = 0; db < DB; ++db) *reinterpret_cast<f32x4*>(a + db * 16 + 4 * g) = oacc[db];
     if (g == 0) {
-      const bool empty = !(l_run[rb] > 0.f);
-      p.m[grow * p.num_splits + s] = empty ? -INFINITY : m_run[rb] * kLn2;
-      p.l[grow * p.num_splits + s] = empty ? 0.f : l_run[rb];
+      const bool empty = !(l_run > 0.f);
+      p.m[grow * p.num_splits + s] = empty ? -INFINITY : m_run * kLn2;
+      p.l[grow * p.num_splits + s] = empty ? 0.f : l_run;
     }
   }
 }
 
-template <int D, bool FP8>
-static hipError_t launch_rb(const DecodeParams& p, int rb, hipStream_t st) {
+#ifndef DECODE_NST
+#define DECODE_NST 2
+#endif
+
+template <int D, bool FP8, int W>
+static hipError_t launch_t(const DecodeParams& p, hipStream_t st) {
   const long items = (long)p.R * p.Hkv * p.num_splits;
-  dim3 grid((unsigned)((items + 3) / 4)), block(256);
-  switch (rb) {
-    case 1: decode_splitk_kernel<D, FP8, 1><<<grid, block, 0, st>>>(p); break;
-    case 2: decode_splitk_kernel<D, FP8, 2><<<grid, block, 0, st>>>(p); break;
-    case 3: decode_splitk_kernel<D, FP8, 3><<<grid, block, 0, st>>>(p); break;
-    case 4: decode_splitk_kernel<D, FP8, 4><<<grid, block, 0, st>>>(p); break;
-    default: return hipErrorInvalidValue;
-  }
+  decode_splitk_kernel<D, FP8, W, DECODE_NST><<<dim3((unsigned)items), dim3(64 * W), 0, st>>>(p);
   return hipGetLastError();
 }
 
-hipError_t launch_decode_splitk(const DecodeParams& p, int head_dim, bool fp8,
-                                int max_seqlen_q, hipStream_t st) {
-  const int rows = max_seqlen_q * (p.Hq / p.Hkv);
-  const int rb = (rows + 15) / 16;
-  if (head_dim == 128) return fp8 ? launch_rb<128, true>(p, rb, st) : launch_rb<128, false>(p, rb, st);
-  if (head_dim == 64) return fp8 ? launch_rb<64, true>(p, rb, st) : launch_rb<64, false>(p, rb, st);
+template <int D, bool FP8>
+static hipError_t launch_w(const DecodeParams& p, hipStream_t st) {
+  if (p.row_blocks <= 1) return launch_t<D, FP8, 1>(p, st);
+  if (p.row_blocks == 2) return launch_t<D, FP8, 2>(p, st);
+  return launch_t<D, FP8, 4>(p, st);
+}
+
+hipError_t launch_decode_splitk(const DecodeParams& p, int head_dim, bool fp8, hipStream_t st) {
+  if (p.row_blocks > 4) return hipErrorInvalidValue;
+  if (head_dim == 128) return fp8 ? launch_w<128, true>(p, st) : launch_w<128, false>(p, st);
+  if (head_dim == 64 && !fp8) return launch_w<64, false>(p, st);
   return hipErrorInvalidValue;
 }
 

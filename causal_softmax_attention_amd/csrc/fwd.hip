@@ -34,6 +34,9 @@
 #ifndef FWD_BN_SMALL
 #define FWD_BN_SMALL 64
 #endif
+#ifndef FWD_NST_SMALL
+#define FWD_NST_SMALL 2
+#endif
 
 namespace attn {
 
@@ -87,22 +90,19 @@ __device__ __forceinline__ int xcd_head(int x, int Hq) {
   return (x % 8) * (Hq / 8) + x / 8;
 }
 
-template <int DQK, int DV, int RW, int BN, bool GATED>
+template <int DQK, int DV, int RW, int BN, int NST, bool GATED>
 __global__ __launch_bounds__(256) void fwd_kernel(FwdParams p) {
   constexpr int BM = 4 * RW;
   constexpr int RBW = RW / 16;       // 16-row blocks per wave
   constexpr int KB = BN / 16;        // 16-key blocks per tile
   constexpr int KS = DQK / 32;       // k-steps over d_qk
   constexpr int DB = DV / 16;        // 16-wide output column blocks
-  constexpr int KROW = DQK + 8;      // LDS row strides (elements)
-  constexpr int VROW = DV + 16;
-  constexpr int KCH = BN * DQK / 8 / 256;   // 16-byte chunks per thread per tile
-  constexpr int VCH = BN * DV / 8 / 256;
+  constexpr int KRB = DQK * 2, VRB = DV * 2;   // bytes per K / V row
   static_assert(KB % 2 == 0, "PV consumes keys in pairs of 16-key blocks");
-  static_assert(KCH * 256 * 8 == BN * DQK && VCH * 256 * 8 == BN * DV, "tile must split evenly");
-  __shared__ __attribute__((aligned(16))) bf16 k_lds[2][BN * KROW];
-  __shared__ __attribute__((aligned(16))) bf16 v_lds[2][BN * VROW];
-  __shared__ __attribute__((aligned(16))) float gk_lds[2][BN];
+  static_assert(NST >= 2 && BN <= 64, "ring of at least two stages; gate copy is one lane per key");
+  __shared__ __attribute__((aligned(1024))) uint8_t k_lds[NST][BN * KRB];
+  __shared__ __attribute__((aligned(1024))) uint8_t v_lds[NST][BN * VRB];
+  __shared__ __attribute__((aligned(16))) float gk_lds[NST][4][64];   // one copy per wave
 
   const int h = xcd_head(blockIdx.x, p.Hq), n = blockIdx.y;
   const int tile = gridDim.z - 1 - blockIdx.z;
@@ -115,7 +115,6 @@ __global__ __launch_bounds__(256) void fwd_kernel(FwdParams p) {
   const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int li = lane & 15, g = lane >> 4;
   const int W = p.window;
-  constexpr bool gated = GATED;
   const float c = p.scale_log2;
 
   const int r0 = i0 + wave * RW;                 // first row of this wave
@@ -134,7 +133,7 @@ __global__ __launch_bounds__(256) void fwd_kernel(FwdParams p) {
       const bf16* qp = reinterpret_cast<const bf16*>(p.q) + ((long)(seq0 + row) * p.Hq + h) * DQK + 8 * g;
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) qop[rb][ks] = *reinterpret_cast<const bf16x8*>(qp + 32 * ks);
-      gq[rb] = gated ? p.G2[(long)(seq0 + row) * p.Hq + h] : 0.f;
+      gq[rb] = GATED ? p.G2[(long)(seq0 + row) * p.Hq + h] : 0.f;
     } else {
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) qop[rb][ks] = bf16x8{};
@@ -150,59 +149,47 @@ __global__ __launch_bounds__(256) void fwd_kernel(FwdParams p) {
   const int kv_hi = min(L, i0 + BM);
   const int t_begin = kv_lo / BN, t_end = (kv_hi + BN - 1) / BN;
 
-  const bf16* kbase = reinterpret_cast<const bf16*>(p.k) + ((long)seq0 * p.Hkv + kvh) * DQK;
-  const bf16* vbase = reinterpret_cast<const bf16*>(p.v) + ((long)seq0 * p.Hkv + kvh) * DV;
-  const long kstride = (long)p.Hkv * DQK, vstride = (long)p.Hkv * DV;
+  const uint8_t* kbase = reinterpret_cast<const uint8_t*>(p.k) + ((long)seq0 * p.Hkv + kvh) * KRB;
+  const uint8_t* vbase = reinterpret_cast<const uint8_t*>(p.v) + ((long)seq0 * p.Hkv + kvh) * VRB;
+  const long kstride = (long)p.Hkv * KRB, vstride = (long)p.Hkv * VRB;
 
-  // ---- register staging of one K/V tile (global -> regs -> LDS) ----
-  i32x4 kreg[KCH], vreg[VCH];
-  float gkreg = 0.f;
-  auto fetch = [&](int j0) {
-#pragma unroll
-    for (int cc = 0; cc < KCH; ++cc) {
-      const int ch = tid + 256 * cc;
-      const int kr = ch / (DQK / 8), col = (ch % (DQK / 8)) * 8;
-      const int key = min(j0 + kr, L - 1);       // rows past the end: any valid row
-      kreg[cc] = *reinterpret_cast<const i32x4*>(kbase + (long)key * kstride + col);
+  // K/V tiles (and each wave's copy of the key-side gate terms) go global ->
+  // LDS directly, NST-1 tiles ahead of the math, into a ring of NST stages.
+  // Every wave issues the same number of loads per tile, so the wait for
+  // the oldest tile is an exact vmcnt.
+  constexpr int LOADS_PER_TILE = (BN * KRB + BN * VRB) / 4096 + (GATED ? 1 : 0);
+  const int G2_tok_stride = p.Hq;
+  TileDma<KRB, BN> kdma;
+  TileDma<VRB, BN> vdma;
+  kdma.init(kstride, wave, lane);
+  vdma.init(vstride, wave, lane);
+  auto fetch = [&](int st, int j0) {
+    kdma.issue(kbase, kstride, j0, L, k_lds[st], wave);
+    vdma.issue(vbase, vstride, j0, L, v_lds[st], wave);
+    if constexpr (GATED) {
+      const float* src = p.G2 + (long)(seq0 + min(j0 + lane, L - 1)) * G2_tok_stride + h;
+      __builtin_amdgcn_global_load_lds((const void __attribute__((address_space(1)))*)src,
+                                       (void LDS_AS*)(&gk_lds[st][wave][0]), 4, 0, 0);
     }
-#pragma unroll
-    for (int cc = 0; cc < VCH; ++cc) {
-      const int ch = tid + 256 * cc;
-      const int kr = ch / (DV / 8), col = (ch % (DV / 8)) * 8;
-      const int key = min(j0 + kr, L - 1);
-      vreg[cc] = *reinterpret_cast<const i32x4*>(vbase + (long)key * vstride + col);
-    }
-    if (gated && tid < BN) gkreg = p.G2[(long)(seq0 + min(j0 + tid, L - 1)) * p.Hq + h];
   };
-  auto stash = [&](int buf, int j0) {
-    const i32x4 z = {0, 0, 0, 0};
-    const bool tail = j0 + BN > L;               // zero-fill rows past the end (last tile only)
-#pragma unroll
-    for (int cc = 0; cc < KCH; ++cc) {
-      const int ch = tid + 256 * cc;
-      const int kr = ch / (DQK / 8), col = (ch % (DQK / 8)) * 8;
-      *reinterpret_cast<i32x4*>(&k_lds[buf][kr * KROW + col]) = (tail && j0 + kr >= L) ? z : kreg[cc];
-    }
-#pragma unroll
-    for (int cc = 0; cc < VCH; ++cc) {
-      const int ch = tid + 256 * cc;
-      const int kr = ch / (DV / 8), col = (ch % (DV / 8)) * 8;
-      *reinterpret_cast<i32x4*>(&v_lds[buf][kr * VROW + col]) = (tail && j0 + kr >= L) ? z : vreg[cc];
-    }
-    if (gated && tid < BN) gk_lds[buf][tid] = gkreg;
+  auto wait_tiles_in_flight = [&](int n) {   // oldest tile landed when <= n tiles remain in flight
+    if (n <= 0) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    else if (n == 1) asm volatile("s_waitcnt vmcnt(%0)" :: "n"(LOADS_PER_TILE) : "memory");
+    else asm volatile("s_waitcnt vmcnt(%0)" :: "n"(2 * LOADS_PER_TILE) : "memory");
   };
 
-  fetch(t_begin * BN);
-  stash(0, t_begin * BN);
-  __syncthreads();
+  // prologue: tiles t_begin .. t_begin+NST-2
+#pragma unroll
+  for (int s = 0; s < NST - 1; ++s)
+    if (t_begin + s < t_end) fetch(s, (t_begin + s) * BN);
 
   for (int t = t_begin; t < t_end; ++t) {
     const int j0 = t * BN;
-    const int buf = (t - t_begin) & 1;
-    const bool more = t + 1 < t_end;
-    // Unconditional (addresses are clamped in range) so the compiler does not
-    // drain the loads at a branch join before the math below.
-    fetch(j0 + BN);
+    const int st = (t - t_begin) % NST;
+    // tiles issued after this one and still possibly in flight
+    wait_tiles_in_flight(min(NST - 2, t_end - 1 - t));
+    __syncthreads();
+    if (t + NST - 1 < t_end) fetch((t - t_begin + NST - 1) % NST, (t + NST - 1) * BN);
 
     // No branch around the math: a tile that is wholly masked for this
     // wave's rows goes through the masked path and contributes zeros.  (A
@@ -211,8 +198,9 @@ __global__ __launch_bounds__(256) void fwd_kernel(FwdParams p) {
     {
       const bool need_mask = (j0 + BN - 1 > r0) || (W > 0 && r_last - j0 >= W) || (j0 + BN > L) ||
                              (r_last < r0 + RW - 1);
-      const bf16* kl = k_lds[buf];
-      const bf16* vl = v_lds[buf];
+      const uint8_t* kl = k_lds[st];
+      const uint8_t* vl = v_lds[st];
+      const float* gkl = gk_lds[st][wave];
       // ---- S^T = K Q^T ----
       f32x4 sc[KB][RBW];
 #pragma unroll
@@ -221,7 +209,7 @@ __global__ __launch_bounds__(256) void fwd_kernel(FwdParams p) {
         for (int rb = 0; rb < RBW; ++rb) sc[kb][rb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
-          const bf16x8 a = lds_read8(kl + (kb * 16 + li) * KROW + ks * 32 + 8 * g);
+          const bf16x8 a = *reinterpret_cast<const bf16x8*>(kl + tile_off<KRB>(kb * 16 + li, 64 * ks + 16 * g));
 #pragma unroll
           for (int rb = 0; rb < RBW; ++rb) sc[kb][rb] = mfma16x16x32(a, qop[rb][ks], sc[kb][rb]);
         }
@@ -230,7 +218,7 @@ __global__ __launch_bounds__(256) void fwd_kernel(FwdParams p) {
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb) {
         f32x4 gk = {0.f, 0.f, 0.f, 0.f};
-        if constexpr (GATED) gk = *reinterpret_cast<const f32x4*>(&gk_lds[buf][kb * 16 + 4 * g]);
+        if constexpr (GATED) gk = *reinterpret_cast<const f32x4*>(gkl + kb * 16 + 4 * g);
 #pragma unroll
         for (int rb = 0; rb < RBW; ++rb)
 #pragma unroll
@@ -284,22 +272,21 @@ __global__ __launch_bounds__(256) void fwd_kernel(FwdParams p) {
         l_run[rb] += xgroup_sum(rs);
       }
       // ---- O^T += V^T P^T, 32 keys per MFMA ----
+      const int mm = li >> 2, c4 = li & 3;
 #pragma unroll
       for (int kp = 0; kp < KB / 2; ++kp) {
-        const int mm = li >> 2, c4 = li & 3;
-        const bf16* vr0 = vl + (kp * 32 + 4 * g + mm) * VROW + 4 * c4;
-        const bf16* vr1 = vl + (kp * 32 + 16 + 4 * g + mm) * VROW + 4 * c4;
+        const int vr0 = kp * 32 + 4 * g + mm, vr1 = vr0 + 16;
 #pragma unroll
         for (int db = 0; db < DB; ++db) {
-          const bf16x8 a = concat(lds_read_tr16(vr0 + db * 16), lds_read_tr16(vr1 + db * 16));
+          const int b = 32 * db + 8 * c4;
+          const bf16x8 a = concat(lds_read_tr16(reinterpret_cast<const bf16*>(vl + tile_off<VRB>(vr0, b))),
+                                  lds_read_tr16(reinterpret_cast<const bf16*>(vl + tile_off<VRB>(vr1, b))));
 #pragma unroll
           for (int rb = 0; rb < RBW; ++rb)
             oacc[rb][db] = mfma16x16x32(a, concat(pb[2 * kp][rb], pb[2 * kp + 1][rb]), oacc[rb][db]);
         }
       }
     }
-    if (more) stash(buf ^ 1, j0 + BN);
-    __syncthreads();
   }
 
   // ---- finalize: O = acc / l, lse = ln 2 * (m + gq + log2 l) ----
@@ -319,24 +306,24 @@ __global__ __launch_bounds__(256) void fwd_kernel(FwdParams p) {
   }
 }
 
-template <int DQK, int DV, int RW, int BN>
+template <int DQK, int DV, int RW, int BN, int NST>
 static hipError_t launch_cfg(const FwdParams& p, hipStream_t st) {
   constexpr int BM = 4 * RW;
   const int tiles = (p.max_seqlen + BM - 1) / BM;
   dim3 grid(p.Hq, p.num_seqs, tiles), block(256);
   if (p.G2 != nullptr)
-    fwd_kernel<DQK, DV, RW, BN, true><<<grid, block, 0, st>>>(p);
+    fwd_kernel<DQK, DV, RW, BN, NST, true><<<grid, block, 0, st>>>(p);
   else
-    fwd_kernel<DQK, DV, RW, BN, false><<<grid, block, 0, st>>>(p);
+    fwd_kernel<DQK, DV, RW, BN, NST, false><<<grid, block, 0, st>>>(p);
   return hipGetLastError();
 }
 
 hipError_t launch_fwd(const FwdParams& p, int dqk, int dv, hipStream_t st) {
   if (p.num_seqs == 0 || p.T == 0 || p.max_seqlen == 0) return hipSuccess;
-  if (dqk == 64 && dv == 64) return launch_cfg<64, 64, FWD_RW_SMALL, FWD_BN_SMALL>(p, st);
-  if (dqk == 128 && dv == 128) return launch_cfg<128, 128, FWD_RW_SMALL, FWD_BN_SMALL>(p, st);
-  if (dqk == 256 && dv == 256) return launch_cfg<256, 256, 16, 32>(p, st);
-  if (dqk == 256 && dv == 512) return launch_cfg<256, 512, 16, 32>(p, st);
+  if (dqk == 64 && dv == 64) return launch_cfg<64, 64, FWD_RW_SMALL, FWD_BN_SMALL, FWD_NST_SMALL>(p, st);
+  if (dqk == 128 && dv == 128) return launch_cfg<128, 128, FWD_RW_SMALL, FWD_BN_SMALL, FWD_NST_SMALL>(p, st);
+  if (dqk == 256 && dv == 256) return launch_cfg<256, 256, 16, 32, 2>(p, st);
+  if (dqk == 256 && dv == 512) return launch_cfg<256, 512, 16, 32, 2>(p, st);
   return hipErrorInvalidValue;
 }
 

@@ -42,10 +42,10 @@ struct DecodeParams {
   float* m;                 // [Tq_max * Hq, S]
   float* l;
   int R, max_pages, Hq, Hkv, B, B_shift, split_len, num_splits;
+  int row_blocks;           // 16-row query blocks per (request, KV head): ceil(max_q * G / 16)
   float scale_log2;         // softmax_scale * log2(e)
 };
-hipError_t launch_decode_splitk(const DecodeParams& p, int head_dim, bool fp8,
-                                int max_seqlen_q, hipStream_t st);
+hipError_t launch_decode_splitk(const DecodeParams& p, int head_dim, bool fp8, hipStream_t st);
 
 struct FwdParams {
   const void* q;            // bf16 [T, Hq, DQK]

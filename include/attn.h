@@ -210,8 +210,8 @@ int attn_bwd_varlen(const void* q, const void* k, const void* v,
  *            and at most 8192
  *   out      bf16 [Tq, Hq, head_dim] (output)
  *   lse      fp32 [Tq, Hq] (output, natural log) or NULL
- * Supported: head_dim 64 or 128; block_size 16, 32, 64 or 128;
- * max_seqlen_q * (Hq / Hkv) <= 64.
+ * Supported: head_dim 128 (bf16 or fp8 cache) or 64 (bf16 cache);
+ * block_size 16, 32, 64 or 128; max_seqlen_q * (Hq / Hkv) <= 64.
  * workspace: attn_decode_workspace_size() bytes (same arguments).
  * ---------------------------------------------------------------------- */
 size_t attn_decode_workspace_size(int num_requests, int max_seqlen_q,

@@ -166,7 +166,7 @@ class DecodeInputs:
 
 def decode_inputs(seq_lens, q_lens, Hq, Hkv, D, B, *, kv_dtype, seed,
                   spread=20.0, spare_pages=64, device="cpu",
-                  keep_unquantized=False, name="") -> DecodeInputs:
+                  keep_unquantized=False, shuffle=True, name="") -> DecodeInputs:
     """A paged KV cache [NB, Hkv, B, D] with a shuffled page table.
 
     Values per (token, KV head) are N(0,1) * spread**u, u ~ U(0,1), drawn
@@ -186,7 +186,7 @@ def decode_inputs(seq_lens, q_lens, Hq, Hkv, D, B, *, kv_dtype, seed,
     pages = [(L + B - 1) // B for L in seq_lens]
     used = int(sum(pages))
     NB = used + int(spare_pages)
-    perm = rng.permutation(NB).astype(np.int32)
+    perm = rng.permutation(NB).astype(np.int32) if shuffle else np.arange(NB, dtype=np.int32)
     max_pages = max(pages)
     # Padding entries point at a spare (poisoned) page: never read by a
     # correct kernel, and NaN if one ever were.

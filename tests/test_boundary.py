@@ -59,6 +59,7 @@ def _decode(**kw):
     (dict(kvd=A.ATTN_DTYPE_BF16), UNSUPPORTED, "only read with an fp8"),
     (dict(kvd=7), UNSUPPORTED, "kv_dtype"),
     (dict(D=96), UNSUPPORTED, "head_dim"),
+    (dict(D=64), UNSUPPORTED, "fp8 KV cache is supported with head_dim 128"),
     (dict(B=24), UNSUPPORTED, "block_size"),
     (dict(Hq=60, Hkv=8), INVALID, "multiple"),
     (dict(Hq=128, Hkv=2, maxq=4), UNSUPPORTED, "exceeds 64"),

@@ -88,7 +88,7 @@ DECODE_CASES = [
     ([5, 130, 2051, 4000], [4, 2, 3, 4], 64, 4, 128, 128, synth.KV_FP8_E4M3FN),
     ([5, 130, 2051, 4000], [4, 2, 3, 4], 64, 4, 128, 128, synth.KV_BF16),
     ([17, 700, 2500], [1, 1, 1], 16, 2, 128, 16, synth.KV_FP8_E4M3FN),      # GQA 8
-    ([17, 700, 2500], [2, 4, 1], 8, 8, 64, 32, synth.KV_FP8_E4M3FN),        # MHA, D 64
+    ([17, 700, 2500], [2, 4, 1], 8, 8, 64, 32, synth.KV_BF16),              # MHA, D 64
     ([64, 65537 // 16], [4, 4], 32, 2, 128, 64, synth.KV_BF16),
 ]
 
