@@ -30,11 +30,13 @@ COMMON_FLAGS = [
     "-Wno-unused-result",
 ]
 
-# Per-file extra flags.  decode.hip: keep MFMA accumulators in VGPRs; the
-# default AGPR form makes the compiler copy every accumulator to VGPRs and
-# back around the (rarely taken) rescale branch on each step.
+# Per-file extra flags.  decode.hip and fwd.hip: keep MFMA accumulators in
+# VGPRs; the default AGPR form makes the compiler copy accumulators between
+# register files around the (rarely taken) rescale branch.  The wide-head
+# forward kernels (fwd_wide.hip) need the AGPRs for capacity.
 FILE_FLAGS = {
     "decode.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+    "fwd.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
 }
 
 

@@ -107,14 +107,51 @@ __device__ __forceinline__ f32x2 fp8x2_to_f32(int word) {
 }
 
 // ---------------------------------------------------------------------------
-// Swizzled LDS tiles filled by direct global->LDS loads.
+// Direct global->LDS copies (global_load_lds) issued through inline asm.
 //
-// A tile of rows of RB bytes is stored without padding; the 16-byte chunk c
-// of row r sits at chunk position c ^ swz(r).  With RB >= 256 the swizzle
-// 2*(r%8) + (r/8)%2 makes both access patterns used by the kernels free of
-// bank conflicts: 16 lanes reading the same logical chunk of 16 consecutive
-// rows (MFMA operand rows), and ds_read_b64_tr_b16 reading two adjacent
-// chunks of 4 consecutive rows.  128-byte rows use (r/2)%8.
+// Lane l of a copy reads sbase + voff (saddr form: a wave-uniform 64-bit base
+// in SGPRs plus a 32-bit per-lane offset) and writes its 16 (or 4) bytes at
+// LDS address m0 + 16 l (or 4 l).  The compiler does not see these copies;
+// had they been issued through the builtin, it would make every later LDS
+// read (and every barrier) wait for all copies in flight, which serialises
+// a prefetch ring.  Kernels therefore wait for them explicitly with
+// wait_vm<N>() (N = copies issued after the ones needed) and must not rely
+// on compiler-inserted waits for LDS data written this way.  M0 is used by
+// nothing else in these kernels.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const LDS_AS void*)p;
+}
+__device__ __forceinline__ void dma16(const void* sbase, uint32_t voff, uint32_t m0) {
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1"
+               :: "v"(voff), "s"(sbase), "s"(m0) : "memory");
+}
+__device__ __forceinline__ void dma4(const void* sbase, uint32_t voff, uint32_t m0) {
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dword %0, %1"
+               :: "v"(voff), "s"(sbase), "s"(m0) : "memory");
+}
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N <= 63, "vmcnt range");
+  asm volatile("s_waitcnt vmcnt(%0)" :: "n"(N) : "memory");
+}
+__device__ __forceinline__ void wait_lgkm0() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
+// Workgroup barrier for kernels that manage their own waits: LDS accesses
+// of this wave are complete, and the compiler moves no memory access across.
+__device__ __forceinline__ void lds_barrier() {
+  wait_lgkm0();
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// ---------------------------------------------------------------------------
+// Swizzled LDS tiles: a tile of rows of RB bytes is stored without padding;
+// the 16-byte chunk c of row r sits at chunk position c ^ swz(r).  With
+// RB >= 256 the swizzle 2*(r%8) + (r/8)%2 makes both access patterns used by
+// the kernels free of bank conflicts: 16 lanes reading the same logical
+// chunk of 16 consecutive rows (MFMA operand rows), and ds_read_b64_tr_b16
+// reading two adjacent chunks of 4 consecutive rows.  128-byte rows use
+// (r/2)%8.
 template <int RB>
 __device__ __forceinline__ int tile_swz(int r) {
   if constexpr (RB >= 256) return ((r & 7) << 1) | ((r >> 3) & 1);
@@ -125,44 +162,5 @@ template <int RB>
 __device__ __forceinline__ int tile_off(int r, int b) {
   return r * RB + ((((b >> 4) ^ tile_swz<RB>(r)) << 4) | (b & 15));
 }
-
-// Direct loads of rows row0 .. row0+ROWS-1 of a row-major global matrix
-// (gstride bytes between rows, RB bytes used per row) into a swizzled LDS
-// tile.  Each of the 4 waves of the workgroup issues every 4th 1 KB block;
-// lane l of a block writes LDS bytes [16 l, 16 l + 16).  The per-lane source
-// offsets inside a tile are fixed, so they are computed once.  Rows at or
-// past `nrows` re-read row nrows-1 (in range and finite; the kernels mask
-// those keys).  Completion is awaited with s_waitcnt vmcnt before a barrier.
-template <int RB, int ROWS>
-struct TileDma {
-  static constexpr int NI = ROWS * RB / 1024;
-  static constexpr int PW = NI / 4;          // blocks per wave
-  static_assert(NI % 4 == 0 && NI * 1024 == ROWS * RB, "tile must split into 4 x k 1 KB blocks");
-  int row[PW];                               // tile row of this lane's chunk
-  int col[PW];                               // byte offset of the chunk in that row
-  int off[PW];                               // row * gstride + col
-  __device__ __forceinline__ void init(long gstride, int wave, int lane) {
-#pragma unroll
-    for (int j = 0; j < PW; ++j) {
-      const int o = (wave + 4 * j) * 1024 + lane * 16;
-      row[j] = o / RB;
-      col[j] = (((o % RB) >> 4) ^ tile_swz<RB>(row[j])) << 4;
-      off[j] = (int)(row[j] * gstride) + col[j];
-    }
-  }
-  __device__ __forceinline__ void issue(const uint8_t* gbase, long gstride, int row0, int nrows,
-                                        uint8_t* lds, int wave) const {
-    const uint8_t* tb = gbase + row0 * gstride;
-    const bool tail = row0 + ROWS > nrows;   // uniform: only the last tile clamps
-#pragma unroll
-    for (int j = 0; j < PW; ++j) {
-      const uint8_t* src = tail ? gbase + min(row0 + row[j], nrows - 1) * gstride + col[j] : tb + off[j];
-      __builtin_amdgcn_global_load_lds((const void __attribute__((address_space(1)))*)src,
-                                       (void LDS_AS*)(lds + (wave + 4 * j) * 1024), 16, 0, 0);
-    }
-  }
-};
-
-__device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
 }  // namespace attn

@@ -45,28 +45,6 @@ namespace attn {
 
 namespace {
 
-// LDS byte address of a pointer into __shared__ memory.
-__device__ __forceinline__ uint32_t lds_addr(const void* p) {
-  return (uint32_t)(uintptr_t)(const LDS_AS void*)p;
-}
-
-// Direct global->LDS copies in saddr form: lane l reads sbase + voff and
-// writes its 16 (or 4) bytes at LDS address m0 + 16 l (or 4 l).  Only the
-// kernel's explicit vmcnt waits order them against LDS reads.
-__device__ __forceinline__ void dma16(const void* sbase, uint32_t voff, uint32_t m0) {
-  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1"
-               :: "v"(voff), "s"(sbase), "s"(m0) : "memory");
-}
-__device__ __forceinline__ void dma4(const void* sbase, uint32_t voff, uint32_t m0) {
-  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dword %0, %1"
-               :: "v"(voff), "s"(sbase), "s"(m0) : "memory");
-}
-template <int N>
-__device__ __forceinline__ void wait_vm() {
-  asm volatile("s_waitcnt vmcnt(%0)" :: "n"(N) : "memory");
-}
-__device__ __forceinline__ void wait_lgkm0() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
-
 // 8 e4m3fn bytes -> 8 bf16 (exact), two bytes per instruction.
 __device__ __forceinline__ bf16x8 fp8x8_to_bf16x8(i32x2 w) {
   const auto a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[0], 1.0f, false);
@@ -342,11 +320,7 @@ __global__ __launch_bounds__(64 * W) void decode_splitk_kernel(DecodeParams p) {
           *reinterpret_cast<i32x4*>(Vt + ci * 1024 + 16 * lane) = i32x4{0, 0, 0, 0};
       }
     }
-    if constexpr (W > 1) {
-      wait_lgkm0();
-      __builtin_amdgcn_s_barrier();
-      asm volatile("" ::: "memory");
-    }
+    if constexpr (W > 1) lds_barrier();
     const int kn = kk + 32 * (NST - 1);
     if (kn < k_end) fetch(kn, nxt, (st + NST - 1) % NST);
     if (active) compute(kk, st);

@@ -63,6 +63,7 @@ struct FwdParams {
 hipError_t launch_gate_prefix(const float* g, const int32_t* cu, float* G2,
                               int num_seqs, int T, int Hq, hipStream_t st);
 hipError_t launch_fwd(const FwdParams& p, int dqk, int dv, hipStream_t st);
+hipError_t launch_fwd_wide(const FwdParams& p, int dqk, int dv, hipStream_t st);
 
 struct BwdParams {
   const void* q;
