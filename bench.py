@@ -37,6 +37,41 @@ MFMA_BF16_PEAK_TFLOPS = 256 * 2.4e9 * 4096 / 1e12   # 2516.6 dense bf16
 HBM_PEAK_GBPS = 8000.0
 
 
+PROFILES = os.path.join(ROOT, "profiles")
+CSRC = os.path.join(ROOT, "causal_softmax_attention_amd", "csrc")
+
+
+def kernel_sources_digest():
+    """sha256 over the HIP sources (file names and bytes, sorted)."""
+    import hashlib
+    h = hashlib.sha256()
+    for name in sorted(os.listdir(CSRC)):
+        if name.endswith((".hip", ".h")):
+            h.update(name.encode())
+            with open(os.path.join(CSRC, name), "rb") as fh:
+                h.update(fh.read())
+    return h.hexdigest()
+
+
+def stored_traffic(call):
+    """HBM bytes per call of `call` measured with rocprofv3 counters
+    (profiles/hbm_traffic.txt, lines `call sources=<sha256> bytes=<n>`), or
+    None when absent or taken on kernel sources other than the current ones."""
+    path = os.path.join(PROFILES, "hbm_traffic.txt")
+    if not os.path.exists(path):
+        return None
+    digest = kernel_sources_digest()
+    with open(path) as fh:
+        for line in fh:
+            parts = line.split()
+            if len(parts) < 3 or line.startswith("#") or parts[0] != call:
+                continue
+            kv = dict(p.split("=", 1) for p in parts[1:] if "=" in p)
+            if kv.get("sources") == digest and "bytes" in kv:
+                return float(kv["bytes"])
+    return None
+
+
 def visible_pairs(seqlens, window):
     tot = 0
     for L in seqlens:
@@ -173,10 +208,12 @@ def main():
         return A.attn_bwd_varlen(x.q, x.k, x.v, o, x.do, lse, x.cu_seqlens, x.max_seqlen, x.scale,
                                  x.window, x.sink, x.g, flags=A.ATTN_BWD_FUSED_DQ)
 
+    dec_max_q, dec_max_len = d.max_seqlen_q, d.max_seq_len   # host values, read once
+
     def dec():
-        return A.attn_decode_paged(d.q, d.cu_seqlens_q, d.max_seqlen_q, d.k_cache, d.v_cache,
+        return A.attn_decode_paged(d.q, d.cu_seqlens_q, dec_max_q, d.k_cache, d.v_cache,
                                    d.kv_dtype, d.k_scale, d.v_scale, d.block_table, d.seq_lens,
-                                   d.max_seq_len, d.scale)
+                                   dec_max_len, d.scale)
 
     tm = Timer()
     for _ in range(args.warmup):
@@ -215,7 +252,8 @@ def main():
     roof = dict(phases[dom])
     roof["frac"] = roof["achieved"] / roof["peak"]
     roof["us_per_launch"] = us[dom]
-    roof["traffic"] = None
+    roof["traffic"] = stored_traffic({"fwd": "attn_fwd_varlen", "bwd": "attn_bwd_varlen",
+                                      "decode": "attn_decode_paged"}[dom])
     for ph in phases.values():
         ph["frac"] = ph["achieved"] / ph["peak"]
 
@@ -258,9 +296,10 @@ def main():
         extra = {}
         for kvd, tag in ((synth.KV_BF16, "bf16"), (synth.KV_FP8_E4M3FN, "fp8")):
             d4 = synth.config4(kv_dtype=kvd, device=dev)
+            mlen4 = d4.max_seq_len
             f = lambda: A.attn_decode_paged(d4.q, d4.cu_seqlens_q, 4, d4.k_cache, d4.v_cache, kvd,
                                             d4.k_scale, d4.v_scale, d4.block_table, d4.seq_lens,
-                                            d4.max_seq_len, d4.scale)
+                                            mlen4, d4.scale)
             for _ in range(3):
                 f()
             t4 = Timer()

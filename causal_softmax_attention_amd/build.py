@@ -30,13 +30,15 @@ COMMON_FLAGS = [
     "-Wno-unused-result",
 ]
 
-# Per-file extra flags.  decode.hip and fwd.hip: keep MFMA accumulators in
-# VGPRs; the default AGPR form makes the compiler copy accumulators between
-# register files around the (rarely taken) rescale branch.  The wide-head
-# forward kernels (fwd_wide.hip) need the AGPRs for capacity.
+# Per-file extra flags.  decode.hip, fwd.hip and bwd2.hip: keep MFMA
+# accumulators in VGPRs; the default AGPR form makes the compiler copy
+# accumulators between register files around branches inside the loops (and
+# spills in the widest backward kernels).  The wide-head forward kernels
+# (fwd_wide.hip) need the AGPRs for capacity.
 FILE_FLAGS = {
     "decode.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
     "fwd.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+    "bwd2.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
 }
 
 

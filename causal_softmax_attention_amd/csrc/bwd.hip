@@ -27,26 +27,33 @@
 namespace attn {
 
 // ---------------------------------------------------------------------------
+// delta[row] = sum_d O[row, d] * dO[row, d] in fp32 (row = token * Hq + head).
+// DV/8 lanes per row, 16 bytes of O and of dO per lane, so a wave streams
+// whole 256-byte rows; also zeroes the fused path's dQ accumulator and the
+// gate / sink gradient accumulators.
 template <int DQK, int DV>
 __global__ __launch_bounds__(256) void bwd_pre_kernel(BwdParams p) {
-  const int lane = threadIdx.x & 63;
-  const long row = (long)blockIdx.x * 4 + (threadIdx.x >> 6);   // token * Hq + head
+  constexpr int LPR = DV / 8;                 // lanes per row
+  constexpr int RPB = 256 / LPR;              // rows per workgroup
+  const int t = threadIdx.x, sub = t % LPR;
+  const long row = (long)blockIdx.x * RPB + t / LPR;
   if (blockIdx.x == 0 && p.dsink_acc != nullptr)
-    for (int h = threadIdx.x; h < p.Hq; h += 256) p.dsink_acc[h] = 0.f;
+    for (int h = t; h < p.Hq; h += 256) p.dsink_acc[h] = 0.f;
   if (row >= (long)p.T * p.Hq) return;
-  const bf16* o = reinterpret_cast<const bf16*>(p.o) + row * DV;
-  const bf16* d = reinterpret_cast<const bf16*>(p.dO) + row * DV;
+  const bf16x8 o = *reinterpret_cast<const bf16x8*>(reinterpret_cast<const bf16*>(p.o) + row * DV + 8 * sub);
+  const bf16x8 d = *reinterpret_cast<const bf16x8*>(reinterpret_cast<const bf16*>(p.dO) + row * DV + 8 * sub);
   float s = 0.f;
-  for (int j = lane; j < DV; j += 64) s += (float)o[j] * (float)d[j];
 #pragma unroll
-  for (int off = 32; off > 0; off >>= 1) s += __shfl_xor(s, off);
-  if (lane == 0) {
+  for (int j = 0; j < 8; ++j) s += (float)o[j] * (float)d[j];
+#pragma unroll
+  for (int off = LPR / 2; off > 0; off >>= 1) s += __shfl_xor(s, off);
+  if (sub == 0) {
     p.delta[row] = s;
     if (p.dG != nullptr) p.dG[row] = 0.f;
   }
   if (p.dq_acc != nullptr) {
     float* dqa = p.dq_acc + row * DQK;
-    for (int j = lane * 4; j < DQK; j += 256) *reinterpret_cast<f32x4*>(dqa + j) = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int j = sub; j < DQK / 4; j += LPR) *reinterpret_cast<f32x4*>(dqa + 4 * j) = f32x4{0.f, 0.f, 0.f, 0.f};
   }
 }
 
@@ -327,7 +334,8 @@ hipError_t launch_fill_zero(float* x, long n, hipStream_t st) {
 template <int DQK, int DV>
 static hipError_t launch_bwd_t(const BwdParams& p, bool fused, hipStream_t st) {
   const long rows = (long)p.T * p.Hq;
-  bwd_pre_kernel<DQK, DV><<<dim3((unsigned)((rows + 3) / 4)), 256, 0, st>>>(p);
+  constexpr int RPB = 256 / (DV / 8);
+  bwd_pre_kernel<DQK, DV><<<dim3((unsigned)((rows + RPB - 1) / RPB)), 256, 0, st>>>(p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (fused) {

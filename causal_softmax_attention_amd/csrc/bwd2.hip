@@ -23,6 +23,9 @@
 #ifndef BWD_KW_SMALL
 #define BWD_KW_SMALL 16
 #endif
+#ifndef BWD_RW_SMALL
+#define BWD_RW_SMALL 16
+#endif
 
 namespace attn {
 
@@ -568,8 +571,8 @@ hipError_t launch_bwd_two_pass_t(const BwdParams& p, hipStream_t st) {
 }
 
 hipError_t launch_bwd_two_pass(const BwdParams& p, int dqk, int dv, hipStream_t st) {
-  if (dqk == 64 && dv == 64) return launch_bwd_two_pass_t<64, 64, BWD_KW_SMALL, 16, 64>(p, st);
-  if (dqk == 128 && dv == 128) return launch_bwd_two_pass_t<128, 128, BWD_KW_SMALL, 16, 64>(p, st);
+  if (dqk == 64 && dv == 64) return launch_bwd_two_pass_t<64, 64, BWD_KW_SMALL, BWD_RW_SMALL, 64>(p, st);
+  if (dqk == 128 && dv == 128) return launch_bwd_two_pass_t<128, 128, BWD_KW_SMALL, BWD_RW_SMALL, 64>(p, st);
   if (dqk == 256 && dv == 256) return launch_bwd_two_pass_t<256, 256, 16, 16, 32>(p, st);
   if (dqk == 256 && dv == 512) return launch_bwd_two_pass_t<256, 512, 16, 16, 32>(p, st);
   return hipErrorInvalidValue;
