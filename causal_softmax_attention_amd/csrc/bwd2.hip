@@ -36,22 +36,25 @@ __device__ __forceinline__ int xcd_remap(int x, int n) {
 }
 
 // ---------------------------------------------------------------------------
-// PF: fetch the next query tile into registers during the current one
-// (off for the largest heads, where those registers are not available).
-template <int DQK, int DV, int KW, bool PF, bool GATED>
+// dK/dV pass.  Each wave keeps KW keys of K and V in registers and walks the
+// query tiles (RQ rows) of every query head of its KV group.  The Q and dO
+// tiles (and the per-row lse, delta and gate terms) reach LDS by direct
+// copies into a two-stage ring of swizzled tiles, one tile ahead of the
+// math; rows past the end re-read the last row (finite) and are masked.
+template <int DQK, int DV, int KW, bool GATED>
 __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdParams p) {
   constexpr int RQ = 32;              // query rows per tile
   constexpr int KBW = KW / 16;        // 16-key blocks per wave
   constexpr int BNW = 4 * KW;         // keys per workgroup
   constexpr int KSQ = DQK / 32, KSV = DV / 32;
   constexpr int DBQ = DQK / 16, DBV = DV / 16;
-  constexpr int QROW = DQK + 8, OROW = DV + 16;
-  constexpr int QCH = RQ * DQK / 8 / 256, OCH = RQ * DV / 8 / 256;   // 16-byte chunks per thread
-  static_assert(QCH * 256 * 8 == RQ * DQK && OCH * 256 * 8 == RQ * DV, "tile must split evenly");
-  constexpr int NB = PF ? 2 : 1;
-  __shared__ __attribute__((aligned(16))) bf16 q_lds[NB][RQ * QROW];
-  __shared__ __attribute__((aligned(16))) bf16 do_lds[NB][RQ * OROW];
-  __shared__ __attribute__((aligned(16))) float lse_lds[NB][RQ], delta_lds[NB][RQ], gq_lds[NB][RQ];
+  constexpr int QRB = DQK * 2, ORB = DV * 2;   // bytes per Q / dO row
+  constexpr int QPW = RQ * QRB / 4096, OPW = RQ * ORB / 4096;   // 1 KB blocks per wave
+  static_assert(QPW * 4096 == RQ * QRB && OPW * 4096 == RQ * ORB, "tile must split into 4 x k 1 KB blocks");
+  __shared__ __attribute__((aligned(1024))) uint8_t q_lds[2][RQ * QRB];
+  __shared__ __attribute__((aligned(1024))) uint8_t do_lds[2][RQ * ORB];
+  __shared__ __attribute__((aligned(16))) float row_lds[2][3][64];   // lse, delta, gq (lanes >= RQ repeat)
+  __shared__ __attribute__((aligned(16))) float gk_lds[2][4][64];    // per wave: its keys' gate terms
 
   const int kvh = xcd_remap(blockIdx.x, p.Hkv), n = blockIdx.y, ktile = blockIdx.z;
   const int seq0 = p.cu[n];
@@ -62,7 +65,6 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdParams p) {
   const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int li = lane & 15, g = lane >> 4;
   const int W = p.window;
-  constexpr bool gated = GATED;
   const int jw = j0 + wave * KW;
 
   bf16x8 kop[KBW][KSQ], vop[KBW][KSV];
@@ -86,122 +88,97 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdParams p) {
     for (int db = 0; db < DBV; ++db) dv_acc[kb][db] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
 
-  // Flattened iteration over (query head of the group, 32-row query tile);
-  // tile it+1 is fetched into registers while tile it is computed.
+  // Flattened iteration over (query head of the group, RQ-row query tile).
   const int i_end = W > 0 ? min(L, j0 + BNW - 1 + W) : L;
   const int nqt = (i_end - j0 + RQ - 1) / RQ;
   const int n_it = grp * nqt;
 
-  i32x4 qreg[QCH], oreg[OCH];
-  float sreg[3] = {0.f, 0.f, 0.f};
-  auto fetch = [&](int it) {
-    const int hh = kvh * grp + min(it / nqt, grp - 1);
+  // fixed per-lane source offsets of the tile copies
+  const int qstride = p.Hq * QRB, ostride = p.Hq * ORB;
+  int qrow[QPW], qoff[QPW], orow[OPW], ooff[OPW];
+#pragma unroll
+  for (int j = 0; j < QPW; ++j) {
+    const int o = (wave + 4 * j) * 1024 + lane * 16;
+    qrow[j] = o / QRB;
+    qoff[j] = qrow[j] * qstride + ((((o % QRB) >> 4) ^ tile_swz<QRB>(qrow[j])) << 4);
+  }
+#pragma unroll
+  for (int j = 0; j < OPW; ++j) {
+    const int o = (wave + 4 * j) * 1024 + lane * 16;
+    orow[j] = o / ORB;
+    ooff[j] = orow[j] * ostride + ((((o % ORB) >> 4) ^ tile_swz<ORB>(orow[j])) << 4);
+  }
+  auto fetch = [&](int it, int st) {
+    const int hh = kvh * grp + it / nqt;
     const int i0 = j0 + (it % nqt) * RQ;
+    const bool tail = i0 + RQ > L;               // uniform: only the last tile clamps
+    const long r0 = (long)(seq0 + i0) * p.Hq + hh;   // (token, head) row of the tile's first query
+    const uint8_t* qb = reinterpret_cast<const uint8_t*>(p.q) + r0 * QRB;
+    const uint8_t* ob = reinterpret_cast<const uint8_t*>(p.dO) + r0 * ORB;
+    const uint32_t ql = lds_addr(q_lds[st]), ol = lds_addr(do_lds[st]);
 #pragma unroll
-    for (int cc = 0; cc < QCH; ++cc) {
-      const int ch = tid + 256 * cc;
-      const int rr = ch / (DQK / 8), col = (ch % (DQK / 8)) * 8;
-      qreg[cc] = *reinterpret_cast<const i32x4*>(reinterpret_cast<const bf16*>(p.q) +
-                                                 ((long)(seq0 + min(i0 + rr, L - 1)) * p.Hq + hh) * DQK + col);
-    }
-#pragma unroll
-    for (int cc = 0; cc < OCH; ++cc) {
-      const int ch = tid + 256 * cc;
-      const int rr = ch / (DV / 8), col = (ch % (DV / 8)) * 8;
-      oreg[cc] = *reinterpret_cast<const i32x4*>(reinterpret_cast<const bf16*>(p.dO) +
-                                                 ((long)(seq0 + min(i0 + rr, L - 1)) * p.Hq + hh) * DV + col);
-    }
-    if (tid < RQ) {
-      const long ri = (long)(seq0 + min(i0 + tid, L - 1)) * p.Hq + hh;
-      sreg[0] = p.lse[ri];
-      sreg[1] = p.delta[ri];
-      sreg[2] = gated ? p.G2[ri] : 0.f;
-    }
-  };
-  auto stash = [&](int buf, int it) {
-    const int i0 = j0 + (it % nqt) * RQ;
-    const i32x4 z = {0, 0, 0, 0};
-#pragma unroll
-    for (int cc = 0; cc < QCH; ++cc) {
-      const int ch = tid + 256 * cc;
-      const int rr = ch / (DQK / 8), col = (ch % (DQK / 8)) * 8;
-      *reinterpret_cast<i32x4*>(&q_lds[buf][rr * QROW + col]) = (i0 + rr < L) ? qreg[cc] : z;
+    for (int j = 0; j < QPW; ++j) {
+      const int over = tail ? max(0, i0 + qrow[j] - (L - 1)) : 0;
+      dma16(qb, (uint32_t)(qoff[j] - over * qstride), ql + (wave + 4 * j) * 1024);
     }
 #pragma unroll
-    for (int cc = 0; cc < OCH; ++cc) {
-      const int ch = tid + 256 * cc;
-      const int rr = ch / (DV / 8), col = (ch % (DV / 8)) * 8;
-      *reinterpret_cast<i32x4*>(&do_lds[buf][rr * OROW + col]) = (i0 + rr < L) ? oreg[cc] : z;
+    for (int j = 0; j < OPW; ++j) {
+      const int over = tail ? max(0, i0 + orow[j] - (L - 1)) : 0;
+      dma16(ob, (uint32_t)(ooff[j] - over * ostride), ol + (wave + 4 * j) * 1024);
     }
-    if (tid < RQ) {
-      const bool ok = i0 + tid < L;
-      lse_lds[buf][tid] = ok ? sreg[0] * kLog2e : 0.f;
-      delta_lds[buf][tid] = ok ? sreg[1] : 0.f;
-      gq_lds[buf][tid] = ok ? sreg[2] : 0.f;
+    if (wave == 0) {
+      // per-row terms, lane l -> row min(i0 + l % RQ, L - 1)
+      const uint32_t ro = (uint32_t)((min(i0 + (lane % RQ), L - 1) - i0) * p.Hq * 4);
+      const float* lb = p.lse + r0;
+      const float* db_ = p.delta + r0;
+      dma4(lb, ro, lds_addr(&row_lds[st][0][0]));
+      dma4(db_, ro, lds_addr(&row_lds[st][1][0]));
+      if constexpr (GATED) dma4(p.G2 + r0, ro, lds_addr(&row_lds[st][2][0]));
+    }
+    if constexpr (GATED) {
+      // this wave's keys for the tile's head, lane l -> key jw + l % KW
+      const uint32_t ko = (uint32_t)(min(jw + (lane % KW), L - 1) * p.Hq * 4);
+      dma4(p.G2 + (long)seq0 * p.Hq + hh, ko, lds_addr(&gk_lds[st][wave][0]));
     }
   };
 
-  if constexpr (PF) {
-    fetch(0);
-    stash(0, 0);
-    __syncthreads();
+  // wait for the register loads above before the copies start, so that the
+  // compiler's own wait for them does not land inside the loop
+#pragma unroll
+  for (int kb = 0; kb < KBW; ++kb) {
+#pragma unroll
+    for (int ks = 0; ks < KSQ; ++ks) asm volatile("" :: "v"(kop[kb][ks]));
+#pragma unroll
+    for (int ks = 0; ks < KSV; ++ks) asm volatile("" :: "v"(vop[kb][ks]));
   }
 
-  float gk[KBW], colsum[KBW];
+  if (n_it > 0) fetch(0, 0);
+  float colsum[KBW];
+#pragma unroll
+  for (int kb = 0; kb < KBW; ++kb) colsum[kb] = 0.f;
   for (int it = 0; it < n_it; ++it) {
-    const int buf = PF ? (it & 1) : 0;
-    if constexpr (!PF) {
-      // chunk by chunk straight into LDS: few live registers
-      const int hh = kvh * grp + it / nqt;
-      const int i0s = j0 + (it % nqt) * RQ;
-      for (int c = tid; c < RQ * DQK / 8; c += 256) {
-        const int rr = c / (DQK / 8), col = (c % (DQK / 8)) * 8;
-        i32x4 val = {0, 0, 0, 0};
-        if (i0s + rr < L)
-          val = *reinterpret_cast<const i32x4*>(reinterpret_cast<const bf16*>(p.q) +
-                                                ((long)(seq0 + i0s + rr) * p.Hq + hh) * DQK + col);
-        *reinterpret_cast<i32x4*>(&q_lds[0][rr * QROW + col]) = val;
-      }
-      for (int c = tid; c < RQ * DV / 8; c += 256) {
-        const int rr = c / (DV / 8), col = (c % (DV / 8)) * 8;
-        i32x4 val = {0, 0, 0, 0};
-        if (i0s + rr < L)
-          val = *reinterpret_cast<const i32x4*>(reinterpret_cast<const bf16*>(p.dO) +
-                                                ((long)(seq0 + i0s + rr) * p.Hq + hh) * DV + col);
-        *reinterpret_cast<i32x4*>(&do_lds[0][rr * OROW + col]) = val;
-      }
-      if (tid < RQ) {
-        const bool ok = i0s + tid < L;
-        const long ri = (long)(seq0 + i0s + tid) * p.Hq + hh;
-        lse_lds[0][tid] = ok ? p.lse[ri] * kLog2e : 0.f;
-        delta_lds[0][tid] = ok ? p.delta[ri] : 0.f;
-        gq_lds[0][tid] = (ok && gated) ? p.G2[ri] : 0.f;
-      }
-      __syncthreads();
-    }
+    const int buf = it & 1;
+    wait_vm<0>();    // this wave's copies of tile it have landed
+    lds_barrier();   // ... and everyone's; the other stage is free again
+    if (it + 1 < n_it) fetch(it + 1, buf ^ 1);
+
     const int hg = it / nqt, qt = it % nqt;
     const int h = kvh * grp + hg;
     const int i0 = j0 + qt * RQ;
-    if (qt == 0) {
+    float gk[KBW];
 #pragma unroll
-      for (int kb = 0; kb < KBW; ++kb) {
-        const int key = jw + kb * 16 + li;
-        gk[kb] = gated ? p.G2[(long)(seq0 + min(key, L - 1)) * p.Hq + h] : 0.f;
-        colsum[kb] = 0.f;
-      }
-    }
-    if constexpr (PF) fetch(it + 1);   // unconditional: indices clamped, no drain at a branch join
+    for (int kb = 0; kb < KBW; ++kb) gk[kb] = GATED ? gk_lds[buf][wave][kb * 16 + li] : 0.f;
 
     // no branch around the math (see the forward kernel): masked pairs give
     // P = dS = 0; the per-element mask runs only on tiles that need it
     const bool need_mask = (i0 < jw + KW - 1) || (W > 0 && i0 + RQ - 1 - jw >= W) || (i0 + RQ > L) ||
                            (jw + KW > L);
     {
-      const bf16* ql = q_lds[buf];
-      const bf16* ol = do_lds[buf];
-      const float* lsel = lse_lds[buf];
-      const float* dell = delta_lds[buf];
-      const float* gql = gq_lds[buf];
+      const uint8_t* ql = q_lds[buf];
+      const uint8_t* ol = do_lds[buf];
+      const float* lsel = row_lds[buf][0];
+      const float* dell = row_lds[buf][1];
+      const float* gql = row_lds[buf][2];
       // ---- S = Q K^T, dP = dO V^T: C lane (key li, rows rb*16+4g+i) ----
       f32x4 s[KBW][2], dp[KBW][2];
 #pragma unroll
@@ -213,13 +190,13 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdParams p) {
         }
 #pragma unroll
         for (int ks = 0; ks < KSQ; ++ks) {
-          const bf16x8 a = lds_read8(ql + (rb * 16 + li) * QROW + ks * 32 + 8 * g);
+          const bf16x8 a = *reinterpret_cast<const bf16x8*>(ql + tile_off<QRB>(rb * 16 + li, 64 * ks + 16 * g));
 #pragma unroll
           for (int kb = 0; kb < KBW; ++kb) s[kb][rb] = mfma16x16x32(a, kop[kb][ks], s[kb][rb]);
         }
 #pragma unroll
         for (int ks = 0; ks < KSV; ++ks) {
-          const bf16x8 a = lds_read8(ol + (rb * 16 + li) * OROW + ks * 32 + 8 * g);
+          const bf16x8 a = *reinterpret_cast<const bf16x8*>(ol + tile_off<ORB>(rb * 16 + li, 64 * ks + 16 * g));
 #pragma unroll
           for (int kb = 0; kb < KBW; ++kb) dp[kb][rb] = mfma16x16x32(a, vop[kb][ks], dp[kb][rb]);
         }
@@ -231,11 +208,14 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdParams p) {
         const f32x4 lse4 = *reinterpret_cast<const f32x4*>(lsel + rb * 16 + 4 * g);
         f32x4 gq4 = {0.f, 0.f, 0.f, 0.f};
         if constexpr (GATED) gq4 = *reinterpret_cast<const f32x4*>(gql + rb * 16 + 4 * g);
+        f32x4 rowt;   // row term in base 2: gate of the row minus lse
+#pragma unroll
+        for (int i = 0; i < 4; ++i) rowt[i] = gq4[i] - lse4[i] * kLog2e;
 #pragma unroll
         for (int kb = 0; kb < KBW; ++kb)
 #pragma unroll
           for (int i = 0; i < 4; ++i)
-            pv[kb][rb][i] = fast_exp2(__builtin_fmaf(s[kb][rb][i], p.scale_log2, (gq4[i] - gk[kb]) - lse4[i]));
+            pv[kb][rb][i] = fast_exp2(__builtin_fmaf(s[kb][rb][i], p.scale_log2, rowt[i] - gk[kb]));
       }
       if (need_mask) {
 #pragma unroll
@@ -270,39 +250,33 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdParams p) {
       }
       // ---- dV^T += dO^T P, dK^T += Q^T dS (32 rows per MFMA) ----
       const int mm = li >> 2, c4 = li & 3;
-      const bf16* o0 = ol + (4 * g + mm) * OROW + 4 * c4;
-      const bf16* o1 = ol + (16 + 4 * g + mm) * OROW + 4 * c4;
-      // (compiler barriers every few column blocks keep the scheduler from
-      //  hoisting every transposed read at once and running out of registers)
+      const int r0 = 4 * g + mm, r1 = r0 + 16;
 #pragma unroll
       for (int db = 0; db < DBV; ++db) {
-        const bf16x8 a = concat(lds_read_tr16(o0 + db * 16), lds_read_tr16(o1 + db * 16));
+        const int b = 32 * db + 8 * c4;
+        const bf16x8 a = concat(lds_read_tr16(reinterpret_cast<const bf16*>(ol + tile_off<ORB>(r0, b))),
+                                lds_read_tr16(reinterpret_cast<const bf16*>(ol + tile_off<ORB>(r1, b))));
 #pragma unroll
         for (int kb = 0; kb < KBW; ++kb) dv_acc[kb][db] = mfma16x16x32(a, pop[kb], dv_acc[kb][db]);
-        if ((db & 3) == 3) asm volatile("" ::: "memory");
       }
-      const bf16* q0 = ql + (4 * g + mm) * QROW + 4 * c4;
-      const bf16* q1 = ql + (16 + 4 * g + mm) * QROW + 4 * c4;
 #pragma unroll
       for (int db = 0; db < DBQ; ++db) {
-        const bf16x8 a = concat(lds_read_tr16(q0 + db * 16), lds_read_tr16(q1 + db * 16));
+        const int b = 32 * db + 8 * c4;
+        const bf16x8 a = concat(lds_read_tr16(reinterpret_cast<const bf16*>(ql + tile_off<QRB>(r0, b))),
+                                lds_read_tr16(reinterpret_cast<const bf16*>(ql + tile_off<QRB>(r1, b))));
 #pragma unroll
         for (int kb = 0; kb < KBW; ++kb) dk_acc[kb][db] = mfma16x16x32(a, dsop[kb], dk_acc[kb][db]);
-        if ((db & 3) == 3) asm volatile("" ::: "memory");
       }
     }
-    if (gated && qt == nqt - 1) {
+    if (GATED && qt == nqt - 1) {
 #pragma unroll
       for (int kb = 0; kb < KBW; ++kb) {
         const float cs = xgroup_sum(colsum[kb]);
         const int key = jw + kb * 16 + li;
         if (g == 0 && key < L) p.dGcol[(long)(seq0 + key) * p.Hq + h] = cs;
+        colsum[kb] = 0.f;
       }
     }
-    if constexpr (PF) {
-      if (it + 1 < n_it) stash(buf ^ 1, it + 1);
-    }
-    __syncthreads();
   }
 
 #pragma unroll
@@ -326,12 +300,12 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(BwdParams p) {
   constexpr int KB = BN / 16;
   constexpr int KSQ = DQK / 32, KSV = DV / 32;
   constexpr int DBQ = DQK / 16;
-  constexpr int KROW = DQK + 8, VROW = DV + 16;
-  constexpr int KCH = BN * DQK / 8 / 256, VCH = BN * DV / 8 / 256;
+  constexpr int KRB = DQK * 2, VRB = DV * 2;   // bytes per K / V row
   static_assert(KB % 2 == 0, "dQ consumes keys in pairs of 16-key blocks");
-  __shared__ __attribute__((aligned(16))) bf16 k_lds[2][BN * KROW];
-  __shared__ __attribute__((aligned(16))) bf16 v_lds[2][BN * VROW];
-  __shared__ __attribute__((aligned(16))) float gk_lds[2][BN];
+  static_assert(BN <= 64, "gate copy is one lane per key");
+  __shared__ __attribute__((aligned(1024))) uint8_t k_lds[2][BN * KRB];
+  __shared__ __attribute__((aligned(1024))) uint8_t v_lds[2][BN * VRB];
+  __shared__ __attribute__((aligned(16))) float gk_lds[2][4][64];   // one copy per wave
 
   const int h = xcd_remap(blockIdx.x, p.Hq), n = blockIdx.y;
   const int tile = gridDim.z - 1 - blockIdx.z;
@@ -375,54 +349,58 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(BwdParams p) {
   const int kv_lo = W > 0 ? max(0, i0 - W + 1) : 0;
   const int kv_hi = min(L, i0 + BM);
   const int t_begin = kv_lo / BN, t_end = (kv_hi + BN - 1) / BN;
-  const bf16* kbase = reinterpret_cast<const bf16*>(p.k) + ((long)seq0 * p.Hkv + kvh) * DQK;
-  const bf16* vbase = reinterpret_cast<const bf16*>(p.v) + ((long)seq0 * p.Hkv + kvh) * DV;
-  const long kstride = (long)p.Hkv * DQK, vstride = (long)p.Hkv * DV;
+  const uint8_t* kbase = reinterpret_cast<const uint8_t*>(p.k) + ((long)seq0 * p.Hkv + kvh) * KRB;
+  const uint8_t* vbase = reinterpret_cast<const uint8_t*>(p.v) + ((long)seq0 * p.Hkv + kvh) * VRB;
+  const int kstride = p.Hkv * KRB, vstride = p.Hkv * VRB;
 
-  i32x4 kreg[KCH], vreg[VCH];
-  float gkreg = 0.f;
-  auto fetch = [&](int j0) {
+  // K/V tiles (and each wave's copy of the key gate terms) go global -> LDS
+  // by direct copies into a two-stage ring of swizzled tiles, one tile
+  // ahead of the math (as in the forward kernel): wave w copies the 1 KB
+  // blocks w, w+4, ... of each tile; rows past the end re-read the last row
+  // (finite; masked).
+  constexpr int KPW = BN * KRB / 4096, VPW = BN * VRB / 4096;
+  static_assert(KPW * 4096 == BN * KRB && VPW * 4096 == BN * VRB, "tile must split into 4 x k 1 KB blocks");
+  int krow[KPW], koff[KPW], vrow[VPW], voff[VPW];
 #pragma unroll
-    for (int cc = 0; cc < KCH; ++cc) {
-      const int ch = tid + 256 * cc;
-      const int kr = ch / (DQK / 8), col = (ch % (DQK / 8)) * 8;
-      kreg[cc] = *reinterpret_cast<const i32x4*>(kbase + (long)min(j0 + kr, L - 1) * kstride + col);
+  for (int j = 0; j < KPW; ++j) {
+    const int o = (wave + 4 * j) * 1024 + lane * 16;
+    krow[j] = o / KRB;
+    koff[j] = krow[j] * kstride + ((((o % KRB) >> 4) ^ tile_swz<KRB>(krow[j])) << 4);
+  }
+#pragma unroll
+  for (int j = 0; j < VPW; ++j) {
+    const int o = (wave + 4 * j) * 1024 + lane * 16;
+    vrow[j] = o / VRB;
+    voff[j] = vrow[j] * vstride + ((((o % VRB) >> 4) ^ tile_swz<VRB>(vrow[j])) << 4);
+  }
+  const float* g2base = GATED ? p.G2 + (long)seq0 * p.Hq + h : nullptr;
+  auto fetch = [&](int st, int j0) {
+    const bool tail = j0 + BN > L;               // uniform: only the last tile clamps
+    const uint8_t* kb = kbase + (long)j0 * kstride;
+    const uint8_t* vb = vbase + (long)j0 * vstride;
+    const uint32_t kl = lds_addr(k_lds[st]), vl = lds_addr(v_lds[st]);
+#pragma unroll
+    for (int j = 0; j < KPW; ++j) {
+      const int over = tail ? max(0, j0 + krow[j] - (L - 1)) : 0;
+      dma16(kb, (uint32_t)(koff[j] - over * kstride), kl + (wave + 4 * j) * 1024);
     }
 #pragma unroll
-    for (int cc = 0; cc < VCH; ++cc) {
-      const int ch = tid + 256 * cc;
-      const int kr = ch / (DV / 8), col = (ch % (DV / 8)) * 8;
-      vreg[cc] = *reinterpret_cast<const i32x4*>(vbase + (long)min(j0 + kr, L - 1) * vstride + col);
+    for (int j = 0; j < VPW; ++j) {
+      const int over = tail ? max(0, j0 + vrow[j] - (L - 1)) : 0;
+      dma16(vb, (uint32_t)(voff[j] - over * vstride), vl + (wave + 4 * j) * 1024);
     }
-    if (gated && tid < BN) gkreg = p.G2[(long)(seq0 + min(j0 + tid, L - 1)) * p.Hq + h];
-  };
-  auto stash = [&](int buf, int j0) {
-    const i32x4 z = {0, 0, 0, 0};
-    const bool tail = j0 + BN > L;               // zero-fill rows past the end (last tile only)
-#pragma unroll
-    for (int cc = 0; cc < KCH; ++cc) {
-      const int ch = tid + 256 * cc;
-      const int kr = ch / (DQK / 8), col = (ch % (DQK / 8)) * 8;
-      *reinterpret_cast<i32x4*>(&k_lds[buf][kr * KROW + col]) = (tail && j0 + kr >= L) ? z : kreg[cc];
-    }
-#pragma unroll
-    for (int cc = 0; cc < VCH; ++cc) {
-      const int ch = tid + 256 * cc;
-      const int kr = ch / (DV / 8), col = (ch % (DV / 8)) * 8;
-      *reinterpret_cast<i32x4*>(&v_lds[buf][kr * VROW + col]) = (tail && j0 + kr >= L) ? z : vreg[cc];
-    }
-    if (gated && tid < BN) gk_lds[buf][tid] = gkreg;
+    if constexpr (GATED)
+      dma4(g2base, (uint32_t)(min(j0 + lane, L - 1) * p.Hq * 4), lds_addr(&gk_lds[st][wave][0]));
   };
 
-  fetch(t_begin * BN);
-  stash(0, t_begin * BN);
-  __syncthreads();
+  if (t_begin < t_end) fetch(0, t_begin * BN);
 
   for (int t = t_begin; t < t_end; ++t) {
     const int j0 = t * BN;
     const int buf = (t - t_begin) & 1;
-    const bool more = t + 1 < t_end;
-    fetch(j0 + BN);   // unconditional: clamped addresses, no drain at a branch join
+    wait_vm<0>();     // this wave's copies of tile t have landed
+    lds_barrier();    // ... and everyone's; the other stage is free again
+    if (t + 1 < t_end) fetch(buf ^ 1, j0 + BN);
 
     // no branch around the math (see the forward kernel): wholly masked
     // tiles contribute zeros; rows past the end are masked too, their lse
@@ -430,8 +408,8 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(BwdParams p) {
     {
       const bool need_mask = (j0 + BN - 1 > r0) || (W > 0 && r_last - j0 >= W) || (j0 + BN > L) ||
                              (r_last < r0 + RW - 1);
-      const bf16* kl = k_lds[buf];
-      const bf16* vl = v_lds[buf];
+      const uint8_t* kl = k_lds[buf];
+      const uint8_t* vl = v_lds[buf];
       f32x4 s[KB][RBW], dp[KB][RBW];
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb) {
@@ -442,13 +420,13 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(BwdParams p) {
         }
 #pragma unroll
         for (int ks = 0; ks < KSQ; ++ks) {
-          const bf16x8 a = lds_read8(kl + (kb * 16 + li) * KROW + ks * 32 + 8 * g);
+          const bf16x8 a = *reinterpret_cast<const bf16x8*>(kl + tile_off<KRB>(kb * 16 + li, 64 * ks + 16 * g));
 #pragma unroll
           for (int rb = 0; rb < RBW; ++rb) s[kb][rb] = mfma16x16x32(a, qop[rb][ks], s[kb][rb]);
         }
 #pragma unroll
         for (int ks = 0; ks < KSV; ++ks) {
-          const bf16x8 a = lds_read8(vl + (kb * 16 + li) * VROW + ks * 32 + 8 * g);
+          const bf16x8 a = *reinterpret_cast<const bf16x8*>(vl + tile_off<VRB>(kb * 16 + li, 64 * ks + 16 * g));
 #pragma unroll
           for (int rb = 0; rb < RBW; ++rb) dp[kb][rb] = mfma16x16x32(a, doop[rb][ks], dp[kb][rb]);
         }
@@ -458,7 +436,7 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(BwdParams p) {
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb) {
         f32x4 gk = {0.f, 0.f, 0.f, 0.f};
-        if constexpr (GATED) gk = *reinterpret_cast<const f32x4*>(&gk_lds[buf][kb * 16 + 4 * g]);
+        if constexpr (GATED) gk = *reinterpret_cast<const f32x4*>(&gk_lds[buf][wave][kb * 16 + 4 * g]);
 #pragma unroll
         for (int rb = 0; rb < RBW; ++rb) {
           const float base = gq[rb] - lse2[rb];
@@ -500,19 +478,18 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(BwdParams p) {
 #pragma unroll
       for (int kp = 0; kp < KB / 2; ++kp) {
         const int mm = li >> 2, c4 = li & 3;
-        const bf16* k0 = kl + (kp * 32 + 4 * g + mm) * KROW + 4 * c4;
-        const bf16* k1 = kl + (kp * 32 + 16 + 4 * g + mm) * KROW + 4 * c4;
+        const int kr0 = kp * 32 + 4 * g + mm, kr1 = kr0 + 16;
 #pragma unroll
         for (int db = 0; db < DBQ; ++db) {
-          const bf16x8 a = concat(lds_read_tr16(k0 + db * 16), lds_read_tr16(k1 + db * 16));
+          const int b = 32 * db + 8 * c4;
+          const bf16x8 a = concat(lds_read_tr16(reinterpret_cast<const bf16*>(kl + tile_off<KRB>(kr0, b))),
+                                  lds_read_tr16(reinterpret_cast<const bf16*>(kl + tile_off<KRB>(kr1, b))));
 #pragma unroll
           for (int rb = 0; rb < RBW; ++rb)
             dq_acc[rb][db] = mfma16x16x32(a, concat(dsb[2 * kp][rb], dsb[2 * kp + 1][rb]), dq_acc[rb][db]);
         }
       }
     }
-    if (more) stash(buf ^ 1, j0 + BN);
-    __syncthreads();
   }
 
   const float sink2 = p.sink ? p.sink[h] * kLog2e : 0.f;
@@ -553,8 +530,8 @@ template <int DQK, int DV, int KW, int RW, int BN>
 hipError_t launch_bwd_two_pass_t(const BwdParams& p, hipStream_t st) {
   const int ktiles = (p.max_seqlen + 4 * KW - 1) / (4 * KW);
   const dim3 gk(p.Hkv, p.num_seqs, ktiles);
-  if (p.G2) bwd_dkdv_kernel<DQK, DV, KW, (DV <= 256), true><<<gk, 256, 0, st>>>(p);
-  else bwd_dkdv_kernel<DQK, DV, KW, (DV <= 256), false><<<gk, 256, 0, st>>>(p);
+  if (p.G2) bwd_dkdv_kernel<DQK, DV, KW, true><<<gk, 256, 0, st>>>(p);
+  else bwd_dkdv_kernel<DQK, DV, KW, false><<<gk, 256, 0, st>>>(p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int qtiles = (p.max_seqlen + 4 * RW - 1) / (4 * RW);
