@@ -24,7 +24,7 @@
 #define BWD_KW_SMALL 16
 #endif
 #ifndef BWD_RW_SMALL
-#define BWD_RW_SMALL 16
+#define BWD_RW_SMALL 32
 #endif
 
 namespace attn {
