@@ -146,16 +146,23 @@ __device__ __forceinline__ void lds_barrier() {
 
 // ---------------------------------------------------------------------------
 // Swizzled LDS tiles: a tile of rows of RB bytes is stored without padding;
-// the 16-byte chunk c of row r sits at chunk position c ^ swz(r).  With
-// RB >= 256 the swizzle 2*(r%8) + (r/8)%2 makes both access patterns used by
-// the kernels free of bank conflicts: 16 lanes reading the same logical
-// chunk of 16 consecutive rows (MFMA operand rows), and ds_read_b64_tr_b16
-// reading two adjacent chunks of 4 consecutive rows.  128-byte rows use
-// (r/2)%8.
+// the 16-byte chunk c of row r sits at chunk position c ^ swz(r).  The
+// kernels read a tile in two ways: MFMA operand rows (ds_read_b128: 16 lanes
+// read the same logical chunk of 16 consecutive rows, 4 lane groups read 4
+// adjacent chunks) and transposed reads (ds_read_b64_tr_b16: each lane group
+// reads two adjacent chunks of 4 consecutive rows).  Measured on gfx950 with
+// the bank-conflict counter, ds_read_b128 is served 32 lanes at a time over
+// 512 bytes of banks and the transposed read 32 lanes at a time over 256
+// bytes.  Under that model these swizzles are free of conflicts for both
+// reads (confirmed by the counter): 256-byte rows XOR the chunk with
+// 2*(r%8) ^ 2*((r/8)%2); 128-byte rows with 2*(((r/2)%4) ^ ((r/8)%2)).
+// (The more obvious 2*(r%8)+(r/8)%2 conflicts 2-way on the row reads, and
+// r%16 2-way on the transposed ones.)  Wider rows use the 256-byte rule on
+// the low four chunk bits.
 template <int RB>
 __device__ __forceinline__ int tile_swz(int r) {
-  if constexpr (RB >= 256) return ((r & 7) << 1) | ((r >> 3) & 1);
-  else return (r >> 1) & (RB / 16 - 1);
+  if constexpr (RB >= 256) return ((r & 7) << 1) ^ (((r >> 3) & 1) << 1);
+  else return (((r >> 1) & 3) ^ ((r >> 3) & 1)) << 1;
 }
 // LDS byte offset of logical byte `b` (within its row) of row r.
 template <int RB>
