@@ -157,8 +157,9 @@ __device__ __forceinline__ void lds_barrier() {
 // reads (confirmed by the counter): 256-byte rows XOR the chunk with
 // 2*(r%8) ^ 2*((r/8)%2); 128-byte rows with 2*(((r/2)%4) ^ ((r/8)%2)).
 // (The more obvious 2*(r%8)+(r/8)%2 conflicts 2-way on the row reads, and
-// r%16 2-way on the transposed ones.)  Wider rows use the 256-byte rule on
-// the low four chunk bits.
+// r%16 2-way on the transposed ones.)  Rows of 512 bytes or more use the
+// 256-byte rule on the low chunk bits (measured faster there than the rule
+// the model suggests for them, so the model is incomplete for wide rows).
 template <int RB>
 __device__ __forceinline__ int tile_swz(int r) {
   if constexpr (RB >= 256) return ((r & 7) << 1) ^ (((r >> 3) & 1) << 1);
