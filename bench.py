@@ -309,6 +309,22 @@ def main():
             u = t4.mean_us("v")
             extra[f"verify_{tag}"] = {"us_per_layer": u, "GBps": decode_bytes(d4) / (u * 1e-6) / 1e9}
             del d4
+        # per-token fp8 KV-cache write: a 32K-token prefill's keys and values
+        xw = synth.kv_write_inputs(32768, 4, 128, 16, 2048 + 64, seed=1, skip_frac=0.0, device=dev)
+        fw = lambda: A.attn_kv_cache_write_fp8(xw["k_new"], xw["v_new"], xw["slot_mapping"], xw["k_cache"],
+                                               xw["v_cache"], xw["k_scale"], xw["v_scale"])
+        for _ in range(3):
+            fw()
+        tw = Timer()
+        for _ in range(20):
+            tw.run("w", fw)
+        torch.cuda.synchronize()
+        uw = tw.mean_us("w")
+        wbytes = 32768 * 4 * 2 * (2 * 128 + 128 + 4)    # bf16 in, fp8 codes + fp32 scale out
+        extra["kv_cache_write_fp8"] = {"tokens": 32768, "kv_heads": 4, "head_dim": 128, "us": uw,
+                                       "GBps": wbytes / (uw * 1e-6) / 1e9,
+                                       "frac_of_hbm_peak": wbytes / (uw * 1e-6) / 1e9 / HBM_PEAK_GBPS}
+        del xw
         x5 = synth.config5(device=dev)
         f5f, f5b, _ = prefill_flops(x5)
         o5, l5 = A.attn_fwd_varlen(x5.q, x5.k, x5.v, x5.cu_seqlens, x5.max_seqlen, x5.scale, 0,

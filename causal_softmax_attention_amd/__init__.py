@@ -24,7 +24,7 @@ from typing import Optional
 import torch
 
 __all__ = ["attn_fwd_varlen", "attn_bwd_varlen", "attn_decode_paged",
-           "attn_splitk_reduce", "attn_fwd_workspace_size",
+           "attn_splitk_reduce", "attn_kv_cache_write_fp8", "attn_fwd_workspace_size",
            "attn_bwd_workspace_size", "attn_decode_workspace_size",
            "ATTN_DTYPE_BF16", "ATTN_DTYPE_FP8_E4M3FN", "ATTN_DTYPE_FP32",
            "ATTN_BWD_DETERMINISTIC", "ATTN_BWD_FUSED_DQ",
@@ -65,6 +65,8 @@ _SIGNATURES = {
                            _vp, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _c_float,
                            _c_int, _vp, _vp, _vp, _c_size, _vp], _c_int),
     "attn_splitk_reduce": ([_vp, _vp, _vp, _c_int, _c_int, _c_int, _vp, _c_int, _vp, _vp], _c_int),
+    "attn_kv_cache_write_fp8": ([_vp, _vp, _vp, _c_int, _c_int, _c_int, _vp, _vp, _vp, _vp, _c_int,
+                                 _c_int, _vp], _c_int),
 }
 
 
@@ -291,3 +293,33 @@ def attn_splitk_reduce(acc, m, l, out_dtype=torch.float32, return_lse=True):
                                     _ptr(lse), _stream(dev))
     _check(st, "attn_splitk_reduce")
     return out, lse
+
+
+def attn_kv_cache_write_fp8(k_new, v_new, slot_mapping, k_cache, v_cache, k_scale, v_scale):
+    """Quantise new tokens into the paged fp8 cache in place.  k_new / v_new
+    bf16 [N, Hkv, D]; slot_mapping int32 [N] (page * block_size + offset,
+    negative = skip); k_cache / v_cache uint8 or float8_e4m3fn [NB, Hkv, B, D];
+    k_scale / v_scale fp32 [NB, Hkv, B]."""
+    dev = k_new.device
+    _need(k_new, "k_new", torch.bfloat16, None, 3)
+    _need(v_new, "v_new", torch.bfloat16, dev, 3)
+    _need(slot_mapping, "slot_mapping", torch.int32, dev, 1)
+    for name, c in (("k_cache", k_cache), ("v_cache", v_cache)):
+        if c.dtype not in (torch.uint8, torch.float8_e4m3fn):
+            raise ValueError(f"{name} must hold fp8 bytes (uint8 or float8_e4m3fn), got {c.dtype}")
+        _need(c, name, c.dtype, dev, 4)
+    _need(k_scale, "k_scale", torch.float32, dev, 3)
+    _need(v_scale, "v_scale", torch.float32, dev, 3)
+    N, Hkv, D = k_new.shape
+    if tuple(v_new.shape) != (N, Hkv, D) or slot_mapping.numel() != N:
+        raise ValueError("k_new, v_new must be [N, Hkv, D] and slot_mapping [N]")
+    NB, Hc, B, Dc = k_cache.shape
+    if (Hc, Dc) != (Hkv, D) or v_cache.shape != k_cache.shape:
+        raise ValueError("caches must be [NB, Hkv, B, D] with the new tokens' Hkv and D")
+    for s_ in (k_scale, v_scale):
+        if tuple(s_.shape) != (NB, Hkv, B):
+            raise ValueError(f"scales must be [{NB}, {Hkv}, {B}]")
+    st = library.attn_kv_cache_write_fp8(_ptr(k_new), _ptr(v_new), _ptr(slot_mapping), N, Hkv, D,
+                                         _ptr(k_cache), _ptr(v_cache), _ptr(k_scale), _ptr(v_scale),
+                                         NB, B, _stream(dev))
+    _check(st, "attn_kv_cache_write_fp8")

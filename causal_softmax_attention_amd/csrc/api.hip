@@ -393,4 +393,34 @@ int attn_splitk_reduce(const float* acc, const float* m, const float* l, int row
   return ok();
 }
 
+int attn_kv_cache_write_fp8(const void* k_new, const void* v_new, const int32_t* slot_mapping,
+                            int num_tokens, int num_kv_heads, int head_dim, void* k_cache,
+                            void* v_cache, float* k_scale, float* v_scale, int num_blocks,
+                            int block_size, void* stream) {
+  REQUIRE(num_tokens >= 0 && num_blocks >= 0, ATTN_ERR_INVALID,
+          "negative size (num_tokens=%d num_blocks=%d)", num_tokens, num_blocks);
+  REQUIRE(num_kv_heads >= 1, ATTN_ERR_INVALID, "num_kv_heads %d must be positive", num_kv_heads);
+  REQUIRE(head_dim == 64 || head_dim == 128, ATTN_ERR_UNSUPPORTED, "head_dim %d not supported (64, 128)",
+          head_dim);
+  REQUIRE(block_size == 16 || block_size == 32 || block_size == 64 || block_size == 128,
+          ATTN_ERR_UNSUPPORTED, "block_size %d not supported (16, 32, 64, 128)", block_size);
+  REQUIRE((long)num_blocks * block_size <= 0x7fffffffL, ATTN_ERR_UNSUPPORTED,
+          "num_blocks * block_size exceeds the int32 slot range");
+  if (num_tokens == 0) return ok();
+  REQ_PTR(k_new, 16);
+  REQ_PTR(v_new, 16);
+  REQ_PTR(slot_mapping, 4);
+  REQ_PTR(k_cache, 8);
+  REQ_PTR(v_cache, 8);
+  REQ_PTR(k_scale, 4);
+  REQ_PTR(v_scale, 4);
+  attn::KvWriteParams p{};
+  p.k_new = k_new; p.v_new = v_new; p.slot_mapping = slot_mapping;
+  p.k_cache = k_cache; p.v_cache = v_cache; p.k_scale = k_scale; p.v_scale = v_scale;
+  p.N = num_tokens; p.Hkv = num_kv_heads; p.NB = num_blocks; p.B = block_size;
+  hipError_t e = attn::launch_kv_cache_write_fp8(p, head_dim, reinterpret_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "kv cache write launch");
+  return ok();
+}
+
 }  // extern "C"

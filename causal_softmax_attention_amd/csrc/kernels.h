@@ -47,6 +47,18 @@ struct DecodeParams {
 };
 hipError_t launch_decode_splitk(const DecodeParams& p, int head_dim, bool fp8, hipStream_t st);
 
+struct KvWriteParams {
+  const void* k_new;        // bf16 [N, Hkv, D]
+  const void* v_new;
+  const int32_t* slot_mapping;  // [N]: page * B + offset, < 0 to skip
+  void* k_cache;            // fp8 bytes [NB, Hkv, B, D]
+  void* v_cache;
+  float* k_scale;           // [NB, Hkv, B]
+  float* v_scale;
+  int N, Hkv, NB, B;
+};
+hipError_t launch_kv_cache_write_fp8(const KvWriteParams& p, int head_dim, hipStream_t st);
+
 struct FwdParams {
   const void* q;            // bf16 [T, Hq, DQK]
   const void* k;            // bf16 [T, Hkv, DQK]

@@ -238,8 +238,9 @@ int attn_decode_paged(const void* q, const int32_t* cu_seqlens_q,
  * For each row r with partials s = 0..num_splits-1:
  *   M = max_s m[r,s];  w_s = e^(m[r,s] - M), or 0 when m[r,s] = -inf
  *   L = sum_s w_s l[r,s];  out[r] = sum_s w_s acc[r,s,:] / L;  lse[r] = M + ln L
- * acc and l of a split with m = -inf are never read.  A row whose partials
- * are all empty gets out = 0 and lse = -inf.
+ * acc and l of a split with m = -inf never enter the sums (they may be
+ * read, and may hold anything, NaN included).  A row whose partials are all
+ * empty gets out = 0 and lse = -inf.
  *
  *   acc fp32 [rows, num_splits, head_dim_v]  (unnormalised accumulators)
  *   m   fp32 [rows, num_splits]  (running max of natural-log logits)
@@ -251,6 +252,35 @@ int attn_decode_paged(const void* q, const int32_t* cu_seqlens_q,
 int attn_splitk_reduce(const float* acc, const float* m, const float* l,
                        int rows, int num_splits, int head_dim_v,
                        void* out, int out_dtype, float* lse, void* stream);
+
+/* ------------------------------------------------------------------------
+ * attn_kv_cache_write_fp8 -- quantise new K/V tokens into a paged fp8 cache
+ * with one scale per token and KV head (aiter PR #6660, commit messages and
+ * Technical details: per-token fp8 KV scales, read back by decode).
+ *
+ * For each new token t and KV head h, separately for K and V:
+ *   amax = max_d |x[t,h,d]|;  scale = amax / 448 (1 when amax = 0)
+ *   code[d] = e4m3fn(clamp(x[t,h,d] / scale, -448, 448)), round to nearest even
+ * written to page slot_mapping[t] / block_size, offset slot_mapping[t] %
+ * block_size of the cache and the scales.  A negative slot (padding token)
+ * or one at or past num_blocks * block_size is skipped.  Two tokens mapped
+ * to the same slot leave one of them there (unspecified which).
+ *
+ *   k_new, v_new   bf16 [num_tokens, num_kv_heads, head_dim] (read)
+ *   slot_mapping   int32 [num_tokens] (read)
+ *   k_cache, v_cache  fp8 e4m3fn bytes [num_blocks, num_kv_heads, block_size,
+ *                  head_dim] (written at the mapped slots only)
+ *   k_scale, v_scale  fp32 [num_blocks, num_kv_heads, block_size] (same)
+ * Supported: head_dim 64 or 128; block_size 16, 32, 64 or 128.
+ * No workspace.  Errors as for the other entry points; nothing is launched
+ * on error.
+ * ---------------------------------------------------------------------- */
+int attn_kv_cache_write_fp8(const void* k_new, const void* v_new,
+                            const int32_t* slot_mapping, int num_tokens,
+                            int num_kv_heads, int head_dim,
+                            void* k_cache, void* v_cache,
+                            float* k_scale, float* v_scale,
+                            int num_blocks, int block_size, void* stream);
 
 #ifdef __cplusplus
 }

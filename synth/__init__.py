@@ -292,3 +292,37 @@ def partials_inputs(rows, S, Dv, *, seed, empty_frac=0.25, device="cpu"):
     l = torch.where(empty, torch.full_like(l, float("nan")), l)
     acc = torch.where(empty[..., None], torch.full_like(acc, float("nan")), acc)
     return acc.contiguous(), m.contiguous(), l.contiguous()
+
+
+# ----------------------------------------------------------------------------
+# KV-cache write inputs
+# ----------------------------------------------------------------------------
+def kv_write_inputs(N, Hkv, D, B, NB, *, seed, skip_frac=0.1, zero_rows=1, device="cpu"):
+    """New tokens for a paged fp8 cache write.
+
+    k_new, v_new bf16 [N, Hkv, D] with per-(token, head) magnitudes varying up
+    to 20x (N(0,1) * 20^u, as in the decode caches); ``zero_rows`` (token,
+    head) rows are all zeros.  slot_mapping int32 [N]: distinct slots drawn
+    from the NB * B slots, a fraction ``skip_frac`` replaced by -1 (padding).
+    The caches start poisoned (0x7F bytes, NaN scales) so that any slot the
+    write should not touch shows."""
+    gen = _gen(seed, "cpu")
+    mag = torch.pow(torch.tensor(20.0), torch.rand((N, Hkv, 1), generator=gen))
+    k = (_randn((N, Hkv, D), gen, "cpu") * mag).to(torch.bfloat16)
+    mag = torch.pow(torch.tensor(20.0), torch.rand((N, Hkv, 1), generator=gen))
+    v = (_randn((N, Hkv, D), gen, "cpu") * mag).to(torch.bfloat16)
+    for i in range(min(zero_rows, N * Hkv)):
+        t, h = divmod((i * 7919) % (N * Hkv), Hkv)
+        k[t, h] = 0
+        v[(t + 1) % N, h] = 0
+    assert N <= NB * B
+    slots = torch.randperm(NB * B, generator=gen)[:N].to(torch.int32)
+    skip = torch.rand((N,), generator=gen) < skip_frac
+    slots = torch.where(skip, torch.full_like(slots, -1), slots)
+    k_cache = torch.full((NB, Hkv, B, D), 0x7F, dtype=torch.uint8)
+    v_cache = k_cache.clone()
+    k_scale = torch.full((NB, Hkv, B), float("nan"), dtype=torch.float32)
+    v_scale = k_scale.clone()
+    out = dict(k_new=k, v_new=v, slot_mapping=slots, k_cache=k_cache, v_cache=v_cache,
+               k_scale=k_scale, v_scale=v_scale)
+    return {n: t.to(device).contiguous() for n, t in out.items()}

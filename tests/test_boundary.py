@@ -182,3 +182,31 @@ def test_python_wrapper_rejects_strided_and_wrong_dtype():
         A.attn_fwd_varlen(q.float(), k, k, cu, 10)
     with pytest.raises(ValueError, match="int32"):
         A.attn_fwd_varlen(q, k, k, cu.long(), 10)
+
+
+def _kvw(**kw):
+    a = dict(k=P, v=P, slots=P, N=4, H=4, D=128, kc=P, vc=P, ks=P, vs=P, NB=8, B=16)
+    a.update(kw)
+    return L.attn_kv_cache_write_fp8(a["k"], a["v"], a["slots"], a["N"], a["H"], a["D"], a["kc"], a["vc"],
+                                     a["ks"], a["vs"], a["NB"], a["B"], NULL)
+
+
+@pytest.mark.parametrize("kw,code,msg", [
+    (dict(N=-1), INVALID, "negative"),
+    (dict(H=0), INVALID, "num_kv_heads"),
+    (dict(D=96), UNSUPPORTED, "head_dim"),
+    (dict(B=24), UNSUPPORTED, "block_size"),
+    (dict(k=NULL), INVALID, "k_new is NULL"),
+    (dict(slots=NULL), INVALID, "slot_mapping is NULL"),
+    (dict(ks=NULL), INVALID, "k_scale is NULL"),
+    (dict(k=P_ODD), INVALID, "aligned"),
+    (dict(NB=1 << 28, B=128), UNSUPPORTED, "int32 slot range"),
+])
+def test_kv_cache_write_validation(kw, code, msg):
+    st = _kvw(**kw)
+    assert st == code
+    assert msg in L.attn_last_error().decode()
+
+
+def test_kv_cache_write_empty_is_a_no_op():
+    assert _kvw(N=0, k=NULL, v=NULL, slots=NULL) == OK
