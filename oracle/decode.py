@@ -17,6 +17,16 @@ split-K"):
     merged by a log-sum-exp reduce; a query whose visible keys end before a
     segment gives an empty partial (M = -inf) of weight 0.
 
+Decode features of the prefill method (fla issue #1322, Description: the
+packed single-query decoding counterparts of the sink, sliding window and
+log gate), with the same definitions as the prefill oracle: a per-query-head
+sink logit adds e^sigma to the denominator; key j is visible from the query
+at position p iff p - j < window (window <= 0: no window); the score gains
+G_p - G_j with G the cumulative log gate of each token and query head, read
+from a paged gate cache [num_blocks, Hq, block_size] at the key's and at the
+query's own position.  Per-tensor scales (one K and one V scale for the whole
+cache) replace the per-token ones when ``per_tensor`` is set.
+
 Readings: the cache data layout is [num_blocks, num_kv_heads, block_size, D];
 token j of request r sits in page block_table[r][j // B], slot j % B; query t
 of a request with KV length L and n new tokens sits at position L - n + t and
@@ -47,10 +57,10 @@ def fp8_e4m3fn_to_f64(codes):
     return np.where((e == 15) & (m == 7), np.nan, out)
 
 
-def gather_request_kv(cache, scale, block_table, r, L, B, fp8):
+def gather_request_kv(cache, scale, block_table, r, L, B, fp8, per_tensor=False):
     """Dequantised keys (or values) of request r: [L, Hkv, D] float64, token
     j read from page block_table[r][j // B], slot j % B, times its per-token
-    scale for fp8."""
+    scale for fp8 (or the single per-tensor scale)."""
     bt = _i64(block_table)
     j = np.arange(L)
     pages = bt[r, j // B]
@@ -58,9 +68,20 @@ def gather_request_kv(cache, scale, block_table, r, L, B, fp8):
     raw = cache[pages, :, slots, :]            # [L, Hkv, D]
     if fp8:
         x = fp8_e4m3fn_to_f64(raw)
+        if per_tensor:
+            return x * float(np.asarray(_f64(scale)).reshape(-1)[0])
         sc = _f64(scale)[pages, :, slots]      # [L, Hkv]
         return x * sc[..., None]
     return _f64(raw)
+
+
+def gather_request_gates(g_cache, block_table, r, L, B):
+    """Cumulative log gates of request r's tokens: [L, Hq] float64, token j
+    read from page block_table[r][j // B], slot j % B of g_cache
+    [num_blocks, Hq, B]."""
+    bt = _i64(block_table)
+    j = np.arange(L)
+    return _f64(g_cache)[bt[r, j // B], :, j % B]
 
 
 def _as_cache(c):
@@ -74,9 +95,13 @@ def _as_cache(c):
 
 
 def decode_paged(q, cu_seqlens_q, k_cache, v_cache, block_table, seq_lens,
-                 scale, fp8, k_scale=None, v_scale=None, requests=None):
-    """o[t, h] = sum_{j <= p_t} softmax_j(scale * q_t . Khat_j) Vhat_j over
-    the dequantised paged cache; also lse[t, h].  No sink, gate or window.
+                 scale, fp8, k_scale=None, v_scale=None, requests=None,
+                 sink=None, window=0, g_cache=None, per_tensor=False):
+    """o[t, h] = softmax over the visible keys of
+    s_j = scale * q_t . Khat_j + (G_p - G_j) (gate term only with a gate
+    cache), with e^sink[h] added to the denominator when a sink is given;
+    visible keys are j <= p with p - j < window (window <= 0: all j <= p).
+    Also lse[t, h] (natural log, sink mass included).
 
     Returns (o [Tq, Hq, D], lse [Tq, Hq]) float64.  With ``requests`` given,
     only those requests' rows are filled (others NaN).
@@ -85,6 +110,7 @@ def decode_paged(q, cu_seqlens_q, k_cache, v_cache, block_table, seq_lens,
     cu = _i64(cu_seqlens_q)
     L_all = _i64(seq_lens)
     kc, vc = _as_cache(k_cache), _as_cache(v_cache)
+    sink = None if sink is None else _f64(sink)
     B = kc.shape[2]
     Tq, Hq, D = q.shape
     Hkv = kc.shape[1]
@@ -95,36 +121,45 @@ def decode_paged(q, cu_seqlens_q, k_cache, v_cache, block_table, seq_lens,
     for r in reqs:
         L = int(L_all[r])
         n = int(cu[r + 1] - cu[r])
-        K = gather_request_kv(kc, k_scale, block_table, r, L, B, fp8)
-        V = gather_request_kv(vc, v_scale, block_table, r, L, B, fp8)
+        K = gather_request_kv(kc, k_scale, block_table, r, L, B, fp8, per_tensor)
+        V = gather_request_kv(vc, v_scale, block_table, r, L, B, fp8, per_tensor)
+        G = None if g_cache is None else gather_request_gates(g_cache, block_table, r, L, B)
         for t in range(n):
             p = L - n + t
+            j0 = 0 if window <= 0 else max(0, p - window + 1)
             for h in range(Hq):
-                s = scale * (K[:p + 1, h // grp] @ q[cu[r] + t, h])
-                m = np.max(s)
+                s = scale * (K[j0:p + 1, h // grp] @ q[cu[r] + t, h])
+                if G is not None:
+                    s = s + (G[p, h] - G[j0:p + 1, h])
+                sh = -np.inf if sink is None else sink[h]
+                m = max(np.max(s), sh)
                 e = np.exp(s - m)
-                l = e.sum()
-                o[cu[r] + t, h] = (e / l) @ V[:p + 1, h // grp]
+                l = e.sum() + (np.exp(sh - m) if np.isfinite(sh) else 0.0)
+                o[cu[r] + t, h] = (e / l) @ V[j0:p + 1, h // grp]
                 lse[cu[r] + t, h] = m + np.log(l)
     return o, lse
 
 
 def decode_partials(q, cu_seqlens_q, k_cache, v_cache, block_table, seq_lens,
                     scale, fp8, split_len, num_splits, k_scale=None,
-                    v_scale=None):
+                    v_scale=None, sink=None, window=0, g_cache=None,
+                    per_tensor=False):
     """Split-K partials over KV segments [s*split_len, (s+1)*split_len) of
     each request, for every query row (row = token * Hq + head):
-      m_s   = max of the scaled logits in the segment that the query sees,
-              or -inf when it sees none of them;
+      m_s   = max of the logits (as in decode_paged) of the segment's keys
+              that the query sees, or -inf when it sees none of them;
       l_s   = sum of exp(logit - m_s) over those keys;
       acc_s = sum of exp(logit - m_s) Vhat_j over those keys.
-    Empty partials carry l = 0 and acc = 0.  Returns (acc [rows, S, D],
-    m [rows, S], l [rows, S]) float64 with S = num_splits.
+    The sink, when given, belongs to segment 0: m_0 = max(sink, ...) and l_0
+    gains exp(sink - m_0) (it carries no value).  Empty partials carry l = 0
+    and acc = 0.  Returns (acc [rows, S, D], m [rows, S], l [rows, S])
+    float64 with S = num_splits.
     """
     q = _f64(q)
     cu = _i64(cu_seqlens_q)
     L_all = _i64(seq_lens)
     kc, vc = _as_cache(k_cache), _as_cache(v_cache)
+    sink = None if sink is None else _f64(sink)
     B = kc.shape[2]
     Tq, Hq, D = q.shape
     Dv = vc.shape[3]
@@ -135,23 +170,31 @@ def decode_partials(q, cu_seqlens_q, k_cache, v_cache, block_table, seq_lens,
     for r in range(len(cu) - 1):
         L = int(L_all[r])
         n = int(cu[r + 1] - cu[r])
-        K = gather_request_kv(kc, k_scale, block_table, r, L, B, fp8)
-        V = gather_request_kv(vc, v_scale, block_table, r, L, B, fp8)
+        K = gather_request_kv(kc, k_scale, block_table, r, L, B, fp8, per_tensor)
+        V = gather_request_kv(vc, v_scale, block_table, r, L, B, fp8, per_tensor)
+        G = None if g_cache is None else gather_request_gates(g_cache, block_table, r, L, B)
         for t in range(n):
             p = L - n + t
+            lo = 0 if window <= 0 else max(0, p - window + 1)
             for h in range(Hq):
                 row = (cu[r] + t) * Hq + h
                 for s_ in range(num_splits):
-                    j0 = s_ * split_len
+                    j0 = max(s_ * split_len, lo)
                     j1 = min((s_ + 1) * split_len, p + 1)
-                    if j1 <= j0:
+                    sh = sink[h] if (sink is not None and s_ == 0) else -np.inf
+                    if j1 <= j0 and not np.isfinite(sh):
                         continue
-                    sc = scale * (K[j0:j1, h // grp] @ q[cu[r] + t, h])
-                    ms = np.max(sc)
+                    if j1 > j0:
+                        sc = scale * (K[j0:j1, h // grp] @ q[cu[r] + t, h])
+                        if G is not None:
+                            sc = sc + (G[p, h] - G[j0:j1, h])
+                    else:
+                        sc = np.zeros(0)
+                    ms = max(np.max(sc) if sc.size else -np.inf, sh)
                     e = np.exp(sc - ms)
                     m[row, s_] = ms
-                    l[row, s_] = e.sum()
-                    acc[row, s_] = e @ V[j0:j1, h // grp]
+                    l[row, s_] = e.sum() + (np.exp(sh - ms) if np.isfinite(sh) else 0.0)
+                    acc[row, s_] = e @ V[j0:j1, h // grp] if sc.size else 0.0
     return acc, m, l
 
 

@@ -151,6 +151,10 @@ class DecodeInputs:
     name: str = ""
     unquantized_k: Optional[torch.Tensor] = field(default=None, repr=False)
     unquantized_v: Optional[torch.Tensor] = field(default=None, repr=False)
+    sink: Optional[torch.Tensor] = None        # fp32 [Hq] sink logits, or None
+    window: int = 0                            # sliding window (<= 0: none)
+    g_cache: Optional[torch.Tensor] = None     # fp32 [NB, Hq, B] cumulative log gates, or None
+    per_tensor: bool = False                   # fp8 with one K and one V scale ([1] each)
 
     @property
     def num_requests(self): return int(self.block_table.shape[0])
@@ -166,7 +170,9 @@ class DecodeInputs:
 
 def decode_inputs(seq_lens, q_lens, Hq, Hkv, D, B, *, kv_dtype, seed,
                   spread=20.0, spare_pages=64, device="cpu",
-                  keep_unquantized=False, shuffle=True, name="") -> DecodeInputs:
+                  keep_unquantized=False, shuffle=True, name="",
+                  window=0, with_sink=False, with_gate=False, per_tensor=False,
+                  gate_slope=0.002) -> DecodeInputs:
     """A paged KV cache [NB, Hkv, B, D] with a shuffled page table.
 
     Values per (token, KV head) are N(0,1) * spread**u, u ~ U(0,1), drawn
@@ -176,6 +182,14 @@ def decode_inputs(seq_lens, q_lens, Hq, Hkv, D, B, *, kv_dtype, seed,
     e4m3fn; unused scale slots hold NaN and unused data bytes a NaN code.  For
     bf16 unused slots hold bf16 NaN.  Spare pages that no request references
     are poisoned the same way.
+
+    Optional decode features: ``with_sink`` draws sink logits N(0,1) per
+    query head; ``window`` is passed through; ``with_gate`` fills a gate cache
+    [NB, Hq, B] with a slowly falling sequence per (token, query head):
+    G = -gate_slope * (token position) * r_h + 0.05 * N(0,1), r_h ~ U(0.5, 1.5)
+    (any values are valid decode inputs; unused slots hold NaN);
+    ``per_tensor`` (fp8) quantises each cache with one scale, the amax of its
+    valid values / 448.
     """
     rng = np.random.default_rng(seed)
     seq_lens = [int(x) for x in seq_lens]
@@ -193,12 +207,14 @@ def decode_inputs(seq_lens, q_lens, Hq, Hkv, D, B, *, kv_dtype, seed,
     pad = int(perm[used]) if spare_pages > 0 else 0
     bt = np.full((R, max_pages), pad, dtype=np.int32)
     owner_len = np.zeros(NB, dtype=np.int64)   # valid slots in each page
+    page_pos = np.zeros(NB, dtype=np.int64)    # index of the page within its request
     off = 0
     for r in range(R):
         ids = perm[off:off + pages[r]]
         bt[r, :pages[r]] = ids
         for p, pid in enumerate(ids):
             owner_len[pid] = min(B, seq_lens[r] - p * B)
+            page_pos[pid] = p
         off += pages[r]
 
     gen = _gen(seed, device)
@@ -216,6 +232,13 @@ def decode_inputs(seq_lens, q_lens, Hq, Hkv, D, B, *, kv_dtype, seed,
         return x
 
     def make(x):
+        if kv_dtype == KV_FP8_E4M3FN and per_tensor:
+            amax = torch.where(valid[..., None], x.abs(), torch.zeros_like(x)).amax()
+            sc1 = (amax / FP8_E4M3FN_MAX).reshape(1).to(torch.float32)
+            codes = (x / sc1).to(torch.float8_e4m3fn).view(torch.uint8)
+            codes = torch.where(valid[..., None], codes,
+                                torch.full_like(codes, FP8_POISON_BYTE))
+            return codes.contiguous(), sc1.contiguous()
         if kv_dtype == KV_FP8_E4M3FN:
             amax = x.abs().amax(dim=-1)
             sc = torch.where(amax > 0, amax / FP8_E4M3FN_MAX, torch.ones_like(amax))
@@ -241,10 +264,20 @@ def decode_inputs(seq_lens, q_lens, Hq, Hkv, D, B, *, kv_dtype, seed,
         xv = None
     cu = torch.tensor(np.concatenate([[0], np.cumsum(q_lens)]).astype(np.int32),
                       device=device)
+    sink = _randn((Hq,), gen, device) if with_sink else None
+    g_cache = None
+    if with_gate:
+        pos = torch.from_numpy(page_pos[:, None] * B + np.arange(B)[None, :]).to(device)   # [NB, B]
+        rate = torch.rand((Hq,), generator=gen, device=device) + 0.5
+        G = (-gate_slope * pos[:, None, :].to(torch.float32) * rate[None, :, None]
+             + 0.05 * _randn((NB, Hq, B), gen, device))
+        gvalid = torch.from_numpy(np.arange(B)[None, :] < owner_len[:, None]).to(device)[:, None, :]
+        g_cache = torch.where(gvalid, G, torch.full_like(G, float("nan"))).contiguous()
     return DecodeInputs(q, cu, q_lens, kc, vc, ks, vs,
                         torch.from_numpy(bt).to(device),
                         torch.tensor(seq_lens, dtype=torch.int32, device=device),
-                        int(kv_dtype), int(B), 1.0 / math.sqrt(D), name, xk, xv)
+                        int(kv_dtype), int(B), 1.0 / math.sqrt(D), name, xk, xv,
+                        sink, int(window), g_cache, bool(per_tensor and kv_dtype == KV_FP8_E4M3FN))
 
 
 def config3_seq_lens():

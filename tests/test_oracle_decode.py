@@ -185,3 +185,86 @@ def test_quantised_cache_close_to_unquantised():
     j = np.arange(200)
     X = d.unquantized_k.numpy()[bt[j // 16], :, j % 16, :]
     assert rel_rms(K, X) < 0.05
+
+
+# ----------------------------------------------------------------------------
+# decode with sink, sliding window, log gate and per-tensor scales
+# ----------------------------------------------------------------------------
+def _dense_request(d, r, fp8=True):
+    B = d.block_size
+    L = int(d.seq_lens[r])
+    host = lambda c: c.double().numpy() if c.dtype == torch.bfloat16 else c.numpy()
+    K = oracle.gather_request_kv(host(d.k_cache), None if d.k_scale is None else d.k_scale.numpy(),
+                                 d.block_table.numpy(), r, L, B, fp8, d.per_tensor)
+    V = oracle.gather_request_kv(host(d.v_cache), None if d.v_scale is None else d.v_scale.numpy(),
+                                 d.block_table.numpy(), r, L, B, fp8, d.per_tensor)
+    return K, V
+
+
+@pytest.mark.parametrize("window,sink,gate", [(0, True, False), (48, False, False), (0, False, True),
+                                              (100, True, True), (1, True, True)])
+def test_decode_features_equal_prefill_rows(window, sink, gate):
+    """Decode with sink / window / gate on the dequantised cache equals the
+    prefill oracle's rows for the same query positions, with the gates given
+    as differences of the cached cumulative gate."""
+    d = synth.decode_inputs([70, 260], [1, 3], 8, 2, 64, 16, kv_dtype=synth.KV_FP8_E4M3FN, seed=21,
+                            window=window, with_sink=sink, with_gate=gate, spare_pages=2)
+    o, lse = oracle.decode_paged(d.q, d.cu_seqlens_q, d.k_cache, d.v_cache, d.block_table, d.seq_lens,
+                                 d.scale, True, d.k_scale, d.v_scale, sink=d.sink, window=d.window,
+                                 g_cache=d.g_cache)
+    cu = d.cu_seqlens_q.numpy()
+    for r in range(2):
+        L = int(d.seq_lens[r]); n = int(cu[r + 1] - cu[r])
+        K, V = _dense_request(d, r)
+        q = np.zeros((L, 8, 64)); q[L - n:] = d.q[cu[r]:cu[r + 1]].double().numpy()
+        g = None
+        if gate:
+            G = oracle.gather_request_gates(d.g_cache.numpy(), d.block_table.numpy(), r, L, d.block_size)
+            g = np.diff(np.concatenate([np.zeros((1, 8)), G]), axis=0)
+        ro, rl = oracle.forward_rows(q, K, V, np.array([0, L]), d.scale, list(range(L - n, L)),
+                                     list(range(8)), window=window, sink=d.sink, g=g)
+        np.testing.assert_allclose(o[cu[r]:cu[r + 1]], ro, rtol=1e-9, atol=1e-9)
+        np.testing.assert_allclose(lse[cu[r]:cu[r + 1]], rl, rtol=1e-9, atol=1e-9)
+
+
+def test_decode_window_one_closed_form():
+    """Window 1: the query sees only its own key, so o = v_p e^s / (e^s + e^sink)."""
+    d = synth.decode_inputs([33], [2], 4, 1, 64, 16, kv_dtype=synth.KV_BF16, seed=22, window=1,
+                            with_sink=True, spare_pages=1)
+    o, _ = oracle.decode_paged(d.q, d.cu_seqlens_q, d.k_cache, d.v_cache, d.block_table, d.seq_lens,
+                               d.scale, False, sink=d.sink, window=1)
+    K, V = _dense_request(d, 0, fp8=False)
+    for t, p in enumerate((31, 32)):
+        for h in range(4):
+            s = d.scale * float(K[p, 0] @ d.q[t, h].double().numpy())
+            w = np.exp(s) / (np.exp(s) + np.exp(float(d.sink[h])))
+            np.testing.assert_allclose(o[t, h], w * V[p, 0], rtol=1e-12, atol=1e-12)
+
+
+def test_per_tensor_scales_equal_uniform_per_token_scales():
+    d = synth.decode_inputs([50, 90], [1, 2], 8, 2, 64, 16, kv_dtype=synth.KV_FP8_E4M3FN, seed=23,
+                            per_tensor=True, spare_pages=1)
+    o1, l1 = oracle.decode_paged(d.q, d.cu_seqlens_q, d.k_cache, d.v_cache, d.block_table, d.seq_lens,
+                                 d.scale, True, d.k_scale, d.v_scale, per_tensor=True)
+    NB, Hkv, B = d.k_cache.shape[:3]
+    ks = np.full((NB, Hkv, B), float(d.k_scale[0])); vs = np.full((NB, Hkv, B), float(d.v_scale[0]))
+    o2, l2 = oracle.decode_paged(d.q, d.cu_seqlens_q, d.k_cache, d.v_cache, d.block_table, d.seq_lens,
+                                 d.scale, True, ks, vs)
+    np.testing.assert_array_equal(o1, o2)
+    np.testing.assert_array_equal(l1, l2)
+
+
+def test_split_invariance_with_sink_window_gate():
+    d = synth.decode_inputs([70, 260], [1, 3], 8, 2, 64, 16, kv_dtype=synth.KV_FP8_E4M3FN, seed=24,
+                            window=40, with_sink=True, with_gate=True, spare_pages=2)
+    o, lse = oracle.decode_paged(d.q, d.cu_seqlens_q, d.k_cache, d.v_cache, d.block_table, d.seq_lens,
+                                 d.scale, True, d.k_scale, d.v_scale, sink=d.sink, window=d.window,
+                                 g_cache=d.g_cache)
+    for split in (16, 32, 64):
+        S = (260 + split - 1) // split
+        acc, m, l = oracle.decode_partials(d.q, d.cu_seqlens_q, d.k_cache, d.v_cache, d.block_table,
+                                           d.seq_lens, d.scale, True, split, S, d.k_scale, d.v_scale,
+                                           sink=d.sink, window=d.window, g_cache=d.g_cache)
+        ro, rl = oracle.splitk_reduce(acc, m, l)
+        np.testing.assert_allclose(ro.reshape(o.shape), o, rtol=1e-10, atol=1e-12)
+        np.testing.assert_allclose(rl.reshape(lse.shape), lse, rtol=1e-10, atol=1e-12)
