@@ -309,6 +309,25 @@ def main():
             u = t4.mean_us("v")
             extra[f"verify_{tag}"] = {"us_per_layer": u, "GBps": decode_bytes(d4) / (u * 1e-6) / 1e9}
             del d4
+        # decode with sink, 4096-token window and log gate on the config-3 cache
+        df = synth.config3(device=dev, with_sink=True, window=4096, with_gate=True)
+        dmax = df.max_seq_len
+        ff = lambda: A.attn_decode_paged(df.q, df.cu_seqlens_q, 1, df.k_cache, df.v_cache, df.kv_dtype,
+                                         df.k_scale, df.v_scale, df.block_table, df.seq_lens, dmax, df.scale,
+                                         sink=df.sink, window=df.window, g_cache=df.g_cache)
+        for _ in range(3):
+            ff()
+        tf_ = Timer()
+        for _ in range(20):
+            tf_.run("f", ff)
+        torch.cuda.synchronize()
+        uf = tf_.mean_us("f")
+        vis = [min(int(L), 4096) for L in df.seq_lens.tolist()]     # keys inside the window (1 query each)
+        Hkv_, D_, Hq_ = df.k_cache.shape[1], df.k_cache.shape[3], df.q.shape[1]
+        fbytes = sum(vis) * (Hkv_ * (2 * D_ + 8) + Hq_ * 4)          # fp8 K+V, two scales, gate per query head
+        extra["decode_sink_window4096_gate"] = {"us_per_layer": uf, "GBps": fbytes / (uf * 1e-6) / 1e9,
+                                                "algorithmic_bytes": fbytes}
+        del df
         # per-token fp8 KV-cache write: a 32K-token prefill's keys and values
         xw = synth.kv_write_inputs(32768, 4, 128, 16, 2048 + 64, seed=1, skip_frac=0.0, device=dev)
         fw = lambda: A.attn_kv_cache_write_fp8(xw["k_new"], xw["v_new"], xw["slot_mapping"], xw["k_cache"],

@@ -64,6 +64,9 @@ _SIGNATURES = {
     "attn_decode_paged": ([_vp, _vp, _c_int, _c_int, _vp, _vp, _c_int, _vp, _vp, _vp, _c_int,
                            _vp, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _c_float,
                            _c_int, _vp, _vp, _vp, _c_size, _vp], _c_int),
+    "attn_decode_paged_ext": ([_vp, _vp, _c_int, _c_int, _vp, _vp, _c_int, _vp, _vp, _c_int, _vp, _c_int,
+                               _vp, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int, ctypes.c_float, _vp,
+                               _c_int, _vp, _c_int, _vp, _vp, _vp, ctypes.c_size_t, _vp], _c_int),
     "attn_splitk_reduce": ([_vp, _vp, _vp, _c_int, _c_int, _c_int, _vp, _c_int, _vp, _vp], _c_int),
     "attn_kv_cache_write_fp8": ([_vp, _vp, _vp, _c_int, _c_int, _c_int, _vp, _vp, _vp, _vp, _c_int,
                                  _c_int, _vp], _c_int),
@@ -228,11 +231,14 @@ def attn_bwd_varlen(q, k, v, o, do, lse, cu_seqlens, max_seqlen, softmax_scale=N
 
 def attn_decode_paged(q, cu_seqlens_q, max_seqlen_q, k_cache, v_cache, kv_dtype,
                       k_scale, v_scale, block_table, seq_lens, max_seq_len,
-                      softmax_scale=None, kv_split_len=0, return_lse=False, out=None):
+                      softmax_scale=None, kv_split_len=0, return_lse=False, out=None,
+                      sink=None, window=0, g_cache=None):
     """Paged decode.  q bf16 [Tq, Hq, D]; k_cache / v_cache [NB, Hkv, B, D]
     as bf16 or as uint8 / float8_e4m3fn codes; k_scale / v_scale fp32
     [NB, Hkv, B] for fp8 (None for bf16); block_table int32 [R, max_pages];
-    seq_lens int32 [R].  Returns out bf16 [Tq, Hq, D] (and lse fp32 [Tq, Hq])."""
+    seq_lens int32 [R].  Returns out bf16 [Tq, Hq, D] (and lse fp32 [Tq, Hq]).
+    Optional: one-element k_scale / v_scale = per-tensor fp8 scales; sink fp32
+    [Hq]; window (> 0); g_cache fp32 [NB, Hq, B] cumulative log gates."""
     dev = q.device
     _need(q, "q", torch.bfloat16, None, 3)
     _need(cu_seqlens_q, "cu_seqlens_q", torch.int32, dev, 1)
@@ -248,14 +254,26 @@ def attn_decode_paged(q, cu_seqlens_q, max_seqlen_q, k_cache, v_cache, kv_dtype,
         _need(c, name, c.dtype, dev, 4)
     for name, s in (("k_scale", k_scale), ("v_scale", v_scale)):
         if s is not None:
-            _need(s, name, torch.float32, dev, 3)
+            _need(s, name, torch.float32, dev, None)   # [NB, Hkv, B], or [1] per tensor
     Tq, Hq, D = q.shape
     NB, Hkv, B, Dc = k_cache.shape
     if v_cache.shape != k_cache.shape or Dc != D:
         raise ValueError("k_cache and v_cache must both be [NB, Hkv, B, D] with q's D")
+    per_tensor = k_scale is not None and k_scale.numel() == 1
     for s in (k_scale, v_scale):
-        if s is not None and tuple(s.shape) != (NB, Hkv, B):
-            raise ValueError(f"scales must be [{NB}, {Hkv}, {B}]")
+        if s is None:
+            continue
+        if per_tensor:
+            if s.numel() != 1:
+                raise ValueError("per-tensor scales: both k_scale and v_scale must hold one value")
+        elif tuple(s.shape) != (NB, Hkv, B):
+            raise ValueError(f"scales must be [{NB}, {Hkv}, {B}] (or one value each)")
+    if sink is not None:
+        _need(sink, "sink", torch.float32, dev, 1)
+    if g_cache is not None:
+        _need(g_cache, "g_cache", torch.float32, dev, 3)
+        if tuple(g_cache.shape) != (NB, Hq, B):
+            raise ValueError(f"g_cache must be [{NB}, {Hq}, {B}]")
     R = seq_lens.numel()
     if softmax_scale is None:
         softmax_scale = 1.0 / math.sqrt(D)
@@ -265,11 +283,12 @@ def attn_decode_paged(q, cu_seqlens_q, max_seqlen_q, k_cache, v_cache, kv_dtype,
     ws_n = attn_decode_workspace_size(R, int(max_seqlen_q), int(max_seq_len), Hq, Hkv, D, B,
                                       int(kv_split_len))
     ws = _workspace(ws_n, dev)
-    st = library.attn_decode_paged(
+    st = library.attn_decode_paged_ext(
         _ptr(q), _ptr(cu_seqlens_q), R, int(max_seqlen_q), _ptr(k_cache), _ptr(v_cache),
-        int(kv_dtype), _ptr(k_scale), _ptr(v_scale), _ptr(block_table), block_table.shape[1],
-        _ptr(seq_lens), int(max_seq_len), NB, B, Hq, Hkv, D, float(softmax_scale),
-        int(kv_split_len), _ptr(out), _ptr(lse), _ptr(ws), ws_n, _stream(dev))
+        int(kv_dtype), _ptr(k_scale), _ptr(v_scale), int(per_tensor), _ptr(block_table),
+        block_table.shape[1], _ptr(seq_lens), int(max_seq_len), NB, B, Hq, Hkv, D,
+        float(softmax_scale), _ptr(sink), int(window), _ptr(g_cache), int(kv_split_len),
+        _ptr(out), _ptr(lse), _ptr(ws), ws_n, _stream(dev))
     _check(st, "attn_decode_paged")
     return (out, lse) if return_lse else out
 

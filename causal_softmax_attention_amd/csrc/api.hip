@@ -293,6 +293,21 @@ int attn_decode_paged(const void* q, const int32_t* cu_seqlens_q, int num_reques
                       int num_q_heads, int num_kv_heads, int head_dim, float softmax_scale,
                       int kv_split_len, void* out, float* lse, void* workspace,
                       size_t workspace_bytes, void* stream) {
+  return attn_decode_paged_ext(q, cu_seqlens_q, num_requests, max_seqlen_q, k_cache, v_cache, kv_dtype,
+                               k_scale, v_scale, 0, block_table, max_pages, seq_lens, max_seq_len,
+                               num_blocks, block_size, num_q_heads, num_kv_heads, head_dim, softmax_scale,
+                               nullptr, 0, nullptr, kv_split_len, out, lse, workspace, workspace_bytes,
+                               stream);
+}
+
+int attn_decode_paged_ext(const void* q, const int32_t* cu_seqlens_q, int num_requests, int max_seqlen_q,
+                          const void* k_cache, const void* v_cache, int kv_dtype, const float* k_scale,
+                          const float* v_scale, int per_tensor_scales, const int32_t* block_table,
+                          int max_pages, const int32_t* seq_lens, int max_seq_len, int num_blocks,
+                          int block_size, int num_q_heads, int num_kv_heads, int head_dim,
+                          float softmax_scale, const float* sink, int window, const float* g_cache,
+                          int kv_split_len, void* out, float* lse, void* workspace,
+                          size_t workspace_bytes, void* stream) {
   REQUIRE(num_requests >= 0, ATTN_ERR_INVALID, "num_requests %d is negative", num_requests);
   REQUIRE(max_seqlen_q >= 1, ATTN_ERR_INVALID, "max_seqlen_q %d must be >= 1", max_seqlen_q);
   REQUIRE(max_seqlen_q <= 4, ATTN_ERR_UNSUPPORTED,
@@ -302,6 +317,9 @@ int attn_decode_paged(const void* q, const int32_t* cu_seqlens_q, int num_reques
   const bool fp8 = kv_dtype == ATTN_DTYPE_FP8_E4M3FN;
   REQUIRE(!fp8 || (k_scale != nullptr && v_scale != nullptr), ATTN_ERR_UNSUPPORTED,
           "fp8 KV cache needs per-token k_scale and v_scale");
+  REQUIRE(per_tensor_scales == 0 || per_tensor_scales == 1, ATTN_ERR_INVALID,
+          "per_tensor_scales must be 0 or 1");
+  REQUIRE(!per_tensor_scales || fp8, ATTN_ERR_UNSUPPORTED, "per-tensor scales need an fp8 KV cache");
   REQUIRE(fp8 || (k_scale == nullptr && v_scale == nullptr), ATTN_ERR_UNSUPPORTED,
           "scales are only read with an fp8 KV cache");
   REQUIRE(head_dim == 64 || head_dim == 128, ATTN_ERR_UNSUPPORTED, "head_dim %d not supported (64, 128)",
@@ -333,7 +351,19 @@ int attn_decode_paged(const void* q, const int32_t* cu_seqlens_q, int num_reques
   REQ_PTR(cu_seqlens_q, 4);
   REQ_PTR(k_cache, 16);
   REQ_PTR(v_cache, 16);
-  if (fp8) { REQ_PTR(k_scale, 16); REQ_PTR(v_scale, 16); }
+  if (fp8 && !per_tensor_scales) {
+    REQ_PTR(k_scale, 16);
+    REQ_PTR(v_scale, 16);
+    REQUIRE((long)num_blocks * num_kv_heads * block_size * 4 <= 0xffffffffL, ATTN_ERR_UNSUPPORTED,
+            "per-token scale arrays larger than 4 GiB are not supported");
+  }
+  if (fp8 && per_tensor_scales) { REQ_PTR(k_scale, 4); REQ_PTR(v_scale, 4); }
+  if (sink) REQ_PTR(sink, 4);
+  if (g_cache) {
+    REQ_PTR(g_cache, 16);
+    REQUIRE((long)num_blocks * num_q_heads * block_size * 4 <= 0xffffffffL, ATTN_ERR_UNSUPPORTED,
+            "gate cache larger than 4 GiB is not supported");
+  }
   REQ_PTR(block_table, 4);
   REQ_PTR(seq_lens, 4);
   REQ_PTR(out, 16);
@@ -356,6 +386,8 @@ int attn_decode_paged(const void* q, const int32_t* cu_seqlens_q, int num_reques
   p.B = block_size; p.B_shift = __builtin_ctz((unsigned)block_size); p.split_len = lay.split_len; p.num_splits = lay.num_splits;
   p.scale_log2 = softmax_scale * attn::kLog2e;
   p.row_blocks = (max_seqlen_q * (num_q_heads / num_kv_heads) + 15) / 16;
+  p.sink = sink; p.g_cache = g_cache; p.window = window > 0 ? window : 0;
+  p.per_tensor = per_tensor_scales;
   hipError_t e = attn::launch_decode_splitk(p, head_dim, fp8, s);
   if (e != hipSuccess) return hip_fail(e, "decode launch");
 

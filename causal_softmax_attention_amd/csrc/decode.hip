@@ -1,6 +1,14 @@
 // Paged split-K decode partials for 1..4 query tokens per request over a
 // bf16 or per-token-scaled fp8 e4m3fn KV cache.
 //
+// Decode features of the prefill method (fla issue #1322, Description): an
+// optional per-query-head sink (its e^sigma joins segment 0's partial), a
+// sliding window (segments wholly before every row's window stream nothing)
+// and the log-gate bias G_query - G_key read from a paged cache of
+// cumulative gates [num_blocks, Hq, B]; and per-tensor K/V scales as an
+// alternative to per-token ones (one K scale folded into the score factor,
+// one V scale applied to the partial).
+//
 // Method (ROCm/aiter PR #6660, commit messages and "Technical details"):
 // the keys of a request are split into segments; each (request, KV head,
 // segment) produces (acc, m, l) partials for the query rows of the request
@@ -76,7 +84,7 @@ __device__ __forceinline__ int swz_v(int r) {
 
 }  // namespace
 
-template <int D, bool FP8, int W, int NST>
+template <int D, bool FP8, int W, int NST, bool GATE>
 __global__ __launch_bounds__(64 * W) void decode_splitk_kernel(DecodeParams p) {
   constexpr int ES = FP8 ? 1 : 2;      // bytes per cache element
   constexpr int ROWB = D * ES;         // bytes per cached token row
@@ -91,7 +99,8 @@ __global__ __launch_bounds__(64 * W) void decode_splitk_kernel(DecodeParams p) {
   constexpr int DB = D / 16;           // 16-wide output column blocks
   constexpr int TILE = 32 * ROWB;
   constexpr int SCB = FP8 ? 256 : 0;   // bytes of one scale copy (64 lanes x 4 B)
-  constexpr int STAGE = 2 * TILE + W * 2 * SCB;
+  constexpr int GTB = GATE ? 64 * 32 * 4 : 0;   // gate tile: up to 64 heads x 32 keys, fp32
+  constexpr int STAGE = 2 * TILE + W * 2 * SCB + GTB;
   constexpr int LPS = 2 * NTW + (FP8 ? 2 : 0);   // copies per step and wave
   static_assert(NST == 2 || NST == 3, "ring depth");
   static_assert((NST - 2) * LPS <= 63, "vmcnt range");
@@ -113,6 +122,11 @@ __global__ __launch_bounds__(64 * W) void decode_splitk_kernel(DecodeParams p) {
   const int qlen = p.cu_q[r + 1] - qs;
   const int G = p.Hq / p.Hkv;
   if (qlen <= 0) return;               // whole workgroup, before any barrier
+  // first key any row of the request can see (sliding window), and where
+  // this segment's streaming starts (32-key steps stay aligned)
+  const int k_lo = p.window > 0 ? max(0, L - qlen - p.window + 1) : 0;
+  const int k_start = max(k_begin, k_lo & ~31);
+  const bool per_tensor = FP8 && p.per_tensor;
   const bool active = wave * 16 < qlen * G;   // wave-uniform; idle waves still copy
 
   // ---- copy set-up: page bases (SGPR) and fixed per-lane offsets ----
@@ -157,20 +171,36 @@ __global__ __launch_bounds__(64 * W) void decode_splitk_kernel(DecodeParams p) {
       dma16(vc + ro, voff_v[i], stage + TILE + ci * 1024);
     }
     if constexpr (FP8) {
-      const int pid = (lane & 16) ? pg.b : pg.a;
-      const int slot = ((kk + (lane & 16)) & bmask) + (lane & 15);
-      const uint32_t so = (uint32_t)((((pid * p.Hkv + kvh) << bsh) + slot) * 4);
-      const uint32_t sc = stage + 2 * TILE + wave * 2 * SCB;
-      dma4(p.k_scale, so, sc);
-      dma4(p.v_scale, so, sc + SCB);
+      if (!per_tensor) {
+        const int pid = (lane & 16) ? pg.b : pg.a;
+        const int slot = ((kk + (lane & 16)) & bmask) + (lane & 15);
+        const uint32_t so = (uint32_t)((((pid * p.Hkv + kvh) << bsh) + slot) * 4);
+        const uint32_t sc = stage + 2 * TILE + wave * 2 * SCB;
+        dma4(p.k_scale, so, sc);
+        dma4(p.v_scale, so, sc + SCB);
+      }
+    }
+    if constexpr (GATE) {
+      // G of the group's heads at the step's keys: [G heads][32 keys], 64
+      // per copy (lane l of copy c: head (64c + l) / 32, key l % 32)
+      const int ngi = (G * 32 + 63) / 64;
+      const uint32_t gt = stage + 2 * TILE + W * 2 * SCB;
+      const int key = lane & 31;
+      const int pid = (key & 16) ? pg.b : pg.a;
+      const int slot = ((kk + (key & 16)) & bmask) + (key & 15);
+      for (int c = wave; c < ngi; c += W) {
+        const int hh = min((64 * c + lane) >> 5, G - 1);
+        const uint32_t go = (uint32_t)((((pid * p.Hq + kvh * G + hh) << bsh) + slot) * 4);
+        dma4(p.g_cache, go, gt + 256 * c);
+      }
     }
   };
 
   // ---- prologue: first NST-1 steps in flight, then the query ----
-  Pages nxt = pages_of(k_begin);
+  Pages nxt = pages_of(k_start);
 #pragma unroll
   for (int j = 0; j < NST - 1; ++j) {
-    const int kk = k_begin + 32 * j;
+    const int kk = k_start + 32 * j;
     if (kk < k_end) fetch(kk, nxt, j);
     nxt = pages_of(kk + 32);
   }
@@ -187,14 +217,29 @@ __global__ __launch_bounds__(64 * W) void decode_splitk_kernel(DecodeParams p) {
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks)
       qop[ks] = rvalid ? *reinterpret_cast<const bf16x8*>(qp + 8 * ks) : bf16x8{};
-    // consume the loads here, while only prologue copies are in flight, so
-    // that the compiler's own wait for them does not land inside the loop
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) asm volatile("" :: "v"(qop[ks]));
   }
+  // gate of the row's own position (the query side of G_query - G_key)
+  float gq2 = 0.f;
+  if constexpr (GATE) {
+    const int prow = min(pos, L - 1);
+    const int pq = p.block_table[(long)r * p.max_pages + (prow >> bsh)];
+    gq2 = p.g_cache[(((long)pq * p.Hq + kvh * G + rho % G) << bsh) + (prow & bmask)] * kLog2e;
+  }
+  // consume the loads here, while only prologue copies are in flight, so
+  // that the compiler's own wait for them does not land inside the loop
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) asm volatile("" :: "v"(qop[ks]));
+  asm volatile("" :: "v"(gq2));
+  // per-tensor scales: K folded into the score factor, V applied at the end
+  const float qk_mul = per_tensor ? p.scale_log2 * p.k_scale[0] : p.scale_log2;
+  const float v_mul = per_tensor ? p.v_scale[0] : 1.f;
 
   f32x4 oacc[DB];
   float m_run = kNegBig, l_run = 0.f;
+  if (p.sink != nullptr && s == 0) {   // the sink's mass belongs to segment 0
+    m_run = p.sink[kvh * G + rho % G] * kLog2e;
+    l_run = 1.f;
+  }
 #pragma unroll
   for (int db = 0; db < DB; ++db) oacc[db] = f32x4{0.f, 0.f, 0.f, 0.f};
   const int vis_all = L - qlen;        // keys below this are visible to every row
@@ -203,7 +248,8 @@ __global__ __launch_bounds__(64 * W) void decode_splitk_kernel(DecodeParams p) {
     const uint8_t* Kt = smem + st * STAGE;
     const uint8_t* Vt = Kt + TILE;
     const float* Sc = reinterpret_cast<const float*>(Kt + 2 * TILE + wave * 2 * SCB);
-    const bool need_mask = kk + 31 > vis_all;   // uniform: a key past some row's position
+    // uniform: a key past some row's position, or before some row's window
+    const bool need_mask = kk + 31 > vis_all || (p.window > 0 && kk <= L - 1 - p.window);
     // ---- scores S^T = K Q^T (C lane: row li, keys kk+kb*16+4g+i) ----
     f32x4 sc[2];
 #pragma unroll
@@ -233,13 +279,20 @@ __global__ __launch_bounds__(64 * W) void decode_splitk_kernel(DecodeParams p) {
     for (int kb = 0; kb < 2; ++kb) {
       f32x4 ks4 = {1.f, 1.f, 1.f, 1.f}, vs4 = {1.f, 1.f, 1.f, 1.f};
       if constexpr (FP8) {
-        ks4 = *reinterpret_cast<const f32x4*>(Sc + kb * 16 + 4 * g);
-        vs4 = *reinterpret_cast<const f32x4*>(Sc + 64 + kb * 16 + 4 * g);
+        if (!per_tensor) {
+          ks4 = *reinterpret_cast<const f32x4*>(Sc + kb * 16 + 4 * g);
+          vs4 = *reinterpret_cast<const f32x4*>(Sc + 64 + kb * 16 + 4 * g);
+        }
       }
+      f32x4 gk4 = {0.f, 0.f, 0.f, 0.f};
+      if constexpr (GATE)
+        gk4 = *reinterpret_cast<const f32x4*>(reinterpret_cast<const float*>(Kt + 2 * TILE + W * 2 * SCB) +
+                                              (rho % G) * 32 + kb * 16 + 4 * g);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         vsc[kb][i] = vs4[i];
-        x[kb][i] = sc[kb][i] * (p.scale_log2 * ks4[i]);
+        x[kb][i] = GATE ? __builtin_fmaf(-kLog2e, gk4[i], __builtin_fmaf(sc[kb][i], qk_mul * ks4[i], gq2))
+                        : sc[kb][i] * (qk_mul * ks4[i]);
       }
     }
     if (need_mask) {
@@ -249,7 +302,8 @@ __global__ __launch_bounds__(64 * W) void decode_splitk_kernel(DecodeParams p) {
         for (int i = 0; i < 4; ++i) {
           const int key = kk + kb * 16 + 4 * g + i;
           const bool ok = key < L;                    // scale slots past seq_len may be NaN
-          x[kb][i] = (ok && key <= pos) ? x[kb][i] : -INFINITY;
+          const bool vis = ok && key <= pos && (p.window <= 0 || key > pos - p.window);
+          x[kb][i] = vis ? x[kb][i] : -INFINITY;
           vsc[kb][i] = ok ? vsc[kb][i] : 0.f;
         }
     }
@@ -333,7 +387,7 @@ __global__ __launch_bounds__(64 * W) void decode_splitk_kernel(DecodeParams p) {
     nxt = pages_of(kq);
   };
 
-  for (int kk = k_begin;; kk += 32 * NST) {
+  for (int kk = k_start; kk < k_end; kk += 32 * NST) {
     step(kk, 0);
     if (kk + 32 >= k_end) break;
     step(kk + 32, 1);
@@ -350,7 +404,7 @@ __global__ __launch_bounds__(64 * W) void decode_splitk_kernel(DecodeParams p) {
     const long grow = (long)(qs + t) * p.Hq + (long)kvh * G + rho % G;
     float* a = p.acc + (grow * p.num_splits + s) * D;
 #pragma unroll
-    for (int db = 0; db < DB; ++db) *reinterpret_cast<f32x4*>(a + db * 16 + 4 * g) = oacc[db];
+    for (int db = 0; db < DB; ++db) *reinterpret_cast<f32x4*>(a + db * 16 + 4 * g) = oacc[db] * v_mul;
     if (g == 0) {
       const bool empty = !(l_run > 0.f);
       p.m[grow * p.num_splits + s] = empty ? -INFINITY : m_run * kLn2;
@@ -366,7 +420,10 @@ __global__ __launch_bounds__(64 * W) void decode_splitk_kernel(DecodeParams p) {
 template <int D, bool FP8, int W>
 static hipError_t launch_t(const DecodeParams& p, hipStream_t st) {
   const long items = (long)p.R * p.Hkv * p.num_splits;
-  decode_splitk_kernel<D, FP8, W, DECODE_NST><<<dim3((unsigned)items), dim3(64 * W), 0, st>>>(p);
+  if (p.g_cache != nullptr)
+    decode_splitk_kernel<D, FP8, W, DECODE_NST, true><<<dim3((unsigned)items), dim3(64 * W), 0, st>>>(p);
+  else
+    decode_splitk_kernel<D, FP8, W, DECODE_NST, false><<<dim3((unsigned)items), dim3(64 * W), 0, st>>>(p);
   return hipGetLastError();
 }
 

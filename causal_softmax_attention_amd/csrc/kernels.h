@@ -43,6 +43,10 @@ struct DecodeParams {
   float* l;
   int R, max_pages, Hq, Hkv, B, B_shift, split_len, num_splits;
   int row_blocks;           // 16-row query blocks per (request, KV head): ceil(max_q * G / 16)
+  const float* sink;        // [Hq] sink logits or nullptr
+  const float* g_cache;     // [NB, Hq, B] cumulative log gates or nullptr
+  int window;               // sliding window (<= 0: none)
+  int per_tensor;           // fp8 with one K and one V scale (k_scale[0], v_scale[0])
   float scale_log2;         // softmax_scale * log2(e)
 };
 hipError_t launch_decode_splitk(const DecodeParams& p, int head_dim, bool fp8, hipStream_t st);

@@ -232,6 +232,42 @@ int attn_decode_paged(const void* q, const int32_t* cu_seqlens_q,
                       void* workspace, size_t workspace_bytes, void* stream);
 
 /* ------------------------------------------------------------------------
+ * attn_decode_paged_ext -- attn_decode_paged with the decode counterparts of
+ * the prefill features (fla issue #1322, Description: sink, sliding window,
+ * log gate) and per-tensor KV scales (aiter PR #6660, Technical details).
+ *
+ * Arguments as attn_decode_paged, plus:
+ *   per_tensor_scales 0: k_scale / v_scale are per-token [num_blocks, Hkv,
+ *            block_size]; 1: each points to one fp32 scale for its whole
+ *            cache (fp8 only)
+ *   sink     fp32 [Hq] sink logits or NULL: e^sink[h] joins the softmax
+ *            denominator (no value); lse includes it
+ *   window   > 0: the query at position p sees keys j with p - j < window;
+ *            <= 0: no window
+ *   g_cache  fp32 [num_blocks, Hq, block_size] or NULL: cumulative log gate
+ *            G of each cached token and query head (same paging as the KV
+ *            cache); the score of key j gains G_p - G_j, with G_p read at the
+ *            query's own position (its slot must hold its G)
+ * The score is  softmax_scale * <q, Khat_j> + (G_p - G_j).  The sink's mass
+ * is part of segment 0's partial, so attn_splitk_reduce is unchanged.
+ * Per-token scale and gate arrays must each stay below 4 GiB
+ * (ATTN_ERR_UNSUPPORTED otherwise).
+ * ---------------------------------------------------------------------- */
+int attn_decode_paged_ext(const void* q, const int32_t* cu_seqlens_q,
+                          int num_requests, int max_seqlen_q,
+                          const void* k_cache, const void* v_cache, int kv_dtype,
+                          const float* k_scale, const float* v_scale,
+                          int per_tensor_scales,
+                          const int32_t* block_table, int max_pages,
+                          const int32_t* seq_lens, int max_seq_len,
+                          int num_blocks, int block_size,
+                          int num_q_heads, int num_kv_heads, int head_dim,
+                          float softmax_scale,
+                          const float* sink, int window, const float* g_cache,
+                          int kv_split_len, void* out, float* lse,
+                          void* workspace, size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
  * attn_splitk_reduce -- merge split-K partials per row (aiter PR #6660,
  * third commit message and Technical details).
  *

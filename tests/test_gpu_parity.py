@@ -241,3 +241,51 @@ def test_forward_empty_and_zero_length_sequences(A):
     torch.cuda.synchronize()
     ro, _ = oracle.forward(x.q, x.k, x.v, x.cu_seqlens, x.scale, 0, x.sink, x.g)
     assert rel_rms(_np(o), ro) <= TOL
+
+
+# ----------------------------------------------------------------------------
+# decode with sink / sliding window / log gate / per-tensor scales
+# ----------------------------------------------------------------------------
+FEATURE_CASES = [
+    # seq_lens, q_lens, Hq, Hkv, D, B, kv, window, sink, gate, per_tensor, split
+    ([40, 700, 2500], [1, 1, 1], 64, 4, 128, 16, synth.KV_FP8_E4M3FN, 0, True, False, False, 0),
+    ([40, 700, 2500], [1, 2, 4], 16, 4, 128, 16, synth.KV_FP8_E4M3FN, 300, False, False, False, 256),
+    ([40, 700, 2500], [1, 1, 3], 32, 2, 128, 32, synth.KV_FP8_E4M3FN, 0, False, True, False, 512),
+    ([5, 900, 4100], [4, 2, 3], 64, 4, 128, 128, synth.KV_FP8_E4M3FN, 1000, True, True, False, 0),
+    ([5, 900, 4100], [4, 2, 3], 64, 4, 128, 16, synth.KV_FP8_E4M3FN, 77, True, True, True, 1024),
+    ([33, 1500], [2, 1], 8, 8, 64, 32, synth.KV_BF16, 200, True, True, False, 256),
+    ([33, 1500], [2, 4], 32, 4, 128, 64, synth.KV_BF16, 0, True, True, False, 0),
+    ([6000], [4], 64, 4, 128, 16, synth.KV_FP8_E4M3FN, 1, True, False, True, 512),
+]
+
+
+def _feat_id(c):
+    L, ql, Hq, Hkv, D, B, kv, W, sk, gt, pt, sp = c
+    return (f"L{max(L)}-q{max(ql)}-h{Hq}kv{Hkv}-d{D}-p{B}-{'fp8' if kv else 'bf16'}-w{W}"
+            f"{'-sink' if sk else ''}{'-gate' if gt else ''}{'-pt' if pt else ''}-s{sp}")
+
+
+@pytest.mark.parametrize("case", FEATURE_CASES, ids=_feat_id)
+def test_decode_features_match_oracle(A, case):
+    L, ql, Hq, Hkv, D, B, kv, W, sk, gt, pt, sp = case
+    _say(f"[case] decode features {_feat_id(case)}")
+    d = synth.decode_inputs(L, ql, Hq, Hkv, D, B, kv_dtype=kv, seed=sum(L) + Hq, device=DEV,
+                            window=W, with_sink=sk, with_gate=gt, per_tensor=pt, spare_pages=4)
+    fp8 = kv == synth.KV_FP8_E4M3FN
+    out, lse = A.attn_decode_paged(d.q, d.cu_seqlens_q, d.max_seqlen_q, d.k_cache, d.v_cache, d.kv_dtype,
+                                   d.k_scale, d.v_scale, d.block_table, d.seq_lens, d.max_seq_len, d.scale,
+                                   kv_split_len=sp, return_lse=True, sink=d.sink, window=d.window,
+                                   g_cache=d.g_cache)
+    torch.cuda.synchronize()
+    ro, rl = oracle.decode_paged(d.q, d.cu_seqlens_q, d.k_cache, d.v_cache, d.block_table, d.seq_lens,
+                                 d.scale, fp8, d.k_scale, d.v_scale, sink=d.sink, window=d.window,
+                                 g_cache=d.g_cache, per_tensor=d.per_tensor)
+    o = _np(out)
+    assert np.isfinite(o).all()
+    err = rel_rms(o, ro)
+    bias = float(np.sum(o * ro) / np.sum(ro * ro) - 1.0)
+    lerr = float(np.max(np.abs(_np(lse) - rl)))
+    _say(f"    rel_rms={err:.3e} bias={bias:.2e} lse max abs={lerr:.2e}")
+    assert err <= TOL
+    assert abs(bias) < 1e-3
+    assert lerr <= 1e-3
