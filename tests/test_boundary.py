@@ -210,3 +210,28 @@ def test_kv_cache_write_validation(kw, code, msg):
 
 def test_kv_cache_write_empty_is_a_no_op():
     assert _kvw(N=0, k=NULL, v=NULL, slots=NULL) == OK
+
+
+def _decode_ext(**kw):
+    a = dict(q=P, cu=P, R=2, maxq=1, kc=P, vc=P, kvd=A.ATTN_DTYPE_FP8_E4M3FN, ks=P, vs=P, pt=0, bt=P,
+             maxp=8, sl=P, maxsl=128, nb=16, B=16, Hq=64, Hkv=4, D=128, scale=0.1, sink=NULL, W=0,
+             gc=NULL, split=0, out=P, lse=NULL, ws=P, wsb=1 << 30)
+    a.update(kw)
+    return L.attn_decode_paged_ext(a["q"], a["cu"], a["R"], a["maxq"], a["kc"], a["vc"], a["kvd"], a["ks"],
+                                   a["vs"], a["pt"], a["bt"], a["maxp"], a["sl"], a["maxsl"], a["nb"], a["B"],
+                                   a["Hq"], a["Hkv"], a["D"], a["scale"], a["sink"], a["W"], a["gc"],
+                                   a["split"], a["out"], a["lse"], a["ws"], a["wsb"], NULL)
+
+
+@pytest.mark.parametrize("kw,code,msg", [
+    (dict(pt=2), INVALID, "per_tensor_scales"),
+    (dict(pt=1, kvd=A.ATTN_DTYPE_BF16, ks=NULL, vs=NULL), UNSUPPORTED, "per-tensor scales need an fp8"),
+    (dict(sink=ctypes.c_void_p(0x10002)), INVALID, "sink is not 4-byte aligned"),
+    (dict(gc=P_ODD), INVALID, "g_cache is not 16-byte aligned"),
+    (dict(gc=P, pt=1, nb=1 << 22, B=128, Hq=64), UNSUPPORTED, "gate cache larger than 4 GiB"),
+    (dict(nb=1 << 23, B=128, Hkv=8, Hq=64), UNSUPPORTED, "per-token scale arrays larger than 4 GiB"),
+])
+def test_decode_ext_validation(kw, code, msg):
+    st = _decode_ext(**kw)
+    assert st == code
+    assert msg in L.attn_last_error().decode()
