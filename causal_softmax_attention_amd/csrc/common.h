@@ -20,6 +20,7 @@ namespace attn {
 typedef __bf16 bf16;
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
@@ -83,13 +84,29 @@ __device__ __forceinline__ bf16x4 to_bf16x4(f32x4 x) {
 // v_permlane32_swap (lane l <-> l^32 between two registers) and
 // v_permlane16_swap (odd 16-lane rows <-> even rows): two VALU steps, no
 // LDS round trip.
+// Maximum of two or three floats as one v_max / v_max3.  fmaxf makes the
+// compiler quiet possible signalling NaNs first (a self-max per operand it
+// cannot prove canonical, e.g. lane-swap results); operands here are
+// arithmetic results or -inf, never signalling NaNs, and for quiet NaNs the
+// instruction already returns the other operand as fmaxf does.
+__device__ __forceinline__ float max_nq(float a, float b) {
+  float r;
+  asm("v_max_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+  return r;
+}
+__device__ __forceinline__ float max3_nq(float a, float b, float c) {
+  float r;
+  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
+}
+
 __device__ __forceinline__ float xgroup_max(float x) {
   const unsigned u = __float_as_uint(x);
   const auto a = __builtin_amdgcn_permlane32_swap(u, u, false, false);
-  x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  x = max_nq(__uint_as_float(a[0]), __uint_as_float(a[1]));
   const unsigned v = __float_as_uint(x);
   const auto b = __builtin_amdgcn_permlane16_swap(v, v, false, false);
-  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+  return max_nq(__uint_as_float(b[0]), __uint_as_float(b[1]));
 }
 __device__ __forceinline__ float xgroup_sum(float x) {
   const unsigned u = __float_as_uint(x);

@@ -20,11 +20,12 @@
 // query whose last visible key precedes the segment stores an empty partial
 // (m = -inf, l = 0).
 //
-// gfx950 mapping: one workgroup per (segment, request, KV head) with one
-// wavefront per 16-row block of query rows; rows are (query token, head of
-// the KV group) pairs, so GQA 16 with one token is a one-wave workgroup and
-// a 4-token verify is four waves that share every K/V tile.  The segment is
-// walked 32 keys at a time through a ring of NST LDS stages:
+// gfx950 mapping: one workgroup per (segment, request, KV head); rows are
+// (query token, head of the KV group) pairs in 16-row blocks, and a wave
+// owns RBW blocks, so that the K/V conversion of a step serves all of them.
+// GQA 16 with one token is a one-wave workgroup; a 4-token verify (four
+// blocks) is two waves of two blocks that share every K/V tile.  The
+// segment is walked 32 keys at a time through a ring of NST LDS stages:
 //   * every byte a step needs (K tile, V tile, and for fp8 the per-token
 //     scales) arrives by direct global->LDS copies (global_load_lds) from a
 //     wave-uniform page base in SGPRs plus a fixed per-lane 32-bit offset;
@@ -84,7 +85,9 @@ __device__ __forceinline__ int swz_v(int r) {
 
 }  // namespace
 
-template <int D, bool FP8, int W, int NST, bool GATE>
+// RBW: 16-row query blocks per wave; the K and V of a step are converted
+// once and serve all of them.
+template <int D, bool FP8, int W, int RBW, int NST, bool GATE>
 __global__ __launch_bounds__(64 * W) void decode_splitk_kernel(DecodeParams p) {
   constexpr int ES = FP8 ? 1 : 2;      // bytes per cache element
   constexpr int ROWB = D * ES;         // bytes per cached token row
@@ -101,9 +104,10 @@ __global__ __launch_bounds__(64 * W) void decode_splitk_kernel(DecodeParams p) {
   constexpr int SCB = FP8 ? 256 : 0;   // bytes of one scale copy (64 lanes x 4 B)
   constexpr int GTB = GATE ? 64 * 32 * 4 : 0;   // gate tile: up to 64 heads x 32 keys, fp32
   constexpr int STAGE = 2 * TILE + W * 2 * SCB + GTB;
-  constexpr int LPS = 2 * NTW + (FP8 ? 2 : 0);   // copies per step and wave
-  static_assert(NST == 2 || NST == 3, "ring depth");
-  static_assert((NST - 2) * LPS <= 63, "vmcnt range");
+  constexpr int LPK = 2 * NTW;         // K and V copies per step and wave (fixed;
+                                       // scale and gate copies come on top)
+  static_assert(NST >= 2 && NST <= 4, "ring depth");
+  static_assert((NST - 2) * LPK <= 63, "vmcnt range");
   __shared__ __attribute__((aligned(1024))) uint8_t smem[NST * STAGE];
 
   const int wave = W == 1 ? 0 : __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -127,7 +131,7 @@ __global__ __launch_bounds__(64 * W) void decode_splitk_kernel(DecodeParams p) {
   const int k_lo = p.window > 0 ? max(0, L - qlen - p.window + 1) : 0;
   const int k_start = max(k_begin, k_lo & ~31);
   const bool per_tensor = FP8 && p.per_tensor;
-  const bool active = wave * 16 < qlen * G;   // wave-uniform; idle waves still copy
+  const bool active = wave * 16 * RBW < qlen * G;   // wave-uniform; idle waves still copy
 
   // ---- copy set-up: page bases (SGPR) and fixed per-lane offsets ----
   const int bsh = p.B_shift, bmask = p.B - 1;   // page size is a power of two
@@ -205,53 +209,66 @@ __global__ __launch_bounds__(64 * W) void decode_splitk_kernel(DecodeParams p) {
     nxt = pages_of(kk + 32);
   }
 
-  // this lane's query row (li of the wave's block) and its Q operand
-  const int rho = wave * 16 + li;
-  const int t = rho / G;
-  const bool rvalid = active && t < qlen;
-  const int pos = L - qlen + t;                       // last key this row sees
-  bf16x8 qop[KS];
-  {
+  // this lane's query rows (li of each of the wave's blocks) and Q operands
+  int rho[RBW], tq[RBW], pos[RBW];
+  bool rvalid[RBW];
+  bf16x8 qop[RBW][KS];
+  float gq2[RBW];
+#pragma unroll
+  for (int rb = 0; rb < RBW; ++rb) {
+    rho[rb] = (wave * RBW + rb) * 16 + li;
+    tq[rb] = rho[rb] / G;
+    rvalid[rb] = active && tq[rb] < qlen;
+    pos[rb] = L - qlen + tq[rb];                       // last key this row sees
     const bf16* qp = reinterpret_cast<const bf16*>(p.q) +
-                     ((long)(qs + min(t, qlen - 1)) * p.Hq + (long)kvh * G + rho % G) * D + g * DPG;
+                     ((long)(qs + min(tq[rb], qlen - 1)) * p.Hq + (long)kvh * G + rho[rb] % G) * D + g * DPG;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks)
-      qop[ks] = rvalid ? *reinterpret_cast<const bf16x8*>(qp + 8 * ks) : bf16x8{};
-  }
-  // gate of the row's own position (the query side of G_query - G_key)
-  float gq2 = 0.f;
-  if constexpr (GATE) {
-    const int prow = min(pos, L - 1);
-    const int pq = p.block_table[(long)r * p.max_pages + (prow >> bsh)];
-    gq2 = p.g_cache[(((long)pq * p.Hq + kvh * G + rho % G) << bsh) + (prow & bmask)] * kLog2e;
+      qop[rb][ks] = rvalid[rb] ? *reinterpret_cast<const bf16x8*>(qp + 8 * ks) : bf16x8{};
+    // gate of the row's own position (the query side of G_query - G_key)
+    gq2[rb] = 0.f;
+    if constexpr (GATE) {
+      const int prow = min(pos[rb], L - 1);
+      const int pq = p.block_table[(long)r * p.max_pages + (prow >> bsh)];
+      gq2[rb] = p.g_cache[(((long)pq * p.Hq + kvh * G + rho[rb] % G) << bsh) + (prow & bmask)] * kLog2e;
+    }
   }
   // consume the loads here, while only prologue copies are in flight, so
   // that the compiler's own wait for them does not land inside the loop
 #pragma unroll
-  for (int ks = 0; ks < KS; ++ks) asm volatile("" :: "v"(qop[ks]));
-  asm volatile("" :: "v"(gq2));
+  for (int rb = 0; rb < RBW; ++rb) {
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) asm volatile("" :: "v"(qop[rb][ks]));
+    asm volatile("" :: "v"(gq2[rb]));
+  }
   // per-tensor scales: K folded into the score factor, V applied at the end
   const float qk_mul = per_tensor ? p.scale_log2 * p.k_scale[0] : p.scale_log2;
   const float v_mul = per_tensor ? p.v_scale[0] : 1.f;
 
-  f32x4 oacc[DB];
-  float m_run = kNegBig, l_run = 0.f;
-  if (p.sink != nullptr && s == 0) {   // the sink's mass belongs to segment 0
-    m_run = p.sink[kvh * G + rho % G] * kLog2e;
-    l_run = 1.f;
-  }
+  f32x4 oacc[RBW][DB];
+  float m_run[RBW], l_run[RBW];
 #pragma unroll
-  for (int db = 0; db < DB; ++db) oacc[db] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int rb = 0; rb < RBW; ++rb) {
+    m_run[rb] = kNegBig;
+    l_run[rb] = 0.f;
+    if (p.sink != nullptr && s == 0) {   // the sink's mass belongs to segment 0
+      m_run[rb] = p.sink[kvh * G + rho[rb] % G] * kLog2e;
+      l_run[rb] = 1.f;
+    }
+#pragma unroll
+    for (int db = 0; db < DB; ++db) oacc[rb][db] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
   const int vis_all = L - qlen;        // keys below this are visible to every row
 
   auto compute = [&](int kk, int st) {
     const uint8_t* Kt = smem + st * STAGE;
     const uint8_t* Vt = Kt + TILE;
     const float* Sc = reinterpret_cast<const float*>(Kt + 2 * TILE + wave * 2 * SCB);
+    const float* Gt = reinterpret_cast<const float*>(Kt + 2 * TILE + W * 2 * SCB);
     // uniform: a key past some row's position, or before some row's window
     const bool need_mask = kk + 31 > vis_all || (p.window > 0 && kk <= L - 1 - p.window);
     // ---- scores S^T = K Q^T (C lane: row li, keys kk+kb*16+4g+i) ----
-    f32x4 sc[2];
+    f32x4 sc[RBW][2];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
       const int row = kb * 16 + li;
@@ -259,7 +276,8 @@ __global__ __launch_bounds__(64 * W) void decode_splitk_kernel(DecodeParams p) {
 #pragma unroll
       for (int c = 0; c < KCH; ++c)
         kraw[c] = *reinterpret_cast<const i32x4*>(Kt + row * ROWB + 16 * ((g * KCH + c) ^ swz_k<ROWB>(row)));
-      f32x4 a = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int rb = 0; rb < RBW; ++rb) sc[rb][kb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
         bf16x8 kop;
@@ -269,73 +287,89 @@ __global__ __launch_bounds__(64 * W) void decode_splitk_kernel(DecodeParams p) {
         } else {
           kop = __builtin_bit_cast(bf16x8, kraw[ks]);
         }
-        a = mfma16x16x32(kop, qop[ks], a);
+#pragma unroll
+        for (int rb = 0; rb < RBW; ++rb) sc[rb][kb] = mfma16x16x32(kop, qop[rb][ks], sc[rb][kb]);
       }
-      sc[kb] = a;
     }
-    // ---- scale (softmax scale x per-token K scale), mask ----
-    float x[2][4], vsc[2][4];
+    // ---- per-key K / V scale factors (shared by all rows) ----
+    f32x4 ks4[2], vs4[2];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
-      f32x4 ks4 = {1.f, 1.f, 1.f, 1.f}, vs4 = {1.f, 1.f, 1.f, 1.f};
+      ks4[kb] = f32x4{1.f, 1.f, 1.f, 1.f};
+      vs4[kb] = f32x4{1.f, 1.f, 1.f, 1.f};
       if constexpr (FP8) {
         if (!per_tensor) {
-          ks4 = *reinterpret_cast<const f32x4*>(Sc + kb * 16 + 4 * g);
-          vs4 = *reinterpret_cast<const f32x4*>(Sc + 64 + kb * 16 + 4 * g);
+          ks4[kb] = *reinterpret_cast<const f32x4*>(Sc + kb * 16 + 4 * g);
+          vs4[kb] = *reinterpret_cast<const f32x4*>(Sc + 64 + kb * 16 + 4 * g);
         }
       }
-      f32x4 gk4 = {0.f, 0.f, 0.f, 0.f};
-      if constexpr (GATE)
-        gk4 = *reinterpret_cast<const f32x4*>(reinterpret_cast<const float*>(Kt + 2 * TILE + W * 2 * SCB) +
-                                              (rho % G) * 32 + kb * 16 + 4 * g);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        vsc[kb][i] = vs4[i];
-        x[kb][i] = GATE ? __builtin_fmaf(-kLog2e, gk4[i], __builtin_fmaf(sc[kb][i], qk_mul * ks4[i], gq2))
-                        : sc[kb][i] * (qk_mul * ks4[i]);
+      for (int i = 0; i < 4; ++i) ks4[kb][i] *= qk_mul;
+      if (need_mask) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)   // scale slots past seq_len may be NaN: select, not multiply
+          vs4[kb][i] = (kk + kb * 16 + 4 * g + i < L) ? vs4[kb][i] : 0.f;
       }
     }
-    if (need_mask) {
+    bf16x8 phi[RBW], plo[RBW];
+#pragma unroll
+    for (int rb = 0; rb < RBW; ++rb) {
+      float x[2][4];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        f32x4 gk4 = {0.f, 0.f, 0.f, 0.f};
+        if constexpr (GATE) gk4 = *reinterpret_cast<const f32x4*>(Gt + (rho[rb] % G) * 32 + kb * 16 + 4 * g);
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          x[kb][i] = GATE ? __builtin_fmaf(-kLog2e, gk4[i], __builtin_fmaf(sc[rb][kb][i], ks4[kb][i], gq2[rb]))
+                          : sc[rb][kb][i] * ks4[kb][i];
+      }
+      if (need_mask) {
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int key = kk + kb * 16 + 4 * g + i;
+            const bool vis = key < L && key <= pos[rb] && (p.window <= 0 || key > pos[rb] - p.window);
+            x[kb][i] = vis ? x[kb][i] : -INFINITY;
+          }
+      }
+      // ---- online softmax (lazy rescale); P' = P * v_scale as bf16 hi + lo ----
+      float mx = max3_nq(max3_nq(x[0][0], x[0][1], x[0][2]), max3_nq(x[0][3], x[1][0], x[1][1]),
+                         max_nq(x[1][2], x[1][3]));
+      mx = xgroup_max(mx);
+      if (__any(mx > m_run[rb] + kRescaleSlack)) {
+        // raise the running max only when a score passes it by more than
+        // the slack, so exp2(score - max) stays below 2^8 in between
+        const float m_new = max_nq(m_run[rb], mx);
+        const float alpha = fast_exp2(m_run[rb] - m_new);
+        l_run[rb] *= alpha;
+#pragma unroll
+        for (int db = 0; db < DB; ++db) oacc[rb][db] *= alpha;
+        m_run[rb] = m_new;
+      }
+      float rs = 0.f;
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int key = kk + kb * 16 + 4 * g + i;
-          const bool ok = key < L;                    // scale slots past seq_len may be NaN
-          const bool vis = ok && key <= pos && (p.window <= 0 || key > pos - p.window);
-          x[kb][i] = vis ? x[kb][i] : -INFINITY;
-          vsc[kb][i] = ok ? vsc[kb][i] : 0.f;
+        for (int i = 0; i < 4; i += 2) {
+          const float p0 = fast_exp2(x[kb][i] - m_run[rb]);
+          const float p1 = fast_exp2(x[kb][i + 1] - m_run[rb]);
+          rs += p0 + p1;
+          // hi = RNE(P'), lo = RNE(P' - hi), two columns per conversion
+          const float a = p0 * vs4[kb][i], b = p1 * vs4[kb][i + 1];
+          const bf16x2 h = __builtin_convertvector(f32x2{a, b}, bf16x2);
+          const unsigned hb = __builtin_bit_cast(unsigned, h);
+          const bf16x2 lo = __builtin_convertvector(
+              f32x2{a - __uint_as_float(hb << 16), b - __uint_as_float(hb & 0xffff0000u)}, bf16x2);
+          phi[rb][kb * 4 + i] = h[0];
+          phi[rb][kb * 4 + i + 1] = h[1];
+          plo[rb][kb * 4 + i] = lo[0];
+          plo[rb][kb * 4 + i + 1] = lo[1];
         }
+      l_run[rb] += xgroup_sum(rs);
     }
-    // ---- online softmax (lazy rescale); P' = P * v_scale as bf16 hi + lo ----
-    float mx = fmaxf(fmaxf(fmaxf(x[0][0], x[0][1]), fmaxf(x[0][2], x[0][3])),
-                     fmaxf(fmaxf(x[1][0], x[1][1]), fmaxf(x[1][2], x[1][3])));
-    mx = xgroup_max(mx);
-    if (__any(mx > m_run + kRescaleSlack)) {
-      // raise the running max only when a score passes it by more than
-      // the slack, so exp2(score - max) stays below 2^8 in between
-      const float m_new = fmaxf(m_run, mx);
-      const float alpha = fast_exp2(m_run - m_new);
-      l_run *= alpha;
-#pragma unroll
-      for (int db = 0; db < DB; ++db) oacc[db] *= alpha;
-      m_run = m_new;
-    }
-    bf16x8 phi, plo;
-    float rs = 0.f;
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float pv = fast_exp2(x[kb][i] - m_run);
-        rs += pv;
-        const float pp = pv * vsc[kb][i];
-        const bf16 h = (bf16)pp;
-        phi[kb * 4 + i] = h;
-        plo[kb * 4 + i] = (bf16)(pp - (float)h);
-      }
-    l_run += xgroup_sum(rs);
-    // ---- O^T += V^T P'^T (hi and lo) ----
+    // ---- O^T += V^T P'^T (hi and lo); V converted once for all rows ----
 #pragma unroll
     for (int db = 0; db < DB; ++db) {
       bf16x8 vop;
@@ -350,16 +384,26 @@ __global__ __launch_bounds__(64 * W) void decode_splitk_kernel(DecodeParams p) {
         const bf16* b1 = reinterpret_cast<const bf16*>(Vt + r1 * ROWB + 16 * (q ^ swz_v<ROWB, FP8>(r1)) + 8 * (c & 1));
         vop = concat(lds_read_tr16(b0), lds_read_tr16(b1));
       }
-      oacc[db] = mfma16x16x32(vop, phi, oacc[db]);
-      oacc[db] = mfma16x16x32(vop, plo, oacc[db]);
+#pragma unroll
+      for (int rb = 0; rb < RBW; ++rb) {
+        oacc[rb][db] = mfma16x16x32(vop, phi[rb], oacc[rb][db]);
+        oacc[rb][db] = mfma16x16x32(vop, plo[rb], oacc[rb][db]);
+      }
     }
   };
 
   // ---- one step of the ring: wait for step kk, release it to the
   // workgroup, put step kk + 32 (NST-1) in flight, compute step kk ----
   auto step = [&](int kk, int st) {
-    if constexpr (NST == 3) {
-      if (kk + 32 < k_end) wait_vm<LPS>(); else wait_vm<0>();
+    // Copies of the steps after kk that are already in flight are newer
+    // than step kk's and number at least LPK each: waiting until no more
+    // than that many are outstanding completes step kk's.
+    if constexpr (NST == 4) {
+      if (kk + 64 < k_end) wait_vm<2 * LPK>();
+      else if (kk + 32 < k_end) wait_vm<LPK>();
+      else wait_vm<0>();
+    } else if constexpr (NST == 3) {
+      if (kk + 32 < k_end) wait_vm<LPK>(); else wait_vm<0>();
     } else {
       wait_vm<0>();
     }
@@ -388,50 +432,67 @@ __global__ __launch_bounds__(64 * W) void decode_splitk_kernel(DecodeParams p) {
   };
 
   for (int kk = k_start; kk < k_end; kk += 32 * NST) {
-    step(kk, 0);
-    if (kk + 32 >= k_end) break;
-    step(kk + 32, 1);
-    if (kk + 64 >= k_end) break;
-    if constexpr (NST == 3) {
-      step(kk + 64, 2);
-      if (kk + 96 >= k_end) break;
+#pragma unroll
+    for (int j = 0; j < NST; ++j) {
+      if (kk + 32 * j >= k_end) break;
+      step(kk + 32 * j, j);
     }
   }
   wait_vm<0>();
 
-  // ---- store the partial ----
-  if (rvalid) {
-    const long grow = (long)(qs + t) * p.Hq + (long)kvh * G + rho % G;
+  // ---- store the partials ----
+#pragma unroll
+  for (int rb = 0; rb < RBW; ++rb) {
+    if (!rvalid[rb]) continue;
+    const long grow = (long)(qs + tq[rb]) * p.Hq + (long)kvh * G + rho[rb] % G;
     float* a = p.acc + (grow * p.num_splits + s) * D;
 #pragma unroll
-    for (int db = 0; db < DB; ++db) *reinterpret_cast<f32x4*>(a + db * 16 + 4 * g) = oacc[db] * v_mul;
+    for (int db = 0; db < DB; ++db) *reinterpret_cast<f32x4*>(a + db * 16 + 4 * g) = oacc[rb][db] * v_mul;
     if (g == 0) {
-      const bool empty = !(l_run > 0.f);
-      p.m[grow * p.num_splits + s] = empty ? -INFINITY : m_run * kLn2;
-      p.l[grow * p.num_splits + s] = empty ? 0.f : l_run;
+      const bool empty = !(l_run[rb] > 0.f);
+      p.m[grow * p.num_splits + s] = empty ? -INFINITY : m_run[rb] * kLn2;
+      p.l[grow * p.num_splits + s] = empty ? 0.f : l_run[rb];
     }
   }
 }
 
-#ifndef DECODE_NST
-#define DECODE_NST 2
+// Ring depth per launch shape.  Every stage in flight holds 32 keys of K
+// and V; the one-wave shapes are limited by LDS per CU, the two-wave verify
+// shape by registers, so it takes a deeper ring to keep enough bytes moving.
+#ifndef DECODE_NST_1
+#define DECODE_NST_1 2
+#endif
+#ifndef DECODE_NST_2
+#define DECODE_NST_2 2
+#endif
+#ifndef DECODE_NST_4_FP8
+#define DECODE_NST_4_FP8 2
+#endif
+#ifndef DECODE_NST_4_BF16
+#define DECODE_NST_4_BF16 2
 #endif
 
-template <int D, bool FP8, int W>
+template <int D, bool FP8, int W, int RBW, int NST>
 static hipError_t launch_t(const DecodeParams& p, hipStream_t st) {
   const long items = (long)p.R * p.Hkv * p.num_splits;
   if (p.g_cache != nullptr)
-    decode_splitk_kernel<D, FP8, W, DECODE_NST, true><<<dim3((unsigned)items), dim3(64 * W), 0, st>>>(p);
+    decode_splitk_kernel<D, FP8, W, RBW, NST, true><<<dim3((unsigned)items), dim3(64 * W), 0, st>>>(p);
   else
-    decode_splitk_kernel<D, FP8, W, DECODE_NST, false><<<dim3((unsigned)items), dim3(64 * W), 0, st>>>(p);
+    decode_splitk_kernel<D, FP8, W, RBW, NST, false><<<dim3((unsigned)items), dim3(64 * W), 0, st>>>(p);
   return hipGetLastError();
 }
 
+// Row blocks of a (request, KV head): 1 -> one wave; 2 -> one wave holding
+// both; 3 or 4 -> two waves of two blocks each.
 template <int D, bool FP8>
 static hipError_t launch_w(const DecodeParams& p, hipStream_t st) {
-  if (p.row_blocks <= 1) return launch_t<D, FP8, 1>(p, st);
-  if (p.row_blocks == 2) return launch_t<D, FP8, 2>(p, st);
-  return launch_t<D, FP8, 4>(p, st);
+  if (p.row_blocks <= 1) return launch_t<D, FP8, 1, 1, DECODE_NST_1>(p, st);
+  if (p.row_blocks == 2) return launch_t<D, FP8, 1, 2, DECODE_NST_2>(p, st);
+#ifdef DECODE_VERIFY_W4
+  return launch_t<D, FP8, 4, 1, FP8 ? DECODE_NST_4_FP8 : DECODE_NST_4_BF16>(p, st);
+#else
+  return launch_t<D, FP8, 2, 2, FP8 ? DECODE_NST_4_FP8 : DECODE_NST_4_BF16>(p, st);
+#endif
 }
 
 hipError_t launch_decode_splitk(const DecodeParams& p, int head_dim, bool fp8, hipStream_t st) {
