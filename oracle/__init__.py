@@ -11,10 +11,10 @@ forms, invariants, brute force, torch's own fp8 decoding).
 from .prefill import (gate_prefix, visible_mask, forward, backward, row_stats,
                       forward_rows)
 from .decode import (fp8_e4m3fn_to_f64, gather_request_kv, gather_request_gates,
-                     decode_paged, decode_partials, splitk_reduce)
+                     decode_paged, prefill_paged, decode_partials, splitk_reduce)
 from .cache import e4m3fn_encode, quantize_token_heads, cache_write_fp8
 
 __all__ = ["gate_prefix", "visible_mask", "forward", "backward", "row_stats",
            "forward_rows", "fp8_e4m3fn_to_f64", "gather_request_kv", "gather_request_gates",
-           "decode_paged", "decode_partials", "splitk_reduce",
+           "decode_paged", "prefill_paged", "decode_partials", "splitk_reduce",
            "e4m3fn_encode", "quantize_token_heads", "cache_write_fp8"]

@@ -140,6 +140,26 @@ def decode_paged(q, cu_seqlens_q, k_cache, v_cache, block_table, seq_lens,
     return o, lse
 
 
+def prefill_paged(q, cu_seqlens_q, k_cache, v_cache, block_table, seq_lens,
+                  scale, fp8, k_scale=None, v_scale=None, sink=None, window=0,
+                  g_cache=None, per_tensor=False):
+    """Paged prefill over the same cache: any number n >= 1 of new tokens per
+    request (chunked prefill, speculative verify longer than four tokens, or
+    a mixed batch of these with decode rows).
+
+    ROCm/aiter PR #6660, "Technical details" and commit message 3: batches
+    that are not all short queries take the other ("2d") kernel, with one
+    program per (KV head, query block) over the paged cache.  The per-row
+    definition does not depend on the route: query t of a request with KV
+    length L and n new tokens sits at position L - n + t and its output is
+    the softmax-weighted sum over its visible keys, exactly as in
+    ``decode_paged``, which this evaluates row by row.
+    """
+    return decode_paged(q, cu_seqlens_q, k_cache, v_cache, block_table, seq_lens, scale, fp8,
+                        k_scale, v_scale, sink=sink, window=window, g_cache=g_cache,
+                        per_tensor=per_tensor)
+
+
 def decode_partials(q, cu_seqlens_q, k_cache, v_cache, block_table, seq_lens,
                     scale, fp8, split_len, num_splits, k_scale=None,
                     v_scale=None, sink=None, window=0, g_cache=None,
