@@ -23,9 +23,10 @@ from typing import Optional
 
 import torch
 
-__all__ = ["attn_fwd_varlen", "attn_bwd_varlen", "attn_decode_paged",
+__all__ = ["attn_fwd_varlen", "attn_bwd_varlen", "attn_decode_paged", "attn_prefill_paged",
            "attn_splitk_reduce", "attn_kv_cache_write_fp8", "attn_fwd_workspace_size",
            "attn_bwd_workspace_size", "attn_decode_workspace_size",
+           "attn_prefill_paged_workspace_size",
            "ATTN_DTYPE_BF16", "ATTN_DTYPE_FP8_E4M3FN", "ATTN_DTYPE_FP32",
            "ATTN_BWD_DETERMINISTIC", "ATTN_BWD_FUSED_DQ",
            "AttnError", "lib_path", "library"]
@@ -67,6 +68,10 @@ _SIGNATURES = {
     "attn_decode_paged_ext": ([_vp, _vp, _c_int, _c_int, _vp, _vp, _c_int, _vp, _vp, _c_int, _vp, _c_int,
                                _vp, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int, ctypes.c_float, _vp,
                                _c_int, _vp, _c_int, _vp, _vp, _vp, ctypes.c_size_t, _vp], _c_int),
+    "attn_prefill_paged_workspace_size": ([_c_int] * 8, _c_size),
+    "attn_prefill_paged": ([_vp, _vp, _c_int, _c_int, _vp, _vp, _c_int, _vp, _vp, _c_int, _vp, _c_int,
+                            _vp, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int, ctypes.c_float, _vp,
+                            _c_int, _vp, _c_int, _vp, _vp, _vp, ctypes.c_size_t, _vp], _c_int),
     "attn_splitk_reduce": ([_vp, _vp, _vp, _c_int, _c_int, _c_int, _vp, _c_int, _vp, _vp], _c_int),
     "attn_kv_cache_write_fp8": ([_vp, _vp, _vp, _c_int, _c_int, _c_int, _vp, _vp, _vp, _vp, _c_int,
                                  _c_int, _vp], _c_int),
@@ -142,6 +147,13 @@ def attn_decode_workspace_size(num_requests, max_seqlen_q, max_seq_len, num_q_he
     return int(library.attn_decode_workspace_size(num_requests, max_seqlen_q, max_seq_len,
                                                   num_q_heads, num_kv_heads, head_dim,
                                                   block_size, kv_split_len))
+
+
+def attn_prefill_paged_workspace_size(num_requests, max_seqlen_q, max_seq_len, num_q_heads,
+                                      num_kv_heads, head_dim, block_size, kv_split_len=0) -> int:
+    return int(library.attn_prefill_paged_workspace_size(num_requests, max_seqlen_q, max_seq_len,
+                                                         num_q_heads, num_kv_heads, head_dim,
+                                                         block_size, kv_split_len))
 
 
 def _workspace(nbytes, device):
@@ -229,16 +241,9 @@ def attn_bwd_varlen(q, k, v, o, do, lse, cu_seqlens, max_seqlen, softmax_scale=N
     return dq, dk, dvv, dsink, dg
 
 
-def attn_decode_paged(q, cu_seqlens_q, max_seqlen_q, k_cache, v_cache, kv_dtype,
-                      k_scale, v_scale, block_table, seq_lens, max_seq_len,
-                      softmax_scale=None, kv_split_len=0, return_lse=False, out=None,
-                      sink=None, window=0, g_cache=None):
-    """Paged decode.  q bf16 [Tq, Hq, D]; k_cache / v_cache [NB, Hkv, B, D]
-    as bf16 or as uint8 / float8_e4m3fn codes; k_scale / v_scale fp32
-    [NB, Hkv, B] for fp8 (None for bf16); block_table int32 [R, max_pages];
-    seq_lens int32 [R].  Returns out bf16 [Tq, Hq, D] (and lse fp32 [Tq, Hq]).
-    Optional: one-element k_scale / v_scale = per-tensor fp8 scales; sink fp32
-    [Hq]; window (> 0); g_cache fp32 [NB, Hq, B] cumulative log gates."""
+def _paged(prefill, q, cu_seqlens_q, max_seqlen_q, k_cache, v_cache, kv_dtype, k_scale, v_scale,
+           block_table, seq_lens, max_seq_len, softmax_scale, kv_split_len, return_lse, out,
+           sink, window, g_cache):
     dev = q.device
     _need(q, "q", torch.bfloat16, None, 3)
     _need(cu_seqlens_q, "cu_seqlens_q", torch.int32, dev, 1)
@@ -280,17 +285,44 @@ def attn_decode_paged(q, cu_seqlens_q, max_seqlen_q, k_cache, v_cache, kv_dtype,
     if out is None:
         out = torch.empty((Tq, Hq, D), dtype=torch.bfloat16, device=dev)
     lse = torch.empty((Tq, Hq), dtype=torch.float32, device=dev) if return_lse else None
-    ws_n = attn_decode_workspace_size(R, int(max_seqlen_q), int(max_seq_len), Hq, Hkv, D, B,
-                                      int(kv_split_len))
+    ws_fn = attn_prefill_paged_workspace_size if prefill else attn_decode_workspace_size
+    ws_n = ws_fn(R, int(max_seqlen_q), int(max_seq_len), Hq, Hkv, D, B, int(kv_split_len))
     ws = _workspace(ws_n, dev)
-    st = library.attn_decode_paged_ext(
+    entry = library.attn_prefill_paged if prefill else library.attn_decode_paged_ext
+    st = entry(
         _ptr(q), _ptr(cu_seqlens_q), R, int(max_seqlen_q), _ptr(k_cache), _ptr(v_cache),
         int(kv_dtype), _ptr(k_scale), _ptr(v_scale), int(per_tensor), _ptr(block_table),
         block_table.shape[1], _ptr(seq_lens), int(max_seq_len), NB, B, Hq, Hkv, D,
         float(softmax_scale), _ptr(sink), int(window), _ptr(g_cache), int(kv_split_len),
         _ptr(out), _ptr(lse), _ptr(ws), ws_n, _stream(dev))
-    _check(st, "attn_decode_paged")
+    _check(st, "attn_prefill_paged" if prefill else "attn_decode_paged")
     return (out, lse) if return_lse else out
+
+
+def attn_decode_paged(q, cu_seqlens_q, max_seqlen_q, k_cache, v_cache, kv_dtype,
+                      k_scale, v_scale, block_table, seq_lens, max_seq_len,
+                      softmax_scale=None, kv_split_len=0, return_lse=False, out=None,
+                      sink=None, window=0, g_cache=None):
+    """Paged decode.  q bf16 [Tq, Hq, D]; k_cache / v_cache [NB, Hkv, B, D]
+    as bf16 or as uint8 / float8_e4m3fn codes; k_scale / v_scale fp32
+    [NB, Hkv, B] for fp8 (None for bf16); block_table int32 [R, max_pages];
+    seq_lens int32 [R].  Returns out bf16 [Tq, Hq, D] (and lse fp32 [Tq, Hq]).
+    Optional: one-element k_scale / v_scale = per-tensor fp8 scales; sink fp32
+    [Hq]; window (> 0); g_cache fp32 [NB, Hq, B] cumulative log gates."""
+    return _paged(False, q, cu_seqlens_q, max_seqlen_q, k_cache, v_cache, kv_dtype, k_scale, v_scale,
+                  block_table, seq_lens, max_seq_len, softmax_scale, kv_split_len, return_lse, out,
+                  sink, window, g_cache)
+
+
+def attn_prefill_paged(q, cu_seqlens_q, max_seqlen_q, k_cache, v_cache, kv_dtype,
+                       k_scale, v_scale, block_table, seq_lens, max_seq_len,
+                       softmax_scale=None, kv_split_len=0, return_lse=False, out=None,
+                       sink=None, window=0, g_cache=None):
+    """Paged prefill: as attn_decode_paged with any number of new tokens per
+    request (each request's new tokens already in its cache)."""
+    return _paged(True, q, cu_seqlens_q, max_seqlen_q, k_cache, v_cache, kv_dtype, k_scale, v_scale,
+                  block_table, seq_lens, max_seq_len, softmax_scale, kv_split_len, return_lse, out,
+                  sink, window, g_cache)
 
 
 def attn_splitk_reduce(acc, m, l, out_dtype=torch.float32, return_lse=True):

@@ -1,6 +1,7 @@
 // C ABI of the attention library: argument validation, workspace layout and
 // launch of the gfx950 kernels.  Every check runs before the first launch,
 // so a call that returns an error has enqueued nothing.
+#include <algorithm>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -259,14 +260,39 @@ int choose_split_len(int R, int Hkv, int max_seq_len, int B) {
   return sl;
 }
 
+// Query blocks per (request, KV head) of the launch: one block of up to 64
+// rows for short queries, blocks of 128 rows beyond that.
+int query_blocks(int max_q, int Hq, int Hkv) {
+  const long rows = (long)max_q * (Hq / Hkv);
+  return rows <= 64 ? 1 : (int)((rows + 127) / 128);
+}
+
+// Paged prefill: enough query blocks already fill the chip, so one segment
+// per block (no partials, no reduce); otherwise segments that bring the
+// work items near 2048.
+int choose_split_len_prefill(int R, int Hkv, int nqb, int max_seq_len, int B) {
+  const int unit = B > 32 ? B : 32;
+  const long items = (long)R * Hkv * nqb;
+  const long whole = ((long)max_seq_len + unit - 1) / unit * unit;
+  if (items >= 1024) return (int)std::min<long>(whole, 1L << 30);
+  const long want = (2048 + items - 1) / items;
+  long sl = ((max_seq_len + want - 1) / want + unit - 1) / unit * unit;
+  sl = std::max<long>(sl, std::max(256, unit));
+  return (int)std::min(sl, whole);
+}
+
 struct DecLayout {
   size_t acc, m, l, total;
   int split_len, num_splits;
 };
-DecLayout dec_layout(int R, int max_q, int max_seq_len, int Hq, int Hkv, int D, int B, int split_len) {
+DecLayout dec_layout(int R, int max_q, int max_seq_len, int Hq, int Hkv, int D, int B, int split_len,
+                     bool prefill = false) {
   DecLayout L{};
-  L.split_len = split_len > 0 ? split_len : choose_split_len(R, Hkv, max_seq_len, B);
+  L.split_len = split_len > 0 ? split_len
+                : prefill ? choose_split_len_prefill(R, Hkv, query_blocks(max_q, Hq, Hkv), max_seq_len, B)
+                          : choose_split_len(R, Hkv, max_seq_len, B);
   L.num_splits = (max_seq_len + L.split_len - 1) / L.split_len;
+  if (L.num_splits == 1) return L;     // single segment: the kernel writes the output
   const size_t rows = (size_t)R * max_q * Hq;
   size_t off = 0;
   L.acc = off; off += round_up(rows * L.num_splits * (size_t)D * sizeof(float));
@@ -300,18 +326,19 @@ int attn_decode_paged(const void* q, const int32_t* cu_seqlens_q, int num_reques
                                stream);
 }
 
-int attn_decode_paged_ext(const void* q, const int32_t* cu_seqlens_q, int num_requests, int max_seqlen_q,
-                          const void* k_cache, const void* v_cache, int kv_dtype, const float* k_scale,
-                          const float* v_scale, int per_tensor_scales, const int32_t* block_table,
-                          int max_pages, const int32_t* seq_lens, int max_seq_len, int num_blocks,
-                          int block_size, int num_q_heads, int num_kv_heads, int head_dim,
-                          float softmax_scale, const float* sink, int window, const float* g_cache,
-                          int kv_split_len, void* out, float* lse, void* workspace,
-                          size_t workspace_bytes, void* stream) {
+namespace {
+int paged_attention(bool prefill, const void* q, const int32_t* cu_seqlens_q, int num_requests,
+                    int max_seqlen_q, const void* k_cache, const void* v_cache, int kv_dtype,
+                    const float* k_scale, const float* v_scale, int per_tensor_scales,
+                    const int32_t* block_table, int max_pages, const int32_t* seq_lens, int max_seq_len,
+                    int num_blocks, int block_size, int num_q_heads, int num_kv_heads, int head_dim,
+                    float softmax_scale, const float* sink, int window, const float* g_cache,
+                    int kv_split_len, void* out, float* lse, void* workspace, size_t workspace_bytes,
+                    void* stream) {
   REQUIRE(num_requests >= 0, ATTN_ERR_INVALID, "num_requests %d is negative", num_requests);
   REQUIRE(max_seqlen_q >= 1, ATTN_ERR_INVALID, "max_seqlen_q %d must be >= 1", max_seqlen_q);
-  REQUIRE(max_seqlen_q <= 4, ATTN_ERR_UNSUPPORTED,
-          "max_seqlen_q %d > 4: prefill is not supported by the split-K decode path", max_seqlen_q);
+  REQUIRE(prefill || max_seqlen_q <= 4, ATTN_ERR_UNSUPPORTED,
+          "max_seqlen_q %d > 4: use attn_prefill_paged for longer queries", max_seqlen_q);
   REQUIRE(kv_dtype == ATTN_DTYPE_BF16 || kv_dtype == ATTN_DTYPE_FP8_E4M3FN, ATTN_ERR_UNSUPPORTED,
           "kv_dtype %d not supported (bf16 or fp8 e4m3fn)", kv_dtype);
   const bool fp8 = kv_dtype == ATTN_DTYPE_FP8_E4M3FN;
@@ -330,7 +357,7 @@ int attn_decode_paged_ext(const void* q, const int32_t* cu_seqlens_q, int num_re
   REQUIRE(num_q_heads >= 1 && num_kv_heads >= 1, ATTN_ERR_INVALID, "head counts must be positive");
   REQUIRE(num_q_heads % num_kv_heads == 0, ATTN_ERR_INVALID,
           "num_q_heads (%d) must be a multiple of num_kv_heads (%d)", num_q_heads, num_kv_heads);
-  REQUIRE(max_seqlen_q * (num_q_heads / num_kv_heads) <= 64, ATTN_ERR_UNSUPPORTED,
+  REQUIRE(prefill || max_seqlen_q * (num_q_heads / num_kv_heads) <= 64, ATTN_ERR_UNSUPPORTED,
           "max_seqlen_q * (Hq/Hkv) = %d exceeds 64 query rows per KV head",
           max_seqlen_q * (num_q_heads / num_kv_heads));
   REQUIRE(std::isfinite(softmax_scale), ATTN_ERR_INVALID, "softmax_scale is not finite");
@@ -339,7 +366,7 @@ int attn_decode_paged_ext(const void* q, const int32_t* cu_seqlens_q, int num_re
     const int unit = block_size > 32 ? block_size : 32;
     REQUIRE(kv_split_len % unit == 0, ATTN_ERR_INVALID,
             "kv_split_len %d must be a multiple of %d", kv_split_len, unit);
-    REQUIRE(kv_split_len <= attn::kDecodeMaxSplit, ATTN_ERR_UNSUPPORTED,
+    REQUIRE(prefill || kv_split_len <= attn::kDecodeMaxSplit, ATTN_ERR_UNSUPPORTED,
             "kv_split_len %d exceeds %d", kv_split_len, attn::kDecodeMaxSplit);
   }
   if (num_requests == 0) return ok();
@@ -361,6 +388,8 @@ int attn_decode_paged_ext(const void* q, const int32_t* cu_seqlens_q, int num_re
   if (sink) REQ_PTR(sink, 4);
   if (g_cache) {
     REQ_PTR(g_cache, 16);
+    REQUIRE(num_q_heads / num_kv_heads <= 64, ATTN_ERR_UNSUPPORTED,
+            "the gate cache is supported with at most 64 query heads per KV head");
     REQUIRE((long)num_blocks * num_q_heads * block_size * 4 <= 0xffffffffL, ATTN_ERR_UNSUPPORTED,
             "gate cache larger than 4 GiB is not supported");
   }
@@ -369,10 +398,13 @@ int attn_decode_paged_ext(const void* q, const int32_t* cu_seqlens_q, int num_re
   REQ_PTR(out, 16);
   if (lse) REQ_PTR(lse, 4);
   const DecLayout lay = dec_layout(num_requests, max_seqlen_q, max_seq_len, num_q_heads, num_kv_heads,
-                                   head_dim, block_size, kv_split_len);
+                                   head_dim, block_size, kv_split_len, prefill);
   REQUIRE(workspace_bytes >= lay.total, ATTN_ERR_INVALID, "workspace too small: %zu < %zu bytes",
           workspace_bytes, lay.total);
-  REQ_PTR(workspace, 256);
+  if (lay.total > 0) REQ_PTR(workspace, 256);
+  REQUIRE((long)num_requests * num_kv_heads * lay.num_splits *
+                  query_blocks(max_seqlen_q, num_q_heads, num_kv_heads) <= 0x7fffffffL,
+          ATTN_ERR_UNSUPPORTED, "more than 2^31 - 1 work items (requests x KV heads x segments x query blocks)");
 
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   char* ws = reinterpret_cast<char*>(workspace);
@@ -388,8 +420,10 @@ int attn_decode_paged_ext(const void* q, const int32_t* cu_seqlens_q, int num_re
   p.row_blocks = (max_seqlen_q * (num_q_heads / num_kv_heads) + 15) / 16;
   p.sink = sink; p.g_cache = g_cache; p.window = window > 0 ? window : 0;
   p.per_tensor = per_tensor_scales;
+  if (lay.num_splits == 1) { p.out = out; p.lse = lse; }
   hipError_t e = attn::launch_decode_splitk(p, head_dim, fp8, s);
-  if (e != hipSuccess) return hip_fail(e, "decode launch");
+  if (e != hipSuccess) return hip_fail(e, prefill ? "paged prefill launch" : "decode launch");
+  if (lay.num_splits == 1) return ok();
 
   attn::ReduceParams r{};
   r.acc = p.acc; r.m = p.m; r.l = p.l; r.out = out; r.lse = lse;
@@ -400,6 +434,48 @@ int attn_decode_paged_ext(const void* q, const int32_t* cu_seqlens_q, int num_re
   e = attn::launch_splitk_reduce(r, s);
   if (e != hipSuccess) return hip_fail(e, "reduce launch");
   return ok();
+}
+}  // namespace
+
+int attn_decode_paged_ext(const void* q, const int32_t* cu_seqlens_q, int num_requests, int max_seqlen_q,
+                          const void* k_cache, const void* v_cache, int kv_dtype, const float* k_scale,
+                          const float* v_scale, int per_tensor_scales, const int32_t* block_table,
+                          int max_pages, const int32_t* seq_lens, int max_seq_len, int num_blocks,
+                          int block_size, int num_q_heads, int num_kv_heads, int head_dim,
+                          float softmax_scale, const float* sink, int window, const float* g_cache,
+                          int kv_split_len, void* out, float* lse, void* workspace,
+                          size_t workspace_bytes, void* stream) {
+  return paged_attention(false, q, cu_seqlens_q, num_requests, max_seqlen_q, k_cache, v_cache, kv_dtype,
+                         k_scale, v_scale, per_tensor_scales, block_table, max_pages, seq_lens,
+                         max_seq_len, num_blocks, block_size, num_q_heads, num_kv_heads, head_dim,
+                         softmax_scale, sink, window, g_cache, kv_split_len, out, lse, workspace,
+                         workspace_bytes, stream);
+}
+
+size_t attn_prefill_paged_workspace_size(int num_requests, int max_seqlen_q, int max_seq_len,
+                                         int num_q_heads, int num_kv_heads, int head_dim, int block_size,
+                                         int kv_split_len) {
+  if (num_requests <= 0 || max_seqlen_q <= 0 || max_seq_len <= 0 || num_q_heads <= 0 ||
+      num_kv_heads <= 0 || head_dim <= 0 || block_size <= 0 || kv_split_len < 0 ||
+      num_q_heads % num_kv_heads != 0)
+    return 0;
+  return dec_layout(num_requests, max_seqlen_q, max_seq_len, num_q_heads, num_kv_heads, head_dim,
+                    block_size, kv_split_len, true).total;
+}
+
+int attn_prefill_paged(const void* q, const int32_t* cu_seqlens_q, int num_requests, int max_seqlen_q,
+                       const void* k_cache, const void* v_cache, int kv_dtype, const float* k_scale,
+                       const float* v_scale, int per_tensor_scales, const int32_t* block_table,
+                       int max_pages, const int32_t* seq_lens, int max_seq_len, int num_blocks,
+                       int block_size, int num_q_heads, int num_kv_heads, int head_dim,
+                       float softmax_scale, const float* sink, int window, const float* g_cache,
+                       int kv_split_len, void* out, float* lse, void* workspace,
+                       size_t workspace_bytes, void* stream) {
+  return paged_attention(true, q, cu_seqlens_q, num_requests, max_seqlen_q, k_cache, v_cache, kv_dtype,
+                         k_scale, v_scale, per_tensor_scales, block_table, max_pages, seq_lens,
+                         max_seq_len, num_blocks, block_size, num_q_heads, num_kv_heads, head_dim,
+                         softmax_scale, sink, window, g_cache, kv_split_len, out, lse, workspace,
+                         workspace_bytes, stream);
 }
 
 // ---------------------------------------------------------------------------

@@ -117,25 +117,36 @@ __global__ __launch_bounds__(64 * W) void decode_splitk_kernel(DecodeParams p) {
   const int kvh = item % p.Hkv;
   item /= p.Hkv;
   const int r = item % p.R;
-  const int s = item / p.R;
+  item /= p.R;
+  const int qb = item % p.nqb;
+  const int s = item / p.nqb;
   const int L = p.seq_lens[r];
-  const int k_begin = s * p.split_len;
-  if (k_begin >= L) return;            // segment beyond this request: none
-  const int k_end = min(L, k_begin + p.split_len);
   const int qs = p.cu_q[r];
   const int qlen = p.cu_q[r + 1] - qs;
   const int G = p.Hq / p.Hkv;
-  if (qlen <= 0) return;               // whole workgroup, before any barrier
-  // first key any row of the request can see (sliding window), and where
+  // this workgroup's rows: block qb of the request's qlen * G rows
+  constexpr int RPB = 16 * W * RBW;
+  const int row0 = qb * RPB;
+  const int nrows = qlen * G - row0;   // rows of the block that exist (may exceed RPB)
+  if (nrows <= 0) return;              // whole workgroup, before any barrier
+  const int pos_min = L - qlen + row0 / G;                       // first row's position
+  const int pos_max = L - qlen + (row0 + min(nrows, RPB) - 1) / G;   // last row's position
+  const bool direct = p.out != nullptr;
+  const int k_begin = s * p.split_len;
+  // A segment that starts past every row's position holds nothing for the
+  // block; the reduce reads a row's segments only up to its own position.
+  if (!direct && k_begin > pos_max) return;
+  const int k_end = min(min(L, k_begin + p.split_len), pos_max + 1);
+  // first key any row of the block can see (sliding window), and where
   // this segment's streaming starts (32-key steps stay aligned)
-  const int k_lo = p.window > 0 ? max(0, L - qlen - p.window + 1) : 0;
+  const int k_lo = p.window > 0 ? max(0, pos_min - p.window + 1) : 0;
   const int k_start = max(k_begin, k_lo & ~31);
   const bool per_tensor = FP8 && p.per_tensor;
-  const bool active = wave * 16 * RBW < qlen * G;   // wave-uniform; idle waves still copy
+  const bool active = wave * 16 * RBW < nrows;   // wave-uniform; idle waves still copy
 
   // ---- copy set-up: page bases (SGPR) and fixed per-lane offsets ----
   const int bsh = p.B_shift, bmask = p.B - 1;   // page size is a power of two
-  const int last_page = (L - 1) >> bsh;
+  const int last_page = max(0, (L - 1) >> bsh);
   // block-table reads are wave-uniform: the constant address space makes
   // them scalar loads
   const __attribute__((address_space(4))) int32_t* bt =
@@ -216,7 +227,7 @@ __global__ __launch_bounds__(64 * W) void decode_splitk_kernel(DecodeParams p) {
   float gq2[RBW];
 #pragma unroll
   for (int rb = 0; rb < RBW; ++rb) {
-    rho[rb] = (wave * RBW + rb) * 16 + li;
+    rho[rb] = row0 + (wave * RBW + rb) * 16 + li;
     tq[rb] = rho[rb] / G;
     rvalid[rb] = active && tq[rb] < qlen;
     pos[rb] = L - qlen + tq[rb];                       // last key this row sees
@@ -228,7 +239,7 @@ __global__ __launch_bounds__(64 * W) void decode_splitk_kernel(DecodeParams p) {
     // gate of the row's own position (the query side of G_query - G_key)
     gq2[rb] = 0.f;
     if constexpr (GATE) {
-      const int prow = min(pos[rb], L - 1);
+      const int prow = max(0, min(pos[rb], L - 1));
       const int pq = p.block_table[(long)r * p.max_pages + (prow >> bsh)];
       gq2[rb] = p.g_cache[(((long)pq * p.Hq + kvh * G + rho[rb] % G) << bsh) + (prow & bmask)] * kLog2e;
     }
@@ -258,7 +269,7 @@ __global__ __launch_bounds__(64 * W) void decode_splitk_kernel(DecodeParams p) {
 #pragma unroll
     for (int db = 0; db < DB; ++db) oacc[rb][db] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
-  const int vis_all = L - qlen;        // keys below this are visible to every row
+  const int vis_all = pos_min;         // keys up to this are visible to every row (before the window)
 
   auto compute = [&](int kk, int st) {
     const uint8_t* Kt = smem + st * STAGE;
@@ -266,7 +277,7 @@ __global__ __launch_bounds__(64 * W) void decode_splitk_kernel(DecodeParams p) {
     const float* Sc = reinterpret_cast<const float*>(Kt + 2 * TILE + wave * 2 * SCB);
     const float* Gt = reinterpret_cast<const float*>(Kt + 2 * TILE + W * 2 * SCB);
     // uniform: a key past some row's position, or before some row's window
-    const bool need_mask = kk + 31 > vis_all || (p.window > 0 && kk <= L - 1 - p.window);
+    const bool need_mask = kk + 31 > vis_all || (p.window > 0 && kk <= pos_max - p.window);
     // ---- scores S^T = K Q^T (C lane: row li, keys kk+kb*16+4g+i) ----
     f32x4 sc[RBW][2];
 #pragma unroll
@@ -440,11 +451,24 @@ __global__ __launch_bounds__(64 * W) void decode_splitk_kernel(DecodeParams p) {
   }
   wait_vm<0>();
 
-  // ---- store the partials ----
+  // ---- store the partials, or with a single segment the output ----
 #pragma unroll
   for (int rb = 0; rb < RBW; ++rb) {
     if (!rvalid[rb]) continue;
     const long grow = (long)(qs + tq[rb]) * p.Hq + (long)kvh * G + rho[rb] % G;
+    if (direct) {
+      const bool empty = !(l_run[rb] > 0.f);
+      const float inv = empty ? 0.f : v_mul / l_run[rb];
+      bf16* o = reinterpret_cast<bf16*>(p.out) + grow * D;
+#pragma unroll
+      for (int db = 0; db < DB; ++db) {
+        const f32x4 v = oacc[rb][db] * inv;
+        *reinterpret_cast<bf16x4*>(o + db * 16 + 4 * g) = bf16x4{(bf16)v[0], (bf16)v[1], (bf16)v[2], (bf16)v[3]};
+      }
+      if (g == 0 && p.lse != nullptr)
+        p.lse[grow] = empty ? -INFINITY : m_run[rb] * kLn2 + logf(l_run[rb]);
+      continue;
+    }
     float* a = p.acc + (grow * p.num_splits + s) * D;
 #pragma unroll
     for (int db = 0; db < DB; ++db) *reinterpret_cast<f32x4*>(a + db * 16 + 4 * g) = oacc[rb][db] * v_mul;
@@ -471,10 +495,15 @@ __global__ __launch_bounds__(64 * W) void decode_splitk_kernel(DecodeParams p) {
 #ifndef DECODE_NST_4_BF16
 #define DECODE_NST_4_BF16 2
 #endif
+#ifndef DECODE_NST_PREFILL
+#define DECODE_NST_PREFILL 2
+#endif
 
 template <int D, bool FP8, int W, int RBW, int NST>
-static hipError_t launch_t(const DecodeParams& p, hipStream_t st) {
-  const long items = (long)p.R * p.Hkv * p.num_splits;
+static hipError_t launch_t(DecodeParams p, hipStream_t st) {
+  p.nqb = (p.row_blocks + W * RBW - 1) / (W * RBW);
+  const long items = (long)p.R * p.Hkv * p.num_splits * p.nqb;
+  if (items > 0x7fffffffL) return hipErrorInvalidConfiguration;
   if (p.g_cache != nullptr)
     decode_splitk_kernel<D, FP8, W, RBW, NST, true><<<dim3((unsigned)items), dim3(64 * W), 0, st>>>(p);
   else
@@ -483,9 +512,11 @@ static hipError_t launch_t(const DecodeParams& p, hipStream_t st) {
 }
 
 // Row blocks of a (request, KV head): 1 -> one wave; 2 -> one wave holding
-// both; 3 or 4 -> two waves of two blocks each.
+// both; 3 or 4 -> two waves of two blocks each; more (prefill) -> query
+// blocks of 128 rows, four waves of two blocks each.
 template <int D, bool FP8>
 static hipError_t launch_w(const DecodeParams& p, hipStream_t st) {
+  if (p.row_blocks > 4) return launch_t<D, FP8, 4, 2, DECODE_NST_PREFILL>(p, st);
   if (p.row_blocks <= 1) return launch_t<D, FP8, 1, 1, DECODE_NST_1>(p, st);
   if (p.row_blocks == 2) return launch_t<D, FP8, 1, 2, DECODE_NST_2>(p, st);
 #ifdef DECODE_VERIFY_W4
@@ -496,7 +527,7 @@ static hipError_t launch_w(const DecodeParams& p, hipStream_t st) {
 }
 
 hipError_t launch_decode_splitk(const DecodeParams& p, int head_dim, bool fp8, hipStream_t st) {
-  if (p.row_blocks > 4) return hipErrorInvalidValue;
+  if (p.row_blocks < 1) return hipErrorInvalidValue;
   if (head_dim == 128) return fp8 ? launch_w<128, true>(p, st) : launch_w<128, false>(p, st);
   if (head_dim == 64 && !fp8) return launch_w<64, false>(p, st);
   return hipErrorInvalidValue;

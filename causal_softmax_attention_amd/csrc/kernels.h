@@ -48,6 +48,12 @@ struct DecodeParams {
   int window;               // sliding window (<= 0: none)
   int per_tensor;           // fp8 with one K and one V scale (k_scale[0], v_scale[0])
   float scale_log2;         // softmax_scale * log2(e)
+  // Single segment (num_splits == 1): the kernel writes the normalised
+  // output bf16 [Tq, Hq, D] and lse [Tq, Hq] (may be nullptr) itself and
+  // acc / m / l are unused; nullptr otherwise.
+  void* out;
+  float* lse;
+  int nqb;                  // query blocks per (request, KV head); set by the launcher
 };
 hipError_t launch_decode_splitk(const DecodeParams& p, int head_dim, bool fp8, hipStream_t st);
 

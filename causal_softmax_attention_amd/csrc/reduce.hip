@@ -41,7 +41,8 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(ReduceParams p) {
 
   int nsplit = p.num_splits;
   if (p.seq_lens != nullptr) {
-    // Decode rows: only the segments that exist for this row's request.
+    // Paged rows: only the segments that start at or before the row's own
+    // position (the partial kernel writes exactly those).
     const int tok = (int)(row / p.heads);
     if (tok >= p.cu_seqlens_q[p.num_requests]) return;   // whole workgroup
     int lo = 0, hi = p.num_requests;          // find r with cu[r] <= tok < cu[r+1]
@@ -49,8 +50,8 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(ReduceParams p) {
       const int mid = (lo + hi) >> 1;
       if (p.cu_seqlens_q[mid] <= tok) lo = mid; else hi = mid;
     }
-    const int L = p.seq_lens[lo];
-    nsplit = min(nsplit, (L + p.split_len - 1) / p.split_len);
+    const int pos = p.seq_lens[lo] - p.cu_seqlens_q[lo + 1] + tok;   // L - qlen + t
+    nsplit = pos < 0 ? 0 : min(nsplit, pos / p.split_len + 1);
   }
   const float* m = p.m + row * p.num_splits;
   const float* l = p.l + row * p.num_splits;

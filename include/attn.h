@@ -212,7 +212,9 @@ int attn_bwd_varlen(const void* q, const void* k, const void* v,
  *   lse      fp32 [Tq, Hq] (output, natural log) or NULL
  * Supported: head_dim 128 (bf16 or fp8 cache) or 64 (bf16 cache);
  * block_size 16, 32, 64 or 128; max_seqlen_q * (Hq / Hkv) <= 64.
- * workspace: attn_decode_workspace_size() bytes (same arguments).
+ * workspace: attn_decode_workspace_size() bytes (same arguments); with a
+ * single segment (kv_split_len >= max_seq_len) the kernel writes out and lse
+ * itself, needs no workspace (size 0, workspace may be NULL) and no reduce.
  * ---------------------------------------------------------------------- */
 size_t attn_decode_workspace_size(int num_requests, int max_seqlen_q,
                                   int max_seq_len, int num_q_heads,
@@ -266,6 +268,52 @@ int attn_decode_paged_ext(const void* q, const int32_t* cu_seqlens_q,
                           const float* sink, int window, const float* g_cache,
                           int kv_split_len, void* out, float* lse,
                           void* workspace, size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
+ * attn_prefill_paged -- paged prefill: any number of new query tokens per
+ * request over the same paged bf16 / per-token fp8 cache (chunked prefill,
+ * verify of more than four tokens, and mixed batches of these with decode
+ * rows).
+ *
+ * aiter PR #6660, Technical details and third commit message: batches that
+ * are not all short queries go to the other ("2d") kernel, one program per
+ * (KV head, query block) over the paged cache.  The result of each row is
+ * defined exactly as in attn_decode_paged_ext (positions, visibility, K and
+ * V scales, sink, window, gate); only the q_len limits are lifted.
+ *
+ * Arguments as attn_decode_paged_ext, except:
+ *   max_seqlen_q  >= 1, no upper limit (the new tokens of every request
+ *            must already be in its cache: seq_lens[r] >= q_len_r)
+ *   kv_split_len 0 = library's choice: one segment per query block when the
+ *            query blocks alone fill the GPU (no partials, no reduce), else
+ *            segments that bring the work items near 2048; or a multiple of
+ *            max(block_size, 32)
+ * Rows are the (token, head of the KV group) pairs of a request; a work
+ * item is (segment, 128-row query block, request, KV head) and streams only
+ * the keys its rows can see (causal limit and window).
+ * workspace: attn_prefill_paged_workspace_size() bytes (same arguments as
+ * attn_decode_workspace_size); 0 when one segment covers max_seq_len.
+ * Errors: as attn_decode_paged_ext; more than 2^31 - 1 work items is
+ * ATTN_ERR_UNSUPPORTED.
+ * ---------------------------------------------------------------------- */
+size_t attn_prefill_paged_workspace_size(int num_requests, int max_seqlen_q,
+                                         int max_seq_len, int num_q_heads,
+                                         int num_kv_heads, int head_dim,
+                                         int block_size, int kv_split_len);
+
+int attn_prefill_paged(const void* q, const int32_t* cu_seqlens_q,
+                       int num_requests, int max_seqlen_q,
+                       const void* k_cache, const void* v_cache, int kv_dtype,
+                       const float* k_scale, const float* v_scale,
+                       int per_tensor_scales,
+                       const int32_t* block_table, int max_pages,
+                       const int32_t* seq_lens, int max_seq_len,
+                       int num_blocks, int block_size,
+                       int num_q_heads, int num_kv_heads, int head_dim,
+                       float softmax_scale,
+                       const float* sink, int window, const float* g_cache,
+                       int kv_split_len, void* out, float* lse,
+                       void* workspace, size_t workspace_bytes, void* stream);
 
 /* ------------------------------------------------------------------------
  * attn_splitk_reduce -- merge split-K partials per row (aiter PR #6660,

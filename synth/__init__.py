@@ -306,6 +306,32 @@ def config4(kv_dtype=KV_FP8_E4M3FN, device="cpu", **kw) -> DecodeInputs:
                          name=f"verify-3x4q-ctx227k-h64kv4-d128-p128-{tag}", **kw)
 
 
+PREFILL_PAGED_NEW_TOKENS = 2048
+
+
+def prefill_paged_bench(device="cpu", **kw) -> DecodeInputs:
+    """Chunked prefill over the paged fp8 cache: 4 requests, each adding 2048
+    new tokens to a context whose total length is drawn uniformly in
+    [4096, 32768] (seeded); 64 query / 4 KV heads, D 128, page 16, per-token
+    fp8 K/V with the 20x token-magnitude spread, shuffled page table."""
+    rng = np.random.default_rng(11)
+    lens = [int(x) for x in rng.integers(4096, 32769, 4)]
+    return decode_inputs(lens, [PREFILL_PAGED_NEW_TOKENS] * 4, 64, 4, 128, 16,
+                         kv_dtype=KV_FP8_E4M3FN, seed=12, device=device,
+                         name="chunked-prefill-4x2048new-ctx4k-32k-h64kv4-d128-p16-fp8", **kw)
+
+
+def paged_attention_flops(seq_lens, q_lens, Hq, D, window=0):
+    """Algorithmic flops of causal paged attention: 4 D per visible
+    (query row, key) pair (QK^T and PV, one multiply-add each)."""
+    total = 0
+    for L, n in zip(seq_lens, q_lens):
+        pos = np.arange(int(L) - int(n), int(L), dtype=np.int64)
+        vis = pos + 1 if window <= 0 else np.minimum(pos + 1, window)
+        total += int(vis.sum())
+    return 4.0 * D * Hq * total
+
+
 # ----------------------------------------------------------------------------
 # Split-K partial tensors (for the reduce entry point on its own)
 # ----------------------------------------------------------------------------

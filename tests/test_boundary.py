@@ -68,7 +68,7 @@ def _decode(**kw):
     (dict(maxp=4), INVALID, "cannot hold"),
     (dict(q=NULL), INVALID, "q is NULL"),
     (dict(kc=P_ODD), INVALID, "aligned"),
-    (dict(wsb=16), INVALID, "workspace too small"),
+    (dict(wsb=16, maxsl=4096, maxp=256), INVALID, "workspace too small"),
     (dict(R=-1), INVALID, "negative"),
     (dict(scale=float("nan")), INVALID, "finite"),
 ])
@@ -235,3 +235,46 @@ def test_decode_ext_validation(kw, code, msg):
     st = _decode_ext(**kw)
     assert st == code
     assert msg in L.attn_last_error().decode()
+
+
+def _prefill(**kw):
+    a = dict(q=P, cu=P, R=2, maxq=512, kc=P, vc=P, kvd=A.ATTN_DTYPE_FP8_E4M3FN, ks=P, vs=P, pt=0, bt=P,
+             maxp=64, sl=P, maxsl=1024, nb=128, B=16, Hq=64, Hkv=4, D=128, scale=0.1, sink=NULL, win=0,
+             g=NULL, split=0, out=P, lse=NULL, ws=P, wsb=1 << 30)
+    a.update(kw)
+    return L.attn_prefill_paged(a["q"], a["cu"], a["R"], a["maxq"], a["kc"], a["vc"], a["kvd"], a["ks"],
+                                a["vs"], a["pt"], a["bt"], a["maxp"], a["sl"], a["maxsl"], a["nb"], a["B"],
+                                a["Hq"], a["Hkv"], a["D"], a["scale"], a["sink"], a["win"], a["g"],
+                                a["split"], a["out"], a["lse"], a["ws"], a["wsb"], NULL)
+
+
+@pytest.mark.parametrize("kw,code,msg", [
+    (dict(maxq=0), INVALID, "max_seqlen_q"),
+    (dict(ks=NULL), UNSUPPORTED, "per-token"),
+    (dict(kvd=A.ATTN_DTYPE_BF16), UNSUPPORTED, "only read with an fp8"),
+    (dict(D=64), UNSUPPORTED, "fp8 KV cache is supported with head_dim 128"),
+    (dict(B=24), UNSUPPORTED, "block_size"),
+    (dict(Hq=60, Hkv=8), INVALID, "multiple"),
+    (dict(split=48), INVALID, "multiple of"),
+    (dict(maxp=4), INVALID, "cannot hold"),
+    (dict(q=NULL), INVALID, "q is NULL"),
+    (dict(split=32, wsb=16), INVALID, "workspace too small"),
+    (dict(R=1 << 10, maxq=1 << 10, split=32, maxsl=1 << 20, maxp=1 << 16, wsb=1 << 62), UNSUPPORTED,
+     "work items"),
+    (dict(pt=2), INVALID, "per_tensor_scales"),
+    (dict(g=P, Hq=128, Hkv=1), UNSUPPORTED, "at most 64 query heads"),
+])
+def test_prefill_validation(kw, code, msg):
+    st = _prefill(**kw)
+    assert st == code
+    assert msg in L.attn_last_error().decode()
+
+
+def test_prefill_workspace_sizes():
+    # enough query blocks for one segment per block: no partials, no workspace
+    assert A.attn_prefill_paged_workspace_size(2, 4096, 8192, 64, 4, 128, 16) == 0
+    # a short chunk over a long context: split-K partials
+    n = A.attn_prefill_paged_workspace_size(1, 8, 200000, 64, 4, 128, 128)
+    assert n >= 1 * 8 * 64 * 2 * (128 + 2) * 4
+    # an explicit split of the whole context is one segment as well
+    assert A.attn_prefill_paged_workspace_size(1, 8, 1000, 64, 4, 128, 16, 1024) == 0
