@@ -344,6 +344,23 @@ def main():
                                        "GBps": wbytes / (uw * 1e-6) / 1e9,
                                        "frac_of_hbm_peak": wbytes / (uw * 1e-6) / 1e9 / HBM_PEAK_GBPS}
         del xw
+        # paged prefill: 4 chunks of 2048 new tokens over 4K-32K contexts, per-token fp8 cache
+        dp = synth.prefill_paged_bench(device=dev)
+        pmax, pq = dp.max_seq_len, dp.max_seqlen_q
+        fp = lambda: A.attn_prefill_paged(dp.q, dp.cu_seqlens_q, pq, dp.k_cache, dp.v_cache, dp.kv_dtype,
+                                          dp.k_scale, dp.v_scale, dp.block_table, dp.seq_lens, pmax, dp.scale)
+        fp()
+        tp = Timer()
+        for _ in range(5):
+            tp.run("p", fp)
+        torch.cuda.synchronize()
+        up = tp.mean_us("p")
+        pfl = synth.paged_attention_flops(dp.seq_lens.tolist(), dp.q_lens, dp.q.shape[1], dp.q.shape[2])
+        extra["prefill_paged_fp8"] = {"workload": "chunked prefill 4 x 2048 new tokens, contexts 4K-32K, "
+                                                  "h64 kv4 d128 page 16, per-token fp8 KV",
+                                      "us": up, "tflops": pfl / (up * 1e-6) / 1e12,
+                                      "frac_of_bf16_mfma_peak": pfl / (up * 1e-6) / 1e12 / MFMA_BF16_PEAK_TFLOPS}
+        del dp
         x5 = synth.config5(device=dev)
         f5f, f5b, _ = prefill_flops(x5)
         o5, l5 = A.attn_fwd_varlen(x5.q, x5.k, x5.v, x5.cu_seqlens, x5.max_seqlen, x5.scale, 0,
