@@ -26,6 +26,9 @@
 #ifndef BWD_RW_SMALL
 #define BWD_RW_SMALL 32
 #endif
+#ifndef BWD_NST_DKDV
+#define BWD_NST_DKDV 2
+#endif
 
 namespace attn {
 
@@ -51,10 +54,15 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdParams p) {
   constexpr int QRB = DQK * 2, ORB = DV * 2;   // bytes per Q / dO row
   constexpr int QPW = RQ * QRB / 4096, OPW = RQ * ORB / 4096;   // 1 KB blocks per wave
   static_assert(QPW * 4096 == RQ * QRB && OPW * 4096 == RQ * ORB, "tile must split into 4 x k 1 KB blocks");
-  __shared__ __attribute__((aligned(1024))) uint8_t q_lds[2][RQ * QRB];
-  __shared__ __attribute__((aligned(1024))) uint8_t do_lds[2][RQ * ORB];
-  __shared__ __attribute__((aligned(16))) float row_lds[2][3][64];   // lse, delta, gq (lanes >= RQ repeat)
-  __shared__ __attribute__((aligned(16))) float gk_lds[2][4][64];    // per wave: its keys' gate terms
+  constexpr int NSQ = BWD_NST_DKDV;    // ring stages (tiles in flight: NSQ - 1)
+  static_assert(NSQ >= 2 && NSQ <= 3, "ring depth");
+  // copies per tile issued by every wave (wave 0 adds the per-row terms):
+  // the exact count of the later tiles' copies a wave waits past
+  constexpr int LPT = QPW + OPW + (GATED ? 1 : 0);
+  __shared__ __attribute__((aligned(1024))) uint8_t q_lds[NSQ][RQ * QRB];
+  __shared__ __attribute__((aligned(1024))) uint8_t do_lds[NSQ][RQ * ORB];
+  __shared__ __attribute__((aligned(16))) float row_lds[NSQ][3][64];   // lse, delta, gq (lanes >= RQ repeat)
+  __shared__ __attribute__((aligned(16))) float gk_lds[NSQ][4][64];    // per wave: its keys' gate terms
 
   const int kvh = xcd_remap(blockIdx.x, p.Hkv), n = blockIdx.y, ktile = blockIdx.z;
   const int seq0 = p.cu[n];
@@ -108,9 +116,14 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdParams p) {
     orow[j] = o / ORB;
     ooff[j] = orow[j] * ostride + ((((o % ORB) >> 4) ^ tile_swz<ORB>(orow[j])) << 4);
   }
-  auto fetch = [&](int it, int st) {
-    const int hh = kvh * grp + it / nqt;
-    const int i0 = j0 + (it % nqt) * RQ;
+  // iteration (head hg of the group, query tile qt); the counters advance
+  // by one per iteration (no division in the loop)
+  auto advance = [&](int& hg, int& qt) {
+    if (++qt == nqt) { qt = 0; ++hg; }
+  };
+  auto fetch = [&](int hg, int qt, int st) {
+    const int hh = kvh * grp + hg;
+    const int i0 = j0 + qt * RQ;
     const bool tail = i0 + RQ > L;               // uniform: only the last tile clamps
     const long r0 = (long)(seq0 + i0) * p.Hq + hh;   // (token, head) row of the tile's first query
     const uint8_t* qb = reinterpret_cast<const uint8_t*>(p.q) + r0 * QRB;
@@ -152,17 +165,28 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdParams p) {
     for (int ks = 0; ks < KSV; ++ks) asm volatile("" :: "v"(vop[kb][ks]));
   }
 
-  if (n_it > 0) fetch(0, 0);
+  int hg = 0, qt = 0;       // this iteration
+  int f_hg = 0, f_qt = 0;   // the next one to fetch
+#pragma unroll
+  for (int s0 = 0; s0 < NSQ - 1; ++s0)
+    if (s0 < n_it) {
+      fetch(f_hg, f_qt, s0);
+      advance(f_hg, f_qt);
+    }
   float colsum[KBW];
 #pragma unroll
   for (int kb = 0; kb < KBW; ++kb) colsum[kb] = 0.f;
-  for (int it = 0; it < n_it; ++it) {
-    const int buf = it & 1;
-    wait_vm<0>();    // this wave's copies of tile it have landed
-    lds_barrier();   // ... and everyone's; the other stage is free again
-    if (it + 1 < n_it) fetch(it + 1, buf ^ 1);
+  int buf = 0;
+  for (int it = 0; it < n_it; ++it, advance(hg, qt), buf = (buf + 1 == NSQ ? 0 : buf + 1)) {
+    // this wave's copies of tile it have landed (the later tiles in flight
+    // each add at least LPT newer copies) ...
+    if (NSQ == 3 && it + 1 < n_it) wait_vm<LPT>(); else wait_vm<0>();
+    lds_barrier();   // ... and everyone's; the stage of tile it-1 is free again
+    if (it + NSQ - 1 < n_it) {
+      fetch(f_hg, f_qt, buf == 0 ? NSQ - 1 : buf - 1);
+      advance(f_hg, f_qt);
+    }
 
-    const int hg = it / nqt, qt = it % nqt;
     const int h = kvh * grp + hg;
     const int i0 = j0 + qt * RQ;
     float gk[KBW];

@@ -88,7 +88,9 @@ __device__ __forceinline__ bf16x4 to_bf16x4(f32x4 x) {
 // compiler quiet possible signalling NaNs first (a self-max per operand it
 // cannot prove canonical, e.g. lane-swap results); operands here are
 // arithmetic results or -inf, never signalling NaNs, and for quiet NaNs the
-// instruction already returns the other operand as fmaxf does.
+// instruction already returns the other operand as fmaxf does.  Only for
+// operands written by ordinary VALU instructions: the compiler does not
+// insert the wait states an MFMA result needs before an inline-asm read.
 __device__ __forceinline__ float max_nq(float a, float b) {
   float r;
   asm("v_max_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));

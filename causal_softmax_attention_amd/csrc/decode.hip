@@ -15,8 +15,10 @@
 // that share the KV head.  K scales multiply the QK columns; V scales
 // multiply the probability columns after the row sum; the scaled
 // probabilities are split into a bf16 high and low part so that PV keeps
-// fp32 accuracy; cache slots past seq_len never contribute (their bytes and
-// scales may be NaN, so they are selected away, not multiplied by 0).  A
+// fp32 accuracy (a bf16 cache has no V scales: its P enters PV as one
+// round-to-nearest bf16, as in the prefill forward); cache slots past
+// seq_len never contribute (their bytes and scales may be NaN, so they are
+// selected away, not multiplied by 0).  A
 // query whose last visible key precedes the segment stores an empty partial
 // (m = -inf, l = 0).
 //
@@ -46,7 +48,8 @@
 //     128 products with about 2^-13 relative error, far coarser than the
 //     fp32 accumulation of the bf16 MFMA.)  V^T is converted the same way.
 //   PV: O^T += V^T (P v_scale)^T with v_mfma_f32_16x16x32_bf16, once for the
-//     bf16 high part of P v_scale and once for the low part.
+//     bf16 high part of P v_scale and once for the low part (fp8 cache);
+//     once with P rounded to bf16 (bf16 cache).
 #include "common.h"
 #include "kernels.h"
 
@@ -367,16 +370,24 @@ __global__ __launch_bounds__(64 * W) void decode_splitk_kernel(DecodeParams p) {
           const float p0 = fast_exp2(x[kb][i] - m_run[rb]);
           const float p1 = fast_exp2(x[kb][i + 1] - m_run[rb]);
           rs += p0 + p1;
-          // hi = RNE(P'), lo = RNE(P' - hi), two columns per conversion
-          const float a = p0 * vs4[kb][i], b = p1 * vs4[kb][i + 1];
-          const bf16x2 h = __builtin_convertvector(f32x2{a, b}, bf16x2);
-          const unsigned hb = __builtin_bit_cast(unsigned, h);
-          const bf16x2 lo = __builtin_convertvector(
-              f32x2{a - __uint_as_float(hb << 16), b - __uint_as_float(hb & 0xffff0000u)}, bf16x2);
-          phi[rb][kb * 4 + i] = h[0];
-          phi[rb][kb * 4 + i + 1] = h[1];
-          plo[rb][kb * 4 + i] = lo[0];
-          plo[rb][kb * 4 + i + 1] = lo[1];
+          if constexpr (FP8) {
+            // hi = RNE(P'), lo = RNE(P' - hi), two columns per conversion
+            const float a = p0 * vs4[kb][i], b = p1 * vs4[kb][i + 1];
+            const bf16x2 h = __builtin_convertvector(f32x2{a, b}, bf16x2);
+            const unsigned hb = __builtin_bit_cast(unsigned, h);
+            const bf16x2 lo = __builtin_convertvector(
+                f32x2{a - __uint_as_float(hb << 16), b - __uint_as_float(hb & 0xffff0000u)}, bf16x2);
+            phi[rb][kb * 4 + i] = h[0];
+            phi[rb][kb * 4 + i + 1] = h[1];
+            plo[rb][kb * 4 + i] = lo[0];
+            plo[rb][kb * 4 + i + 1] = lo[1];
+          } else {
+            // no V scales: P itself, rounded to bf16 (RNE, unbiased, as in
+            // the prefill forward); masked keys already have P = 0
+            const bf16x2 h = __builtin_convertvector(f32x2{p0, p1}, bf16x2);
+            phi[rb][kb * 4 + i] = h[0];
+            phi[rb][kb * 4 + i + 1] = h[1];
+          }
         }
       l_run[rb] += xgroup_sum(rs);
     }
@@ -398,7 +409,7 @@ __global__ __launch_bounds__(64 * W) void decode_splitk_kernel(DecodeParams p) {
 #pragma unroll
       for (int rb = 0; rb < RBW; ++rb) {
         oacc[rb][db] = mfma16x16x32(vop, phi[rb], oacc[rb][db]);
-        oacc[rb][db] = mfma16x16x32(vop, plo[rb], oacc[rb][db]);
+        if constexpr (FP8) oacc[rb][db] = mfma16x16x32(vop, plo[rb], oacc[rb][db]);
       }
     }
   };
