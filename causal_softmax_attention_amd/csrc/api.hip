@@ -139,7 +139,7 @@ int attn_fwd_varlen(const void* q, const void* k, const void* v, const int32_t* 
 // ---------------------------------------------------------------------------
 namespace {
 struct BwdLayout {
-  size_t delta, G2, dq_acc, dG, dGrow, dGcol, sink_rows, total;
+  size_t delta, G2, dq_acc, dG, dGrow, dGcol, sink_rows, rowt, total;
   bool fused;
 };
 // Which backward runs: the fused-dQ kernel (fp32 atomics; the pages keep it
@@ -163,6 +163,7 @@ BwdLayout bwd_layout(int T, int Hq, int dqk, int has_gate, int has_sink, int fla
     L.dGrow = off; if (has_gate) off += r4;
     L.dGcol = off; if (has_gate) off += r4;
     L.sink_rows = off; if (has_sink) off += r4;
+    L.rowt = off; off += r4;
   }
   L.total = off;
   return L;
@@ -229,6 +230,7 @@ int attn_bwd_varlen(const void* q, const void* k, const void* v, const void* o, 
     p.dGrow = g ? reinterpret_cast<float*>(ws + lay.dGrow) : nullptr;
     p.dGcol = g ? reinterpret_cast<float*>(ws + lay.dGcol) : nullptr;
     p.sink_rows = sink ? reinterpret_cast<float*>(ws + lay.sink_rows) : nullptr;
+    p.rowt = reinterpret_cast<float*>(ws + lay.rowt);
   }
   p.dsink_acc = dsink;
   p.dq = dq; p.dk = dk; p.dv = dv; p.dg = dg;

@@ -27,7 +27,9 @@
 namespace attn {
 
 // ---------------------------------------------------------------------------
-// delta[row] = sum_d O[row, d] * dO[row, d] in fp32 (row = token * Hq + head).
+// delta = sum_d O[row, d] * dO[row, d] in fp32 (row = token * Hq + head),
+// stored head-major [Hq, T]; for the two-pass kernels also the row term
+// G2 - lse * log2(e), head-major, so that a tile's rows are contiguous.
 // DV/8 lanes per row, 16 bytes of O and of dO per lane, so a wave streams
 // whole 256-byte rows; also zeroes the fused path's dQ accumulator and the
 // gate / sink gradient accumulators.
@@ -48,7 +50,10 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(BwdParams p) {
 #pragma unroll
   for (int off = LPR / 2; off > 0; off >>= 1) s += __shfl_xor(s, off);
   if (sub == 0) {
-    p.delta[row] = s;
+    const long tok = row / p.Hq;
+    const long hm = (row - tok * p.Hq) * p.T + tok;   // head-major index
+    p.delta[hm] = s;
+    if (p.rowt != nullptr) p.rowt[hm] = (p.G2 != nullptr ? p.G2[hm] : 0.f) - p.lse[row] * kLog2e;
     if (p.dG != nullptr) p.dG[row] = 0.f;
   }
   if (p.dq_acc != nullptr) {
@@ -122,7 +127,7 @@ __global__ __launch_bounds__(256) void bwd_fused_kernel(BwdParams p) {
   for (int hg = 0; hg < grp; ++hg) {
     const int h = kvh * grp + hg;
     const float sink2 = p.sink ? p.sink[h] * kLog2e : 0.f;
-    const float gk = (gated && key_ok) ? p.G2[(long)(seq0 + my_key) * p.Hq + h] : 0.f;
+    const float gk = (gated && key_ok) ? p.G2[(long)h * p.T + seq0 + my_key] : 0.f;
     float sink_part = 0.f;   // sum over this lane's elements of psink * P * dP
     float colsum = 0.f;      // sum over rows of dS for this lane's key
 
@@ -149,8 +154,8 @@ __global__ __launch_bounds__(256) void bwd_fused_kernel(BwdParams p) {
         const bool ok = i0 + tid < L;
         const long ri = (long)(seq0 + i0 + tid) * p.Hq + h;
         lse_lds[tid] = ok ? p.lse[ri] * kLog2e : 0.f;
-        delta_lds[tid] = ok ? p.delta[ri] : 0.f;
-        gq_lds[tid] = (ok && gated) ? p.G2[ri] : 0.f;
+        delta_lds[tid] = ok ? p.delta[(long)h * p.T + seq0 + i0 + tid] : 0.f;
+        gq_lds[tid] = (ok && gated) ? p.G2[(long)h * p.T + seq0 + i0 + tid] : 0.f;
       }
       __syncthreads();
 

@@ -61,7 +61,7 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdParams p) {
   constexpr int LPT = QPW + OPW + (GATED ? 1 : 0);
   __shared__ __attribute__((aligned(1024))) uint8_t q_lds[NSQ][RQ * QRB];
   __shared__ __attribute__((aligned(1024))) uint8_t do_lds[NSQ][RQ * ORB];
-  __shared__ __attribute__((aligned(16))) float row_lds[NSQ][3][64];   // lse, delta, gq (lanes >= RQ repeat)
+  __shared__ __attribute__((aligned(16))) float row_lds[NSQ][2][64];   // row term, delta (lanes >= RQ repeat)
   __shared__ __attribute__((aligned(16))) float gk_lds[NSQ][4][64];    // per wave: its keys' gate terms
 
   const int kvh = xcd_remap(blockIdx.x, p.Hkv), n = blockIdx.y, ktile = blockIdx.z;
@@ -140,18 +140,17 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdParams p) {
       dma16(ob, (uint32_t)(ooff[j] - over * ostride), ol + (wave + 4 * j) * 1024);
     }
     if (wave == 0) {
-      // per-row terms, lane l -> row min(i0 + l % RQ, L - 1)
-      const uint32_t ro = (uint32_t)((min(i0 + (lane % RQ), L - 1) - i0) * p.Hq * 4);
-      const float* lb = p.lse + r0;
-      const float* db_ = p.delta + r0;
-      dma4(lb, ro, lds_addr(&row_lds[st][0][0]));
-      dma4(db_, ro, lds_addr(&row_lds[st][1][0]));
-      if constexpr (GATED) dma4(p.G2 + r0, ro, lds_addr(&row_lds[st][2][0]));
+      // per-row terms (head-major: the tile's rows are contiguous),
+      // lane l -> row min(i0 + l % RQ, L - 1)
+      const uint32_t ro = (uint32_t)((min(i0 + (lane % RQ), L - 1) - i0) * 4);
+      const long hr = (long)hh * p.T + seq0 + i0;
+      dma4(p.rowt + hr, ro, lds_addr(&row_lds[st][0][0]));
+      dma4(p.delta + hr, ro, lds_addr(&row_lds[st][1][0]));
     }
     if constexpr (GATED) {
       // this wave's keys for the tile's head, lane l -> key jw + l % KW
-      const uint32_t ko = (uint32_t)(min(jw + (lane % KW), L - 1) * p.Hq * 4);
-      dma4(p.G2 + (long)seq0 * p.Hq + hh, ko, lds_addr(&gk_lds[st][wave][0]));
+      const uint32_t ko = (uint32_t)(min(jw + (lane % KW), L - 1) * 4);
+      dma4(p.G2 + (long)hh * p.T + seq0, ko, lds_addr(&gk_lds[st][wave][0]));
     }
   };
 
@@ -200,9 +199,8 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdParams p) {
     {
       const uint8_t* ql = q_lds[buf];
       const uint8_t* ol = do_lds[buf];
-      const float* lsel = row_lds[buf][0];
+      const float* rowl = row_lds[buf][0];
       const float* dell = row_lds[buf][1];
-      const float* gql = row_lds[buf][2];
       // ---- S = Q K^T, dP = dO V^T: C lane (key li, rows rb*16+4g+i) ----
       f32x4 s[KBW][2], dp[KBW][2];
 #pragma unroll
@@ -229,12 +227,8 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdParams p) {
       f32x4 pv[KBW][2];
 #pragma unroll
       for (int rb = 0; rb < 2; ++rb) {
-        const f32x4 lse4 = *reinterpret_cast<const f32x4*>(lsel + rb * 16 + 4 * g);
-        f32x4 gq4 = {0.f, 0.f, 0.f, 0.f};
-        if constexpr (GATED) gq4 = *reinterpret_cast<const f32x4*>(gql + rb * 16 + 4 * g);
-        f32x4 rowt;   // row term in base 2: gate of the row minus lse
-#pragma unroll
-        for (int i = 0; i < 4; ++i) rowt[i] = gq4[i] - lse4[i] * kLog2e;
+        // row term in base 2: gate of the row minus lse
+        const f32x4 rowt = *reinterpret_cast<const f32x4*>(rowl + rb * 16 + 4 * g);
 #pragma unroll
         for (int kb = 0; kb < KBW; ++kb)
 #pragma unroll
@@ -362,8 +356,8 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(BwdParams p) {
 #pragma unroll
     for (int ks = 0; ks < KSV; ++ks) doop[rb][ks] = ok ? *reinterpret_cast<const bf16x8*>(dp + 32 * ks) : bf16x8{};
     lse2[rb] = ok ? p.lse[ri] * kLog2e : 0.f;
-    dlt[rb] = ok ? p.delta[ri] : 0.f;
-    gq[rb] = (ok && gated) ? p.G2[ri] : 0.f;
+    dlt[rb] = ok ? p.delta[(long)h * p.T + seq0 + row] : 0.f;
+    gq[rb] = (ok && gated) ? p.G2[(long)h * p.T + seq0 + min(row, L - 1)] : 0.f;
     rowsum[rb] = 0.f;
     pdp[rb] = 0.f;
 #pragma unroll
@@ -397,7 +391,7 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(BwdParams p) {
     vrow[j] = o / VRB;
     voff[j] = vrow[j] * vstride + ((((o % VRB) >> 4) ^ tile_swz<VRB>(vrow[j])) << 4);
   }
-  const float* g2base = GATED ? p.G2 + (long)seq0 * p.Hq + h : nullptr;
+  const float* g2base = GATED ? p.G2 + (long)h * p.T + seq0 : nullptr;
   auto fetch = [&](int st, int j0) {
     const bool tail = j0 + BN > L;               // uniform: only the last tile clamps
     const uint8_t* kb = kbase + (long)j0 * kstride;
@@ -414,7 +408,7 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(BwdParams p) {
       dma16(vb, (uint32_t)(voff[j] - over * vstride), vl + (wave + 4 * j) * 1024);
     }
     if constexpr (GATED)
-      dma4(g2base, (uint32_t)(min(j0 + lane, L - 1) * p.Hq * 4), lds_addr(&gk_lds[st][wave][0]));
+      dma4(g2base, (uint32_t)(min(j0 + lane, L - 1) * 4), lds_addr(&gk_lds[st][wave][0]));
   };
 
   if (t_begin < t_end) fetch(0, t_begin * BN);

@@ -17,13 +17,14 @@
 namespace attn {
 
 // ---------------------------------------------------------------------------
-// Gate prefix: G2[t, h] = log2(e) * sum of g[s, h] over s from the start of
-// t's sequence to t.  One workgroup per (sequence, head); each thread scans a
+// Gate prefix: G2[h, t] = log2(e) * sum of g[s, h] over s from the start of
+// t's sequence to t.  Head-major, so that the gate terms of a tile's
+// consecutive keys (or rows) of one head are contiguous.  One workgroup per (sequence, head); each thread scans a
 // contiguous chunk, chunk totals are scanned in LDS.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void gate_prefix_kernel(const float* __restrict__ g,
                                                           const int32_t* __restrict__ cu,
-                                                          float* __restrict__ G2, int Hq) {
+                                                          float* __restrict__ G2, int Hq, int T) {
   const int h = blockIdx.x, n = blockIdx.y;
   const int a = cu[n], L = cu[n + 1] - a;
   if (L <= 0) return;
@@ -45,14 +46,14 @@ __global__ __launch_bounds__(256) void gate_prefix_kernel(const float* __restric
   float run = threadIdx.x > 0 ? part[threadIdx.x - 1] : 0.f;
   for (int t = t0; t < t1; ++t) {
     run += g[(long)(a + t) * Hq + h];
-    G2[(long)(a + t) * Hq + h] = run * kLog2e;
+    G2[(long)h * T + a + t] = run * kLog2e;
   }
 }
 
 hipError_t launch_gate_prefix(const float* g, const int32_t* cu, float* G2, int num_seqs,
                               int T, int Hq, hipStream_t st) {
   if (num_seqs == 0 || T == 0) return hipSuccess;
-  gate_prefix_kernel<<<dim3(Hq, num_seqs), 256, 0, st>>>(g, cu, G2, Hq);
+  gate_prefix_kernel<<<dim3(Hq, num_seqs), 256, 0, st>>>(g, cu, G2, Hq, T);
   return hipGetLastError();
 }
 

@@ -84,7 +84,7 @@ __global__ __launch_bounds__(256) void fwd_kernel(FwdParams p) {
       const bf16* qp = reinterpret_cast<const bf16*>(p.q) + ((long)(seq0 + row) * p.Hq + h) * DQK + 8 * g;
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) qop[rb][ks] = *reinterpret_cast<const bf16x8*>(qp + 32 * ks);
-      gq[rb] = GATED ? p.G2[(long)(seq0 + row) * p.Hq + h] : 0.f;
+      gq[rb] = GATED ? p.G2[(long)h * p.T + seq0 + row] : 0.f;
     } else {
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) qop[rb][ks] = bf16x8{};
@@ -130,7 +130,7 @@ __global__ __launch_bounds__(256) void fwd_kernel(FwdParams p) {
     vrow[j] = o / VRB;
     voff[j] = (int)(vrow[j] * vstride) + ((((o % VRB) >> 4) ^ tile_swz<VRB>(vrow[j])) << 4);
   }
-  const float* g2base = GATED ? p.G2 + (long)seq0 * p.Hq + h : nullptr;
+  const float* g2base = GATED ? p.G2 + (long)h * p.T + seq0 : nullptr;
   auto fetch = [&](int st, int j0) {
     const bool tail = j0 + BN > L;         // uniform: only the last tile clamps
     const uint8_t* kb = kbase + j0 * kstride;
@@ -147,7 +147,7 @@ __global__ __launch_bounds__(256) void fwd_kernel(FwdParams p) {
       dma16(vb, (uint32_t)(voff[j] - over * (int)vstride), vl + (wave + 4 * j) * 1024);
     }
     if constexpr (GATED)
-      dma4(g2base, (uint32_t)(min(j0 + lane, L - 1) * p.Hq * 4), lds_addr(&gk_lds[st][wave][0]));
+      dma4(g2base, (uint32_t)(min(j0 + lane, L - 1) * 4), lds_addr(&gk_lds[st][wave][0]));
   };
 
   // prologue: tiles t_begin .. t_begin+NST-2

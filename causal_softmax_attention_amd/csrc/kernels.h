@@ -76,7 +76,7 @@ struct FwdParams {
   const int32_t* cu;        // [N+1]
   const float* sink;        // [Hq] or nullptr
   const float* g;           // [T, Hq] log gates or nullptr
-  float* G2;                // [T, Hq] workspace: gate prefix * log2(e)
+  float* G2;                // [Hq, T] workspace: gate prefix * log2(e) (head-major)
   void* o;                  // bf16 [T, Hq, DV]
   float* lse;               // [T, Hq]
   int num_seqs, max_seqlen, T, Hq, Hkv, window;
@@ -96,8 +96,9 @@ struct BwdParams {
   const float* lse;         // [T, Hq]
   const int32_t* cu;
   const float* sink;
-  const float* G2;          // [T, Hq] gate prefix * log2(e) or nullptr
-  float* delta;             // [T, Hq] workspace
+  const float* G2;          // [Hq, T] gate prefix * log2(e) (head-major) or nullptr
+  float* delta;             // [Hq, T] workspace (head-major)
+  float* rowt;              // [Hq, T] workspace, two-pass only: G2 - lse * log2(e) (head-major)
   float* dq_acc;            // [T, Hq, DQK] fp32 workspace (fused dQ only)
   float* dG;                // [T, Hq] fp32 (fused: row minus column sums, by atomics)
   float* dGrow;             // [T, Hq] fp32 (two-pass: row sums of dS, stored)
