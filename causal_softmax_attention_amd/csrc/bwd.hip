@@ -289,40 +289,28 @@ __global__ __launch_bounds__(256) void bwd_dq_convert_kernel(const float* __rest
   reinterpret_cast<bf16x4*>(dq)[i] = to_bf16x4(x);
 }
 
-// dg[t, h] = sum over s >= t within t's sequence of dG[s, h]: one workgroup
-// per (sequence, head), chunked reverse scan.
-// dG[t, h] = a[t, h] - b[t, h] (b may be null).
+// dg[t, h] = sum over s >= t within t's sequence of dG[s, h] (a reverse
+// scan): one workgroup per (head, sequence).  dG[t, h] = a[t, h] - b[t, h]
+// (b may be null), both read at t * st_t + h * st_h (head-major partials of
+// the two-pass path, token-major accumulator of the fused one).
 __global__ __launch_bounds__(256) void gate_grad_kernel(const float* __restrict__ a_,
                                                         const float* __restrict__ b_,
                                                         const int32_t* __restrict__ cu,
-                                                        float* __restrict__ dg, int Hq) {
+                                                        float* __restrict__ dg, int Hq, long st_t,
+                                                        long st_h) {
   const int h = blockIdx.x, n = blockIdx.y;
   const int a = cu[n], L = cu[n + 1] - a;
   if (L <= 0) return;
-  const int chunk = (L + 255) / 256;
-  const int t0 = threadIdx.x * chunk;
-  const int t1 = min(L, t0 + chunk);
-  auto dG = [&](int t) {
-    const long i = (long)(a + t) * Hq + h;
-    return b_ ? a_[i] - b_[i] : a_[i];
-  };
-  float s = 0.f;
-  for (int t = t0; t < t1; ++t) s += dG(t);
-  __shared__ float part[256];
-  part[threadIdx.x] = s;
-  __syncthreads();
-  // inclusive suffix scan of the chunk totals
-  for (int off = 1; off < 256; off <<= 1) {
-    float v = threadIdx.x + off < 256 ? part[threadIdx.x + off] : 0.f;
-    __syncthreads();
-    part[threadIdx.x] += v;
-    __syncthreads();
-  }
-  float run = threadIdx.x < 255 ? part[threadIdx.x + 1] : 0.f;
-  for (int t = t1 - 1; t >= t0; --t) {
-    run += dG(t);
-    dg[(long)(a + t) * Hq + h] = run;
-  }
+  const long base = (long)a * st_t + h * st_h;
+  float* out = dg + (long)a * Hq + h;
+  // scan order q runs from the sequence's last token to its first
+  block_scan_256(
+      L,
+      [&](int q) {
+        const long i = base + (long)(L - 1 - q) * st_t;
+        return b_ ? a_[i] - b_[i] : a_[i];
+      },
+      [&](int q, float v) { out[(long)(L - 1 - q) * Hq] = v; });
 }
 
 __global__ __launch_bounds__(256) void fill_zero_kernel(float* x, long n) {
@@ -354,7 +342,7 @@ static hipError_t launch_bwd_t(const BwdParams& p, bool fused, hipStream_t st) {
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     if (p.dg != nullptr) {
-      gate_grad_kernel<<<dim3(p.Hq, p.num_seqs), 256, 0, st>>>(p.dG, nullptr, p.cu, p.dg, p.Hq);
+      gate_grad_kernel<<<dim3(p.Hq, p.num_seqs), 256, 0, st>>>(p.dG, nullptr, p.cu, p.dg, p.Hq, p.Hq, 1);
       e = hipGetLastError();
     }
     return e;
@@ -362,7 +350,7 @@ static hipError_t launch_bwd_t(const BwdParams& p, bool fused, hipStream_t st) {
   e = launch_bwd_two_pass(p, DQK, DV, st);
   if (e != hipSuccess) return e;
   if (p.dg != nullptr) {
-    gate_grad_kernel<<<dim3(p.Hq, p.num_seqs), 256, 0, st>>>(p.dGrow, p.dGcol, p.cu, p.dg, p.Hq);
+    gate_grad_kernel<<<dim3(p.Hq, p.num_seqs), 256, 0, st>>>(p.dGrow, p.dGcol, p.cu, p.dg, p.Hq, 1, p.T);
     e = hipGetLastError();
   }
   return e;

@@ -291,7 +291,7 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdParams p) {
       for (int kb = 0; kb < KBW; ++kb) {
         const float cs = xgroup_sum(colsum[kb]);
         const int key = jw + kb * 16 + li;
-        if (g == 0 && key < L) p.dGcol[(long)(seq0 + key) * p.Hq + h] = cs;
+        if (g == 0 && key < L) p.dGcol[(long)h * p.T + seq0 + key] = cs;   // head-major
         colsum[kb] = 0.f;
       }
     }
@@ -522,26 +522,39 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(BwdParams p) {
 #pragma unroll
     for (int db = 0; db < DBQ; ++db) *reinterpret_cast<bf16x4*>(dqp + db * 16) = to_bf16x4(dq_acc[rb][db] * p.scale);
     if (g == 0) {
-      if (gated) p.dGrow[ri] = rs;
-      if (p.sink) p.sink_rows[ri] = fast_exp2(sink2 - lse2[rb]) * sp;
+      const long hm = (long)h * p.T + seq0 + row;   // head-major
+      if (gated) p.dGrow[hm] = rs;
+      if (p.sink) p.sink_rows[hm] = fast_exp2(sink2 - lse2[rb]) * sp;
     }
   }
 }
 
-// dsink[h] = -sum over all tokens of sink_rows[t, h] (fixed order).
-__global__ __launch_bounds__(256) void sink_reduce_kernel(const float* __restrict__ rows, float* __restrict__ dsink,
-                                                          int T, int Hq) {
-  const int h = blockIdx.x;
+// dsink[h] = -sum over all tokens of sink_rows[h, t] (fixed order).
+__global__ __launch_bounds__(1024) void sink_reduce_kernel(const float* __restrict__ rows, float* __restrict__ dsink,
+                                                           int T, int Hq) {
+  // rows head-major [Hq, T]: thread t sums its contiguous share, 16 values
+  // per round held in registers (one memory latency per round; one round up
+  // to 16K tokens)
+  const int h = blockIdx.x, tid = threadIdx.x;
+  const float* r = rows + (long)h * T;
+  const int share = (T + 1023) / 1024;
+  const int t0 = tid * share, t1 = min(T, t0 + share);
   float s = 0.f;
-  for (int t = threadIdx.x; t < T; t += 256) s += rows[(long)t * Hq + h];
-  __shared__ float part[256];
-  part[threadIdx.x] = s;
+  for (int b0 = t0; b0 < t1; b0 += 16) {
+    float v[16];
+#pragma unroll
+    for (int j = 0; j < 16; ++j) v[j] = b0 + j < t1 ? r[b0 + j] : 0.f;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) s += v[j];
+  }
+  __shared__ float part[1024];
+  part[tid] = s;
   __syncthreads();
-  for (int off = 128; off > 0; off >>= 1) {
-    if (threadIdx.x < off) part[threadIdx.x] += part[threadIdx.x + off];
+  for (int off = 512; off > 0; off >>= 1) {
+    if (tid < off) part[tid] += part[tid + off];
     __syncthreads();
   }
-  if (threadIdx.x == 0) dsink[h] = -part[0];
+  if (tid == 0) dsink[h] = -part[0];
 }
 
 template <int DQK, int DV, int KW, int RW, int BN>
@@ -559,7 +572,7 @@ hipError_t launch_bwd_two_pass_t(const BwdParams& p, hipStream_t st) {
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (p.sink) {
-    sink_reduce_kernel<<<dim3(p.Hq), 256, 0, st>>>(p.sink_rows, p.dsink_acc, p.T, p.Hq);
+    sink_reduce_kernel<<<dim3(p.Hq), 1024, 0, st>>>(p.sink_rows, p.dsink_acc, p.T, p.Hq);
     e = hipGetLastError();
   }
   return e;

@@ -164,6 +164,47 @@ __device__ __forceinline__ void lds_barrier() {
 }
 
 // ---------------------------------------------------------------------------
+// Inclusive scan of L values by one 256-thread workgroup, in scan order
+// q = 0 .. L-1 (load(q) / store(q, v) map q to memory).  Rounds of 4096
+// values, 16 consecutive ones per thread held in registers, so that each
+// round costs one memory latency rather than one per value; the chunk totals
+// are scanned in LDS.  Summation order is fixed (deterministic).
+template <typename Load, typename Store>
+__device__ __forceinline__ void block_scan_256(int L, Load load, Store store) {
+  __shared__ float part[256];
+  const int tid = threadIdx.x;
+  float carry = 0.f;
+  for (int base = 0; base < L; base += 4096) {
+    float v[16];
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      const int q = base + 16 * tid + j;
+      v[j] = q < L ? load(q) : 0.f;
+    }
+    float s = 0.f;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) s += v[j];
+    part[tid] = s;
+    __syncthreads();
+    for (int off = 1; off < 256; off <<= 1) {   // Hillis-Steele inclusive scan
+      const float x = tid >= off ? part[tid - off] : 0.f;
+      __syncthreads();
+      part[tid] += x;
+      __syncthreads();
+    }
+    float run = carry + part[tid] - s;            // exclusive prefix of this chunk
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      const int q = base + 16 * tid + j;
+      run += v[j];
+      if (q < L) store(q, run);
+    }
+    carry += part[255];
+    __syncthreads();                              // part is reused by the next round
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Swizzled LDS tiles: a tile of rows of RB bytes is stored without padding;
 // the 16-byte chunk c of row r sits at chunk position c ^ swz(r).  The
 // kernels read a tile in two ways: MFMA operand rows (ds_read_b128: 16 lanes

@@ -19,7 +19,8 @@ namespace attn {
 // ---------------------------------------------------------------------------
 // Gate prefix: G2[h, t] = log2(e) * sum of g[s, h] over s from the start of
 // t's sequence to t.  Head-major, so that the gate terms of a tile's
-// consecutive keys (or rows) of one head are contiguous.  One workgroup per (sequence, head); each thread scans a
+// consecutive keys (or rows) of one head are contiguous.  One workgroup per
+// (head, sequence).  One workgroup per (sequence, head); each thread scans a
 // contiguous chunk, chunk totals are scanned in LDS.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void gate_prefix_kernel(const float* __restrict__ g,
@@ -28,26 +29,9 @@ __global__ __launch_bounds__(256) void gate_prefix_kernel(const float* __restric
   const int h = blockIdx.x, n = blockIdx.y;
   const int a = cu[n], L = cu[n + 1] - a;
   if (L <= 0) return;
-  const int chunk = (L + 255) / 256;
-  const int t0 = threadIdx.x * chunk;
-  const int t1 = min(L, t0 + chunk);
-  float s = 0.f;
-  for (int t = t0; t < t1; ++t) s += g[(long)(a + t) * Hq + h];
-  __shared__ float part[256];
-  part[threadIdx.x] = s;
-  __syncthreads();
-  // inclusive Hillis-Steele scan of the 256 chunk totals
-  for (int off = 1; off < 256; off <<= 1) {
-    float v = threadIdx.x >= off ? part[threadIdx.x - off] : 0.f;
-    __syncthreads();
-    part[threadIdx.x] += v;
-    __syncthreads();
-  }
-  float run = threadIdx.x > 0 ? part[threadIdx.x - 1] : 0.f;
-  for (int t = t0; t < t1; ++t) {
-    run += g[(long)(a + t) * Hq + h];
-    G2[(long)h * T + a + t] = run * kLog2e;
-  }
+  const float* gs = g + (long)a * Hq + h;
+  float* out = G2 + (long)h * T + a;
+  block_scan_256(L, [&](int t) { return gs[(long)t * Hq]; }, [&](int t, float v) { out[t] = v * kLog2e; });
 }
 
 hipError_t launch_gate_prefix(const float* g, const int32_t* cu, float* G2, int num_seqs,

@@ -101,9 +101,9 @@ struct BwdParams {
   float* rowt;              // [Hq, T] workspace, two-pass only: G2 - lse * log2(e) (head-major)
   float* dq_acc;            // [T, Hq, DQK] fp32 workspace (fused dQ only)
   float* dG;                // [T, Hq] fp32 (fused: row minus column sums, by atomics)
-  float* dGrow;             // [T, Hq] fp32 (two-pass: row sums of dS, stored)
-  float* dGcol;             // [T, Hq] fp32 (two-pass: column sums of dS, stored)
-  float* sink_rows;         // [T, Hq] fp32 (two-pass: psink_i * sum_j P_ij dP_ij)
+  float* dGrow;             // [Hq, T] fp32 (two-pass: row sums of dS, stored; head-major)
+  float* dGcol;             // [Hq, T] fp32 (two-pass: column sums of dS, stored; head-major)
+  float* sink_rows;         // [Hq, T] fp32 (two-pass: psink_i * sum_j P_ij dP_ij; head-major)
   float* dsink_acc;         // [Hq] fp32 (the dsink output itself)
   void* dq;
   void* dk;
