@@ -165,6 +165,65 @@ def cpu_oracle_baseline(x, budget_s=12.0):
                       f"{flops / 1e9:.1f} GFLOP in {spent:.1f} s"}
 
 
+def cpu_oracle_decode_baseline(d, budget_s=6.0):
+    """The float64 decode oracle, as it stands, on whole requests of the
+    decode workload (in request order) until ~budget_s; GB/s of the same
+    algorithmic bytes the GPU figure counts."""
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        threads = os.cpu_count() or 1
+    kc, vc = d.k_cache.cpu().numpy(), d.v_cache.cpu().numpy()
+    ks, vs = d.k_scale.cpu().numpy(), d.v_scale.cpu().numpy()
+    q, cu, bt, sl = d.q.cpu(), d.cu_seqlens_q.cpu(), d.block_table.cpu().numpy(), d.seq_lens.cpu()
+    Hkv, D, Hq = kc.shape[1], kc.shape[3], q.shape[1]
+    spent, done, nbytes = 0.0, [], 0
+    for r in range(len(d.q_lens)):
+        t0 = time.perf_counter()
+        oracle.decode_paged(q, cu, kc, vc, bt, sl, d.scale, True, ks, vs, requests=[r])
+        spent += time.perf_counter() - t0
+        L = int(sl[r])
+        nbytes += L * Hkv * (2 * D + 8) + d.q_lens[r] * Hq * D * 4 + math.ceil(L / d.block_size) * 4
+        done.append(r)
+        if spent >= budget_s:
+            break
+    return {"value": nbytes / spent / 1e9, "unit": "GB/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"float64 decode oracle on requests {done[0]}..{done[-1]} of the decode workload "
+                      f"({nbytes / 1e6:.0f} MB of cache) in {spent:.1f} s"}
+
+
+def decode_graph_us(fn, reps=50):
+    """The decode layer (partials + reduce) captured once as a HIP graph and
+    replayed; each of the first replays is checked against the eager result
+    (with eager work between them) before the timed replays."""
+    ref = fn().clone()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        fn()
+    torch.cuda.current_stream().wait_stream(side)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        out = fn()
+    for _ in range(3):
+        out.zero_()
+        graph.replay()
+        torch.cuda.synchronize()
+        if not torch.equal(out, ref):
+            raise RuntimeError("decode graph replay differs from the eager result")
+        fn()
+    torch.cuda.synchronize()
+    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    s.record()
+    for _ in range(reps):
+        graph.replay()
+    e.record()
+    torch.cuda.synchronize()
+    return 1e3 * s.elapsed_time(e) / reps
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -228,6 +287,8 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_step = 1e3 * wall / args.steps
+    # the decode layer as a HIP graph (the pages time decode that way), outside the step
+    dec_graph_us = decode_graph_us(dec)
     # the fused-dQ variant of the backward, timed outside the step
     tf = Timer()
     bwd_fused()
@@ -287,7 +348,8 @@ def main():
                     "fwdbwd_frac_of_mfma_peak": tf_fb / MFMA_BF16_PEAK_TFLOPS,
                     "flops_fwd": f_fwd, "flops_bwd": f_bwd},
         "decode": {"us_per_layer": us["decode"], "GBps": gbps, "frac_of_hbm_peak": gbps / HBM_PEAK_GBPS,
-                   "algorithmic_bytes": dec_bytes},
+                   "algorithmic_bytes": dec_bytes, "graph_us_per_layer": dec_graph_us,
+                   "graph_GBps": dec_bytes / (dec_graph_us * 1e-6) / 1e9},
         "roofline": roof,
         "phases": phases,
     }
@@ -380,6 +442,7 @@ def main():
 
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_oracle_baseline(x)
+        out["decode"]["cpu_oracle"] = cpu_oracle_decode_baseline(d)
     print(json.dumps(out), flush=True)
 
 
