@@ -284,7 +284,7 @@ int choose_split_len_prefill(int R, int Hkv, int nqb, int max_seq_len, int B) {
 }
 
 struct DecLayout {
-  size_t acc, m, l, total;
+  size_t acc, m, l, units, total;
   int split_len, num_splits;
 };
 DecLayout dec_layout(int R, int max_q, int max_seq_len, int Hq, int Hkv, int D, int B, int split_len,
@@ -295,11 +295,19 @@ DecLayout dec_layout(int R, int max_q, int max_seq_len, int Hq, int Hkv, int D, 
                           : choose_split_len(R, Hkv, max_seq_len, B);
   L.num_splits = (max_seq_len + L.split_len - 1) / L.split_len;
   if (L.num_splits == 1) return L;     // single segment: the kernel writes the output
-  const size_t rows = (size_t)R * max_q * Hq;
+  // partial slots: rows x splits (fixed-length split), and for a decode with
+  // the library's split also pieces x rows-per-unit (balanced split, used
+  // when there is no window); room for the larger
+  size_t slots = (size_t)R * max_q * Hq * L.num_splits;
+  if (!prefill && split_len == 0) {
+    const size_t pieces = (size_t)attn::kDecodeMaxBalancedWG + (size_t)R * Hkv;
+    slots = std::max(slots, pieces * (size_t)max_q * (Hq / Hkv));
+  }
   size_t off = 0;
-  L.acc = off; off += round_up(rows * L.num_splits * (size_t)D * sizeof(float));
-  L.m = off; off += round_up(rows * L.num_splits * sizeof(float));
-  L.l = off; off += round_up(rows * L.num_splits * sizeof(float));
+  L.acc = off; off += round_up(slots * (size_t)D * sizeof(float));
+  L.m = off; off += round_up(slots * sizeof(float));
+  L.l = off; off += round_up(slots * sizeof(float));
+  L.units = off; off += round_up((size_t)R * Hkv * 2 * sizeof(int32_t));
   L.total = off;
   return L;
 }
@@ -423,6 +431,13 @@ int paged_attention(bool prefill, const void* q, const int32_t* cu_seqlens_q, in
   p.sink = sink; p.g_cache = g_cache; p.window = window > 0 ? window : 0;
   p.per_tensor = per_tensor_scales;
   if (lay.num_splits == 1) { p.out = out; p.lse = lse; }
+  // decode with the library's split and no window: equal shares of all keys
+  // per workgroup (request lengths vary; fixed-length segments leave the
+  // longest ones alone at the end)
+  p.balanced = !prefill && kv_split_len == 0 && p.window == 0 && lay.num_splits > 1 &&
+               (long)num_requests * num_kv_heads * max_seq_len < 0x7fffffffL;   // line fits 31 bits
+  p.rpu = max_seqlen_q * (num_q_heads / num_kv_heads);
+  p.unit_info = reinterpret_cast<int32_t*>(ws + lay.units);
   hipError_t e = attn::launch_decode_splitk(p, head_dim, fp8, s);
   if (e != hipSuccess) return hip_fail(e, prefill ? "paged prefill launch" : "decode launch");
   if (lay.num_splits == 1) return ok();
@@ -433,6 +448,7 @@ int paged_attention(bool prefill, const void* q, const int32_t* cu_seqlens_q, in
   r.num_splits = lay.num_splits; r.dv = head_dim; r.out_fp32 = 0;
   r.seq_lens = seq_lens; r.cu_seqlens_q = cu_seqlens_q; r.num_requests = num_requests;
   r.heads = num_q_heads; r.split_len = lay.split_len;
+  r.balanced = p.balanced; r.rpu = p.rpu; r.Hkv = num_kv_heads; r.unit_info = p.unit_info;
   e = attn::launch_splitk_reduce(r, s);
   if (e != hipSuccess) return hip_fail(e, "reduce launch");
   return ok();

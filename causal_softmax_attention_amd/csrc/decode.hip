@@ -50,6 +50,8 @@
 //   PV: O^T += V^T (P v_scale)^T with v_mfma_f32_16x16x32_bf16, once for the
 //     bf16 high part of P v_scale and once for the low part (fp8 cache);
 //     once with P rounded to bf16 (bf16 cache).
+#include <atomic>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -116,13 +118,10 @@ __global__ __launch_bounds__(64 * W) void decode_splitk_kernel(DecodeParams p) {
   const int wave = W == 1 ? 0 : __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63, li = lane & 15, g = lane >> 4;
 
-  int item = blockIdx.x;
-  const int kvh = item % p.Hkv;
-  item /= p.Hkv;
-  const int r = item % p.R;
-  item /= p.R;
-  const int qb = item % p.nqb;
-  const int s = item / p.nqb;
+  // ---- one segment: keys [k0, k1) of (request r, KV head kvh) for query
+  // block qb; its partials go to split s (fixed-length split) or to piece
+  // number s (balanced split) ----
+  auto segment = [&](const int r, const int kvh, const int qb, const int k0, const int k1, const long s) {
   const int L = p.seq_lens[r];
   const int qs = p.cu_q[r];
   const int qlen = p.cu_q[r + 1] - qs;
@@ -135,15 +134,15 @@ __global__ __launch_bounds__(64 * W) void decode_splitk_kernel(DecodeParams p) {
   const int pos_min = L - qlen + row0 / G;                       // first row's position
   const int pos_max = L - qlen + (row0 + min(nrows, RPB) - 1) / G;   // last row's position
   const bool direct = p.out != nullptr;
-  const int k_begin = s * p.split_len;
   // A segment that starts past every row's position holds nothing for the
   // block; the reduce reads a row's segments only up to its own position.
-  if (!direct && k_begin > pos_max) return;
-  const int k_end = min(min(L, k_begin + p.split_len), pos_max + 1);
+  if (!direct && k0 > pos_max) return;
+  const int k_end = min(min(L, k1), pos_max + 1);
   // first key any row of the block can see (sliding window), and where
-  // this segment's streaming starts (32-key steps stay aligned)
+  // this segment's streaming starts (32-key steps stay aligned; a balanced
+  // piece may start and end mid-step, its other keys are masked)
   const int k_lo = p.window > 0 ? max(0, pos_min - p.window + 1) : 0;
-  const int k_start = max(k_begin, k_lo & ~31);
+  const int k_start = max(k0, k_lo) & ~31;
   const bool per_tensor = FP8 && p.per_tensor;
   const bool active = wave * 16 * RBW < nrows;   // wave-uniform; idle waves still copy
 
@@ -265,7 +264,7 @@ __global__ __launch_bounds__(64 * W) void decode_splitk_kernel(DecodeParams p) {
   for (int rb = 0; rb < RBW; ++rb) {
     m_run[rb] = kNegBig;
     l_run[rb] = 0.f;
-    if (p.sink != nullptr && s == 0) {   // the sink's mass belongs to segment 0
+    if (p.sink != nullptr && k0 == 0) {  // the sink's mass belongs to the segment at key 0
       m_run[rb] = p.sink[kvh * G + rho[rb] % G] * kLog2e;
       l_run[rb] = 1.f;
     }
@@ -280,7 +279,8 @@ __global__ __launch_bounds__(64 * W) void decode_splitk_kernel(DecodeParams p) {
     const float* Sc = reinterpret_cast<const float*>(Kt + 2 * TILE + wave * 2 * SCB);
     const float* Gt = reinterpret_cast<const float*>(Kt + 2 * TILE + W * 2 * SCB);
     // uniform: a key past some row's position, or before some row's window
-    const bool need_mask = kk + 31 > vis_all || (p.window > 0 && kk <= pos_max - p.window);
+    const bool need_mask = kk + 31 > vis_all || (p.window > 0 && kk <= pos_max - p.window) || kk < k0 ||
+                           kk + 31 >= k1;
     // ---- scores S^T = K Q^T (C lane: row li, keys kk+kb*16+4g+i) ----
     f32x4 sc[RBW][2];
 #pragma unroll
@@ -344,7 +344,8 @@ __global__ __launch_bounds__(64 * W) void decode_splitk_kernel(DecodeParams p) {
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             const int key = kk + kb * 16 + 4 * g + i;
-            const bool vis = key < L && key <= pos[rb] && (p.window <= 0 || key > pos[rb] - p.window);
+            const bool vis = key >= k0 && key < k1 && key < L && key <= pos[rb] &&
+                             (p.window <= 0 || key > pos[rb] - p.window);
             x[kb][i] = vis ? x[kb][i] : -INFINITY;
           }
       }
@@ -480,14 +481,63 @@ __global__ __launch_bounds__(64 * W) void decode_splitk_kernel(DecodeParams p) {
         p.lse[grow] = empty ? -INFINITY : m_run[rb] * kLn2 + logf(l_run[rb]);
       continue;
     }
-    float* a = p.acc + (grow * p.num_splits + s) * D;
+    const long slot = p.balanced ? s * p.rpu + rho[rb] : grow * p.num_splits + s;
+    float* a = p.acc + slot * D;
 #pragma unroll
     for (int db = 0; db < DB; ++db) *reinterpret_cast<f32x4*>(a + db * 16 + 4 * g) = oacc[rb][db] * v_mul;
     if (g == 0) {
       const bool empty = !(l_run[rb] > 0.f);
-      p.m[grow * p.num_splits + s] = empty ? -INFINITY : m_run[rb] * kLn2;
-      p.l[grow * p.num_splits + s] = empty ? 0.f : l_run[rb];
+      p.m[slot] = empty ? -INFINITY : m_run[rb] * kLn2;
+      p.l[slot] = empty ? 0.f : l_run[rb];
     }
+  }
+  };
+
+  if (!p.balanced) {
+    int item = blockIdx.x;
+    const int kvh = item % p.Hkv;
+    item /= p.Hkv;
+    const int r = item % p.R;
+    item /= p.R;
+    const int qb = item % p.nqb;
+    const int s = item / p.nqb;
+    segment(r, kvh, qb, s * p.split_len, (s + 1) * p.split_len, s);
+    return;
+  }
+  // ---- balanced split: the requests' keys laid end to end on one line;
+  // workgroups w .. w + Hkv - 1 (dispatched together) take the same share
+  // [x0, x1) of the line for the Hkv heads, so the head slices of a page are
+  // read at about the same time.  Piece k of request r for head h is
+  // partial (base(r) + k) * Hkv + h. ----
+  const int kvh_w = blockIdx.x % p.Hkv;
+  const int share = blockIdx.x / p.Hkv;
+  const long total = sk_total(p.seq_lens, p.R, 1, lane);
+  const long P = sk_piece_len(total, p.sk_G / p.Hkv);
+  const long x0 = (long)share * P;
+  if (x0 >= total) return;             // whole workgroup, before any barrier
+  const long x1 = min(total, x0 + P);
+  SkUnit u = sk_find(p.seq_lens, p.R, 1, P, x0, false, 0, 0, lane);
+  if (u.r < 0) return;
+  long piece = u.base + ((long)share - u.start / P);
+  for (;;) {
+    if (u.start >= x0 && threadIdx.x == 0) {
+      // this share holds the request's first key: publish its pieces for the reduce
+      const int ui = (u.r * p.Hkv + kvh_w) * 2;
+      p.unit_info[ui] = (int)u.base;
+      p.unit_info[ui + 1] = sk_pieces(u.start, u.L, P);
+    }
+    segment(sk_uni(u.r), kvh_w, 0, sk_uni((int)(max(x0, u.start) - u.start)),
+            sk_uni((int)(min(x1, u.start + u.L) - u.start)), sk_uni(piece * p.Hkv + kvh_w));
+    if (u.start + u.L >= x1) break;
+    // the next request starts inside this share: its first piece is this one's
+    u.base += sk_pieces(u.start, u.L, P);
+    u.start += u.L;
+    do {
+      ++u.r;
+    } while (u.r < p.R && (u.L = p.seq_lens[u.r]) == 0);
+    if (u.r >= p.R) break;
+    piece = u.base;
+    if constexpr (W > 1) lds_barrier();   // the next piece's copies reuse the ring
   }
 }
 
@@ -510,10 +560,44 @@ __global__ __launch_bounds__(64 * W) void decode_splitk_kernel(DecodeParams p) {
 #define DECODE_NST_PREFILL 2
 #endif
 
+// Balanced grid size: resident workgroups per CU of the instantiation that
+// runs, capped for one-wave workgroups, times the CUs.  One-wave decode
+// measured fastest at 3-6 workgroups per CU (fewer concurrent page streams),
+// against 9 resident; two-wave verify at full residency.
+#ifndef DECODE_BAL_PER_CU_1
+#define DECODE_BAL_PER_CU_1 4
+#endif
+template <typename K>
+static int balanced_wgs(K kernel, int threads, int cap_per_cu) {
+  // per device, once per instantiation (the answer depends on nothing else)
+  static std::atomic<int> cache[16];
+  int dev = 0, cus = 0, per_cu = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 0;
+  if (dev >= 0 && dev < 16 && cache[dev].load() > 0) return cache[dev].load();
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, threads, 0) != hipSuccess) return 0;
+  if (cap_per_cu > 0 && per_cu > cap_per_cu) per_cu = cap_per_cu;
+  if (dev >= 0 && dev < 16) cache[dev].store(cus * per_cu);
+  return cus * per_cu;
+}
+
 template <int D, bool FP8, int W, int RBW, int NST>
-static hipError_t launch_t(DecodeParams p, hipStream_t st) {
+static hipError_t launch_t(DecodeParams& p, hipStream_t st) {
   p.nqb = (p.row_blocks + W * RBW - 1) / (W * RBW);
-  const long items = (long)p.R * p.Hkv * p.num_splits * p.nqb;
+  long items = (long)p.R * p.Hkv * p.num_splits * p.nqb;
+  if (p.balanced) {
+    // workgroups that stay resident together, so each share runs in one
+    // round (queried for the instantiation that runs)
+    const int cap = W == 1 ? DECODE_BAL_PER_CU_1 : 0;
+    const int res = p.g_cache != nullptr
+                        ? balanced_wgs(decode_splitk_kernel<D, FP8, W, RBW, NST, true>, 64 * W, cap)
+                        : balanced_wgs(decode_splitk_kernel<D, FP8, W, RBW, NST, false>, 64 * W, cap);
+    if (res <= 0) return hipErrorInvalidConfiguration;
+    int want = res < kDecodeMaxBalancedWG ? res : kDecodeMaxBalancedWG;
+    want -= want % p.Hkv;                // whole groups of Hkv (one per head)
+    p.sk_G = want > 0 ? want : p.Hkv;
+    items = p.sk_G;
+  }
   if (items > 0x7fffffffL) return hipErrorInvalidConfiguration;
   if (p.g_cache != nullptr)
     decode_splitk_kernel<D, FP8, W, RBW, NST, true><<<dim3((unsigned)items), dim3(64 * W), 0, st>>>(p);
@@ -526,7 +610,7 @@ static hipError_t launch_t(DecodeParams p, hipStream_t st) {
 // both; 3 or 4 -> two waves of two blocks each; more (prefill) -> query
 // blocks of 128 rows, four waves of two blocks each.
 template <int D, bool FP8>
-static hipError_t launch_w(const DecodeParams& p, hipStream_t st) {
+static hipError_t launch_w(DecodeParams& p, hipStream_t st) {
   if (p.row_blocks > 4) return launch_t<D, FP8, 4, 2, DECODE_NST_PREFILL>(p, st);
   if (p.row_blocks <= 1) return launch_t<D, FP8, 1, 1, DECODE_NST_1>(p, st);
   if (p.row_blocks == 2) return launch_t<D, FP8, 1, 2, DECODE_NST_2>(p, st);
@@ -537,7 +621,7 @@ static hipError_t launch_w(const DecodeParams& p, hipStream_t st) {
 #endif
 }
 
-hipError_t launch_decode_splitk(const DecodeParams& p, int head_dim, bool fp8, hipStream_t st) {
+hipError_t launch_decode_splitk(DecodeParams& p, int head_dim, bool fp8, hipStream_t st) {
   if (p.row_blocks < 1) return hipErrorInvalidValue;
   if (head_dim == 128) return fp8 ? launch_w<128, true>(p, st) : launch_w<128, false>(p, st);
   if (head_dim == 64 && !fp8) return launch_w<64, false>(p, st);

@@ -23,6 +23,10 @@ struct ReduceParams {
   int num_requests;
   int heads;
   int split_len;
+  // Balanced decode partials (see sk_* below): piece-major, rpu rows each;
+  // unit_info[(r * Hkv + h) * 2 + {0, 1}] = first piece, pieces of unit (r, h).
+  int balanced, rpu, Hkv;
+  const int32_t* unit_info;
 };
 hipError_t launch_splitk_reduce(const ReduceParams& p, hipStream_t st);
 
@@ -54,8 +58,103 @@ struct DecodeParams {
   void* out;
   float* lse;
   int nqb;                  // query blocks per (request, KV head); set by the launcher
+  // Balanced split (decode without a window): every workgroup takes an equal
+  // share of all keys (see sk_* below); partials are indexed by piece:
+  // acc [pieces, rpu, D], m / l [pieces, rpu] with rpu = rows per
+  // (request, KV head).  sk_G (workgroups) is set by the launcher.
+  int balanced;
+  int rpu;
+  int sk_G;
+  int32_t* unit_info;       // [R * Hkv][2]: first piece and piece count of each unit (written here)
 };
-hipError_t launch_decode_splitk(const DecodeParams& p, int head_dim, bool fp8, hipStream_t st);
+// Sets p.nqb and, for a balanced launch, p.sk_G.
+hipError_t launch_decode_splitk(DecodeParams& p, int head_dim, bool fp8, hipStream_t st);
+// Workgroups of a balanced launch never exceed this (sizes the partials).
+constexpr int kDecodeMaxBalancedWG = 4096;
+
+// ---------------------------------------------------------------------------
+// Balanced split of a decode call.  Units (requests, or (request, head)
+// pairs) are laid end to end on one line; share w of n takes the keys
+// [w P, (w + 1) P) of the line, P = ceil(total / n) rounded up to 32.  Each
+// overlap of a unit with a share is one piece; pieces are numbered unit by
+// unit, so unit u's pieces are base(u) .. base(u) + n(u) - 1.  Every wave
+// computes the plan itself from seq_lens (no extra launch).
+// Line positions stay below 2^31 (the host enables the balanced split only
+// then), so the divisions are 32-bit.
+__device__ __forceinline__ int sk_pieces(long c, int L, long P) {
+  const unsigned cu = (unsigned)c, Pu = (unsigned)P;
+  return L > 0 ? (int)((cu + (unsigned)L - 1u) / Pu - cu / Pu + 1u) : 0;
+}
+__device__ __forceinline__ long wave_incl_scan(long v, int lane) {
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const long u = __shfl_up(v, d, 64);
+    if (lane >= d) v += u;
+  }
+  return v;
+}
+__device__ __forceinline__ int sk_uni(int v);
+__device__ __forceinline__ long sk_uni(long v);
+__device__ __forceinline__ long sk_total(const int32_t* seq_lens, int R, int Hkv, int lane) {
+  long t = 0;
+  for (int c = 0; c < R; c += 64) t += (c + lane < R) ? seq_lens[c + lane] : 0;
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) t += __shfl_xor(t, o, 64);
+  return sk_uni(t * Hkv);
+}
+__device__ __forceinline__ long sk_piece_len(long total, int nwg) {
+  const long P = (total + nwg - 1) / nwg;
+  return P < 32 ? 32 : (P + 31) / 32 * 32;
+}
+// wave-uniform copies (scalar registers) of values every lane holds alike
+__device__ __forceinline__ int sk_uni(int v) { return __builtin_amdgcn_readfirstlane(v); }
+__device__ __forceinline__ long sk_uni(long v) {
+  const unsigned lo = __builtin_amdgcn_readfirstlane((unsigned)(v & 0xffffffffL));
+  const unsigned hi = __builtin_amdgcn_readfirstlane((unsigned)((unsigned long)v >> 32));
+  return (long)(((unsigned long)hi << 32) | lo);
+}
+struct SkUnit {
+  int r, kvh, L;
+  long start, base;   // first key of the unit on the line; its first piece's number
+};
+// The unit that holds line position x (by_unit: the unit (r_want, kvh_want)
+// instead).  Uniform across the wave.
+__device__ __forceinline__ SkUnit sk_find(const int32_t* seq_lens, int R, int Hkv, long P, long x,
+                                          bool by_unit, int r_want, int kvh_want, int lane) {
+  long S = 0, B = 0;   // keys and pieces of the requests before this chunk
+  SkUnit u{-1, 0, 0, 0, 0};
+  for (int c = 0; c < R; c += 64) {
+    const int i = c + lane;
+    const int Li = i < R ? seq_lens[i] : 0;
+    const long incl = wave_incl_scan(Li, lane);
+    const long rs = (long)Hkv * (S + incl - Li);   // first key of request i
+    int Ni = 0;
+    for (int k = 0; k < Hkv; ++k) Ni += sk_pieces(rs + (long)k * Li, Li, P);
+    const long Nincl = wave_incl_scan(Ni, lane);
+    const bool hit = i < R && (by_unit ? i == r_want : (Li > 0 && rs <= x && x < rs + (long)Hkv * Li));
+    const unsigned long long m = __ballot(hit);
+    if (m != 0) {
+      const int j = __builtin_ctzll(m);
+      u.r = c + j;
+      u.L = __shfl(Li, j, 64);
+      const long rsj = __shfl(rs, j, 64);
+      u.kvh = by_unit ? kvh_want : (int)((unsigned)(x - rsj) / (unsigned)u.L);
+      u.start = rsj + (long)u.kvh * u.L;
+      long b = B + __shfl(Nincl, j, 64) - __shfl(Ni, j, 64);
+      for (int k = 0; k < u.kvh; ++k) b += sk_pieces(rsj + (long)k * u.L, u.L, P);
+      u.base = b;
+      u.r = sk_uni(u.r);
+      u.kvh = sk_uni(u.kvh);
+      u.L = sk_uni(u.L);
+      u.start = sk_uni(u.start);
+      u.base = sk_uni(u.base);
+      return u;
+    }
+    S += __shfl(incl, 63, 64);
+    B += __shfl(Nincl, 63, 64);
+  }
+  return u;
+}
 
 struct KvWriteParams {
   const void* k_new;        // bf16 [N, Hkv, D]

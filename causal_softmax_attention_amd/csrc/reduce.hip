@@ -40,9 +40,8 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(ReduceParams p) {
   const int t = threadIdx.x, sg = t / CH, c = t % CH, wave = t >> 6, lane = t & 63;
 
   int nsplit = p.num_splits;
+  long first = row * (long)p.num_splits, step = 1;   // partial index of split 0, and stride
   if (p.seq_lens != nullptr) {
-    // Paged rows: only the segments that start at or before the row's own
-    // position (the partial kernel writes exactly those).
     const int tok = (int)(row / p.heads);
     if (tok >= p.cu_seqlens_q[p.num_requests]) return;   // whole workgroup
     int lo = 0, hi = p.num_requests;          // find r with cu[r] <= tok < cu[r+1]
@@ -50,16 +49,31 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(ReduceParams p) {
       const int mid = (lo + hi) >> 1;
       if (p.cu_seqlens_q[mid] <= tok) lo = mid; else hi = mid;
     }
-    const int pos = p.seq_lens[lo] - p.cu_seqlens_q[lo + 1] + tok;   // L - qlen + t
-    nsplit = pos < 0 ? 0 : min(nsplit, pos / p.split_len + 1);
+    if (p.balanced) {
+      // the row's request: its pieces base .. base + n - 1 (published by the
+      // partial kernel); piece k of head h is partial (base + k) * Hkv + h,
+      // row t * (heads / Hkv) + head-in-group
+      const int h = (int)(row % p.heads), grp = p.heads / p.Hkv;
+      const int ui = (lo * p.Hkv + h / grp) * 2;
+      const bool has_keys = p.seq_lens[lo] > 0;
+      nsplit = has_keys ? p.unit_info[ui + 1] : 0;
+      first = (has_keys ? ((long)p.unit_info[ui] * p.Hkv + h / grp) * p.rpu : 0) +
+              (long)(tok - p.cu_seqlens_q[lo]) * grp + h % grp;
+      step = (long)p.Hkv * p.rpu;
+    } else {
+      // only the segments that start at or before the row's own position
+      // (the partial kernel writes exactly those)
+      const int pos = p.seq_lens[lo] - p.cu_seqlens_q[lo + 1] + tok;   // L - qlen + t
+      nsplit = pos < 0 ? 0 : min(nsplit, pos / p.split_len + 1);
+    }
   }
-  const float* m = p.m + row * p.num_splits;
-  const float* l = p.l + row * p.num_splits;
-  const float* acc = p.acc + row * (long)p.num_splits * p.dv + 4 * c;
+  const float* m = p.m + first;
+  const float* l = p.l + first;
+  const float* acc = p.acc + first * p.dv + 4 * c;
 
   // ---- pass 1: max of m ----
   float M = -INFINITY;
-  for (int s = t; s < nsplit; s += 256) M = fmaxf(M, m[s]);
+  for (int s = t; s < nsplit; s += 256) M = fmaxf(M, m[s * step]);
   M = wave_max(M);
   if (lane == 0) red[0][wave] = M;
   __syncthreads();
@@ -75,9 +89,9 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(ReduceParams p) {
 #pragma unroll
       for (int u = 0; u < U; ++u) {
         const int s = min(s0 + u * SG, nsplit - 1);     // clamped: loads stay unconditional
-        ms[u] = m[s];
-        ls[u] = l[s];
-        a[u] = *reinterpret_cast<const f32x4*>(acc + (long)s * p.dv);
+        ms[u] = m[s * step];
+        ls[u] = l[s * step];
+        a[u] = *reinterpret_cast<const f32x4*>(acc + (long)s * step * p.dv);
       }
 #pragma unroll
       for (int u = 0; u < U; ++u) {

@@ -120,6 +120,51 @@ def test_decode_matches_oracle(A, case):
     assert np.max(np.abs(_np(lse) - rl)) <= 1e-3
 
 
+BALANCED_CASES = [
+    # seq_lens, q_lens, Hq, Hkv, D, B, kv, sink, gate, per-tensor
+    ([1, 2, 3, 40, 5000, 7, 31, 32, 33, 900], [1] * 10, 64, 4, 128, 16, synth.KV_FP8_E4M3FN, False, False, False),
+    ([3000, 17, 64, 2049, 4], [4, 3, 1, 2, 4], 64, 4, 128, 16, synth.KV_FP8_E4M3FN, True, True, False),
+    ([129, 4100, 1, 600], [2, 1, 1, 4], 16, 2, 64, 32, synth.KV_BF16, True, False, False),
+    ([6000, 6000, 5], [1, 4, 1], 64, 4, 128, 128, synth.KV_FP8_E4M3FN, False, True, True),
+]
+
+
+def _bal_id(c):
+    L, q, Hq, Hkv, D, B, kv, sk, gt, pt = c
+    return (f"r{len(L)}-L{max(L)}-q{max(q)}-h{Hq}kv{Hkv}-d{D}-p{B}-{'fp8' if kv else 'bf16'}"
+            f"{'-sink' if sk else ''}{'-gate' if gt else ''}{'-pt' if pt else ''}")
+
+
+@pytest.mark.parametrize("case", BALANCED_CASES, ids=_bal_id)
+def test_decode_balanced_split(A, case):
+    """The library's split of a decode without a window gives every
+    workgroup an equal share of all keys (pieces that cross requests and
+    start or end mid-step); it matches the oracle and the fixed-length
+    split."""
+    L, q, Hq, Hkv, D, B, kv, sk, gt, pt = case
+    _say(f"[case] decode balanced {_bal_id(case)}")
+    d = synth.decode_inputs(L, q, Hq, Hkv, D, B, kv_dtype=kv, seed=sum(L) % 1000, device=DEV,
+                            with_sink=sk, with_gate=gt, per_tensor=pt, spare_pages=4)
+    args = (d.q, d.cu_seqlens_q, d.max_seqlen_q, d.k_cache, d.v_cache, d.kv_dtype, d.k_scale, d.v_scale,
+            d.block_table, d.seq_lens, d.max_seq_len, d.scale)
+    kw = dict(return_lse=True, sink=d.sink, g_cache=d.g_cache)
+    out, lse = A.attn_decode_paged(*args, **kw)
+    fix_o, fix_l = A.attn_decode_paged(*args, kv_split_len=B if B > 32 else 256, **kw)
+    torch.cuda.synchronize()
+    ro, rl = oracle.decode_paged(d.q, d.cu_seqlens_q, d.k_cache, d.v_cache, d.block_table, d.seq_lens,
+                                 d.scale, kv == synth.KV_FP8_E4M3FN, d.k_scale, d.v_scale, sink=d.sink,
+                                 g_cache=d.g_cache, per_tensor=d.per_tensor)
+    o = _np(out)
+    assert np.isfinite(o).all()
+    err = rel_rms(o, ro)
+    lerr = float(np.max(np.abs(_np(lse) - rl)))
+    _say(f"    rel_rms={err:.3e} lse max abs={lerr:.2e} vs fixed split {rel_rms(o, _np(fix_o)):.2e}")
+    assert err <= TOL
+    assert lerr <= 1e-3
+    assert rel_rms(o, _np(fix_o)) <= 2e-3
+    assert float(np.max(np.abs(_np(lse) - _np(fix_l)))) <= 1e-4
+
+
 @pytest.mark.parametrize("split", [32, 128, 512, 2048])
 def test_decode_split_invariance(A, split):
     _say(f"[case] decode split={split}")
