@@ -431,10 +431,10 @@ int paged_attention(bool prefill, const void* q, const int32_t* cu_seqlens_q, in
   p.sink = sink; p.g_cache = g_cache; p.window = window > 0 ? window : 0;
   p.per_tensor = per_tensor_scales;
   if (lay.num_splits == 1) { p.out = out; p.lse = lse; }
-  // decode with the library's split and no window: equal shares of all keys
+  // decode with the library's split: equal shares of all visible keys
   // per workgroup (request lengths vary; fixed-length segments leave the
   // longest ones alone at the end)
-  p.balanced = !prefill && kv_split_len == 0 && p.window == 0 && lay.num_splits > 1 &&
+  p.balanced = !prefill && kv_split_len == 0 && lay.num_splits > 1 &&
                (long)num_requests * num_kv_heads * max_seq_len < 0x7fffffffL;   // line fits 31 bits
   p.rpu = max_seqlen_q * (num_q_heads / num_kv_heads);
   p.unit_info = reinterpret_cast<int32_t*>(ws + lay.units);

@@ -121,7 +121,8 @@ __global__ __launch_bounds__(64 * W) void decode_splitk_kernel(DecodeParams p) {
   // ---- one segment: keys [k0, k1) of (request r, KV head kvh) for query
   // block qb; its partials go to split s (fixed-length split) or to piece
   // number s (balanced split) ----
-  auto segment = [&](const int r, const int kvh, const int qb, const int k0, const int k1, const long s) {
+  auto segment = [&](const int r, const int kvh, const int qb, const int k0, const int k1, const long s,
+                     const bool with_sink) {
   const int L = p.seq_lens[r];
   const int qs = p.cu_q[r];
   const int qlen = p.cu_q[r + 1] - qs;
@@ -264,7 +265,7 @@ __global__ __launch_bounds__(64 * W) void decode_splitk_kernel(DecodeParams p) {
   for (int rb = 0; rb < RBW; ++rb) {
     m_run[rb] = kNegBig;
     l_run[rb] = 0.f;
-    if (p.sink != nullptr && k0 == 0) {  // the sink's mass belongs to the segment at key 0
+    if (p.sink != nullptr && with_sink) {   // the sink's mass belongs to one segment
       m_run[rb] = p.sink[kvh * G + rho[rb] % G] * kLog2e;
       l_run[rb] = 1.f;
     }
@@ -501,40 +502,48 @@ __global__ __launch_bounds__(64 * W) void decode_splitk_kernel(DecodeParams p) {
     item /= p.R;
     const int qb = item % p.nqb;
     const int s = item / p.nqb;
-    segment(r, kvh, qb, s * p.split_len, (s + 1) * p.split_len, s);
+    segment(r, kvh, qb, s * p.split_len, (s + 1) * p.split_len, s, s == 0);
     return;
   }
-  // ---- balanced split: the requests' keys laid end to end on one line;
+  // ---- balanced split: the requests' visible keys laid end to end on one line;
   // workgroups w .. w + Hkv - 1 (dispatched together) take the same share
   // [x0, x1) of the line for the Hkv heads, so the head slices of a page are
   // read at about the same time.  Piece k of request r for head h is
   // partial (base(r) + k) * Hkv + h. ----
   const int kvh_w = blockIdx.x % p.Hkv;
   const int share = blockIdx.x / p.Hkv;
-  const long total = sk_total(p.seq_lens, p.R, 1, lane);
+  const long total = sk_total(p.seq_lens, p.cu_q, p.window, p.R, lane);
   const long P = sk_piece_len(total, p.sk_G / p.Hkv);
   const long x0 = (long)share * P;
   if (x0 >= total) return;             // whole workgroup, before any barrier
   const long x1 = min(total, x0 + P);
-  SkUnit u = sk_find(p.seq_lens, p.R, 1, P, x0, false, 0, 0, lane);
+  SkUnit u = sk_find(p.seq_lens, p.cu_q, p.window, p.R, P, x0, lane);
   if (u.r < 0) return;
   long piece = u.base + ((long)share - u.start / P);
   for (;;) {
-    if (u.start >= x0 && threadIdx.x == 0) {
-      // this share holds the request's first key: publish its pieces for the reduce
+    // keep the cursor in scalar registers (the copies need uniform bases)
+    u.r = sk_uni(u.r);
+    u.L = sk_uni(u.L);
+    u.start = sk_uni(u.start);
+    u.base = sk_uni(u.base);
+    piece = sk_uni(piece);
+    const bool first = u.start >= x0;  // this share holds the request's first key
+    if (first && threadIdx.x == 0) {
+      // publish the request's pieces for the reduce
       const int ui = (u.r * p.Hkv + kvh_w) * 2;
       p.unit_info[ui] = (int)u.base;
       p.unit_info[ui + 1] = sk_pieces(u.start, u.L, P);
     }
-    segment(sk_uni(u.r), kvh_w, 0, sk_uni((int)(max(x0, u.start) - u.start)),
-            sk_uni((int)(min(x1, u.start + u.L) - u.start)), sk_uni(piece * p.Hkv + kvh_w));
+    const int lo = sk_uni(p.seq_lens[u.r] - u.L);   // the request's first visible key
+    segment(sk_uni(u.r), kvh_w, 0, sk_uni(lo + (int)(max(x0, u.start) - u.start)),
+            sk_uni(lo + (int)(min(x1, u.start + u.L) - u.start)), sk_uni(piece * p.Hkv + kvh_w), first);
     if (u.start + u.L >= x1) break;
     // the next request starts inside this share: its first piece is this one's
     u.base += sk_pieces(u.start, u.L, P);
     u.start += u.L;
     do {
       ++u.r;
-    } while (u.r < p.R && (u.L = p.seq_lens[u.r]) == 0);
+    } while (u.r < p.R && (u.L = sk_len(p.seq_lens, p.cu_q, p.window, u.r)) == 0);
     if (u.r >= p.R) break;
     piece = u.base;
     if constexpr (W > 1) lds_barrier();   // the next piece's copies reuse the ring

@@ -93,19 +93,6 @@ __device__ __forceinline__ long wave_incl_scan(long v, int lane) {
   }
   return v;
 }
-__device__ __forceinline__ int sk_uni(int v);
-__device__ __forceinline__ long sk_uni(long v);
-__device__ __forceinline__ long sk_total(const int32_t* seq_lens, int R, int Hkv, int lane) {
-  long t = 0;
-  for (int c = 0; c < R; c += 64) t += (c + lane < R) ? seq_lens[c + lane] : 0;
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) t += __shfl_xor(t, o, 64);
-  return sk_uni(t * Hkv);
-}
-__device__ __forceinline__ long sk_piece_len(long total, int nwg) {
-  const long P = (total + nwg - 1) / nwg;
-  return P < 32 ? 32 : (P + 31) / 32 * 32;
-}
 // wave-uniform copies (scalar registers) of values every lane holds alike
 __device__ __forceinline__ int sk_uni(int v) { return __builtin_amdgcn_readfirstlane(v); }
 __device__ __forceinline__ long sk_uni(long v) {
@@ -113,41 +100,52 @@ __device__ __forceinline__ long sk_uni(long v) {
   const unsigned hi = __builtin_amdgcn_readfirstlane((unsigned)((unsigned long)v >> 32));
   return (long)(((unsigned long)hi << 32) | lo);
 }
+// Keys of request i on the line: those its queries can see (all of them
+// without a window; from the first query's window start with one).
+__device__ __forceinline__ int sk_len(const int32_t* seq_lens, const int32_t* cu, int window, int i) {
+  const int L = seq_lens[i];
+  if (window <= 0) return L;
+  const int lo = L - (cu[i + 1] - cu[i]) - window + 1;
+  return lo > 0 ? L - lo : L;
+}
+__device__ __forceinline__ long sk_total(const int32_t* seq_lens, const int32_t* cu, int window, int R,
+                                         int lane) {
+  long t = 0;
+  for (int c = 0; c < R; c += 64) t += (c + lane < R) ? sk_len(seq_lens, cu, window, c + lane) : 0;
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) t += __shfl_xor(t, o, 64);
+  return sk_uni(t);
+}
+__device__ __forceinline__ long sk_piece_len(long total, int nshares) {
+  const long P = (total + nshares - 1) / nshares;
+  return P < 32 ? 32 : (P + 31) / 32 * 32;
+}
 struct SkUnit {
-  int r, kvh, L;
-  long start, base;   // first key of the unit on the line; its first piece's number
+  int r, kvh, L;      // request, (unused), keys on the line
+  long start, base;   // first line position of the request; its first piece's number
 };
 // The unit that holds line position x (by_unit: the unit (r_want, kvh_want)
 // instead).  Uniform across the wave.
-__device__ __forceinline__ SkUnit sk_find(const int32_t* seq_lens, int R, int Hkv, long P, long x,
-                                          bool by_unit, int r_want, int kvh_want, int lane) {
+// The request whose keys hold line position x (uniform across the wave).
+__device__ __forceinline__ SkUnit sk_find(const int32_t* seq_lens, const int32_t* cu, int window, int R,
+                                          long P, long x, int lane) {
   long S = 0, B = 0;   // keys and pieces of the requests before this chunk
   SkUnit u{-1, 0, 0, 0, 0};
   for (int c = 0; c < R; c += 64) {
     const int i = c + lane;
-    const int Li = i < R ? seq_lens[i] : 0;
+    const int Li = i < R ? sk_len(seq_lens, cu, window, i) : 0;
     const long incl = wave_incl_scan(Li, lane);
-    const long rs = (long)Hkv * (S + incl - Li);   // first key of request i
-    int Ni = 0;
-    for (int k = 0; k < Hkv; ++k) Ni += sk_pieces(rs + (long)k * Li, Li, P);
+    const long rs = S + incl - Li;   // first line position of request i
+    const int Ni = sk_pieces(rs, Li, P);
     const long Nincl = wave_incl_scan(Ni, lane);
-    const bool hit = i < R && (by_unit ? i == r_want : (Li > 0 && rs <= x && x < rs + (long)Hkv * Li));
+    const bool hit = i < R && Li > 0 && rs <= x && x < rs + Li;
     const unsigned long long m = __ballot(hit);
     if (m != 0) {
       const int j = __builtin_ctzll(m);
-      u.r = c + j;
-      u.L = __shfl(Li, j, 64);
-      const long rsj = __shfl(rs, j, 64);
-      u.kvh = by_unit ? kvh_want : (int)((unsigned)(x - rsj) / (unsigned)u.L);
-      u.start = rsj + (long)u.kvh * u.L;
-      long b = B + __shfl(Nincl, j, 64) - __shfl(Ni, j, 64);
-      for (int k = 0; k < u.kvh; ++k) b += sk_pieces(rsj + (long)k * u.L, u.L, P);
-      u.base = b;
-      u.r = sk_uni(u.r);
-      u.kvh = sk_uni(u.kvh);
-      u.L = sk_uni(u.L);
-      u.start = sk_uni(u.start);
-      u.base = sk_uni(u.base);
+      u.r = sk_uni(c + j);
+      u.L = sk_uni(__shfl(Li, j, 64));
+      u.start = sk_uni(__shfl(rs, j, 64));
+      u.base = sk_uni(B + __shfl(Nincl, j, 64) - __shfl(Ni, j, 64));
       return u;
     }
     S += __shfl(incl, 63, 64);
