@@ -6,36 +6,22 @@
 // chunk c) with CH = dv/4 chunks of 4 floats and SG = 256/CH groups: group
 // sg sums splits sg, sg+SG, ... of chunk c, four splits' loads in flight at
 // a time, so a row with a hundred splits costs a few memory latencies, not
-// one per split.  Two passes: the max of m over the row's splits, then the
-// exp(m_s - max) weighted sums of acc and l; the groups meet in LDS.  acc
-// and l of an empty split (m = -inf) may be loaded (they are in range) but
-// never enter a sum.
+// one per split.  One pass: each group keeps its own running max over its
+// splits (rescaling what it holds when the max rises); the groups meet in
+// LDS, weighted by exp(group max - row max).  acc and l of an empty split
+// (m = -inf) may be loaded (they are in range) but never enter a sum.
 #include "common.h"
 #include "kernels.h"
 
 namespace attn {
 
-namespace {
-
-__device__ __forceinline__ float wave_max(float x) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) x = fmaxf(x, __shfl_xor(x, o, 64));
-  return x;
-}
-__device__ __forceinline__ float wave_sum(float x) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o, 64);
-  return x;
-}
-
-}  // namespace
 
 template <int CH, typename OutT>
 __global__ __launch_bounds__(256) void splitk_reduce_kernel(ReduceParams p) {
   constexpr int SG = 256 / CH;
   constexpr int U = 4;                       // splits per group in flight
   __shared__ f32x4 part[SG][CH];
-  __shared__ float red[2][4];
+  __shared__ float gm[SG], gl[SG];        // each split group's max and weighted l
   const long row = blockIdx.x;
   const int t = threadIdx.x, sg = t / CH, c = t % CH, wave = t >> 6, lane = t & 63;
 
@@ -43,12 +29,18 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(ReduceParams p) {
   long first = row * (long)p.num_splits, step = 1;   // partial index of split 0, and stride
   if (p.seq_lens != nullptr) {
     const int tok = (int)(row / p.heads);
-    if (tok >= p.cu_seqlens_q[p.num_requests]) return;   // whole workgroup
-    int lo = 0, hi = p.num_requests;          // find r with cu[r] <= tok < cu[r+1]
-    while (hi - lo > 1) {
-      const int mid = (lo + hi) >> 1;
-      if (p.cu_seqlens_q[mid] <= tok) lo = mid; else hi = mid;
+    // the row's request r: the last with cu[r] <= tok (a request with no
+    // tokens shares its start with the next one), 64 starts per wave load
+    // instead of a chain of dependent loads
+    const int T = p.cu_seqlens_q[p.num_requests];
+    int lo = 0;
+    for (int c0 = 0; c0 < p.num_requests; c0 += 64) {
+      const int i = c0 + lane;
+      const unsigned long long le = __ballot(i < p.num_requests && p.cu_seqlens_q[i] <= tok);
+      if (le != 0) lo = c0 + 63 - __builtin_clzll(le);
+      if (le != ~0ull) break;
     }
+    if (tok >= T) return;                     // whole workgroup
     if (p.balanced) {
       // the row's request: its pieces base .. base + n - 1 (published by the
       // partial kernel); piece k of head h is partial (base + k) * Hkv + h,
@@ -71,49 +63,58 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(ReduceParams p) {
   const float* l = p.l + first;
   const float* acc = p.acc + first * p.dv + 4 * c;
 
-  // ---- pass 1: max of m ----
-  float M = -INFINITY;
-  for (int s = t; s < nsplit; s += 256) M = fmaxf(M, m[s * step]);
-  M = wave_max(M);
-  if (lane == 0) red[0][wave] = M;
-  __syncthreads();
-  M = fmaxf(fmaxf(red[0][0], red[0][1]), fmaxf(red[0][2], red[0][3]));
-
-  // ---- pass 2: weighted sums ----
+  // ---- one pass: each split group merges its splits under its own running
+  // max (m, l and acc loaded together); the groups meet in LDS ----
+  float Mg = -INFINITY;
   f32x4 o = {0.f, 0.f, 0.f, 0.f};
   float lsum = 0.f;
-  if (M != -INFINITY) {
-    for (int s0 = sg; s0 < nsplit; s0 += U * SG) {
-      float ms[U], ls[U];
-      f32x4 a[U];
+  for (int s0 = sg; s0 < nsplit; s0 += U * SG) {
+    float ms[U], ls[U];
+    f32x4 a[U];
 #pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int s = min(s0 + u * SG, nsplit - 1);     // clamped: loads stay unconditional
-        ms[u] = m[s * step];
-        ls[u] = l[s * step];
-        a[u] = *reinterpret_cast<const f32x4*>(acc + (long)s * step * p.dv);
-      }
+    for (int u = 0; u < U; ++u) {
+      const int s = min(s0 + u * SG, nsplit - 1);     // clamped: loads stay unconditional
+      ms[u] = m[s * step];
+      ls[u] = l[s * step];
+      a[u] = *reinterpret_cast<const f32x4*>(acc + (long)s * step * p.dv);
+    }
 #pragma unroll
-      for (int u = 0; u < U; ++u) {
-        if (s0 + u * SG < nsplit && ms[u] != -INFINITY) {
-          const float w = expf(ms[u] - M);
-          o += w * a[u];
-          lsum += w * ls[u];
+    for (int u = 0; u < U; ++u) {
+      if (s0 + u * SG < nsplit && ms[u] != -INFINITY) {
+        if (ms[u] > Mg) {                 // rescale what this group holds
+          const float f = expf(Mg - ms[u]);
+          o *= f;
+          lsum *= f;
+          Mg = ms[u];
         }
+        const float w = expf(ms[u] - Mg);
+        o += w * a[u];
+        lsum += w * ls[u];
       }
     }
   }
   part[sg][c] = o;
-  // every thread of a split group saw the same splits: take l from chunk 0
-  float lpart = (c == 0) ? lsum : 0.f;
-  lpart = wave_sum(lpart);
-  if (lane == 0) red[1][wave] = lpart;
+  if (c == 0) {                           // every thread of a group saw the same splits
+    gm[sg] = Mg;
+    gl[sg] = lsum;
+  }
   __syncthreads();
-  const float Lsum = red[1][0] + red[1][1] + red[1][2] + red[1][3];
-  if (t < CH) {
-    f32x4 sum = part[0][t];
+  float M = -INFINITY;
 #pragma unroll
-    for (int j = 1; j < SG; ++j) sum += part[j][t];
+  for (int j = 0; j < SG; ++j) M = fmaxf(M, gm[j]);
+  float Lsum = 0.f;
+  if (M != -INFINITY) {
+#pragma unroll
+    for (int j = 0; j < SG; ++j)
+      if (gm[j] != -INFINITY) Lsum += gl[j] * expf(gm[j] - M);
+  }
+  if (t < CH) {
+    f32x4 sum = {0.f, 0.f, 0.f, 0.f};
+    if (M != -INFINITY) {
+#pragma unroll
+      for (int j = 0; j < SG; ++j)
+        if (gm[j] != -INFINITY) sum += part[j][t] * expf(gm[j] - M);
+    }
     const float inv = (M == -INFINITY) ? 0.f : 1.0f / Lsum;
     OutT* out = reinterpret_cast<OutT*>(p.out) + row * p.dv + 4 * t;
 #pragma unroll
