@@ -82,7 +82,7 @@ def _load():
     path = lib_path()
     if not os.path.exists(path):
         raise ImportError(
-            f"{path} is missing: build it with `python -m causal_softmax_attention_amd.build` "
+            f"{path} is missing: build it with `python causal_softmax_attention_amd/build.py` "
             "(hipcc for gfx950); there is no fallback implementation")
     lib = ctypes.CDLL(path)
     for name, (argtypes, restype) in _SIGNATURES.items():

@@ -1,6 +1,7 @@
 """Build libattn.so (the gfx950 HIP kernels and their C ABI) in-tree.
 
-Usage: python -m causal_softmax_attention_amd.build [--verbose]
+Usage: python causal_softmax_attention_amd/build.py [--verbose]
+(run as a script: importing the package first would look for the library)
 
 Each csrc/*.hip file is compiled by hipcc for gfx950 into an object under
 _build/, then linked into causal_softmax_attention_amd/libattn.so.  Packed
