@@ -61,6 +61,11 @@ __device__ __forceinline__ bf16x4 lds_read_tr16(const bf16* p) {
       (LDS_AS i16x4*)(LDS_AS void*)(const_cast<bf16*>(p)));
   return __builtin_bit_cast(bf16x4, v);
 }
+// The same read from a pointer already in the LDS address space (lets the
+// compiler fold constant parts of the address into the offset field).
+__device__ __forceinline__ bf16x4 lds_tr16(const LDS_AS uint8_t* p) {
+  return __builtin_bit_cast(bf16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS i16x4*)p));
+}
 // Transposed 8 x byte read.
 __device__ __forceinline__ i32x2 lds_read_tr8(const uint8_t* p) {
   return __builtin_amdgcn_ds_read_tr8_b64_v2i32(

@@ -576,10 +576,14 @@ __global__ __launch_bounds__(64 * W) void decode_splitk_kernel(DecodeParams p) {
 #ifndef DECODE_BAL_PER_CU_1
 #define DECODE_BAL_PER_CU_1 4
 #endif
+#ifndef DECODE_BAL_PER_CU_2
+#define DECODE_BAL_PER_CU_2 0
+#endif
+// `cache` belongs to one kernel instantiation: every instantiation has the
+// same function type, so the caller keeps one cache per instantiation.
 template <typename K>
-static int balanced_wgs(K kernel, int threads, int cap_per_cu) {
+static int balanced_wgs(K kernel, int threads, int cap_per_cu, std::atomic<int> (&cache)[16]) {
   // per device, once per instantiation (the answer depends on nothing else)
-  static std::atomic<int> cache[16];
   int dev = 0, cus = 0, per_cu = 0;
   if (hipGetDevice(&dev) != hipSuccess) return 0;
   if (dev >= 0 && dev < 16 && cache[dev].load() > 0) return cache[dev].load();
@@ -597,10 +601,11 @@ static hipError_t launch_t(DecodeParams& p, hipStream_t st) {
   if (p.balanced) {
     // workgroups that stay resident together, so each share runs in one
     // round (queried for the instantiation that runs)
-    const int cap = W == 1 ? DECODE_BAL_PER_CU_1 : 0;
+    const int cap = W == 1 ? DECODE_BAL_PER_CU_1 : DECODE_BAL_PER_CU_2;
+    static std::atomic<int> cache_gate[16], cache_plain[16];
     const int res = p.g_cache != nullptr
-                        ? balanced_wgs(decode_splitk_kernel<D, FP8, W, RBW, NST, true>, 64 * W, cap)
-                        : balanced_wgs(decode_splitk_kernel<D, FP8, W, RBW, NST, false>, 64 * W, cap);
+                        ? balanced_wgs(decode_splitk_kernel<D, FP8, W, RBW, NST, true>, 64 * W, cap, cache_gate)
+                        : balanced_wgs(decode_splitk_kernel<D, FP8, W, RBW, NST, false>, 64 * W, cap, cache_plain);
     if (res <= 0) return hipErrorInvalidConfiguration;
     int want = res < kDecodeMaxBalancedWG ? res : kDecodeMaxBalancedWG;
     want -= want % p.Hkv;                // whole groups of Hkv (one per head)

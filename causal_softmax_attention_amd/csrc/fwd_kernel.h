@@ -34,6 +34,31 @@ namespace attn {
 // ---------------------------------------------------------------------------
 // Forward kernel
 // ---------------------------------------------------------------------------
+// Row max of a tile held as sc[kb][rb][i] (keys kb*16 + 4g + i), and a sum
+// of per-block partials, both as trees: independent steps instead of one
+// dependent chain per row (the softmax sits between MFMA phases, so its
+// latency counts).  The summation order is fixed.
+template <int KB, int RBW>
+__device__ __forceinline__ float tile_row_max(const f32x4 (&sc)[KB][RBW], int rb) {
+  float m[KB];
+#pragma unroll
+  for (int kb = 0; kb < KB; ++kb)
+    m[kb] = fmaxf(fmaxf(fmaxf(sc[kb][rb][0], sc[kb][rb][1]), sc[kb][rb][2]), sc[kb][rb][3]);
+#pragma unroll
+  for (int w = 1; w < KB; w *= 2)
+#pragma unroll
+    for (int kb = 0; kb + w < KB; kb += 2 * w) m[kb] = fmaxf(m[kb], m[kb + w]);
+  return m[0];
+}
+template <int N>
+__device__ __forceinline__ float tree_sum(float (&v)[N]) {
+#pragma unroll
+  for (int w = 1; w < N; w *= 2)
+#pragma unroll
+    for (int i = 0; i + w < N; i += 2 * w) v[i] += v[i + w];
+  return v[0];
+}
+
 // Blocks are dispatched round-robin over the 8 XCDs (each with its own L2);
 // map block x so that the query heads of one KV group land on one XCD.
 __device__ __forceinline__ int xcd_head(int x, int Hq) {
@@ -150,6 +175,16 @@ __global__ __launch_bounds__(256) void fwd_kernel(FwdParams p) {
       dma4(g2base, (uint32_t)(min(j0 + lane, L - 1) * 4), lds_addr(&gk_lds[st][wave][0]));
   };
 
+  // Per-lane LDS offsets of the operands this lane reads (a row's swizzle
+  // depends only on its index mod 16): K rows kb*16 + li at k-step ks, V^T
+  // rows kp*32 + 4g + mm (and 16 below) at output block db.
+  const int mm = li >> 2, c4 = li & 3;
+  uint32_t k_lane[KS], v_lane[DB];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) k_lane[ks] = (uint32_t)tile_off<KRB>(li, 64 * ks + 16 * g);
+#pragma unroll
+  for (int db = 0; db < DB; ++db) v_lane[db] = (uint32_t)tile_off<VRB>(4 * g + mm, 32 * db + 8 * c4);
+
   // prologue: tiles t_begin .. t_begin+NST-2
 #pragma unroll
   for (int s = 0; s < NST - 1; ++s)
@@ -173,8 +208,18 @@ __global__ __launch_bounds__(256) void fwd_kernel(FwdParams p) {
     {
       const bool need_mask = (j0 + BN - 1 > r0) || (W > 0 && r_last - j0 >= W) || (j0 + BN > L) ||
                              (r_last < r0 + RW - 1);
-      const uint8_t* kl = k_lds[st];
-      const uint8_t* vl = v_lds[st];
+      // (the empty asm keeps each per-tile address whole, so that the
+      // compiler folds the constant parts into the reads' offset fields
+      // instead of hoisting one register per read out of the loop)
+      const uint32_t kst = lds_addr(k_lds[st]), vst = lds_addr(v_lds[st]);
+      const LDS_AS uint8_t* ka[KS];
+      const LDS_AS uint8_t* va[DB];
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        uint32_t a = kst + k_lane[ks];
+        asm volatile("" : "+v"(a));
+        ka[ks] = (const LDS_AS uint8_t*)a;
+      }
       const float* gkl = gk_lds[st][wave];
       // ---- S^T = K Q^T ----
       f32x4 sc[KB][RBW];
@@ -184,7 +229,7 @@ __global__ __launch_bounds__(256) void fwd_kernel(FwdParams p) {
         for (int rb = 0; rb < RBW; ++rb) sc[kb][rb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
-          const bf16x8 a = *reinterpret_cast<const bf16x8*>(kl + tile_off<KRB>(kb * 16 + li, 64 * ks + 16 * g));
+          const bf16x8 a = *reinterpret_cast<const LDS_AS bf16x8*>(ka[ks] + kb * 16 * KRB);
 #pragma unroll
           for (int rb = 0; rb < RBW; ++rb) sc[kb][rb] = mfma16x16x32(a, qop[rb][ks], sc[kb][rb]);
         }
@@ -221,12 +266,7 @@ __global__ __launch_bounds__(256) void fwd_kernel(FwdParams p) {
       bf16x4 pb[KB][RBW];
 #pragma unroll
       for (int rb = 0; rb < RBW; ++rb) {
-        float mx = -INFINITY;
-#pragma unroll
-        for (int kb = 0; kb < KB; ++kb) {   // three-input max steps
-          mx = fmaxf(fmaxf(mx, sc[kb][rb][0]), sc[kb][rb][1]);
-          mx = fmaxf(fmaxf(mx, sc[kb][rb][2]), sc[kb][rb][3]);
-        }
+        float mx = tile_row_max<KB>(sc, rb);
         mx = xgroup_max(mx);
         if constexpr (!GATED) mx *= c;
         if (__builtin_expect(__any(mx > m_run[rb] + kRescaleSlack), 0)) {
@@ -238,29 +278,31 @@ __global__ __launch_bounds__(256) void fwd_kernel(FwdParams p) {
           m_run[rb] = m_new;
         }
         const float mr = m_run[rb];
-        float rs = 0.f;
+        float part[KB];
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb) {
           f32x4 e;
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
+          for (int i = 0; i < 4; ++i)
             e[i] = fast_exp2(GATED ? sc[kb][rb][i] - mr : __builtin_fmaf(sc[kb][rb][i], c, -mr));
-            rs += e[i];
-          }
+          part[kb] = (e[0] + e[1]) + (e[2] + e[3]);
           pb[kb][rb] = to_bf16x4(e);
         }
+        const float rs = tree_sum<KB>(part);
         l_run[rb] += xgroup_sum(rs);   // fp32 row sum: lse feeds the backward
       }
       // ---- O^T += V^T P^T, 32 keys per MFMA ----
-      const int mm = li >> 2, c4 = li & 3;
+#pragma unroll
+      for (int db = 0; db < DB; ++db) {
+        uint32_t a = vst + v_lane[db];
+        asm volatile("" : "+v"(a));
+        va[db] = (const LDS_AS uint8_t*)a;
+      }
 #pragma unroll
       for (int kp = 0; kp < KB / 2; ++kp) {
-        const int vr0 = kp * 32 + 4 * g + mm, vr1 = vr0 + 16;
 #pragma unroll
         for (int db = 0; db < DB; ++db) {
-          const int b = 32 * db + 8 * c4;
-          const bf16x8 a = concat(lds_read_tr16(reinterpret_cast<const bf16*>(vl + tile_off<VRB>(vr0, b))),
-                                  lds_read_tr16(reinterpret_cast<const bf16*>(vl + tile_off<VRB>(vr1, b))));
+          const bf16x8 a = concat(lds_tr16(va[db] + kp * 32 * VRB), lds_tr16(va[db] + (kp * 32 + 16) * VRB));
 #pragma unroll
           for (int rb = 0; rb < RBW; ++rb)
             oacc[rb][db] = mfma16x16x32(a, concat(pb[2 * kp][rb], pb[2 * kp + 1][rb]), oacc[rb][db]);
