@@ -59,6 +59,26 @@ namespace attn {
 
 namespace {
 
+// Copies of the cache (K, V and their scales).  NT: the non-temporal policy,
+// for the decode and verify shapes, which read every cache byte once per
+// call (measured: config-3 decode 235 -> 224 us, 227K-context bf16 verify
+// 290 -> 261 us); the paged prefill, whose query blocks of one request read
+// the same keys, keeps the default policy.
+template <bool NT>
+__device__ __forceinline__ void dma16_kv(const void* sbase, uint32_t voff, uint32_t m0) {
+  if constexpr (NT)
+    asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1 nt" :: "v"(voff), "s"(sbase), "s"(m0) : "memory");
+  else
+    dma16(sbase, voff, m0);
+}
+template <bool NT>
+__device__ __forceinline__ void dma4_kv(const void* sbase, uint32_t voff, uint32_t m0) {
+  if constexpr (NT)
+    asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dword %0, %1 nt" :: "v"(voff), "s"(sbase), "s"(m0) : "memory");
+  else
+    dma4(sbase, voff, m0);
+}
+
 // 8 e4m3fn bytes -> 8 bf16 (exact), two bytes per instruction.
 __device__ __forceinline__ bf16x8 fp8x8_to_bf16x8(i32x2 w) {
   const auto a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[0], 1.0f, false);
@@ -112,6 +132,7 @@ __global__ __launch_bounds__(64 * W) void decode_splitk_kernel(DecodeParams p) {
   constexpr int LPK = 2 * NTW;         // K and V copies per step and wave (fixed;
                                        // scale and gate copies come on top)
   static_assert(NST >= 2 && NST <= 4, "ring depth");
+  constexpr bool STREAM = W * RBW <= 4;   // decode / verify shapes (not the paged prefill)
   static_assert((NST - 2) * LPK <= 63, "vmcnt range");
   __shared__ __attribute__((aligned(1024))) uint8_t smem[NST * STAGE];
 
@@ -185,8 +206,8 @@ __global__ __launch_bounds__(64 * W) void decode_splitk_kernel(DecodeParams p) {
     for (int i = 0; i < NTW; ++i) {
       const int ci = wave + W * i;
       const long ro = ci * RPI < 16 ? ra : rb;
-      dma16(kc + ro, voff_k[i], stage + ci * 1024);
-      dma16(vc + ro, voff_v[i], stage + TILE + ci * 1024);
+      dma16_kv<STREAM>(kc + ro, voff_k[i], stage + ci * 1024);
+      dma16_kv<STREAM>(vc + ro, voff_v[i], stage + TILE + ci * 1024);
     }
     if constexpr (FP8) {
       if (!per_tensor) {
@@ -194,8 +215,8 @@ __global__ __launch_bounds__(64 * W) void decode_splitk_kernel(DecodeParams p) {
         const int slot = ((kk + (lane & 16)) & bmask) + (lane & 15);
         const uint32_t so = (uint32_t)((((pid * p.Hkv + kvh) << bsh) + slot) * 4);
         const uint32_t sc = stage + 2 * TILE + wave * 2 * SCB;
-        dma4(p.k_scale, so, sc);
-        dma4(p.v_scale, so, sc + SCB);
+        dma4_kv<STREAM>(p.k_scale, so, sc);
+        dma4_kv<STREAM>(p.v_scale, so, sc + SCB);
       }
     }
     if constexpr (GATE) {
@@ -551,8 +572,9 @@ __global__ __launch_bounds__(64 * W) void decode_splitk_kernel(DecodeParams p) {
 }
 
 // Ring depth per launch shape.  Every stage in flight holds 32 keys of K
-// and V; the one-wave shapes are limited by LDS per CU, the two-wave verify
-// shape by registers, so it takes a deeper ring to keep enough bytes moving.
+// and V.  Measured on one MI355X: deeper rings change neither the one-wave
+// decode nor the fp8 verify (compute-bound); the bf16 verify (256-byte
+// rows) gains ~3 % from four stages.
 #ifndef DECODE_NST_1
 #define DECODE_NST_1 2
 #endif
@@ -563,7 +585,7 @@ __global__ __launch_bounds__(64 * W) void decode_splitk_kernel(DecodeParams p) {
 #define DECODE_NST_4_FP8 2
 #endif
 #ifndef DECODE_NST_4_BF16
-#define DECODE_NST_4_BF16 2
+#define DECODE_NST_4_BF16 4
 #endif
 #ifndef DECODE_NST_PREFILL
 #define DECODE_NST_PREFILL 2
