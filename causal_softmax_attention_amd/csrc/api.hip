@@ -449,6 +449,9 @@ int paged_attention(bool prefill, const void* q, const int32_t* cu_seqlens_q, in
   r.seq_lens = seq_lens; r.cu_seqlens_q = cu_seqlens_q; r.num_requests = num_requests;
   r.heads = num_q_heads; r.split_len = lay.split_len;
   r.balanced = p.balanced; r.rpu = p.rpu; r.Hkv = num_kv_heads; r.unit_info = p.unit_info;
+  // balanced: a unit's pieces are about its share of the workgroups, plus
+  // the pieces cut at its two ends
+  r.splits_hint = p.balanced ? p.sk_G / (num_kv_heads * num_requests) + 2 : lay.num_splits;
   e = attn::launch_splitk_reduce(r, s);
   if (e != hipSuccess) return hip_fail(e, "reduce launch");
   return ok();

@@ -27,6 +27,9 @@ struct ReduceParams {
   // unit_info[(r * Hkv + h) * 2 + {0, 1}] = first piece, pieces of unit (r, h).
   int balanced, rpu, Hkv;
   const int32_t* unit_info;
+  // Splits (or pieces) a row is expected to hold; picks the workgroup
+  // shape (more split groups for more splits).  0: num_splits.
+  int splits_hint;
 };
 hipError_t launch_splitk_reduce(const ReduceParams& p, hipStream_t st);
 

@@ -2,8 +2,10 @@
 // message and "Technical details": segment partials merged by a reduce, an
 // empty partial with M = -inf weighs 0).
 //
-// One 256-thread workgroup per row.  Thread t = (split group sg, column
-// chunk c) with CH = dv/4 chunks of 4 floats and SG = 256/CH groups: group
+// One workgroup per row.  Thread t = (split group sg, column chunk c) with
+// CH = dv/4 chunks of 4 floats and SG split groups (SG = 256/CH when a row
+// holds many splits, 2 when it holds a few: then a workgroup is one wave
+// for dv = 128 and every row's workgroup is resident at once): group
 // sg sums splits sg, sg+SG, ... of chunk c, four splits' loads in flight at
 // a time, so a row with a hundred splits costs a few memory latencies, not
 // one per split.  One pass: each group keeps its own running max over its
@@ -16,14 +18,14 @@
 namespace attn {
 
 
-template <int CH, typename OutT>
-__global__ __launch_bounds__(256) void splitk_reduce_kernel(ReduceParams p) {
-  constexpr int SG = 256 / CH;
+template <int CH, int SG, typename OutT>
+__global__ __launch_bounds__(CH * SG) void splitk_reduce_kernel(ReduceParams p) {
+  static_assert(CH * SG <= 256 && (CH * SG) % 64 == 0, "block of whole waves, at most 256 threads");
   constexpr int U = 4;                       // splits per group in flight
   __shared__ f32x4 part[SG][CH];
   __shared__ float gm[SG], gl[SG];        // each split group's max and weighted l
   const long row = blockIdx.x;
-  const int t = threadIdx.x, sg = t / CH, c = t % CH, wave = t >> 6, lane = t & 63;
+  const int t = threadIdx.x, sg = t / CH, c = t % CH, lane = t & 63;
 
   int nsplit = p.num_splits;
   long first = row * (long)p.num_splits, step = 1;   // partial index of split 0, and stride
@@ -124,14 +126,27 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(ReduceParams p) {
     p.lse[row] = (M == -INFINITY) ? -INFINITY : M + logf(Lsum);
 }
 
+template <int CH, typename OutT>
+static void launch_ch(const ReduceParams& p, bool few, hipStream_t st) {
+  constexpr int SG_MANY = 256 / CH, SG_FEW = CH >= 32 ? 2 : 4;
+  const dim3 grid((unsigned)p.rows);
+  if (few)
+    splitk_reduce_kernel<CH, SG_FEW, OutT><<<grid, dim3(CH * SG_FEW), 0, st>>>(p);
+  else
+    splitk_reduce_kernel<CH, SG_MANY, OutT><<<grid, dim3(CH * SG_MANY), 0, st>>>(p);
+}
+
 template <typename OutT>
 static hipError_t launch_t(const ReduceParams& p, hipStream_t st) {
-  dim3 grid((unsigned)p.rows), block(256);
+  // a few splits per row: two split groups (U = 4 loads in flight each)
+  // cover up to 8 splits in one round of loads
+  const int splits = p.splits_hint > 0 ? p.splits_hint : p.num_splits;
+  const bool few = splits <= 8;
   switch (p.dv) {
-    case 64: splitk_reduce_kernel<16, OutT><<<grid, block, 0, st>>>(p); break;
-    case 128: splitk_reduce_kernel<32, OutT><<<grid, block, 0, st>>>(p); break;
-    case 256: splitk_reduce_kernel<64, OutT><<<grid, block, 0, st>>>(p); break;
-    case 512: splitk_reduce_kernel<128, OutT><<<grid, block, 0, st>>>(p); break;
+    case 64: launch_ch<16, OutT>(p, few, st); break;
+    case 128: launch_ch<32, OutT>(p, few, st); break;
+    case 256: launch_ch<64, OutT>(p, false, st); break;
+    case 512: launch_ch<128, OutT>(p, false, st); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
