@@ -66,9 +66,9 @@ __device__ __forceinline__ int xcd_head(int x, int Hq) {
   return (x % 8) * (Hq / 8) + x / 8;
 }
 
-template <int DQK, int DV, int RW, int BN, int NST, bool GATED>
-__global__ __launch_bounds__(256) void fwd_kernel(FwdParams p) {
-  constexpr int BM = 4 * RW;
+template <int DQK, int DV, int RW, int BN, int NST, bool GATED, int NWV>
+__global__ __launch_bounds__(64 * NWV) void fwd_kernel(FwdParams p) {
+  constexpr int BM = NWV * RW;
   constexpr int RBW = RW / 16;       // 16-row blocks per wave
   constexpr int KB = BN / 16;        // 16-key blocks per tile
   constexpr int KS = DQK / 32;       // k-steps over d_qk
@@ -78,7 +78,7 @@ __global__ __launch_bounds__(256) void fwd_kernel(FwdParams p) {
   static_assert(NST >= 2 && BN <= 64, "ring of at least two stages; gate copy is one lane per key");
   __shared__ __attribute__((aligned(1024))) uint8_t k_lds[NST][BN * KRB];
   __shared__ __attribute__((aligned(1024))) uint8_t v_lds[NST][BN * VRB];
-  __shared__ __attribute__((aligned(16))) float gk_lds[NST][4][64];   // one copy per wave
+  __shared__ __attribute__((aligned(16))) float gk_lds[NST][NWV][64];   // one copy per wave
 
   const int h = xcd_head(blockIdx.x, p.Hq), n = blockIdx.y;
   const int tile = gridDim.z - 1 - blockIdx.z;
@@ -139,19 +139,20 @@ __global__ __launch_bounds__(256) void fwd_kernel(FwdParams p) {
   // the last row (in range and finite; those keys are masked).  Every wave
   // issues the same number of copies per tile, so the wait for the oldest
   // tile is an exact vmcnt.
-  constexpr int KPW = BN * KRB / 4096, VPW = BN * VRB / 4096;   // blocks per wave
+  constexpr int KPW = BN * KRB / (NWV * 1024), VPW = BN * VRB / (NWV * 1024);   // blocks per wave
   constexpr int LOADS_PER_TILE = KPW + VPW + (GATED ? 1 : 0);
-  static_assert(KPW * 4096 == BN * KRB && VPW * 4096 == BN * VRB, "tile must split into 4 x k 1 KB blocks");
+  static_assert(KPW * NWV * 1024 == BN * KRB && VPW * NWV * 1024 == BN * VRB,
+                "tile must split into NWV x k 1 KB blocks");
   int krow[KPW], koff[KPW], vrow[VPW], voff[VPW];
 #pragma unroll
   for (int j = 0; j < KPW; ++j) {
-    const int o = (wave + 4 * j) * 1024 + lane * 16;
+    const int o = (wave + NWV * j) * 1024 + lane * 16;
     krow[j] = o / KRB;
     koff[j] = (int)(krow[j] * kstride) + ((((o % KRB) >> 4) ^ tile_swz<KRB>(krow[j])) << 4);
   }
 #pragma unroll
   for (int j = 0; j < VPW; ++j) {
-    const int o = (wave + 4 * j) * 1024 + lane * 16;
+    const int o = (wave + NWV * j) * 1024 + lane * 16;
     vrow[j] = o / VRB;
     voff[j] = (int)(vrow[j] * vstride) + ((((o % VRB) >> 4) ^ tile_swz<VRB>(vrow[j])) << 4);
   }
@@ -164,12 +165,12 @@ __global__ __launch_bounds__(256) void fwd_kernel(FwdParams p) {
 #pragma unroll
     for (int j = 0; j < KPW; ++j) {
       const int over = tail ? max(0, j0 + krow[j] - (L - 1)) : 0;
-      dma16(kb, (uint32_t)(koff[j] - over * (int)kstride), kl + (wave + 4 * j) * 1024);
+      dma16(kb, (uint32_t)(koff[j] - over * (int)kstride), kl + (wave + NWV * j) * 1024);
     }
 #pragma unroll
     for (int j = 0; j < VPW; ++j) {
       const int over = tail ? max(0, j0 + vrow[j] - (L - 1)) : 0;
-      dma16(vb, (uint32_t)(voff[j] - over * (int)vstride), vl + (wave + 4 * j) * 1024);
+      dma16(vb, (uint32_t)(voff[j] - over * (int)vstride), vl + (wave + NWV * j) * 1024);
     }
     if constexpr (GATED)
       dma4(g2base, (uint32_t)(min(j0 + lane, L - 1) * 4), lds_addr(&gk_lds[st][wave][0]));
@@ -328,15 +329,15 @@ __global__ __launch_bounds__(256) void fwd_kernel(FwdParams p) {
   }
 }
 
-template <int DQK, int DV, int RW, int BN, int NST>
+template <int DQK, int DV, int RW, int BN, int NST, int NWV = 4>
 static hipError_t launch_cfg(const FwdParams& p, hipStream_t st) {
-  constexpr int BM = 4 * RW;
+  constexpr int BM = NWV * RW;
   const int tiles = (p.max_seqlen + BM - 1) / BM;
-  dim3 grid(p.Hq, p.num_seqs, tiles), block(256);
+  dim3 grid(p.Hq, p.num_seqs, tiles), block(64 * NWV);
   if (p.G2 != nullptr)
-    fwd_kernel<DQK, DV, RW, BN, NST, true><<<grid, block, 0, st>>>(p);
+    fwd_kernel<DQK, DV, RW, BN, NST, true, NWV><<<grid, block, 0, st>>>(p);
   else
-    fwd_kernel<DQK, DV, RW, BN, NST, false><<<grid, block, 0, st>>>(p);
+    fwd_kernel<DQK, DV, RW, BN, NST, false, NWV><<<grid, block, 0, st>>>(p);
   return hipGetLastError();
 }
 
