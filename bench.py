@@ -246,8 +246,8 @@ def main():
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    x = synth.config2(device=dev)
-    d = synth.config3(device=dev)
+    x = synth.varlen_8seq_window1024(device=dev)
+    d = synth.decode_64req_fp8(device=dev)
     f_fwd, f_bwd, pairs = prefill_flops(x)
     dec_bytes = decode_bytes(d)
     print(f"[bench] prefill T={x.total_tokens} pairs={pairs} fwd={f_fwd:.3e} bwd={f_bwd:.3e} flop; "
@@ -357,7 +357,7 @@ def main():
     if args.extra:
         extra = {}
         for kvd, tag in ((synth.KV_BF16, "bf16"), (synth.KV_FP8_E4M3FN, "fp8")):
-            d4 = synth.config4(kv_dtype=kvd, device=dev)
+            d4 = synth.verify_3x4_227k(kv_dtype=kvd, device=dev)
             mlen4 = d4.max_seq_len
             f = lambda: A.attn_decode_paged(d4.q, d4.cu_seqlens_q, 4, d4.k_cache, d4.v_cache, kvd,
                                             d4.k_scale, d4.v_scale, d4.block_table, d4.seq_lens,
@@ -371,8 +371,8 @@ def main():
             u = t4.mean_us("v")
             extra[f"verify_{tag}"] = {"us_per_layer": u, "GBps": decode_bytes(d4) / (u * 1e-6) / 1e9}
             del d4
-        # decode with sink, 4096-token window and log gate on the config-3 cache
-        df = synth.config3(device=dev, with_sink=True, window=4096, with_gate=True)
+        # decode with sink, 4096-token window and log gate on the 64-request decode cache
+        df = synth.decode_64req_fp8(device=dev, with_sink=True, window=4096, with_gate=True)
         dmax = df.max_seq_len
         ff = lambda: A.attn_decode_paged(df.q, df.cu_seqlens_q, 1, df.k_cache, df.v_cache, df.kv_dtype,
                                          df.k_scale, df.v_scale, df.block_table, df.seq_lens, dmax, df.scale,
@@ -423,7 +423,7 @@ def main():
                                       "us": up, "tflops": pfl / (up * 1e-6) / 1e12,
                                       "frac_of_bf16_mfma_peak": pfl / (up * 1e-6) / 1e12 / MFMA_BF16_PEAK_TFLOPS}
         del dp
-        x5 = synth.config5(device=dev)
+        x5 = synth.varlen_4x8192_wide_heads(device=dev)
         f5f, f5b, _ = prefill_flops(x5)
         o5, l5 = A.attn_fwd_varlen(x5.q, x5.k, x5.v, x5.cu_seqlens, x5.max_seqlen, x5.scale, 0,
                                    x5.sink, x5.g)

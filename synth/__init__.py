@@ -102,7 +102,7 @@ def prefill_inputs(seqlens, Hq, Hkv, d_qk, d_v, *, seed, window=0,
                          sink, g, name)
 
 
-def config1(device="cpu") -> PrefillInputs:
+def dense_128_gqa4(device="cpu") -> PrefillInputs:
     """Dense causal fwd+bwd: one sequence of 128, 4 query heads over 1 KV head,
     head dim 64, sink per head, scale 1/8; no gate, no window."""
     return prefill_inputs([128], 4, 1, 64, 64, seed=1, window=0, with_sink=True,
@@ -110,20 +110,20 @@ def config1(device="cpu") -> PrefillInputs:
                           name="dense-128-gqa4-d64-sink")
 
 
-def config2_seqlens():
+def varlen_8seq_lengths():
     return [int(x) for x in np.random.default_rng(2).integers(256, 4097, 8)]
 
 
-def config2(device="cpu") -> PrefillInputs:
+def varlen_8seq_window1024(device="cpu") -> PrefillInputs:
     """Packed varlen causal prefill: 8 sequences of length U[256, 4096]
     (seed 2), 32 query / 8 KV heads, head dim 128, window 1024, sink and
     log gates."""
-    return prefill_inputs(config2_seqlens(), 32, 8, 128, 128, seed=2, window=1024,
+    return prefill_inputs(varlen_8seq_lengths(), 32, 8, 128, 128, seed=2, window=1024,
                           with_sink=True, with_gate=True, device=device,
                           name="varlen-8seq-h32kv8-d128-w1024-sink-gate")
 
 
-def config5(device="cpu") -> PrefillInputs:
+def varlen_4x8192_wide_heads(device="cpu") -> PrefillInputs:
     """Packed varlen fwd+bwd with large heads: 4 x 8192 tokens, 16 query /
     4 KV heads, d_qk 256, d_v 512, sinks and log gates, no window."""
     return prefill_inputs([8192] * 4, 16, 4, 256, 512, seed=5, window=0,
@@ -280,28 +280,28 @@ def decode_inputs(seq_lens, q_lens, Hq, Hkv, D, B, *, kv_dtype, seed,
                         sink, int(window), g_cache, bool(per_tensor and kv_dtype == KV_FP8_E4M3FN))
 
 
-def config3_seq_lens():
+def decode_64req_lengths():
     return [int(x) for x in np.random.default_rng(3).integers(1, 32769, 64)]
 
 
-def config3(device="cpu", **kw) -> DecodeInputs:
+def decode_64req_fp8(device="cpu", **kw) -> DecodeInputs:
     """Paged single-query decode: 64 requests with contexts U[1, 32768]
     (seed 3), 64 query / 4 KV heads, D 128, page 16, per-token fp8."""
-    L = config3_seq_lens()
+    L = decode_64req_lengths()
     return decode_inputs(L, [1] * len(L), 64, 4, 128, 16,
                          kv_dtype=KV_FP8_E4M3FN, seed=3, device=device,
                          name="decode-64req-ctx1-32768-h64kv4-d128-p16-fp8", **kw)
 
 
-CONFIG4_SEQ_LENS = [226_944 + 1, 226_944 + 2, 226_944 + 4]
+VERIFY_227K_SEQ_LENS = [226_944 + 1, 226_944 + 2, 226_944 + 4]
 
 
-def config4(kv_dtype=KV_FP8_E4M3FN, device="cpu", **kw) -> DecodeInputs:
+def verify_3x4_227k(kv_dtype=KV_FP8_E4M3FN, device="cpu", **kw) -> DecodeInputs:
     """Short-query verify: 3 requests x 4 query tokens over ~227K-token
     contexts ending 1, 2 and 4 tokens into the last 128-token page; 64 query /
     4 KV heads, D 128; bf16 or per-token fp8 KV (token magnitudes N(0,1))."""
     tag = "fp8" if kv_dtype == KV_FP8_E4M3FN else "bf16"
-    return decode_inputs(CONFIG4_SEQ_LENS, [4, 4, 4], 64, 4, 128, 128,
+    return decode_inputs(VERIFY_227K_SEQ_LENS, [4, 4, 4], 64, 4, 128, 128,
                          kv_dtype=kv_dtype, seed=4, spread=1.0, device=device,
                          name=f"verify-3x4q-ctx227k-h64kv4-d128-p128-{tag}", **kw)
 

@@ -51,9 +51,9 @@ def _run_prefill(A, x):
     return o, lse, grads
 
 
-def test_config1_dense_full(A):
-    _say("[case] config 1 full")
-    x = synth.config1(device=DEV)
+def test_dense_128_full(A):
+    _say("[case] dense 128 tokens gqa4 d64 full")
+    x = synth.dense_128_gqa4(device=DEV)
     o, lse, (dq, dk, dv, ds, dg) = _run_prefill(A, x)
     ro, rl = oracle.forward(x.q, x.k, x.v, x.cu_seqlens, x.scale, x.window, x.sink, x.g)
     rq, rk, rv, rs, _ = oracle.backward(x.q, x.k, x.v, x.do, x.cu_seqlens, x.scale, x.window, x.sink, x.g)
@@ -65,9 +65,9 @@ def test_config1_dense_full(A):
     assert np.max(np.abs(_np(lse) - rl)) < 1e-3
 
 
-def test_config2_varlen_window_full_forward_sampled_backward(A):
-    _say("[case] config 2")
-    x = synth.config2(device=DEV)
+def test_varlen_8seq_window_full_forward_sampled_backward(A):
+    _say("[case] varlen 8 seqs window 1024 sink gate")
+    x = synth.varlen_8seq_window1024(device=DEV)
     o, lse, (dq, dk, dv, ds, dg) = _run_prefill(A, x)
     ro, rl = oracle.forward(x.q, x.k, x.v, x.cu_seqlens, x.scale, x.window, x.sink, x.g)
     e_o = rel_rms(_np(o), ro)
@@ -87,9 +87,9 @@ def test_config2_varlen_window_full_forward_sampled_backward(A):
     assert max(errs.values()) <= TOL
 
 
-def test_config3_decode_sampled_requests(A):
-    _say("[case] config 3")
-    d = synth.config3(device=DEV)
+def test_decode_64req_sampled_requests(A):
+    _say("[case] decode 64 requests fp8 page 16")
+    d = synth.decode_64req_fp8(device=DEV)
     out, lse = A.attn_decode_paged(d.q, d.cu_seqlens_q, d.max_seqlen_q, d.k_cache, d.v_cache, d.kv_dtype,
                                    d.k_scale, d.v_scale, d.block_table, d.seq_lens, d.max_seq_len,
                                    d.scale, return_lse=True)
@@ -114,9 +114,9 @@ def test_config3_decode_sampled_requests(A):
 
 
 @pytest.mark.parametrize("kv", [synth.KV_BF16, synth.KV_FP8_E4M3FN], ids=["bf16", "fp8"])
-def test_config4_verify_227k(A, kv):
-    _say(f"[case] config 4 {kv}")
-    d = synth.config4(kv_dtype=kv, device=DEV)
+def test_verify_3x4_227k(A, kv):
+    _say(f"[case] verify 3x4 tokens 227K context {kv}")
+    d = synth.verify_3x4_227k(kv_dtype=kv, device=DEV)
     out, lse = A.attn_decode_paged(d.q, d.cu_seqlens_q, 4, d.k_cache, d.v_cache, kv, d.k_scale, d.v_scale,
                                    d.block_table, d.seq_lens, d.max_seq_len, d.scale, return_lse=True)
     torch.cuda.synchronize()
@@ -132,9 +132,9 @@ def test_config4_verify_227k(A, kv):
     assert np.max(np.abs(_np(lse) - rl)) < 1e-3
 
 
-def test_config5_large_heads_sampled(A):
-    _say("[case] config 5")
-    x = synth.config5(device=DEV)
+def test_varlen_wide_heads_sampled(A):
+    _say("[case] varlen 4x8192 d_qk 256 d_v 512")
+    x = synth.varlen_4x8192_wide_heads(device=DEV)
     o, lse, (dq, dk, dv, ds, dg) = _run_prefill(A, x)
     cu = x.cu_seqlens.cpu().numpy()
     rng = np.random.default_rng(5)
