@@ -41,7 +41,7 @@ def _np(t):
 # split-K reduce
 # ----------------------------------------------------------------------------
 @pytest.mark.parametrize("dv", [64, 128, 512])
-@pytest.mark.parametrize("S", [1, 3, 17])
+@pytest.mark.parametrize("S", [1, 3, 8, 17])
 def test_splitk_reduce_random_partials(A, dv, S):
     _say(f"[case] splitk_reduce dv={dv} S={S}")
     acc, m, l = synth.partials_inputs(301, S, dv, seed=S * 7 + dv, device=DEV)
