@@ -35,9 +35,8 @@ namespace attn {
 // Forward kernel
 // ---------------------------------------------------------------------------
 // Row max of a tile held as sc[kb][rb][i] (keys kb*16 + 4g + i), and a sum
-// of per-block partials, both as trees: independent steps instead of one
-// dependent chain per row (the softmax sits between MFMA phases, so its
-// latency counts).  The summation order is fixed.
+// of per-block partials, both as trees (independent steps instead of one
+// dependent chain per row).  The summation order is fixed.
 template <int KB, int RBW>
 __device__ __forceinline__ float tile_row_max(const f32x4 (&sc)[KB][RBW], int rb) {
   float m[KB];
