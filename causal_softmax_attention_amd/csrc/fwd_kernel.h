@@ -73,6 +73,7 @@ __global__ __launch_bounds__(64 * NWV) void fwd_kernel(FwdParams p) {
   constexpr int KS = DQK / 32;       // k-steps over d_qk
   constexpr int DB = DV / 16;        // 16-wide output column blocks
   constexpr int KRB = DQK * 2, VRB = DV * 2;   // bytes per K / V row
+  constexpr bool PIPE = DQK <= 128 && DV <= 128;   // operand reads one step ahead
   static_assert(KB % 2 == 0, "PV consumes keys in pairs of 16-key blocks");
   static_assert(NST >= 2 && BN <= 64, "ring of at least two stages; gate copy is one lane per key");
   __shared__ __attribute__((aligned(1024))) uint8_t k_lds[NST][BN * KRB];
@@ -222,16 +223,58 @@ __global__ __launch_bounds__(64 * NWV) void fwd_kernel(FwdParams p) {
       }
       const float* gkl = gk_lds[st][wave];
       // ---- S^T = K Q^T ----
+      // Head dims up to 128 (PIPE): operand reads run one step ahead, the K
+      // fragments of key block kb+1 read while block kb's MFMAs run, so the
+      // LDS latency hides behind a block of MFMAs instead of stalling every
+      // pair (the scheduling fences keep that order; measured ~2 % on the
+      // 8-sequence window-1024 workload).  Wider heads keep the plain order:
+      // the extra fragments would cost them occupancy.
       f32x4 sc[KB][RBW];
+      constexpr int VG = DB < 4 ? DB : 4;           // output blocks per PV group
+      constexpr int NGV = (KB / 2) * (DB / VG);     // PV groups per tile
+      bf16x8 vf[2][VG];
+      if constexpr (PIPE) {
+        bf16x8 kf[2][KS];
 #pragma unroll
-      for (int kb = 0; kb < KB; ++kb) {
+        for (int ks = 0; ks < KS; ++ks) kf[0][ks] = *reinterpret_cast<const LDS_AS bf16x8*>(ka[ks]);
 #pragma unroll
-        for (int rb = 0; rb < RBW; ++rb) sc[kb][rb] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int kb = 0; kb < KB; ++kb) {
+          if (kb + 1 < KB) {
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-          const bf16x8 a = *reinterpret_cast<const LDS_AS bf16x8*>(ka[ks] + kb * 16 * KRB);
+            for (int ks = 0; ks < KS; ++ks)
+              kf[(kb + 1) & 1][ks] = *reinterpret_cast<const LDS_AS bf16x8*>(ka[ks] + (kb + 1) * 16 * KRB);
+          }
+          __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-          for (int rb = 0; rb < RBW; ++rb) sc[kb][rb] = mfma16x16x32(a, qop[rb][ks], sc[kb][rb]);
+          for (int rb = 0; rb < RBW; ++rb) sc[kb][rb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+            for (int rb = 0; rb < RBW; ++rb) sc[kb][rb] = mfma16x16x32(kf[kb & 1][ks], qop[rb][ks], sc[kb][rb]);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        // V^T addresses, and the first group of V^T fragments read now so
+        // that their latency hides behind the softmax
+#pragma unroll
+        for (int db = 0; db < DB; ++db) {
+          uint32_t a = vst + v_lane[db];
+          asm volatile("" : "+v"(a));
+          va[db] = (const LDS_AS uint8_t*)a;
+        }
+#pragma unroll
+        for (int j = 0; j < VG; ++j) vf[0][j] = concat(lds_tr16(va[j]), lds_tr16(va[j] + 16 * VRB));
+        __builtin_amdgcn_sched_barrier(0);
+      } else {
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) {
+#pragma unroll
+          for (int rb = 0; rb < RBW; ++rb) sc[kb][rb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int ks = 0; ks < KS; ++ks) {
+            const bf16x8 a = *reinterpret_cast<const LDS_AS bf16x8*>(ka[ks] + kb * 16 * KRB);
+#pragma unroll
+            for (int rb = 0; rb < RBW; ++rb) sc[kb][rb] = mfma16x16x32(a, qop[rb][ks], sc[kb][rb]);
+          }
         }
       }
       // ---- gated: y = s*c - gk (base 2, without the row's gate term);
@@ -292,20 +335,44 @@ __global__ __launch_bounds__(64 * NWV) void fwd_kernel(FwdParams p) {
         l_run[rb] += xgroup_sum(rs);   // fp32 row sum: lse feeds the backward
       }
       // ---- O^T += V^T P^T, 32 keys per MFMA ----
+      if constexpr (PIPE) {
+        // in groups of VG output blocks; group n+1's fragments are read
+        // while group n's MFMAs run
 #pragma unroll
-      for (int db = 0; db < DB; ++db) {
-        uint32_t a = vst + v_lane[db];
-        asm volatile("" : "+v"(a));
-        va[db] = (const LDS_AS uint8_t*)a;
-      }
+        for (int n = 0; n < NGV; ++n) {
+          const int kp = n / (DB / VG), db0 = (n % (DB / VG)) * VG;
+          if (n + 1 < NGV) {
+            const int kp1 = (n + 1) / (DB / VG), db1 = ((n + 1) % (DB / VG)) * VG;
 #pragma unroll
-      for (int kp = 0; kp < KB / 2; ++kp) {
+            for (int j = 0; j < VG; ++j)
+              vf[(n + 1) & 1][j] = concat(lds_tr16(va[db1 + j] + kp1 * 32 * VRB),
+                                          lds_tr16(va[db1 + j] + (kp1 * 32 + 16) * VRB));
+          }
+          __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+          for (int j = 0; j < VG; ++j)
+#pragma unroll
+            for (int rb = 0; rb < RBW; ++rb)
+              oacc[rb][db0 + j] =
+                  mfma16x16x32(vf[n & 1][j], concat(pb[2 * kp][rb], pb[2 * kp + 1][rb]), oacc[rb][db0 + j]);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      } else {
 #pragma unroll
         for (int db = 0; db < DB; ++db) {
-          const bf16x8 a = concat(lds_tr16(va[db] + kp * 32 * VRB), lds_tr16(va[db] + (kp * 32 + 16) * VRB));
+          uint32_t a = vst + v_lane[db];
+          asm volatile("" : "+v"(a));
+          va[db] = (const LDS_AS uint8_t*)a;
+        }
 #pragma unroll
-          for (int rb = 0; rb < RBW; ++rb)
-            oacc[rb][db] = mfma16x16x32(a, concat(pb[2 * kp][rb], pb[2 * kp + 1][rb]), oacc[rb][db]);
+        for (int kp = 0; kp < KB / 2; ++kp) {
+#pragma unroll
+          for (int db = 0; db < DB; ++db) {
+            const bf16x8 a = concat(lds_tr16(va[db] + kp * 32 * VRB), lds_tr16(va[db] + (kp * 32 + 16) * VRB));
+#pragma unroll
+            for (int rb = 0; rb < RBW; ++rb)
+              oacc[rb][db] = mfma16x16x32(a, concat(pb[2 * kp][rb], pb[2 * kp + 1][rb]), oacc[rb][db]);
+          }
         }
       }
     }
