@@ -121,6 +121,10 @@ class Timer:
         ev = self.t.get(name, [])
         return 1e3 * sum(s.elapsed_time(e) for s, e in ev) / max(1, len(ev))
 
+    def median_us(self, name):
+        ev = self.t.get(name, [])
+        return 1e3 * float(np.median([s.elapsed_time(e) for s, e in ev])) if ev else 0.0
+
 
 def cpu_oracle_baseline(x, budget_s=12.0):
     """The float64 oracle, as it stands, on a bounded sample of the prefill
@@ -339,6 +343,7 @@ def main():
             "global_batch": len(x.seqlens), "seq_len": x.max_seqlen, "parallelism": "single-gpu",
         },
         "prefill": {"fwd_us": us["fwd"], "bwd_us": us["bwd"],
+                    "fwd_us_median": tm.median_us("fwd"), "bwd_us_median": tm.median_us("bwd"),
                     "bwd_path": "two-pass (deterministic)",
                     "bwd_fused_dq_us": tf.mean_us("bwd_fused"),
                     "bwd_fused_dq_tflops": f_bwd / (tf.mean_us("bwd_fused") * 1e-6) / 1e12,
@@ -347,7 +352,8 @@ def main():
                     "fwd_frac_of_mfma_peak": tf_fwd / MFMA_BF16_PEAK_TFLOPS,
                     "fwdbwd_frac_of_mfma_peak": tf_fb / MFMA_BF16_PEAK_TFLOPS,
                     "flops_fwd": f_fwd, "flops_bwd": f_bwd},
-        "decode": {"us_per_layer": us["decode"], "GBps": gbps, "frac_of_hbm_peak": gbps / HBM_PEAK_GBPS,
+        "decode": {"us_per_layer": us["decode"], "us_per_layer_median": tm.median_us("decode"),
+                   "GBps": gbps, "frac_of_hbm_peak": gbps / HBM_PEAK_GBPS,
                    "algorithmic_bytes": dec_bytes, "graph_us_per_layer": dec_graph_us,
                    "graph_GBps": dec_bytes / (dec_graph_us * 1e-6) / 1e9},
         "roofline": roof,
