@@ -42,7 +42,9 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(BwdParams p) {
   if (blockIdx.x == 0 && p.dsink_acc != nullptr)
     for (int h = t; h < p.Hq; h += 256) p.dsink_acc[h] = 0.f;
   if (row >= (long)p.T * p.Hq) return;
-  const bf16x8 o = *reinterpret_cast<const bf16x8*>(reinterpret_cast<const bf16*>(p.o) + row * DV + 8 * sub);
+  // O is read once, here (non-temporal); dO is read again by both passes
+  const bf16x8 o = __builtin_bit_cast(bf16x8, __builtin_nontemporal_load(
+      reinterpret_cast<const i32x4*>(reinterpret_cast<const bf16*>(p.o) + row * DV + 8 * sub)));
   const bf16x8 d = *reinterpret_cast<const bf16x8*>(reinterpret_cast<const bf16*>(p.dO) + row * DV + 8 * sub);
   float s = 0.f;
 #pragma unroll
