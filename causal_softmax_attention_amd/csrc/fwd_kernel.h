@@ -58,6 +58,10 @@ __device__ __forceinline__ float tree_sum(float (&v)[N]) {
   return v[0];
 }
 
+#ifndef FWD_WAVE_SKIP
+#define FWD_WAVE_SKIP 1
+#endif
+
 // Blocks are dispatched round-robin over the 8 XCDs (each with its own L2);
 // map block x so that the query heads of one KV group land on one XCD.
 __device__ __forceinline__ int xcd_head(int x, int Hq) {
@@ -191,9 +195,8 @@ __global__ __launch_bounds__(64 * NWV) void fwd_kernel(FwdParams p) {
   for (int s = 0; s < NST - 1; ++s)
     if (t_begin + s < t_end) fetch(s, (t_begin + s) * BN);
 
-  for (int t = t_begin; t < t_end; ++t) {
-    const int j0 = t * BN;
-    const int st = (t - t_begin) % NST;
+  // Every wave takes part in every tile's wait, barrier and copies ...
+  auto sync = [&](int t) {
     // wait for tile t: the tiles issued after it that may still be in flight
     const int later = min(NST - 2, t_end - 1 - t);
     if (later <= 0) wait_vm<0>();
@@ -201,11 +204,23 @@ __global__ __launch_bounds__(64 * NWV) void fwd_kernel(FwdParams p) {
     else wait_vm<2 * LOADS_PER_TILE>();
     lds_barrier();   // tile t visible to all waves; stage of tile t-1 free
     if (t + NST - 1 < t_end) fetch((t - t_begin + NST - 1) % NST, (t + NST - 1) * BN);
-
-    // No branch around the math: a tile that is wholly masked for this
-    // wave's rows goes through the masked path and contributes zeros.  (A
-    // branch here makes the compiler shuttle every accumulator between
-    // AGPRs and VGPRs on each iteration.)
+  };
+  // ... but computes only the tiles its rows can see: [tw_lo, tw_hi), keys
+  // from the first row's window start to the last row.  The three loops
+  // keep the tile body free of a branch (a branch around it costs the
+  // kernel registers and occupancy).  Inside the range, a tile that
+  // crosses the diagonal, the window edge or the end is masked per element.
+  int tw_lo = t_begin, tw_hi = t_end;
+  if (FWD_WAVE_SKIP) {
+    if (W > 0 && r0 - W + 1 > 0) tw_lo = max(t_begin, (r0 - W + 1) / BN);
+    tw_hi = r_last >= r0 ? min(t_end, r_last / BN + 1) : t_begin;
+    tw_lo = min(tw_lo, tw_hi);
+  }
+  for (int t = t_begin; t < tw_lo; ++t) sync(t);
+  for (int t = tw_lo; t < tw_hi; ++t) {
+    const int j0 = t * BN;
+    const int st = (t - t_begin) % NST;
+    sync(t);
     {
       const bool need_mask = (j0 + BN - 1 > r0) || (W > 0 && r_last - j0 >= W) || (j0 + BN > L) ||
                              (r_last < r0 + RW - 1);
@@ -377,6 +392,7 @@ __global__ __launch_bounds__(64 * NWV) void fwd_kernel(FwdParams p) {
       }
     }
   }
+  for (int t = tw_hi; t < t_end; ++t) sync(t);
 
   // ---- finalize: O = acc / l, lse = ln 2 * (m + gq + log2 l) ----
 #pragma unroll
