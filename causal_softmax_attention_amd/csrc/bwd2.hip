@@ -20,6 +20,9 @@
 #include "common.h"
 #include "kernels.h"
 
+#ifndef BWD_WAVE_SKIP
+#define BWD_WAVE_SKIP 1
+#endif
 #ifndef BWD_KW_SMALL
 #define BWD_KW_SMALL 16
 #endif
@@ -413,16 +416,27 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(BwdParams p) {
 
   if (t_begin < t_end) fetch(0, t_begin * BN);
 
-  for (int t = t_begin; t < t_end; ++t) {
-    const int j0 = t * BN;
-    const int buf = (t - t_begin) & 1;
+  // Every wave takes part in every tile's wait, barrier and copies, but
+  // computes only the key tiles its rows can see (from the first row's
+  // window start to the last row); three loops keep the tile body free of
+  // a branch.  Inside that range, masked pairs contribute zeros; rows past
+  // the end are masked too, their lse is not defined.
+  auto sync = [&](int t) {
     wait_vm<0>();     // this wave's copies of tile t have landed
     lds_barrier();    // ... and everyone's; the other stage is free again
-    if (t + 1 < t_end) fetch(buf ^ 1, j0 + BN);
-
-    // no branch around the math (see the forward kernel): wholly masked
-    // tiles contribute zeros; rows past the end are masked too, their lse
-    // is not defined
+    if (t + 1 < t_end) fetch(((t - t_begin) & 1) ^ 1, t * BN + BN);
+  };
+  int tw_lo = t_begin, tw_hi = t_end;
+  if (BWD_WAVE_SKIP) {
+    if (W > 0 && r0 - W + 1 > 0) tw_lo = max(t_begin, (r0 - W + 1) / BN);
+    tw_hi = r_last >= r0 ? min(t_end, r_last / BN + 1) : t_begin;
+    tw_lo = min(tw_lo, tw_hi);
+  }
+  for (int t = t_begin; t < tw_lo; ++t) sync(t);
+  for (int t = tw_lo; t < tw_hi; ++t) {
+    const int j0 = t * BN;
+    const int buf = (t - t_begin) & 1;
+    sync(t);
     {
       const bool need_mask = (j0 + BN - 1 > r0) || (W > 0 && r_last - j0 >= W) || (j0 + BN > L) ||
                              (r_last < r0 + RW - 1);
@@ -509,6 +523,7 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(BwdParams p) {
       }
     }
   }
+  for (int t = tw_hi; t < t_end; ++t) sync(t);
 
   const float sink2 = p.sink ? p.sink[h] * kLog2e : 0.f;
 #pragma unroll
