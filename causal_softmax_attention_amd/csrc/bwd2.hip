@@ -167,8 +167,7 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdParams p) {
     for (int ks = 0; ks < KSV; ++ks) asm volatile("" :: "v"(vop[kb][ks]));
   }
 
-  int hg = 0, qt = 0;       // this iteration
-  int f_hg = 0, f_qt = 0;   // the next one to fetch
+  int f_hg = 0, f_qt = 0;   // the next tile to fetch
 #pragma unroll
   for (int s0 = 0; s0 < NSQ - 1; ++s0)
     if (s0 < n_it) {
@@ -178,118 +177,139 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdParams p) {
   float colsum[KBW];
 #pragma unroll
   for (int kb = 0; kb < KBW; ++kb) colsum[kb] = 0.f;
-  int buf = 0;
-  for (int it = 0; it < n_it; ++it, advance(hg, qt), buf = (buf + 1 == NSQ ? 0 : buf + 1)) {
+  // Every wave takes part in every tile's wait, barrier and copies (tile
+  // `it` of the flattened (head, query tile) order lives in stage it % NSQ),
+  // but computes only the query tiles its keys can see: per head, rows from
+  // its first key to its last key's window end.  Three loops per head keep
+  // the tile body free of a branch.
+  auto sync = [&](int it) {
     // this wave's copies of tile it have landed (the later tiles in flight
     // each add at least LPT newer copies) ...
     if (NSQ == 3 && it + 1 < n_it) wait_vm<LPT>(); else wait_vm<0>();
     lds_barrier();   // ... and everyone's; the stage of tile it-1 is free again
     if (it + NSQ - 1 < n_it) {
-      fetch(f_hg, f_qt, buf == 0 ? NSQ - 1 : buf - 1);
+      const int b = it % NSQ;
+      fetch(f_hg, f_qt, b == 0 ? NSQ - 1 : b - 1);
       advance(f_hg, f_qt);
     }
+  };
+  int qt_lo = 0, qt_hi = nqt;
+  if (BWD_WAVE_SKIP) {
+    qt_lo = min(nqt, (jw - j0) / RQ);                                   // rows before the first key
+    if (W > 0) qt_hi = min(nqt, (jw - j0 + KW - 1 + W - 1) / RQ + 1);   // rows past the last key's window
+    if (jw >= L) qt_hi = qt_lo;                                         // no keys
+    qt_hi = max(qt_hi, qt_lo);
+  }
+  int it = 0;
+  for (int hg = 0; hg < grp; ++hg) {
+    for (int qt = 0; qt < qt_lo; ++qt, ++it) sync(it);
+    for (int qt = qt_lo; qt < qt_hi; ++qt, ++it) {
+      sync(it);
+      const int buf = it % NSQ;
+      const int h = kvh * grp + hg;
+      const int i0 = j0 + qt * RQ;
+      float gk[KBW];
+#pragma unroll
+      for (int kb = 0; kb < KBW; ++kb) gk[kb] = GATED ? gk_lds[buf][wave][kb * 16 + li] : 0.f;
 
-    const int h = kvh * grp + hg;
-    const int i0 = j0 + qt * RQ;
-    float gk[KBW];
-#pragma unroll
-    for (int kb = 0; kb < KBW; ++kb) gk[kb] = GATED ? gk_lds[buf][wave][kb * 16 + li] : 0.f;
-
-    // no branch around the math (see the forward kernel): masked pairs give
-    // P = dS = 0; the per-element mask runs only on tiles that need it
-    const bool need_mask = (i0 < jw + KW - 1) || (W > 0 && i0 + RQ - 1 - jw >= W) || (i0 + RQ > L) ||
-                           (jw + KW > L);
-    {
-      const uint8_t* ql = q_lds[buf];
-      const uint8_t* ol = do_lds[buf];
-      const float* rowl = row_lds[buf][0];
-      const float* dell = row_lds[buf][1];
-      // ---- S = Q K^T, dP = dO V^T: C lane (key li, rows rb*16+4g+i) ----
-      f32x4 s[KBW][2], dp[KBW][2];
-#pragma unroll
-      for (int rb = 0; rb < 2; ++rb) {
-#pragma unroll
-        for (int kb = 0; kb < KBW; ++kb) {
-          s[kb][rb] = f32x4{0.f, 0.f, 0.f, 0.f};
-          dp[kb][rb] = f32x4{0.f, 0.f, 0.f, 0.f};
-        }
-#pragma unroll
-        for (int ks = 0; ks < KSQ; ++ks) {
-          const bf16x8 a = *reinterpret_cast<const bf16x8*>(ql + tile_off<QRB>(rb * 16 + li, 64 * ks + 16 * g));
-#pragma unroll
-          for (int kb = 0; kb < KBW; ++kb) s[kb][rb] = mfma16x16x32(a, kop[kb][ks], s[kb][rb]);
-        }
-#pragma unroll
-        for (int ks = 0; ks < KSV; ++ks) {
-          const bf16x8 a = *reinterpret_cast<const bf16x8*>(ol + tile_off<ORB>(rb * 16 + li, 64 * ks + 16 * g));
-#pragma unroll
-          for (int kb = 0; kb < KBW; ++kb) dp[kb][rb] = mfma16x16x32(a, vop[kb][ks], dp[kb][rb]);
-        }
-      }
-      // ---- P (masked only on tiles that need it) and dS ----
-      f32x4 pv[KBW][2];
-#pragma unroll
-      for (int rb = 0; rb < 2; ++rb) {
-        // row term in base 2: gate of the row minus lse
-        const f32x4 rowt = *reinterpret_cast<const f32x4*>(rowl + rb * 16 + 4 * g);
-#pragma unroll
-        for (int kb = 0; kb < KBW; ++kb)
-#pragma unroll
-          for (int i = 0; i < 4; ++i)
-            pv[kb][rb][i] = fast_exp2(__builtin_fmaf(s[kb][rb][i], p.scale_log2, rowt[i] - gk[kb]));
-      }
-      if (need_mask) {
-#pragma unroll
-        for (int kb = 0; kb < KBW; ++kb) {
-          const int key = jw + kb * 16 + li;
-#pragma unroll
-          for (int rb = 0; rb < 2; ++rb)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              const int row = i0 + rb * 16 + 4 * g + i;
-              const bool vis = key < L && row < L && key <= row && (W <= 0 || row - key < W);
-              pv[kb][rb][i] = vis ? pv[kb][rb][i] : 0.f;
-            }
-        }
-      }
-      bf16x8 pop[KBW], dsop[KBW];
-#pragma unroll
-      for (int kb = 0; kb < KBW; ++kb) {
-        f32x4 dsv[2];
+      // masked pairs give P = dS = 0; the per-element mask runs only on
+      // tiles that need it
+      const bool need_mask = (i0 < jw + KW - 1) || (W > 0 && i0 + RQ - 1 - jw >= W) || (i0 + RQ > L) ||
+                             (jw + KW > L);
+      {
+        const uint8_t* ql = q_lds[buf];
+        const uint8_t* ol = do_lds[buf];
+        const float* rowl = row_lds[buf][0];
+        const float* dell = row_lds[buf][1];
+        // ---- S = Q K^T, dP = dO V^T: C lane (key li, rows rb*16+4g+i) ----
+        f32x4 s[KBW][2], dp[KBW][2];
 #pragma unroll
         for (int rb = 0; rb < 2; ++rb) {
-          const f32x4 del4 = *reinterpret_cast<const f32x4*>(dell + rb * 16 + 4 * g);
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const float d = pv[kb][rb][i] * (dp[kb][rb][i] - del4[i]);
-            colsum[kb] += d;
-            dsv[rb][i] = d;
+          for (int kb = 0; kb < KBW; ++kb) {
+            s[kb][rb] = f32x4{0.f, 0.f, 0.f, 0.f};
+            dp[kb][rb] = f32x4{0.f, 0.f, 0.f, 0.f};
+          }
+#pragma unroll
+          for (int ks = 0; ks < KSQ; ++ks) {
+            const bf16x8 a = *reinterpret_cast<const bf16x8*>(ql + tile_off<QRB>(rb * 16 + li, 64 * ks + 16 * g));
+#pragma unroll
+            for (int kb = 0; kb < KBW; ++kb) s[kb][rb] = mfma16x16x32(a, kop[kb][ks], s[kb][rb]);
+          }
+#pragma unroll
+          for (int ks = 0; ks < KSV; ++ks) {
+            const bf16x8 a = *reinterpret_cast<const bf16x8*>(ol + tile_off<ORB>(rb * 16 + li, 64 * ks + 16 * g));
+#pragma unroll
+            for (int kb = 0; kb < KBW; ++kb) dp[kb][rb] = mfma16x16x32(a, vop[kb][ks], dp[kb][rb]);
           }
         }
-        pop[kb] = concat(to_bf16x4(pv[kb][0]), to_bf16x4(pv[kb][1]));
-        dsop[kb] = concat(to_bf16x4(dsv[0]), to_bf16x4(dsv[1]));
-      }
-      // ---- dV^T += dO^T P, dK^T += Q^T dS (32 rows per MFMA) ----
-      const int mm = li >> 2, c4 = li & 3;
-      const int r0 = 4 * g + mm, r1 = r0 + 16;
+        // ---- P (masked only on tiles that need it) and dS ----
+        f32x4 pv[KBW][2];
 #pragma unroll
-      for (int db = 0; db < DBV; ++db) {
-        const int b = 32 * db + 8 * c4;
-        const bf16x8 a = concat(lds_read_tr16(reinterpret_cast<const bf16*>(ol + tile_off<ORB>(r0, b))),
-                                lds_read_tr16(reinterpret_cast<const bf16*>(ol + tile_off<ORB>(r1, b))));
+        for (int rb = 0; rb < 2; ++rb) {
+          // row term in base 2: gate of the row minus lse
+          const f32x4 rowt = *reinterpret_cast<const f32x4*>(rowl + rb * 16 + 4 * g);
 #pragma unroll
-        for (int kb = 0; kb < KBW; ++kb) dv_acc[kb][db] = mfma16x16x32(a, pop[kb], dv_acc[kb][db]);
-      }
+          for (int kb = 0; kb < KBW; ++kb)
 #pragma unroll
-      for (int db = 0; db < DBQ; ++db) {
-        const int b = 32 * db + 8 * c4;
-        const bf16x8 a = concat(lds_read_tr16(reinterpret_cast<const bf16*>(ql + tile_off<QRB>(r0, b))),
-                                lds_read_tr16(reinterpret_cast<const bf16*>(ql + tile_off<QRB>(r1, b))));
+            for (int i = 0; i < 4; ++i)
+              pv[kb][rb][i] = fast_exp2(__builtin_fmaf(s[kb][rb][i], p.scale_log2, rowt[i] - gk[kb]));
+        }
+        if (need_mask) {
 #pragma unroll
-        for (int kb = 0; kb < KBW; ++kb) dk_acc[kb][db] = mfma16x16x32(a, dsop[kb], dk_acc[kb][db]);
+          for (int kb = 0; kb < KBW; ++kb) {
+            const int key = jw + kb * 16 + li;
+#pragma unroll
+            for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+              for (int i = 0; i < 4; ++i) {
+                const int row = i0 + rb * 16 + 4 * g + i;
+                const bool vis = key < L && row < L && key <= row && (W <= 0 || row - key < W);
+                pv[kb][rb][i] = vis ? pv[kb][rb][i] : 0.f;
+              }
+          }
+        }
+        bf16x8 pop[KBW], dsop[KBW];
+#pragma unroll
+        for (int kb = 0; kb < KBW; ++kb) {
+          f32x4 dsv[2];
+#pragma unroll
+          for (int rb = 0; rb < 2; ++rb) {
+            const f32x4 del4 = *reinterpret_cast<const f32x4*>(dell + rb * 16 + 4 * g);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const float d = pv[kb][rb][i] * (dp[kb][rb][i] - del4[i]);
+              colsum[kb] += d;
+              dsv[rb][i] = d;
+            }
+          }
+          pop[kb] = concat(to_bf16x4(pv[kb][0]), to_bf16x4(pv[kb][1]));
+          dsop[kb] = concat(to_bf16x4(dsv[0]), to_bf16x4(dsv[1]));
+        }
+        // ---- dV^T += dO^T P, dK^T += Q^T dS (32 rows per MFMA) ----
+        const int mm = li >> 2, c4 = li & 3;
+        const int r0 = 4 * g + mm, r1 = r0 + 16;
+#pragma unroll
+        for (int db = 0; db < DBV; ++db) {
+          const int b = 32 * db + 8 * c4;
+          const bf16x8 a = concat(lds_read_tr16(reinterpret_cast<const bf16*>(ol + tile_off<ORB>(r0, b))),
+                                  lds_read_tr16(reinterpret_cast<const bf16*>(ol + tile_off<ORB>(r1, b))));
+#pragma unroll
+          for (int kb = 0; kb < KBW; ++kb) dv_acc[kb][db] = mfma16x16x32(a, pop[kb], dv_acc[kb][db]);
+        }
+#pragma unroll
+        for (int db = 0; db < DBQ; ++db) {
+          const int b = 32 * db + 8 * c4;
+          const bf16x8 a = concat(lds_read_tr16(reinterpret_cast<const bf16*>(ql + tile_off<QRB>(r0, b))),
+                                  lds_read_tr16(reinterpret_cast<const bf16*>(ql + tile_off<QRB>(r1, b))));
+#pragma unroll
+          for (int kb = 0; kb < KBW; ++kb) dk_acc[kb][db] = mfma16x16x32(a, dsop[kb], dk_acc[kb][db]);
+        }
       }
     }
-    if (GATED && qt == nqt - 1) {
+    for (int qt = qt_hi; qt < nqt; ++qt, ++it) sync(it);
+    if (GATED) {
+      const int h = kvh * grp + hg;
 #pragma unroll
       for (int kb = 0; kb < KBW; ++kb) {
         const float cs = xgroup_sum(colsum[kb]);
