@@ -77,7 +77,7 @@ __global__ __launch_bounds__(256) void bwd_fused_kernel(BwdParams p) {
   __shared__ __attribute__((aligned(16))) bf16 ds_lds[4][16 * RQ];
   __shared__ float lse_lds[RQ], delta_lds[RQ], gq_lds[RQ];
 
-  const int kvh = blockIdx.x, n = blockIdx.y, ktile = blockIdx.z;
+  const int kvh = blockIdx.x, n = blockIdx.z, ktile = blockIdx.y;
   const int seq0 = p.cu[n];
   const int L = p.cu[n + 1] - seq0;
   const int j0 = ktile * BNW;
@@ -335,7 +335,7 @@ static hipError_t launch_bwd_t(const BwdParams& p, bool fused, hipStream_t st) {
   if (e != hipSuccess) return e;
   if (fused) {
     const int ktiles = (p.max_seqlen + 63) / 64;
-    bwd_fused_kernel<DQK, DV><<<dim3(p.Hkv, p.num_seqs, ktiles), 256, 0, st>>>(p);
+    bwd_fused_kernel<DQK, DV><<<dim3(p.Hkv, ktiles, p.num_seqs), 256, 0, st>>>(p);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     const long n4 = rows * DQK / 4;

@@ -67,7 +67,7 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdParams p) {
   __shared__ __attribute__((aligned(16))) float row_lds[NSQ][2][64];   // row term, delta (lanes >= RQ repeat)
   __shared__ __attribute__((aligned(16))) float gk_lds[NSQ][4][64];    // per wave: its keys' gate terms
 
-  const int kvh = xcd_remap(blockIdx.x, p.Hkv), n = blockIdx.y, ktile = blockIdx.z;
+  const int kvh = xcd_remap(blockIdx.x, p.Hkv), n = blockIdx.z, ktile = blockIdx.y;
   const int seq0 = p.cu[n];
   const int L = p.cu[n + 1] - seq0;
   const int j0 = ktile * BNW;
@@ -348,8 +348,8 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(BwdParams p) {
   __shared__ __attribute__((aligned(1024))) uint8_t v_lds[2][BN * VRB];
   __shared__ __attribute__((aligned(16))) float gk_lds[2][4][64];   // one copy per wave
 
-  const int h = xcd_remap(blockIdx.x, p.Hq), n = blockIdx.y;
-  const int tile = gridDim.z - 1 - blockIdx.z;
+  const int h = xcd_remap(blockIdx.x, p.Hq), n = blockIdx.z;
+  const int tile = gridDim.y - 1 - blockIdx.y;
   const int seq0 = p.cu[n];
   const int L = p.cu[n + 1] - seq0;
   const int i0 = tile * BM;
@@ -595,13 +595,13 @@ __global__ __launch_bounds__(1024) void sink_reduce_kernel(const float* __restri
 template <int DQK, int DV, int KW, int RW, int BN>
 hipError_t launch_bwd_two_pass_t(const BwdParams& p, hipStream_t st) {
   const int ktiles = (p.max_seqlen + 4 * KW - 1) / (4 * KW);
-  const dim3 gk(p.Hkv, p.num_seqs, ktiles);
+  const dim3 gk(p.Hkv, ktiles, p.num_seqs);   // sequence-major: a sequence's tiles share L2
   if (p.G2) bwd_dkdv_kernel<DQK, DV, KW, true><<<gk, 256, 0, st>>>(p);
   else bwd_dkdv_kernel<DQK, DV, KW, false><<<gk, 256, 0, st>>>(p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int qtiles = (p.max_seqlen + 4 * RW - 1) / (4 * RW);
-  const dim3 gq(p.Hq, p.num_seqs, qtiles);
+  const dim3 gq(p.Hq, qtiles, p.num_seqs);
   if (p.G2) bwd_dq_kernel<DQK, DV, RW, BN, true><<<gq, 256, 0, st>>>(p);
   else bwd_dq_kernel<DQK, DV, RW, BN, false><<<gq, 256, 0, st>>>(p);
   e = hipGetLastError();

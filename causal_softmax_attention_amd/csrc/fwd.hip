@@ -1,21 +1,8 @@
 // Forward entry points: the gate prefix and the head-dim 64 and 128 forward
-// kernels (the kernel itself is in fwd_kernel.h; head dims 256 and 512 are
-// instantiated in fwd_wide.hip, which is built with different register
-// allocation options).
-#include "fwd_kernel.h"
-
-#ifndef FWD_RW_SMALL
-#define FWD_RW_SMALL 32
-#endif
-#ifndef FWD_BN_SMALL
-#define FWD_BN_SMALL 64
-#endif
-#ifndef FWD_NWV
-#define FWD_NWV 4
-#endif
-#ifndef FWD_NST_SMALL
-#define FWD_NST_SMALL 2
-#endif
+// kernels (the kernel itself is in fwd_pipe.h; head dims 256 and 512 use the
+// kernel in fwd_kernel.h, instantiated in fwd_wide.hip, which is built with
+// different register allocation options).
+#include "fwd_pipe.h"
 
 namespace attn {
 
@@ -46,8 +33,8 @@ hipError_t launch_gate_prefix(const float* g, const int32_t* cu, float* G2, int 
 
 hipError_t launch_fwd(const FwdParams& p, int dqk, int dv, hipStream_t st) {
   if (p.num_seqs == 0 || p.T == 0 || p.max_seqlen == 0) return hipSuccess;
-  if (dqk == 64 && dv == 64) return launch_cfg<64, 64, FWD_RW_SMALL, FWD_BN_SMALL, FWD_NST_SMALL>(p, st);
-  if (dqk == 128 && dv == 128) return launch_cfg<128, 128, FWD_RW_SMALL, FWD_BN_SMALL, FWD_NST_SMALL, FWD_NWV>(p, st);
+  if (dqk == 64 && dv == 64) return launch_pipe<64, 64>(p, st);
+  if (dqk == 128 && dv == 128) return launch_pipe<128, 128>(p, st);
   if (dqk == 256) return launch_fwd_wide(p, dqk, dv, st);
   return hipErrorInvalidValue;
 }

@@ -84,8 +84,8 @@ __global__ __launch_bounds__(64 * NWV) void fwd_kernel(FwdParams p) {
   __shared__ __attribute__((aligned(1024))) uint8_t v_lds[NST][BN * VRB];
   __shared__ __attribute__((aligned(16))) float gk_lds[NST][NWV][64];   // one copy per wave
 
-  const int h = xcd_head(blockIdx.x, p.Hq), n = blockIdx.y;
-  const int tile = gridDim.z - 1 - blockIdx.z;
+  const int h = xcd_head(blockIdx.x, p.Hq), n = blockIdx.z;
+  const int tile = gridDim.y - 1 - blockIdx.y;
   const int seq0 = p.cu[n];
   const int L = p.cu[n + 1] - seq0;
   const int i0 = tile * BM;
@@ -415,7 +415,7 @@ template <int DQK, int DV, int RW, int BN, int NST, int NWV = 4>
 static hipError_t launch_cfg(const FwdParams& p, hipStream_t st) {
   constexpr int BM = NWV * RW;
   const int tiles = (p.max_seqlen + BM - 1) / BM;
-  dim3 grid(p.Hq, p.num_seqs, tiles), block(64 * NWV);
+  dim3 grid(p.Hq, tiles, p.num_seqs), block(64 * NWV);   // sequence-major: a sequence's tiles share L2
   if (p.G2 != nullptr)
     fwd_kernel<DQK, DV, RW, BN, NST, true, NWV><<<grid, block, 0, st>>>(p);
   else
