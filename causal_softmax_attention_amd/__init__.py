@@ -23,7 +23,8 @@ from typing import Optional
 
 import torch
 
-__all__ = ["attn_fwd_varlen", "attn_bwd_varlen", "attn_decode_paged", "attn_prefill_paged",
+__all__ = ["attn_fwd_varlen", "attn_bwd_varlen", "attn_decode_paged", "attn_decode_paged_noalloc",
+           "attn_prefill_paged",
            "attn_splitk_reduce", "attn_kv_cache_write_fp8", "attn_fwd_workspace_size",
            "attn_bwd_workspace_size", "attn_decode_workspace_size",
            "attn_prefill_paged_workspace_size",
@@ -68,6 +69,9 @@ _SIGNATURES = {
     "attn_decode_paged_ext": ([_vp, _vp, _c_int, _c_int, _vp, _vp, _c_int, _vp, _vp, _c_int, _vp, _c_int,
                                _vp, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int, ctypes.c_float, _vp,
                                _c_int, _vp, _c_int, _vp, _vp, _vp, ctypes.c_size_t, _vp], _c_int),
+    "attn_decode_paged_noalloc": ([_vp, _vp, _c_int, _c_int, _vp, _vp, _c_int, _vp, _vp, _vp, _c_int,
+                                   _vp, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _c_float,
+                                   _c_int, _vp, _vp, _vp], _c_int),
     "attn_prefill_paged_workspace_size": ([_c_int] * 8, _c_size),
     "attn_prefill_paged": ([_vp, _vp, _c_int, _c_int, _vp, _vp, _c_int, _vp, _vp, _c_int, _vp, _c_int,
                             _vp, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int, ctypes.c_float, _vp,
@@ -312,6 +316,39 @@ def attn_decode_paged(q, cu_seqlens_q, max_seqlen_q, k_cache, v_cache, kv_dtype,
     return _paged(False, q, cu_seqlens_q, max_seqlen_q, k_cache, v_cache, kv_dtype, k_scale, v_scale,
                   block_table, seq_lens, max_seq_len, softmax_scale, kv_split_len, return_lse, out,
                   sink, window, g_cache)
+
+
+def attn_decode_paged_noalloc(q, cu_seqlens_q, max_seqlen_q, k_cache, v_cache, kv_dtype,
+                              k_scale, v_scale, block_table, seq_lens, max_seq_len, out, lse=None,
+                              softmax_scale=None, kv_split_len=0):
+    """attn_decode_paged without a workspace: the split-K partials live in the
+    library's own per-GPU scratch, so neither this call nor the library
+    allocates anything.  The caller passes the outputs: out bf16 [Tq, Hq, D]
+    and optionally lse fp32 [Tq, Hq].  Calls that may overlap on one GPU
+    share that scratch and must be serialised.  Returns out."""
+    dev = q.device
+    _need(q, "q", torch.bfloat16, None, 3)
+    _need(cu_seqlens_q, "cu_seqlens_q", torch.int32, dev, 1)
+    _need(block_table, "block_table", torch.int32, dev, 2)
+    _need(seq_lens, "seq_lens", torch.int32, dev, 1)
+    Tq, Hq, D = q.shape
+    NB, Hkv, B, Dc = k_cache.shape
+    if v_cache.shape != k_cache.shape or Dc != D:
+        raise ValueError("k_cache and v_cache must both be [NB, Hkv, B, D] with q's D")
+    _need(out, "out", torch.bfloat16, dev, 3)
+    if tuple(out.shape) != (Tq, Hq, D):
+        raise ValueError(f"out must be [{Tq}, {Hq}, {D}]")
+    if lse is not None:
+        _need(lse, "lse", torch.float32, dev, 2)
+    if softmax_scale is None:
+        softmax_scale = 1.0 / math.sqrt(D)
+    st = library.attn_decode_paged_noalloc(
+        _ptr(q), _ptr(cu_seqlens_q), seq_lens.numel(), int(max_seqlen_q), _ptr(k_cache), _ptr(v_cache),
+        int(kv_dtype), _ptr(k_scale), _ptr(v_scale), _ptr(block_table), block_table.shape[1],
+        _ptr(seq_lens), int(max_seq_len), NB, B, Hq, Hkv, D, float(softmax_scale), int(kv_split_len),
+        _ptr(out), _ptr(lse), _stream(dev))
+    _check(st, "attn_decode_paged_noalloc")
+    return out
 
 
 def attn_prefill_paged(q, cu_seqlens_q, max_seqlen_q, k_cache, v_cache, kv_dtype,

@@ -2,6 +2,7 @@
 // launch of the gfx950 kernels.  Every check runs before the first launch,
 // so a call that returns an error has enqueued nothing.
 #include <algorithm>
+#include <atomic>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -287,8 +288,12 @@ struct DecLayout {
   size_t acc, m, l, units, total;
   int split_len, num_splits;
 };
+// balanced_groups > 0: the call is known to run the balanced split with
+// that many workgroups, and the partials are sized for exactly its pieces
+// ((groups + R * Hkv) per row of a unit); 0: room for either split, with
+// the largest balanced grid.
 DecLayout dec_layout(int R, int max_q, int max_seq_len, int Hq, int Hkv, int D, int B, int split_len,
-                     bool prefill = false) {
+                     bool prefill = false, int balanced_groups = 0) {
   DecLayout L{};
   L.split_len = split_len > 0 ? split_len
                 : prefill ? choose_split_len_prefill(R, Hkv, query_blocks(max_q, Hq, Hkv), max_seq_len, B)
@@ -298,9 +303,10 @@ DecLayout dec_layout(int R, int max_q, int max_seq_len, int Hq, int Hkv, int D, 
   // partial slots: rows x splits (fixed-length split), and for a decode with
   // the library's split also pieces x rows-per-unit (balanced split, used
   // when there is no window); room for the larger
-  size_t slots = (size_t)R * max_q * Hq * L.num_splits;
+  size_t slots = balanced_groups > 0 ? 0 : (size_t)R * max_q * Hq * L.num_splits;
   if (!prefill && split_len == 0) {
-    const size_t pieces = (size_t)attn::kDecodeMaxBalancedWG + (size_t)R * Hkv;
+    const size_t groups = balanced_groups > 0 ? (size_t)balanced_groups : (size_t)attn::kDecodeMaxBalancedWG;
+    const size_t pieces = groups + (size_t)R * Hkv;
     slots = std::max(slots, pieces * (size_t)max_q * (Hq / Hkv));
   }
   size_t off = 0;
@@ -337,6 +343,10 @@ int attn_decode_paged(const void* q, const int32_t* cu_seqlens_q, int num_reques
 }
 
 namespace {
+void* scratch_on_current_device(int* status);
+
+// noalloc: the partials go to the library's own scratch array on the current
+// device (the allocation-free decode) instead of the caller's workspace.
 int paged_attention(bool prefill, const void* q, const int32_t* cu_seqlens_q, int num_requests,
                     int max_seqlen_q, const void* k_cache, const void* v_cache, int kv_dtype,
                     const float* k_scale, const float* v_scale, int per_tensor_scales,
@@ -344,7 +354,7 @@ int paged_attention(bool prefill, const void* q, const int32_t* cu_seqlens_q, in
                     int num_blocks, int block_size, int num_q_heads, int num_kv_heads, int head_dim,
                     float softmax_scale, const float* sink, int window, const float* g_cache,
                     int kv_split_len, void* out, float* lse, void* workspace, size_t workspace_bytes,
-                    void* stream) {
+                    void* stream, bool noalloc = false) {
   REQUIRE(num_requests >= 0, ATTN_ERR_INVALID, "num_requests %d is negative", num_requests);
   REQUIRE(max_seqlen_q >= 1, ATTN_ERR_INVALID, "max_seqlen_q %d must be >= 1", max_seqlen_q);
   REQUIRE(prefill || max_seqlen_q <= 4, ATTN_ERR_UNSUPPORTED,
@@ -407,11 +417,39 @@ int paged_attention(bool prefill, const void* q, const int32_t* cu_seqlens_q, in
   REQ_PTR(seq_lens, 4);
   REQ_PTR(out, 16);
   if (lse) REQ_PTR(lse, 4);
-  const DecLayout lay = dec_layout(num_requests, max_seqlen_q, max_seq_len, num_q_heads, num_kv_heads,
-                                   head_dim, block_size, kv_split_len, prefill);
-  REQUIRE(workspace_bytes >= lay.total, ATTN_ERR_INVALID, "workspace too small: %zu < %zu bytes",
-          workspace_bytes, lay.total);
-  if (lay.total > 0) REQ_PTR(workspace, 256);
+  DecLayout lay = dec_layout(num_requests, max_seqlen_q, max_seq_len, num_q_heads, num_kv_heads,
+                             head_dim, block_size, kv_split_len, prefill);
+  if (noalloc) {
+    // allocation-free path: size the partials for the grid that will run
+    // (the balanced split's exact piece count needs the occupancy of its
+    // kernel), check them against the scratch before any other runtime
+    // call, then use the scratch array
+    const bool will_balance = !prefill && kv_split_len == 0 && lay.num_splits > 1 &&
+                              (long)num_requests * num_kv_heads * max_seq_len < 0x7fffffffL;
+    if (will_balance) {
+      attn::DecodeParams q0{};
+      q0.Hkv = num_kv_heads;
+      q0.row_blocks = (max_seqlen_q * (num_q_heads / num_kv_heads) + 15) / 16;
+      q0.g_cache = g_cache;
+      const int groups = attn::decode_balanced_groups(q0, head_dim, kv_dtype == ATTN_DTYPE_FP8_E4M3FN);
+      if (groups <= 0) return fail(ATTN_ERR_HIP, "occupancy query failed");
+      lay = dec_layout(num_requests, max_seqlen_q, max_seq_len, num_q_heads, num_kv_heads, head_dim,
+                       block_size, kv_split_len, prefill, groups);
+    }
+    REQUIRE(lay.total <= (size_t)ATTN_DECODE_NOALLOC_SCRATCH_BYTES, ATTN_ERR_UNSUPPORTED,
+            "this call needs %zu bytes of partials, more than the %zu-byte scratch of the "
+            "allocation-free decode; use attn_decode_paged with a workspace",
+            lay.total, (size_t)ATTN_DECODE_NOALLOC_SCRATCH_BYTES);
+    if (lay.total > 0) {
+      int st = ATTN_OK;
+      workspace = scratch_on_current_device(&st);
+      if (workspace == nullptr) return st;
+    }
+  } else {
+    REQUIRE(workspace_bytes >= lay.total, ATTN_ERR_INVALID, "workspace too small: %zu < %zu bytes",
+            workspace_bytes, lay.total);
+    if (lay.total > 0) REQ_PTR(workspace, 256);
+  }
   REQUIRE((long)num_requests * num_kv_heads * lay.num_splits *
                   query_blocks(max_seqlen_q, num_q_heads, num_kv_heads) <= 0x7fffffffL,
           ATTN_ERR_UNSUPPORTED, "more than 2^31 - 1 work items (requests x KV heads x segments x query blocks)");
@@ -471,6 +509,51 @@ int attn_decode_paged_ext(const void* q, const int32_t* cu_seqlens_q, int num_re
                          max_seq_len, num_blocks, block_size, num_q_heads, num_kv_heads, head_dim,
                          softmax_scale, sink, window, g_cache, kv_split_len, out, lse, workspace,
                          workspace_bytes, stream);
+}
+
+// ---------------------------------------------------------------------------
+// Allocation-free decode: the partials live in this file-scope array (one
+// copy per GPU, held until the process ends).  Host code never uses the
+// array's name as an address: the device address comes from
+// hipGetSymbolAddress, once per device, with that device current.
+static __device__ __align__(256) uint8_t scratch[ATTN_DECODE_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::atomic<void*> g_scratch_ptr[kMaxDevices];
+
+// The device address of `scratch` on the current device, or nullptr (error
+// recorded) on a runtime failure.
+void* scratch_on_current_device(int* status) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) { *status = hip_fail(e, "hipGetDevice"); return nullptr; }
+  if (dev < 0 || dev >= kMaxDevices) {
+    *status = fail(ATTN_ERR_UNSUPPORTED, "device %d: at most %d devices are supported", dev, kMaxDevices);
+    return nullptr;
+  }
+  void* ptr = g_scratch_ptr[dev].load(std::memory_order_acquire);
+  if (ptr != nullptr) return ptr;
+  e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+  if (e != hipSuccess || ptr == nullptr) {
+    *status = hip_fail(e != hipSuccess ? e : hipErrorInvalidSymbol, "hipGetSymbolAddress(scratch)");
+    return nullptr;
+  }
+  g_scratch_ptr[dev].store(ptr, std::memory_order_release);
+  return ptr;
+}
+}  // namespace
+
+int attn_decode_paged_noalloc(const void* q, const int32_t* cu_seqlens_q, int num_requests, int max_seqlen_q,
+                              const void* k_cache, const void* v_cache, int kv_dtype, const float* k_scale,
+                              const float* v_scale, const int32_t* block_table, int max_pages,
+                              const int32_t* seq_lens, int max_seq_len, int num_blocks, int block_size,
+                              int num_q_heads, int num_kv_heads, int head_dim, float softmax_scale,
+                              int kv_split_len, void* out, float* lse, void* stream) {
+  return paged_attention(false, q, cu_seqlens_q, num_requests, max_seqlen_q, k_cache, v_cache, kv_dtype,
+                         k_scale, v_scale, 0, block_table, max_pages, seq_lens, max_seq_len, num_blocks,
+                         block_size, num_q_heads, num_kv_heads, head_dim, softmax_scale, nullptr, 0, nullptr,
+                         kv_split_len, out, lse, nullptr, 0, stream, true);
 }
 
 size_t attn_prefill_paged_workspace_size(int num_requests, int max_seqlen_q, int max_seq_len,

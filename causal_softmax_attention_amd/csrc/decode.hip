@@ -616,22 +616,30 @@ static int balanced_wgs(K kernel, int threads, int cap_per_cu, std::atomic<int> 
   return cus * per_cu;
 }
 
+// Workgroups of a balanced launch of this instantiation: the resident
+// workgroups (queried for the instantiation that runs), capped, in whole
+// groups of Hkv (one per head).  0 on a runtime error.
+template <int D, bool FP8, int W, int RBW, int NST>
+static int balanced_groups_t(const DecodeParams& p) {
+  const int cap = W == 1 ? DECODE_BAL_PER_CU_1 : DECODE_BAL_PER_CU_2;
+  static std::atomic<int> cache_gate[16], cache_plain[16];
+  const int res = p.g_cache != nullptr
+                      ? balanced_wgs(decode_splitk_kernel<D, FP8, W, RBW, NST, true>, 64 * W, cap, cache_gate)
+                      : balanced_wgs(decode_splitk_kernel<D, FP8, W, RBW, NST, false>, 64 * W, cap, cache_plain);
+  if (res <= 0) return 0;
+  int want = res < kDecodeMaxBalancedWG ? res : kDecodeMaxBalancedWG;
+  want -= want % p.Hkv;
+  return want > 0 ? want : p.Hkv;
+}
+
 template <int D, bool FP8, int W, int RBW, int NST>
 static hipError_t launch_t(DecodeParams& p, hipStream_t st) {
   p.nqb = (p.row_blocks + W * RBW - 1) / (W * RBW);
   long items = (long)p.R * p.Hkv * p.num_splits * p.nqb;
   if (p.balanced) {
-    // workgroups that stay resident together, so each share runs in one
-    // round (queried for the instantiation that runs)
-    const int cap = W == 1 ? DECODE_BAL_PER_CU_1 : DECODE_BAL_PER_CU_2;
-    static std::atomic<int> cache_gate[16], cache_plain[16];
-    const int res = p.g_cache != nullptr
-                        ? balanced_wgs(decode_splitk_kernel<D, FP8, W, RBW, NST, true>, 64 * W, cap, cache_gate)
-                        : balanced_wgs(decode_splitk_kernel<D, FP8, W, RBW, NST, false>, 64 * W, cap, cache_plain);
-    if (res <= 0) return hipErrorInvalidConfiguration;
-    int want = res < kDecodeMaxBalancedWG ? res : kDecodeMaxBalancedWG;
-    want -= want % p.Hkv;                // whole groups of Hkv (one per head)
-    p.sk_G = want > 0 ? want : p.Hkv;
+    // workgroups that stay resident together, so each share runs in one round
+    p.sk_G = balanced_groups_t<D, FP8, W, RBW, NST>(p);
+    if (p.sk_G <= 0) return hipErrorInvalidConfiguration;
     items = p.sk_G;
   }
   if (items > 0x7fffffffL) return hipErrorInvalidConfiguration;
@@ -644,17 +652,26 @@ static hipError_t launch_t(DecodeParams& p, hipStream_t st) {
 
 // Row blocks of a (request, KV head): 1 -> one wave; 2 -> one wave holding
 // both; 3 or 4 -> two waves of two blocks each; more (prefill) -> query
-// blocks of 128 rows, four waves of two blocks each.
+// blocks of 128 rows, four waves of two blocks each.  `f` is called with
+// the instantiation's parameters as a tag.
+template <int D, bool FP8, int W_, int RBW_, int NST_>
+struct DecodeShape {
+  static constexpr int W = W_, RBW = RBW_, NST = NST_;
+};
+template <int D, bool FP8, typename F>
+static auto with_shape(int row_blocks, F f) {
+  if (row_blocks > 4) return f(DecodeShape<D, FP8, 4, 2, DECODE_NST_PREFILL>{});
+  if (row_blocks <= 1) return f(DecodeShape<D, FP8, 1, 1, DECODE_NST_1>{});
+  if (row_blocks == 2) return f(DecodeShape<D, FP8, 1, 2, DECODE_NST_2>{});
+  return f(DecodeShape<D, FP8, 2, 2, FP8 ? DECODE_NST_4_FP8 : DECODE_NST_4_BF16>{});
+}
+
 template <int D, bool FP8>
 static hipError_t launch_w(DecodeParams& p, hipStream_t st) {
-  if (p.row_blocks > 4) return launch_t<D, FP8, 4, 2, DECODE_NST_PREFILL>(p, st);
-  if (p.row_blocks <= 1) return launch_t<D, FP8, 1, 1, DECODE_NST_1>(p, st);
-  if (p.row_blocks == 2) return launch_t<D, FP8, 1, 2, DECODE_NST_2>(p, st);
-#ifdef DECODE_VERIFY_W4
-  return launch_t<D, FP8, 4, 1, FP8 ? DECODE_NST_4_FP8 : DECODE_NST_4_BF16>(p, st);
-#else
-  return launch_t<D, FP8, 2, 2, FP8 ? DECODE_NST_4_FP8 : DECODE_NST_4_BF16>(p, st);
-#endif
+  return with_shape<D, FP8>(p.row_blocks, [&](auto sh) {
+    using S = decltype(sh);
+    return launch_t<D, FP8, S::W, S::RBW, S::NST>(p, st);
+  });
 }
 
 hipError_t launch_decode_splitk(DecodeParams& p, int head_dim, bool fp8, hipStream_t st) {
@@ -662,6 +679,26 @@ hipError_t launch_decode_splitk(DecodeParams& p, int head_dim, bool fp8, hipStre
   if (head_dim == 128) return fp8 ? launch_w<128, true>(p, st) : launch_w<128, false>(p, st);
   if (head_dim == 64 && !fp8) return launch_w<64, false>(p, st);
   return hipErrorInvalidValue;
+}
+
+int decode_balanced_groups(const DecodeParams& p, int head_dim, bool fp8) {
+  if (p.row_blocks < 1) return 0;
+  if (head_dim == 128 && fp8)
+    return with_shape<128, true>(p.row_blocks, [&](auto sh) {
+      using S = decltype(sh);
+      return balanced_groups_t<128, true, S::W, S::RBW, S::NST>(p);
+    });
+  if (head_dim == 128)
+    return with_shape<128, false>(p.row_blocks, [&](auto sh) {
+      using S = decltype(sh);
+      return balanced_groups_t<128, false, S::W, S::RBW, S::NST>(p);
+    });
+  if (head_dim == 64 && !fp8)
+    return with_shape<64, false>(p.row_blocks, [&](auto sh) {
+      using S = decltype(sh);
+      return balanced_groups_t<64, false, S::W, S::RBW, S::NST>(p);
+    });
+  return 0;
 }
 
 }  // namespace attn

@@ -72,6 +72,9 @@ struct DecodeParams {
 };
 // Sets p.nqb and, for a balanced launch, p.sk_G.
 hipError_t launch_decode_splitk(DecodeParams& p, int head_dim, bool fp8, hipStream_t st);
+// The workgroup count (p.sk_G) a balanced launch with these parameters
+// would use (host side; 0 on a runtime error).
+int decode_balanced_groups(const DecodeParams& p, int head_dim, bool fp8);
 // Workgroups of a balanced launch never exceed this (sizes the partials).
 constexpr int kDecodeMaxBalancedWG = 4096;
 

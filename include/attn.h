@@ -234,6 +234,38 @@ int attn_decode_paged(const void* q, const int32_t* cu_seqlens_q,
                       void* workspace, size_t workspace_bytes, void* stream);
 
 /* ------------------------------------------------------------------------
+ * attn_decode_paged_noalloc -- attn_decode_paged for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid allocation): the same operation, arguments
+ * and results as attn_decode_paged, without the workspace.
+ *
+ * The split-K partials live in a scratch array inside the library (one copy
+ * per GPU, ATTN_DECODE_NOALLOC_SCRATCH_BYTES, held until the process ends);
+ * its device address is looked up once per device on the first call there.
+ * The call allocates and frees nothing, and calls no allocating routine.
+ * The caller still passes the inputs and the outputs (out, lse).
+ *
+ * The partials are sized for the grid the call actually launches; a call
+ * that needs more than the scratch returns ATTN_ERR_UNSUPPORTED (the
+ * message names the size) and enqueues nothing.  Every call on a GPU shares
+ * that GPU's scratch: calls that may overlap on one GPU (several streams,
+ * or several host threads) race and must be serialised by the caller.
+ * Nothing in the scratch needs to start at zero: a call reads only the
+ * partials it wrote itself.
+ * ------------------------------------------------------------------------ */
+#define ATTN_DECODE_NOALLOC_SCRATCH_BYTES (64u << 20)
+int attn_decode_paged_noalloc(const void* q, const int32_t* cu_seqlens_q,
+                              int num_requests, int max_seqlen_q,
+                              const void* k_cache, const void* v_cache, int kv_dtype,
+                              const float* k_scale, const float* v_scale,
+                              const int32_t* block_table, int max_pages,
+                              const int32_t* seq_lens, int max_seq_len,
+                              int num_blocks, int block_size,
+                              int num_q_heads, int num_kv_heads, int head_dim,
+                              float softmax_scale, int kv_split_len,
+                              void* out, float* lse, void* stream);
+
+/* ------------------------------------------------------------------------
  * attn_decode_paged_ext -- attn_decode_paged with the decode counterparts of
  * the prefill features (fla issue #1322, Description: sink, sliding window,
  * log gate) and per-tensor KV scales (aiter PR #6660, Technical details).

@@ -278,3 +278,32 @@ def test_prefill_workspace_sizes():
     assert n >= 1 * 8 * 64 * 2 * (128 + 2) * 4
     # an explicit split of the whole context is one segment as well
     assert A.attn_prefill_paged_workspace_size(1, 8, 1000, 64, 4, 128, 16, 1024) == 0
+
+
+# ---------------------------------------------------------------------------
+# allocation-free decode: a call whose partials exceed the scratch is
+# rejected by arithmetic alone, before any runtime call (this machine has no
+# GPU, so reaching the runtime would give ATTN_ERR_HIP instead)
+def _decode_noalloc(**kw):
+    a = dict(q=P, cu=P, R=64, maxq=4, kc=P, vc=P, kvd=A.ATTN_DTYPE_FP8_E4M3FN, ks=P, vs=P, bt=P, maxp=2048,
+             sl=P, maxsl=32768, nb=200000, B=16, Hq=64, Hkv=4, D=128, scale=0.1, split=512, out=P, lse=NULL)
+    a.update(kw)
+    return L.attn_decode_paged_noalloc(a["q"], a["cu"], a["R"], a["maxq"], a["kc"], a["vc"], a["kvd"],
+                                       a["ks"], a["vs"], a["bt"], a["maxp"], a["sl"], a["maxsl"], a["nb"],
+                                       a["B"], a["Hq"], a["Hkv"], a["D"], a["scale"], a["split"], a["out"],
+                                       a["lse"], NULL)
+
+
+def test_noalloc_decode_rejects_calls_beyond_the_scratch():
+    # 64 requests x 4 tokens x 64 heads x 64 segments of 512 keys: 16384 rows
+    # x 64 partials x 520 bytes, far beyond the scratch
+    assert _decode_noalloc() == UNSUPPORTED
+    msg = L.attn_last_error().decode()
+    assert "scratch" in msg and str(64 << 20) in msg
+
+
+def test_noalloc_decode_validates_like_the_workspace_decode():
+    assert _decode_noalloc(maxq=5) == UNSUPPORTED
+    assert "prefill" in L.attn_last_error().decode()
+    assert _decode_noalloc(ks=NULL) == UNSUPPORTED
+    assert _decode_noalloc(R=0) == OK
