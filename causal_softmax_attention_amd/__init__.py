@@ -40,9 +40,8 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 
 
 def lib_path() -> str:
-    """The in-tree library, or the file named by ATTN_LIBRARY when set (for
-    comparing builds of the same sources)."""
-    return os.environ.get("ATTN_LIBRARY") or os.path.join(_HERE, "libattn.so")
+    """The in-tree library this package loads."""
+    return os.path.join(_HERE, "libattn.so")
 
 
 class AttnError(RuntimeError):

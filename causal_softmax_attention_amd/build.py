@@ -85,5 +85,59 @@ def build(verbose: bool = False) -> str:
     return LIB
 
 
+# Host-side AddressSanitizer build of the C ABI (argument validation,
+# workspace layout, launch set-up).  Only the host pass is instrumented: each
+# sanitizer flag sits behind -Xarch_host, so the gfx950 code objects are the
+# ordinary ones.  Load it with the ASan runtime preloaded (asan_runtime()).
+ASAN_DIR = os.path.join(BUILD, "asan")
+ASAN_LIB = os.path.join(ASAN_DIR, "libattn.so")
+ASAN_HOST_FLAGS = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fno-omit-frame-pointer",
+                   "-Xarch_host", "-shared-libasan"]
+
+
+def asan_runtime() -> str:
+    """Path of the clang ASan runtime that the ASan build links against."""
+    out = subprocess.run([hipcc(), "-print-file-name=libclang_rt.asan-x86_64.so"], capture_output=True,
+                         text=True).stdout.strip()
+    if out and os.path.isabs(out) and os.path.exists(out):
+        return out
+    import glob
+    for pat in ("/opt/rocm/llvm/lib/clang/*/lib/linux/libclang_rt.asan-x86_64.so",
+                "/opt/rocm/lib/llvm/lib/clang/*/lib/linux/libclang_rt.asan-x86_64.so"):
+        hits = sorted(glob.glob(pat))
+        if hits:
+            return hits[-1]
+    raise RuntimeError("clang ASan runtime not found")
+
+
+def build_asan(verbose: bool = False) -> str:
+    """The library with the host code of api.hip built under ASan (the
+    kernels' objects are shared with the regular build, built first)."""
+    os.makedirs(ASAN_DIR, exist_ok=True)
+    objs = []
+    for src in sources():
+        base = os.path.basename(src)
+        if base != "api.hip":
+            obj = os.path.join(BUILD, base + ".o")
+            if not os.path.exists(obj):
+                _compile(src, verbose)
+            objs.append(obj)
+            continue
+        obj = os.path.join(ASAN_DIR, base + ".o")
+        cmd = [hipcc(), *COMMON_FLAGS, *ASAN_HOST_FLAGS, "-c", src, "-o", obj]
+        r = subprocess.run(cmd, capture_output=True, text=True)
+        if r.returncode != 0:
+            raise RuntimeError(f"hipcc (asan) failed for {src}:\n{r.stdout}{r.stderr}")
+        objs.append(obj)
+    cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *ASAN_HOST_FLAGS, *objs, "-o", ASAN_LIB]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"link (asan) failed:\n{r.stdout}{r.stderr}")
+    return ASAN_LIB
+
+
 if __name__ == "__main__":
-    print(build(verbose="--verbose" in sys.argv))
+    if "--asan" in sys.argv:
+        print(build_asan(verbose="--verbose" in sys.argv))
+    else:
+        print(build(verbose="--verbose" in sys.argv))

@@ -62,7 +62,8 @@ int check_prefill_common(const void* q, const void* k, const void* v, const int3
   REQUIRE(fwd_dims_supported(dqk, dv), ATTN_ERR_UNSUPPORTED,
           "head dims (d_qk=%d, d_v=%d) not supported; supported: (64,64) (128,128) (256,256) (256,512)",
           dqk, dv);
-  REQUIRE(std::isfinite(scale), ATTN_ERR_INVALID, "softmax_scale is not finite");
+  REQUIRE(std::isfinite(scale) && scale > 0.f, ATTN_ERR_INVALID,
+          "softmax_scale must be finite and positive (got %g)", (double)scale);
   REQUIRE(num_seqs <= 65535, ATTN_ERR_UNSUPPORTED, "num_seqs %d exceeds 65535", num_seqs);
   REQUIRE(Hq <= 65535, ATTN_ERR_UNSUPPORTED, "num_q_heads %d exceeds 65535", Hq);
   if (num_seqs > 0 && T > 0) {

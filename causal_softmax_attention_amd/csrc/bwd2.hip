@@ -20,20 +20,12 @@
 #include "common.h"
 #include "kernels.h"
 
-#ifndef BWD_WAVE_SKIP
-#define BWD_WAVE_SKIP 1
-#endif
-#ifndef BWD_KW_SMALL
-#define BWD_KW_SMALL 16
-#endif
-#ifndef BWD_RW_SMALL
-#define BWD_RW_SMALL 32
-#endif
-#ifndef BWD_NST_DKDV
-#define BWD_NST_DKDV 2
-#endif
-
 namespace attn {
+
+// Tile shapes of the head-dim 64 / 128 kernels (measured on config-sized
+// workloads: 16 keys per dK/dV wave keep three waves per SIMD; 32 query rows
+// per dQ wave; a two-stage Q/dO ring, three stages measured slower).
+constexpr int kBwdKwSmall = 16, kBwdRwSmall = 32, kBwdNstDkdv = 2;
 
 __device__ __forceinline__ int xcd_remap(int x, int n) {
   // consecutive logical indices -> same XCD (blocks go round-robin over 8)
@@ -57,7 +49,7 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdParams p) {
   constexpr int QRB = DQK * 2, ORB = DV * 2;   // bytes per Q / dO row
   constexpr int QPW = RQ * QRB / 4096, OPW = RQ * ORB / 4096;   // 1 KB blocks per wave
   static_assert(QPW * 4096 == RQ * QRB && OPW * 4096 == RQ * ORB, "tile must split into 4 x k 1 KB blocks");
-  constexpr int NSQ = BWD_NST_DKDV;    // ring stages (tiles in flight: NSQ - 1)
+  constexpr int NSQ = kBwdNstDkdv;    // ring stages (tiles in flight: NSQ - 1)
   static_assert(NSQ >= 2 && NSQ <= 3, "ring depth");
   // copies per tile issued by every wave (wave 0 adds the per-row terms):
   // the exact count of the later tiles' copies a wave waits past
@@ -194,7 +186,7 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdParams p) {
     }
   };
   int qt_lo = 0, qt_hi = nqt;
-  if (BWD_WAVE_SKIP) {
+  {
     qt_lo = min(nqt, (jw - j0) / RQ);                                   // rows before the first key
     if (W > 0) qt_hi = min(nqt, (jw - j0 + KW - 1 + W - 1) / RQ + 1);   // rows past the last key's window
     if (jw >= L) qt_hi = qt_lo;                                         // no keys
@@ -447,7 +439,7 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(BwdParams p) {
     if (t + 1 < t_end) fetch(((t - t_begin) & 1) ^ 1, t * BN + BN);
   };
   int tw_lo = t_begin, tw_hi = t_end;
-  if (BWD_WAVE_SKIP) {
+  {
     if (W > 0 && r0 - W + 1 > 0) tw_lo = max(t_begin, (r0 - W + 1) / BN);
     tw_hi = r_last >= r0 ? min(t_end, r_last / BN + 1) : t_begin;
     tw_lo = min(tw_lo, tw_hi);
@@ -614,8 +606,8 @@ hipError_t launch_bwd_two_pass_t(const BwdParams& p, hipStream_t st) {
 }
 
 hipError_t launch_bwd_two_pass(const BwdParams& p, int dqk, int dv, hipStream_t st) {
-  if (dqk == 64 && dv == 64) return launch_bwd_two_pass_t<64, 64, BWD_KW_SMALL, BWD_RW_SMALL, 64>(p, st);
-  if (dqk == 128 && dv == 128) return launch_bwd_two_pass_t<128, 128, BWD_KW_SMALL, BWD_RW_SMALL, 64>(p, st);
+  if (dqk == 64 && dv == 64) return launch_bwd_two_pass_t<64, 64, kBwdKwSmall, kBwdRwSmall, 64>(p, st);
+  if (dqk == 128 && dv == 128) return launch_bwd_two_pass_t<128, 128, kBwdKwSmall, kBwdRwSmall, 64>(p, st);
   if (dqk == 256 && dv == 256) return launch_bwd_two_pass_t<256, 256, 16, 16, 32>(p, st);
   if (dqk == 256 && dv == 512) return launch_bwd_two_pass_t<256, 512, 16, 16, 32>(p, st);
   return hipErrorInvalidValue;

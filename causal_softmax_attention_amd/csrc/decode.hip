@@ -12,10 +12,10 @@
 // Method (ROCm/aiter PR #6660, commit messages and "Technical details"):
 // the keys of a request are split into segments; each (request, KV head,
 // segment) produces (acc, m, l) partials for the query rows of the request
-// that share the KV head.  K scales multiply the QK columns; V scales
-// multiply the probability columns after the row sum; the scaled
-// probabilities are split into a bf16 high and low part so that PV keeps
-// fp32 accuracy (a bf16 cache has no V scales: its P enters PV as one
+// that share the KV head.  Each score column is scaled by its key's K scale;
+// each probability column is scaled by its key's V scale once the row sum
+// has been taken, and that product is split into a bf16 high and low part
+// so that PV keeps fp32 accuracy (a bf16 cache has no V scales: its P enters PV as one
 // round-to-nearest bf16, as in the prefill forward); cache slots past
 // seq_len never contribute (their bytes and scales may be NaN, so they are
 // selected away, not multiplied by 0).  A
@@ -213,7 +213,9 @@ __global__ __launch_bounds__(64 * W) void decode_splitk_kernel(DecodeParams p) {
       if (!per_tensor) {
         const int pid = (lane & 16) ? pg.b : pg.a;
         const int slot = ((kk + (lane & 16)) & bmask) + (lane & 15);
-        const uint32_t so = (uint32_t)((((pid * p.Hkv + kvh) << bsh) + slot) * 4);
+        // byte offset in unsigned 32-bit arithmetic (the host admits scale
+        // arrays up to 4 GiB)
+        const uint32_t so = ((((uint32_t)pid * (uint32_t)p.Hkv + (uint32_t)kvh) << bsh) + (uint32_t)slot) * 4u;
         const uint32_t sc = stage + 2 * TILE + wave * 2 * SCB;
         dma4_kv<STREAM>(p.k_scale, so, sc);
         dma4_kv<STREAM>(p.v_scale, so, sc + SCB);
@@ -229,7 +231,8 @@ __global__ __launch_bounds__(64 * W) void decode_splitk_kernel(DecodeParams p) {
       const int slot = ((kk + (key & 16)) & bmask) + (key & 15);
       for (int c = wave; c < ngi; c += W) {
         const int hh = min((64 * c + lane) >> 5, G - 1);
-        const uint32_t go = (uint32_t)((((pid * p.Hq + kvh * G + hh) << bsh) + slot) * 4);
+        const uint32_t go =
+            ((((uint32_t)pid * (uint32_t)p.Hq + (uint32_t)(kvh * G + hh)) << bsh) + (uint32_t)slot) * 4u;
         dma4(p.g_cache, go, gt + 256 * c);
       }
     }
@@ -575,32 +578,13 @@ __global__ __launch_bounds__(64 * W) void decode_splitk_kernel(DecodeParams p) {
 // and V.  Measured on one MI355X: deeper rings change neither the one-wave
 // decode nor the fp8 verify (compute-bound); the bf16 verify (256-byte
 // rows) gains ~3 % from four stages.
-#ifndef DECODE_NST_1
-#define DECODE_NST_1 2
-#endif
-#ifndef DECODE_NST_2
-#define DECODE_NST_2 2
-#endif
-#ifndef DECODE_NST_4_FP8
-#define DECODE_NST_4_FP8 2
-#endif
-#ifndef DECODE_NST_4_BF16
-#define DECODE_NST_4_BF16 4
-#endif
-#ifndef DECODE_NST_PREFILL
-#define DECODE_NST_PREFILL 2
-#endif
+constexpr int kDecNst1 = 2, kDecNst2 = 2, kDecNst4Fp8 = 2, kDecNst4Bf16 = 4, kDecNstPrefill = 2;
 
 // Balanced grid size: resident workgroups per CU of the instantiation that
 // runs, capped for one-wave workgroups, times the CUs.  One-wave decode
 // measured fastest at 3-6 workgroups per CU (fewer concurrent page streams),
 // against 9 resident; two-wave verify at full residency.
-#ifndef DECODE_BAL_PER_CU_1
-#define DECODE_BAL_PER_CU_1 4
-#endif
-#ifndef DECODE_BAL_PER_CU_2
-#define DECODE_BAL_PER_CU_2 0
-#endif
+constexpr int kDecBalPerCu1 = 4, kDecBalPerCu2 = 0;   // 0: no cap
 // `cache` belongs to one kernel instantiation: every instantiation has the
 // same function type, so the caller keeps one cache per instantiation.
 template <typename K>
@@ -621,7 +605,7 @@ static int balanced_wgs(K kernel, int threads, int cap_per_cu, std::atomic<int> 
 // groups of Hkv (one per head).  0 on a runtime error.
 template <int D, bool FP8, int W, int RBW, int NST>
 static int balanced_groups_t(const DecodeParams& p) {
-  const int cap = W == 1 ? DECODE_BAL_PER_CU_1 : DECODE_BAL_PER_CU_2;
+  const int cap = W == 1 ? kDecBalPerCu1 : kDecBalPerCu2;
   static std::atomic<int> cache_gate[16], cache_plain[16];
   const int res = p.g_cache != nullptr
                       ? balanced_wgs(decode_splitk_kernel<D, FP8, W, RBW, NST, true>, 64 * W, cap, cache_gate)
@@ -660,10 +644,10 @@ struct DecodeShape {
 };
 template <int D, bool FP8, typename F>
 static auto with_shape(int row_blocks, F f) {
-  if (row_blocks > 4) return f(DecodeShape<D, FP8, 4, 2, DECODE_NST_PREFILL>{});
-  if (row_blocks <= 1) return f(DecodeShape<D, FP8, 1, 1, DECODE_NST_1>{});
-  if (row_blocks == 2) return f(DecodeShape<D, FP8, 1, 2, DECODE_NST_2>{});
-  return f(DecodeShape<D, FP8, 2, 2, FP8 ? DECODE_NST_4_FP8 : DECODE_NST_4_BF16>{});
+  if (row_blocks > 4) return f(DecodeShape<D, FP8, 4, 2, kDecNstPrefill>{});
+  if (row_blocks <= 1) return f(DecodeShape<D, FP8, 1, 1, kDecNst1>{});
+  if (row_blocks == 2) return f(DecodeShape<D, FP8, 1, 2, kDecNst2>{});
+  return f(DecodeShape<D, FP8, 2, 2, FP8 ? kDecNst4Fp8 : kDecNst4Bf16>{});
 }
 
 template <int D, bool FP8>

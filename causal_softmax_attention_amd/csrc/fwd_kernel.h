@@ -18,9 +18,10 @@
 //    registers as the B operand of S^T = K Q^T (v_mfma_f32_16x16x32_bf16),
 //    so each lane owns one query row of every 16-row block and a row's
 //    max / sum needs only two cross-lane steps.
-//  * K and V tiles of BN keys are staged in LDS (row strides padded against
-//    bank conflicts); V^T operands come from ds_read_b64_tr_b16, so P leaves
-//    the score registers straight into the PV MFMA with no shuffle.
+//  * K and V tiles of BN keys are staged in LDS with their 16-byte chunks
+//    permuted per row (tile_swz: conflict-free for the MFMA-row and the
+//    transposed reads); V^T operands come from ds_read_b64_tr_b16, so P
+//    leaves the score registers straight into the PV MFMA with no shuffle.
 //  * Online softmax in base 2: scores are scaled by softmax_scale*log2(e)
 //    and the gate prefix is stored pre-multiplied by log2(e); the running
 //    max starts at the sink logit with l = 1.  Masking is applied only on
@@ -57,10 +58,6 @@ __device__ __forceinline__ float tree_sum(float (&v)[N]) {
     for (int i = 0; i + w < N; i += 2 * w) v[i] += v[i + w];
   return v[0];
 }
-
-#ifndef FWD_WAVE_SKIP
-#define FWD_WAVE_SKIP 1
-#endif
 
 // Blocks are dispatched round-robin over the 8 XCDs (each with its own L2);
 // map block x so that the query heads of one KV group land on one XCD.
@@ -211,7 +208,7 @@ __global__ __launch_bounds__(64 * NWV) void fwd_kernel(FwdParams p) {
   // kernel registers and occupancy).  Inside the range, a tile that
   // crosses the diagonal, the window edge or the end is masked per element.
   int tw_lo = t_begin, tw_hi = t_end;
-  if (FWD_WAVE_SKIP) {
+  {
     if (W > 0 && r0 - W + 1 > 0) tw_lo = max(t_begin, (r0 - W + 1) / BN);
     tw_hi = r_last >= r0 ? min(t_end, r_last / BN + 1) : t_begin;
     tw_lo = min(tw_lo, tw_hi);

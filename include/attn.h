@@ -97,6 +97,7 @@ const char* attn_version(void);
  *   G_i  = sum of g over the sequence's tokens 0..i       (gate prefix)
  *   m_i  = max(sink_h, max_j s_ij);  l_i = e^(sink_h - m_i) + sum_j e^(s_ij - m_i)
  *   o_i  = sum_j e^(s_ij - m_i) v_j / l_i;   lse_i = m_i + ln l_i
+ * softmax_scale must be finite and positive (ATTN_ERR_INVALID otherwise).
  * The sink is a raw per-query-head logit with no value; without a sink,
  * sink_h = -inf; without gates, G = 0.
  *
@@ -191,7 +192,9 @@ int attn_bwd_varlen(const void* q, const void* k, const void* v,
  * slot j % block_size.  With fp8, Khat_j = k_scale[page, kv, slot] * K_j and
  * Vhat_j likewise; with bf16 the cache values are used as they are.
  *   o_t = sum_j softmax_j(softmax_scale * <q_t, Khat_j>) Vhat_j
- * Cache slots past seq_len are never read (they may hold NaN).  The keys are
+ * Cache slots past seq_len never contribute: they may hold NaN (data or
+ * scales); the kernel may copy them with the rest of their page, but masks
+ * their scores, selects their scales away and zeroes their V rows.  The keys are
  * split into segments of kv_split_len tokens; each (request, KV head,
  * segment) yields partials merged by the same log-sum-exp reduce as
  * attn_splitk_reduce.  A query whose last visible key precedes a segment

@@ -8,8 +8,9 @@ Written from ROCm/aiter PR #6660 ("per-token fp8 KV scales and short-query
 split-K"):
   * commit message 1 and "Technical details": one float32 K and one V scale
     per cached token and KV head, laid out [num_blocks, num_kv_heads,
-    block_size]; K scales multiply the QK columns, V scales the probability
-    columns after the row sum; slots past seq_len contribute nothing;
+    block_size]; each score column is scaled by its key's K scale, each
+    probability column by its key's V scale once the row sum has been taken;
+    slots past seq_len contribute nothing;
   * commit message 2: the scaled probabilities must meet V at fp32 accuracy
     (here: exactly, in float64);
   * commit message 3 and "Technical details": queries of a few tokens per

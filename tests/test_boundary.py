@@ -103,6 +103,8 @@ def _fwd(**kw):
     (dict(o=NULL), INVALID, "o is NULL"),
     (dict(g=P, wsb=0), INVALID, "workspace too small"),
     (dict(scale=float("inf")), INVALID, "finite"),
+    (dict(scale=0.0), INVALID, "positive"),
+    (dict(scale=-0.1), INVALID, "positive"),
     (dict(N=70000), UNSUPPORTED, "num_seqs"),
 ])
 def test_forward_validation(kw, code, msg):

@@ -67,14 +67,26 @@ def test_wrong_gqa_mapping_is_caught():
     assert np.max(np.abs(o_wrong - ro)) > 1e-3
 
 
-def test_fp8_wrong_bias_is_caught():
-    codes = np.arange(256, dtype=np.uint8)
-    ref = torch.from_numpy(codes).view(torch.float8_e4m3fn).float().double().numpy()
-    c = codes.astype(np.int64)
-    e, m = (c >> 3) & 0xF, c & 7
-    wrong = (1 + m / 8.0) * 2.0 ** (e - 8.0)          # bias 8 instead of 7
-    ok = ~np.isnan(ref) & (e > 0) & (c < 128)
-    assert not np.allclose(wrong[ok], ref[ok])
+def test_fp8_wrong_bias_is_caught(monkeypatch):
+    # an oracle whose e4m3fn decoder uses exponent bias 8 instead of 7 must
+    # fail both fp8 pins (all 256 codes against torch, and the format's
+    # fixed points)
+    from tests import test_oracle_decode as pins
+
+    def wrong(codes):
+        c = np.asarray(codes).astype(np.int64)
+        s, e, m = (c >> 7) & 1, (c >> 3) & 0xF, c & 7
+        sign = np.where(s == 1, -1.0, 1.0)
+        out = np.where(e == 0, sign * (m / 8.0) * 2.0 ** -7,
+                       sign * (1.0 + m / 8.0) * np.power(2.0, (e - 8).astype(np.float64)))
+        return np.where((e == 15) & (m == 7), np.nan, out)
+
+    monkeypatch.setattr(oracle, "fp8_e4m3fn_to_f64", wrong)
+    monkeypatch.setattr(od, "fp8_e4m3fn_to_f64", wrong)
+    with pytest.raises(AssertionError):
+        pins.test_fp8_decode_matches_torch_on_all_codes()
+    with pytest.raises(AssertionError):
+        pins.test_fp8_format_fixed_points()
 
 
 def test_sink_gradient_sign_flip_is_caught():
