@@ -1,22 +1,32 @@
 #!/usr/bin/env python3
 """Benchmark of the causal softmax attention hot path on one MI355X.
 
-One step = one pass over every hot-path step on synthetic inputs already
-resident in HBM:
-  * prefill: attn_fwd_varlen + attn_bwd_varlen on the packed varlen workload
-    (8 sequences of seeded lengths in [256, 4096], 32 query / 8 KV heads,
-    head dim 128, window 1024, sink and log gates) -- tile schedule, gate
-    prefix, forward tile loop, backward pre / fused / post;
-  * decode: attn_decode_paged on 64 requests with contexts in [1, 32768],
-    64 query / 4 KV heads, head dim 128, page 16, per-token fp8 KV, one query
-    token each -- split-K partials and the LSE reduce (one layer).
+One step = one pass over every hot-path step, on synthetic inputs already
+resident in HBM, for every workload of the method's benchmark set:
+  * prefill, 8 packed sequences (lengths U[256, 4096], seed 2), 32 query /
+    8 KV heads, head dim 128, window 1024, sink and log gates:
+    attn_fwd_varlen + attn_bwd_varlen (tile schedule, gate prefix, forward
+    tile loop, backward pre / tile loops / post);
+  * prefill with large heads, 4 x 8192 tokens, 16 / 4 heads, d_qk 256,
+    d_v 512, sink and log gates, no window: attn_fwd_varlen + attn_bwd_varlen;
+  * decode, 64 requests with contexts U[1, 32768] (seed 3), 64 / 4 heads,
+    head dim 128, page 16, per-token fp8 KV: attn_decode_paged (split-K
+    partials + LSE reduce), one layer;
+  * short-query verify, 3 requests x 4 tokens over ~227K-token contexts,
+    page 128, with a bf16 and with a per-token fp8 KV cache.
 
-Prints ONE JSON line.  `value` is the prefill fwd+bwd throughput in TFLOP/s
-(algorithmic flops: visible (query, key) pairs only); the decode figures
-(us per layer, GB/s of algorithmic bytes) sit in `decode`.  Every API call is
-bracketed by HIP events on the stream it runs on.  `roofline` describes the
-call with the largest share of the step; `cpu_baseline` is the float64 CPU
-oracle timed on a bounded sample of the same prefill workload.
+Prints ONE JSON line.  `value` is the prefill forward + backward throughput
+(TFLOP/s of algorithmic flops: visible (query, key) pairs only) on the
+8-sequence window-1024 workload; every workload's own figures (us, TFLOP/s or
+GB/s, fraction of the MI355X peak) sit in `workloads`, each beside the
+float64 CPU oracle timed on a bounded sample of it.
+
+Timing: the K steps of the contract run back to back (wall clock around
+them gives ms_per_step; HIP events around every call on its stream give the
+in-step per-call times).  Separately, each call is timed over `--iters`
+(>= 100) iterations with HIP events, `--repeats` (5) times; the per-call
+figures and `value` use the median of those repeats.  `roofline` describes
+the call that takes the largest share of the step.
 """
 from __future__ import annotations
 
@@ -24,6 +34,8 @@ import argparse
 import json
 import math
 import os
+import platform
+import subprocess
 import sys
 import time
 
@@ -36,9 +48,16 @@ sys.path.insert(0, ROOT)
 MFMA_BF16_PEAK_TFLOPS = 256 * 2.4e9 * 4096 / 1e12   # 2516.6 dense bf16
 HBM_PEAK_GBPS = 8000.0
 
-
 PROFILES = os.path.join(ROOT, "profiles")
 CSRC = os.path.join(ROOT, "causal_softmax_attention_amd", "csrc")
+
+# The pages' own figures for the verify workload (context only: another GPU).
+PAGES_VERIFY_CONTEXT = {
+    "gpu": "gfx1250 (MI455), not this GPU",
+    "source": "ROCm/aiter PR #6660, third commit message",
+    "workload": "3 requests x 4 query tokens, 227K-token context, per layer",
+    "us_2d_kernel": 16500.0, "us_split_k_bf16_kv": 75.0, "us_split_k_per_token_fp8_kv": 177.0,
+}
 
 
 def kernel_sources_digest():
@@ -89,21 +108,27 @@ def prefill_flops(x):
     return 2 * pairs * Hq * (dqk + dv), 2 * pairs * Hq * (3 * dqk + 2 * dv), pairs
 
 
-def decode_bytes(d):
-    L = d.seq_lens.to(torch.int64).sum().item()
-    Hkv, D = d.k_cache.shape[1], d.k_cache.shape[3]
-    elem = 1 if d.kv_dtype == 1 else 2
+def decode_bytes(seq_lens, Hkv, D, fp8, q_tokens, Hq, block_size):
+    """Algorithmic bytes of one decode layer: every visible cache byte once
+    (K and V, plus the two fp32 scales per token and KV head with fp8), q in,
+    o out, and the block-table entries read."""
+    L = sum(int(x) for x in seq_lens)
+    elem = 1 if fp8 else 2
     b = L * Hkv * 2 * D * elem
-    if d.kv_dtype == 1:
+    if fp8:
         b += L * Hkv * 8
-    b += d.q.numel() * 2 * 2                       # q in, o out (bf16)
-    pages = sum(math.ceil(int(x) / d.block_size) for x in d.seq_lens.tolist())
-    b += pages * 4                                 # block-table entries read
+    b += q_tokens * Hq * D * 2 * 2
+    b += sum(math.ceil(int(x) / block_size) for x in seq_lens) * 4
     return b
 
 
+def _dec_bytes(d):
+    return decode_bytes(d.seq_lens.tolist(), d.k_cache.shape[1], d.k_cache.shape[3], d.kv_dtype == 1,
+                        d.q.shape[0], d.q.shape[1], d.block_size)
+
+
 class Timer:
-    """HIP events on the current stream around each API call."""
+    """HIP events on the current stream (the stream every call runs on)."""
 
     def __init__(self):
         self.t = {}
@@ -117,88 +142,29 @@ class Timer:
         self.t.setdefault(name, []).append((s, e))
         return r
 
-    def mean_us(self, name):
-        ev = self.t.get(name, [])
-        return 1e3 * sum(s.elapsed_time(e) for s, e in ev) / max(1, len(ev))
-
-    def median_us(self, name):
-        ev = self.t.get(name, [])
-        return 1e3 * float(np.median([s.elapsed_time(e) for s, e in ev])) if ev else 0.0
+    def us(self, name):
+        return [1e3 * s.elapsed_time(e) for s, e in self.t.get(name, [])]
 
 
-def cpu_oracle_baseline(x, budget_s=12.0):
-    """The float64 oracle, as it stands, on a bounded sample of the prefill
-    workload: whole KV-head groups of the first sequences, until ~budget_s."""
-    import oracle
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    except Exception:
-        threads = os.cpu_count() or 1
-    cu = x.cu_seqlens.cpu().numpy()
-    Hq, Hkv = x.q.shape[1], x.k.shape[1]
-    grp = Hq // Hkv
-    q, k, v, do = (t.cpu() for t in (x.q, x.k, x.v, x.do))
-    sink = x.sink.cpu() if x.sink is not None else None
-    g = x.g.cpu() if x.g is not None else None
-    flops, spent, done = 0, 0.0, []
-    for n in range(len(cu) - 1):
-        a, b = int(cu[n]), int(cu[n + 1])
-        c1 = np.array([0, b - a])
-        for kv in range(Hkv):
-            hs = slice(kv * grp, (kv + 1) * grp)
-            t0 = time.perf_counter()
-            oracle.forward(q[a:b, hs], k[a:b, kv:kv + 1], v[a:b, kv:kv + 1], c1, x.scale, x.window,
-                           None if sink is None else sink[hs], None if g is None else g[a:b, hs])
-            oracle.backward(q[a:b, hs], k[a:b, kv:kv + 1], v[a:b, kv:kv + 1], do[a:b, hs], c1,
-                            x.scale, x.window, None if sink is None else sink[hs],
-                            None if g is None else g[a:b, hs])
-            spent += time.perf_counter() - t0
-            pairs = visible_pairs([b - a], x.window)
-            dqk, dv = x.q.shape[2], x.v.shape[2]
-            flops += 2 * pairs * grp * ((dqk + dv) + (3 * dqk + 2 * dv))
-            done.append(f"seq{n}(L={b - a})/kv{kv}")
-            if spent >= budget_s:
-                break
-        if spent >= budget_s:
-            break
-    return {"value": flops / spent / 1e12, "unit": "TFLOP/s", "cores": int(threads),
-            "kind": "oracle",
-            "sample": f"float64 oracle forward+backward on {len(done)} (sequence, KV-head group) "
-                      f"slices of the prefill workload ({done[0]} .. {done[-1]}), "
-                      f"{flops / 1e9:.1f} GFLOP in {spent:.1f} s"}
+def time_call(fn, iters, repeats):
+    """Median over `repeats` of the mean per-call time of `iters` back-to-back
+    calls, each repeat bracketed by HIP events on the current stream."""
+    fn()
+    torch.cuda.synchronize()
+    per = []
+    for _ in range(repeats):
+        s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s.record()
+        for _ in range(iters):
+            fn()
+        e.record()
+        torch.cuda.synchronize()
+        per.append(1e3 * s.elapsed_time(e) / iters)
+    return {"median_us": float(np.median(per)), "repeats_us": [round(x, 2) for x in per],
+            "iters_per_repeat": iters, "repeats": repeats}
 
 
-def cpu_oracle_decode_baseline(d, budget_s=6.0):
-    """The float64 decode oracle, as it stands, on whole requests of the
-    decode workload (in request order) until ~budget_s; GB/s of the same
-    algorithmic bytes the GPU figure counts."""
-    import oracle
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    except Exception:
-        threads = os.cpu_count() or 1
-    kc, vc = d.k_cache.cpu().numpy(), d.v_cache.cpu().numpy()
-    ks, vs = d.k_scale.cpu().numpy(), d.v_scale.cpu().numpy()
-    q, cu, bt, sl = d.q.cpu(), d.cu_seqlens_q.cpu(), d.block_table.cpu().numpy(), d.seq_lens.cpu()
-    Hkv, D, Hq = kc.shape[1], kc.shape[3], q.shape[1]
-    spent, done, nbytes = 0.0, [], 0
-    for r in range(len(d.q_lens)):
-        t0 = time.perf_counter()
-        oracle.decode_paged(q, cu, kc, vc, bt, sl, d.scale, True, ks, vs, requests=[r])
-        spent += time.perf_counter() - t0
-        L = int(sl[r])
-        nbytes += L * Hkv * (2 * D + 8) + d.q_lens[r] * Hq * D * 4 + math.ceil(L / d.block_size) * 4
-        done.append(r)
-        if spent >= budget_s:
-            break
-    return {"value": nbytes / spent / 1e9, "unit": "GB/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"float64 decode oracle on requests {done[0]}..{done[-1]} of the decode workload "
-                      f"({nbytes / 1e6:.0f} MB of cache) in {spent:.1f} s"}
-
-
-def decode_graph_us(fn, reps=50):
+def decode_graph_us(fn, reps=100):
     """The decode layer (partials + reduce) captured once as a HIP graph and
     replayed; each of the first replays is checked against the eager result
     (with eager work between them) before the timed replays."""
@@ -228,14 +194,134 @@ def decode_graph_us(fn, reps=50):
     return 1e3 * s.elapsed_time(e) / reps
 
 
+# ---------------------------------------------------------------------------
+# the float64 CPU oracle on bounded samples (the oracle as it stands)
+def _blas_threads():
+    try:
+        from threadpoolctl import threadpool_info
+        return max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        return os.cpu_count() or 1
+
+
+def cpu_prefill(x, budget_s, slice_len=None, label="prefill"):
+    """forward + backward of the oracle on (sequence, KV-head group) slices
+    of the workload, in order, until ~budget_s; TFLOP/s of the same
+    algorithmic flops.  slice_len: clip each slice to its first tokens."""
+    import oracle
+    cu = x.cu_seqlens.cpu().numpy()
+    Hq, Hkv = x.q.shape[1], x.k.shape[1]
+    grp = Hq // Hkv
+    dqk, dv = x.q.shape[2], x.v.shape[2]
+    q, k, v, do = (t.cpu() for t in (x.q, x.k, x.v, x.do))
+    sink = x.sink.cpu() if x.sink is not None else None
+    g = x.g.cpu() if x.g is not None else None
+    flops, spent, done = 0, 0.0, []
+    for n in range(len(cu) - 1):
+        a, b = int(cu[n]), int(cu[n + 1])
+        if slice_len:
+            b = min(b, a + slice_len)
+        c1 = np.array([0, b - a])
+        for kv in range(Hkv):
+            hs = slice(kv * grp, (kv + 1) * grp)
+            t0 = time.perf_counter()
+            oracle.forward(q[a:b, hs], k[a:b, kv:kv + 1], v[a:b, kv:kv + 1], c1, x.scale, x.window,
+                           None if sink is None else sink[hs], None if g is None else g[a:b, hs])
+            oracle.backward(q[a:b, hs], k[a:b, kv:kv + 1], v[a:b, kv:kv + 1], do[a:b, hs], c1,
+                            x.scale, x.window, None if sink is None else sink[hs],
+                            None if g is None else g[a:b, hs])
+            spent += time.perf_counter() - t0
+            pairs = visible_pairs([b - a], x.window)
+            flops += 2 * pairs * grp * ((dqk + dv) + (3 * dqk + 2 * dv))
+            done.append(f"seq{n}[0:{b - a}]/kv{kv}")
+            if spent >= budget_s:
+                break
+        if spent >= budget_s:
+            break
+    return {"value": flops / spent / 1e12, "unit": "TFLOP/s", "cores": int(_blas_threads()),
+            "kind": "oracle",
+            "sample": f"float64 oracle forward+backward of the {label} workload on {len(done)} "
+                      f"(sequence, KV-head group) slices ({done[0]} .. {done[-1]}), "
+                      f"{flops / 1e9:.1f} GFLOP in {spent:.1f} s"}
+
+
+def cpu_decode(d, budget_s, clip=None, label="decode"):
+    """The decode oracle on whole requests of the workload in order until
+    ~budget_s (clip: each request's context cut to its first `clip` tokens,
+    its query tokens at the end of the cut); GB/s of the same algorithmic
+    bytes the GPU figure counts.  Each request's pages are gathered (and a
+    bf16 cache widened to float64) before its timed call, so the timed work
+    is the oracle on that request alone."""
+    import oracle
+    fp8 = d.kv_dtype == 1
+    q, cu = d.q.cpu(), d.cu_seqlens_q.cpu()
+    bt, sl = d.block_table.cpu(), d.seq_lens.cpu()
+    Hkv, B, D, Hq = d.k_cache.shape[1], d.k_cache.shape[2], d.k_cache.shape[3], q.shape[1]
+    spent, done, nbytes = 0.0, [], 0
+    for r in range(len(d.q_lens)):
+        L = int(sl[r]) if not clip else min(int(sl[r]), clip)
+        n = d.q_lens[r]
+        pages = bt[r, :(L + B - 1) // B].to(d.k_cache.device)
+        kc = d.k_cache.index_select(0, pages).cpu()
+        vc = d.v_cache.index_select(0, pages).cpu()
+        kc, vc = (c.numpy() if fp8 else c.double().numpy() for c in (kc, vc))
+        ks = d.k_scale.index_select(0, pages).cpu().numpy() if fp8 else None
+        vs = d.v_scale.index_select(0, pages).cpu().numpy() if fp8 else None
+        qr = q[int(cu[r]):int(cu[r + 1])]
+        one_bt = torch.arange(len(pages), dtype=torch.int32)[None, :]
+        t0 = time.perf_counter()
+        oracle.decode_paged(qr, torch.tensor([0, n], dtype=torch.int32), kc, vc, one_bt,
+                            torch.tensor([L], dtype=torch.int32), d.scale, fp8, ks, vs)
+        spent += time.perf_counter() - t0
+        nbytes += decode_bytes([L], Hkv, D, fp8, n, Hq, B)
+        done.append(r)
+        if spent >= budget_s:
+            break
+    clip_txt = f", contexts clipped to their first {clip} tokens" if clip else ""
+    return {"value": nbytes / spent / 1e9, "unit": "GB/s", "cores": int(_blas_threads()), "kind": "oracle",
+            "sample": f"float64 decode oracle on requests {done[0]}..{done[-1]} of the {label} workload"
+                      f"{clip_txt} ({nbytes / 1e6:.0f} MB of algorithmic bytes) in {spent:.1f} s"}
+
+
+def machine_info():
+    info = {"torch": torch.__version__, "hip": getattr(torch.version, "hip", None),
+            "python": platform.python_version(), "os_cpu_count": os.cpu_count(),
+            "blas_threads": _blas_threads()}
+    try:
+        info["gpu"] = torch.cuda.get_device_name(0)
+        props = torch.cuda.get_device_properties(0)
+        info["gpu_arch"] = getattr(props, "gcnArchName", None)
+        info["gpu_cus"] = props.multi_processor_count
+    except Exception:
+        pass
+    for path in ("/opt/rocm/.info/version", "/opt/rocm/.info/version-dev"):
+        if os.path.exists(path):
+            info["rocm"] = open(path).read().strip()
+            break
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    info["cpu_model"] = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        import causal_softmax_attention_amd as A
+        info["library"] = A.library.attn_version().decode()
+    except Exception:
+        pass
+    return info
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--iters", type=int, default=100, help="calls per timed repeat (>= 100)")
+    ap.add_argument("--repeats", type=int, default=5, help="timed repeats per call (median reported)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--extra", action="store_true",
-                    help="also time the 227K-context verify and the large-head prefill")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on exactly one GPU (asked for {args.gpus}): the hot path here is the "
@@ -250,81 +336,128 @@ def main():
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    x = synth.varlen_8seq_window1024(device=dev)
-    d = synth.decode_64req_fp8(device=dev)
-    f_fwd, f_bwd, pairs = prefill_flops(x)
-    dec_bytes = decode_bytes(d)
-    print(f"[bench] prefill T={x.total_tokens} pairs={pairs} fwd={f_fwd:.3e} bwd={f_bwd:.3e} flop; "
-          f"decode tokens={int(d.seq_lens.sum())} bytes={dec_bytes:.3e}", file=sys.stderr, flush=True)
+    x2 = synth.varlen_8seq_window1024(device=dev)
+    x5 = synth.varlen_4x8192_wide_heads(device=dev)
+    d3 = synth.decode_64req_fp8(device=dev)
+    d4f = synth.verify_3x4_227k(kv_dtype=synth.KV_FP8_E4M3FN, device=dev)
+    d4b = synth.verify_3x4_227k(kv_dtype=synth.KV_BF16, device=dev)
+    f2f, f2b, pairs2 = prefill_flops(x2)
+    f5f, f5b, pairs5 = prefill_flops(x5)
+    b3, b4f, b4b = _dec_bytes(d3), _dec_bytes(d4f), _dec_bytes(d4b)
+    print(f"[bench] prefill T={x2.total_tokens} pairs={pairs2}; large heads T={x5.total_tokens} "
+          f"pairs={pairs5}; decode bytes={b3:.3e}; verify bytes fp8={b4f:.3e} bf16={b4b:.3e}",
+          file=sys.stderr, flush=True)
 
-    def fwd():
-        return A.attn_fwd_varlen(x.q, x.k, x.v, x.cu_seqlens, x.max_seqlen, x.scale, x.window,
-                                 x.sink, x.g)
+    def fwd(x):
+        return lambda: A.attn_fwd_varlen(x.q, x.k, x.v, x.cu_seqlens, x.max_seqlen, x.scale, x.window,
+                                         x.sink, x.g)
 
-    o, lse = fwd()
+    o2, l2 = fwd(x2)()
+    o5, l5 = fwd(x5)()
 
-    def bwd():
-        return A.attn_bwd_varlen(x.q, x.k, x.v, o, x.do, lse, x.cu_seqlens, x.max_seqlen, x.scale,
-                                 x.window, x.sink, x.g)
+    def bwd(x, o, lse, flags=0):
+        return lambda: A.attn_bwd_varlen(x.q, x.k, x.v, o, x.do, lse, x.cu_seqlens, x.max_seqlen, x.scale,
+                                         x.window, x.sink, x.g, flags=flags)
 
-    def bwd_fused():
-        return A.attn_bwd_varlen(x.q, x.k, x.v, o, x.do, lse, x.cu_seqlens, x.max_seqlen, x.scale,
-                                 x.window, x.sink, x.g, flags=A.ATTN_BWD_FUSED_DQ)
+    def dec(d):
+        mq, ml = d.max_seqlen_q, d.max_seq_len   # host values, read once
+        return lambda: A.attn_decode_paged(d.q, d.cu_seqlens_q, mq, d.k_cache, d.v_cache, d.kv_dtype,
+                                           d.k_scale, d.v_scale, d.block_table, d.seq_lens, ml, d.scale)
 
-    dec_max_q, dec_max_len = d.max_seqlen_q, d.max_seq_len   # host values, read once
+    calls = {
+        "prefill_fwd": fwd(x2), "prefill_bwd": bwd(x2, o2, l2),
+        "large_heads_fwd": fwd(x5), "large_heads_bwd": bwd(x5, o5, l5),
+        "decode": dec(d3), "verify_fp8": dec(d4f), "verify_bf16": dec(d4b),
+    }
 
-    def dec():
-        return A.attn_decode_paged(d.q, d.cu_seqlens_q, dec_max_q, d.k_cache, d.v_cache,
-                                   d.kv_dtype, d.k_scale, d.v_scale, d.block_table, d.seq_lens,
-                                   dec_max_len, d.scale)
+    def step(tm=None):
+        for name, fn in calls.items():
+            if tm is None:
+                fn()
+            else:
+                tm.run(name, fn)
 
-    tm = Timer()
     for _ in range(args.warmup):
-        fwd(); bwd(); dec()
+        step()
     torch.cuda.synchronize()
     tm = Timer()
     t0 = time.perf_counter()
     for _ in range(args.steps):
-        tm.run("fwd", fwd)
-        tm.run("bwd", bwd)
-        tm.run("decode", dec)
+        step(tm)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_step = 1e3 * wall / args.steps
-    # the decode layer as a HIP graph (the pages time decode that way), outside the step
-    dec_graph_us = decode_graph_us(dec)
-    # the fused-dQ variant of the backward, timed outside the step
-    tf = Timer()
-    bwd_fused()
-    for _ in range(max(3, args.steps // 4)):
-        tf.run("bwd_fused", bwd_fused)
-    torch.cuda.synchronize()
-    us = {k: tm.mean_us(k) for k in ("fwd", "bwd", "decode")}
-    tf_fwd = f_fwd / (us["fwd"] * 1e-6) / 1e12
-    tf_bwd = f_bwd / (us["bwd"] * 1e-6) / 1e12
-    tf_fb = (f_fwd + f_bwd) / ((us["fwd"] + us["bwd"]) * 1e-6) / 1e12
-    gbps = dec_bytes / (us["decode"] * 1e-6) / 1e9
 
-    phases = {
-        "fwd": dict(kernel="attn_fwd_varlen (gate prefix + forward tile loop)", bound="mfma",
-                    achieved=tf_fwd, peak=MFMA_BF16_PEAK_TFLOPS, unit="TFLOP/s"),
-        "bwd": dict(kernel="attn_bwd_varlen (gate prefix + pre + dK/dV pass + dQ pass + post)",
-                    bound="mfma", achieved=tf_bwd, peak=MFMA_BF16_PEAK_TFLOPS, unit="TFLOP/s"),
-        "decode": dict(kernel="attn_decode_paged (split-K partials + LSE reduce)", bound="hbm",
-                       achieved=gbps, peak=HBM_PEAK_GBPS, unit="GB/s"),
+    # per-call timing: median of `repeats` x `iters` calls each
+    med = {}
+    for name, fn in calls.items():
+        med[name] = time_call(fn, args.iters, args.repeats)
+    dec_graph_us = decode_graph_us(calls["decode"])
+    fused = time_call(bwd(x2, o2, l2, flags=A.ATTN_BWD_FUSED_DQ), 10, 3)
+
+    us = {k: v["median_us"] for k, v in med.items()}
+    in_step = {k: float(np.median(tm.us(k))) for k in calls}
+    tf = lambda f, u: f / (u * 1e-6) / 1e12
+    gb = lambda b, u: b / (u * 1e-6) / 1e9
+    work = {
+        "prefill_fwd": ("mfma", f2f), "prefill_bwd": ("mfma", f2b),
+        "large_heads_fwd": ("mfma", f5f), "large_heads_bwd": ("mfma", f5b),
+        "decode": ("hbm", b3), "verify_fp8": ("hbm", b4f), "verify_bf16": ("hbm", b4b),
     }
+    figures = {}
+    for k, (bound, w) in work.items():
+        if bound == "mfma":
+            a = tf(w, us[k])
+            figures[k] = {"us": us[k], "us_in_step": in_step[k], "flops": w, "tflops": a,
+                          "frac_of_bf16_mfma_peak": a / MFMA_BF16_PEAK_TFLOPS, "timing": med[k]}
+        else:
+            a = gb(w, us[k])
+            figures[k] = {"us": us[k], "us_in_step": in_step[k], "bytes": w, "GBps": a,
+                          "frac_of_hbm_peak": a / HBM_PEAK_GBPS, "timing": med[k]}
+
+    value = tf(f2f + f2b, us["prefill_fwd"] + us["prefill_bwd"])
+    api = {"prefill_fwd": "attn_fwd_varlen", "prefill_bwd": "attn_bwd_varlen",
+           "large_heads_fwd": "attn_fwd_varlen", "large_heads_bwd": "attn_bwd_varlen",
+           "decode": "attn_decode_paged", "verify_fp8": "attn_decode_paged", "verify_bf16": "attn_decode_paged"}
     dom = max(us, key=us.get)
-    roof = dict(phases[dom])
+    bound, w = work[dom]
+    roof = {"bound": bound, "call": f"{api[dom]} ({dom})",
+            "achieved": tf(w, us[dom]) if bound == "mfma" else gb(w, us[dom]),
+            "peak": MFMA_BF16_PEAK_TFLOPS if bound == "mfma" else HBM_PEAK_GBPS,
+            "unit": "TFLOP/s" if bound == "mfma" else "GB/s", "us_per_launch": us[dom],
+            "algorithmic_work_per_launch": w, "traffic": stored_traffic(dom)}
     roof["frac"] = roof["achieved"] / roof["peak"]
-    roof["us_per_launch"] = us[dom]
-    roof["traffic"] = stored_traffic({"fwd": "attn_fwd_varlen", "bwd": "attn_bwd_varlen",
-                                      "decode": "attn_decode_paged"}[dom])
-    for ph in phases.values():
-        ph["frac"] = ph["achieved"] / ph["peak"]
+
+    workloads = {
+        "prefill_8seq_window1024": {
+            "config": "8 packed seqs, lengths U[256,4096] (seed 2), T=%d, 32q/8kv heads, d 128, window 1024, "
+                      "sink, log gates" % x2.total_tokens,
+            "fwd": figures["prefill_fwd"], "bwd": figures["prefill_bwd"],
+            "fwdbwd_tflops": value, "fwdbwd_frac_of_bf16_mfma_peak": value / MFMA_BF16_PEAK_TFLOPS,
+            "bwd_path": "two-pass (deterministic)",
+            "bwd_fused_dq": {"us": fused["median_us"], "tflops": tf(f2b, fused["median_us"]), "timing": fused},
+            "target": "forward >= 50% of bf16 MFMA peak (<= 142.5 us)"},
+        "prefill_4x8192_large_heads": {
+            "config": "4 x 8192 tokens, 16q/4kv heads, d_qk 256, d_v 512, sink, log gates, no window",
+            "fwd": figures["large_heads_fwd"], "bwd": figures["large_heads_bwd"],
+            "fwdbwd_tflops": tf(f5f + f5b, us["large_heads_fwd"] + us["large_heads_bwd"]),
+            "target": "forward >= 50% of bf16 MFMA peak (<= 2.62 ms); backward reported"},
+        "decode_64req_fp8": {
+            "config": "64 requests, contexts U[1,32768] (seed 3), 64q/4kv heads, d 128, page 16, "
+                      "per-token fp8 e4m3fn KV, 1 query token each, split-K + LSE reduce",
+            **figures["decode"], "us_per_layer_hip_graph": dec_graph_us,
+            "target": ">= 70% of HBM peak (<= 183 us)"},
+        "verify_3x4_227k": {
+            "config": "3 requests x 4 query tokens, contexts 226945/226946/226948, 64q/4kv heads, d 128, "
+                      "page 128, split-K + LSE reduce",
+            "fp8": {**figures["verify_fp8"], "target": ">= 70% of HBM peak (<= 128.5 us)"},
+            "bf16": {**figures["verify_bf16"], "target": ">= 70% of HBM peak (<= 249.1 us)"},
+            "pages_context_other_gpu": PAGES_VERIFY_CONTEXT},
+    }
 
     out = {
         "metric": "decode µs/layer + HBM GB/s; prefill fwd+bwd TFLOP/s vs MFMA peak",
-        "value": tf_fb,
+        "value": value,
         "unit": "TFLOP/s",
         "n_gpus": 1,
         "steps": args.steps,
@@ -336,119 +469,29 @@ def main():
         "dtype": "bf16",
         "data": "synthetic (seeded; no dataset)",
         "config": {
-            "workload": "prefill fwd+bwd: 8 packed seqs (lengths U[256,4096], seed 2, T=%d), "
-                        "32q/8kv heads, d 128, window 1024, sink, log gates; decode: 64 requests "
-                        "(contexts U[1,32768], seed 3), 64q/4kv heads, d 128, page 16, "
-                        "per-token fp8 e4m3fn KV, split-K + LSE reduce" % x.total_tokens,
-            "global_batch": len(x.seqlens), "seq_len": x.max_seqlen, "parallelism": "single-gpu",
+            "workload": "value: prefill forward+backward TFLOP/s on 8 packed seqs (lengths U[256,4096], "
+                        "seed 2, T=%d), 32q/8kv heads, d 128, window 1024, sink, log gates; the step also "
+                        "runs the 4x8192 d_qk 256 / d_v 512 prefill fwd+bwd, the 64-request per-token fp8 "
+                        "decode layer and the 3x4-token 227K verify (bf16 and fp8)" % x2.total_tokens,
+            "global_batch": len(x2.seqlens), "seq_len": x2.max_seqlen, "parallelism": "single-gpu",
         },
-        "prefill": {"fwd_us": us["fwd"], "bwd_us": us["bwd"],
-                    "fwd_us_median": tm.median_us("fwd"), "bwd_us_median": tm.median_us("bwd"),
-                    "bwd_path": "two-pass (deterministic)",
-                    "bwd_fused_dq_us": tf.mean_us("bwd_fused"),
-                    "bwd_fused_dq_tflops": f_bwd / (tf.mean_us("bwd_fused") * 1e-6) / 1e12,
-                    "fwd_tflops": tf_fwd,
-                    "bwd_tflops": tf_bwd, "fwdbwd_tflops": tf_fb,
-                    "fwd_frac_of_mfma_peak": tf_fwd / MFMA_BF16_PEAK_TFLOPS,
-                    "fwdbwd_frac_of_mfma_peak": tf_fb / MFMA_BF16_PEAK_TFLOPS,
-                    "flops_fwd": f_fwd, "flops_bwd": f_bwd},
-        "decode": {"us_per_layer": us["decode"], "us_per_layer_median": tm.median_us("decode"),
-                   "GBps": gbps, "frac_of_hbm_peak": gbps / HBM_PEAK_GBPS,
-                   "algorithmic_bytes": dec_bytes, "graph_us_per_layer": dec_graph_us,
-                   "graph_GBps": dec_bytes / (dec_graph_us * 1e-6) / 1e9},
+        "timing_method": f"per call: median of {args.repeats} repeats of the mean over "
+                         f"{args.iters} back-to-back calls, HIP events on the call's stream",
+        "workloads": workloads,
         "roofline": roof,
-        "phases": phases,
+        "machine": machine_info(),
     }
 
-    if args.extra:
-        extra = {}
-        for kvd, tag in ((synth.KV_BF16, "bf16"), (synth.KV_FP8_E4M3FN, "fp8")):
-            d4 = synth.verify_3x4_227k(kv_dtype=kvd, device=dev)
-            mlen4 = d4.max_seq_len
-            f = lambda: A.attn_decode_paged(d4.q, d4.cu_seqlens_q, 4, d4.k_cache, d4.v_cache, kvd,
-                                            d4.k_scale, d4.v_scale, d4.block_table, d4.seq_lens,
-                                            mlen4, d4.scale)
-            for _ in range(3):
-                f()
-            t4 = Timer()
-            for _ in range(20):
-                t4.run("v", f)
-            torch.cuda.synchronize()
-            u = t4.mean_us("v")
-            extra[f"verify_{tag}"] = {"us_per_layer": u, "GBps": decode_bytes(d4) / (u * 1e-6) / 1e9}
-            del d4
-        # decode with sink, 4096-token window and log gate on the 64-request decode cache
-        df = synth.decode_64req_fp8(device=dev, with_sink=True, window=4096, with_gate=True)
-        dmax = df.max_seq_len
-        ff = lambda: A.attn_decode_paged(df.q, df.cu_seqlens_q, 1, df.k_cache, df.v_cache, df.kv_dtype,
-                                         df.k_scale, df.v_scale, df.block_table, df.seq_lens, dmax, df.scale,
-                                         sink=df.sink, window=df.window, g_cache=df.g_cache)
-        for _ in range(3):
-            ff()
-        tf_ = Timer()
-        for _ in range(20):
-            tf_.run("f", ff)
-        torch.cuda.synchronize()
-        uf = tf_.mean_us("f")
-        vis = [min(int(L), 4096) for L in df.seq_lens.tolist()]     # keys inside the window (1 query each)
-        Hkv_, D_, Hq_ = df.k_cache.shape[1], df.k_cache.shape[3], df.q.shape[1]
-        fbytes = sum(vis) * (Hkv_ * (2 * D_ + 8) + Hq_ * 4)          # fp8 K+V, two scales, gate per query head
-        extra["decode_sink_window4096_gate"] = {"us_per_layer": uf, "GBps": fbytes / (uf * 1e-6) / 1e9,
-                                                "algorithmic_bytes": fbytes}
-        del df
-        # per-token fp8 KV-cache write: a 32K-token prefill's keys and values
-        xw = synth.kv_write_inputs(32768, 4, 128, 16, 2048 + 64, seed=1, skip_frac=0.0, device=dev)
-        fw = lambda: A.attn_kv_cache_write_fp8(xw["k_new"], xw["v_new"], xw["slot_mapping"], xw["k_cache"],
-                                               xw["v_cache"], xw["k_scale"], xw["v_scale"])
-        for _ in range(3):
-            fw()
-        tw = Timer()
-        for _ in range(20):
-            tw.run("w", fw)
-        torch.cuda.synchronize()
-        uw = tw.mean_us("w")
-        wbytes = 32768 * 4 * 2 * (2 * 128 + 128 + 4)    # bf16 in, fp8 codes + fp32 scale out
-        extra["kv_cache_write_fp8"] = {"tokens": 32768, "kv_heads": 4, "head_dim": 128, "us": uw,
-                                       "GBps": wbytes / (uw * 1e-6) / 1e9,
-                                       "frac_of_hbm_peak": wbytes / (uw * 1e-6) / 1e9 / HBM_PEAK_GBPS}
-        del xw
-        # paged prefill: 4 chunks of 2048 new tokens over 4K-32K contexts, per-token fp8 cache
-        dp = synth.prefill_paged_bench(device=dev)
-        pmax, pq = dp.max_seq_len, dp.max_seqlen_q
-        fp = lambda: A.attn_prefill_paged(dp.q, dp.cu_seqlens_q, pq, dp.k_cache, dp.v_cache, dp.kv_dtype,
-                                          dp.k_scale, dp.v_scale, dp.block_table, dp.seq_lens, pmax, dp.scale)
-        fp()
-        tp = Timer()
-        for _ in range(5):
-            tp.run("p", fp)
-        torch.cuda.synchronize()
-        up = tp.mean_us("p")
-        pfl = synth.paged_attention_flops(dp.seq_lens.tolist(), dp.q_lens, dp.q.shape[1], dp.q.shape[2])
-        extra["prefill_paged_fp8"] = {"workload": "chunked prefill 4 x 2048 new tokens, contexts 4K-32K, "
-                                                  "h64 kv4 d128 page 16, per-token fp8 KV",
-                                      "us": up, "tflops": pfl / (up * 1e-6) / 1e12,
-                                      "frac_of_bf16_mfma_peak": pfl / (up * 1e-6) / 1e12 / MFMA_BF16_PEAK_TFLOPS}
-        del dp
-        x5 = synth.varlen_4x8192_wide_heads(device=dev)
-        f5f, f5b, _ = prefill_flops(x5)
-        o5, l5 = A.attn_fwd_varlen(x5.q, x5.k, x5.v, x5.cu_seqlens, x5.max_seqlen, x5.scale, 0,
-                                   x5.sink, x5.g)
-        t5 = Timer()
-        for _ in range(3):
-            t5.run("f", lambda: A.attn_fwd_varlen(x5.q, x5.k, x5.v, x5.cu_seqlens, x5.max_seqlen,
-                                                  x5.scale, 0, x5.sink, x5.g))
-            t5.run("b", lambda: A.attn_bwd_varlen(x5.q, x5.k, x5.v, o5, x5.do, l5, x5.cu_seqlens,
-                                                  x5.max_seqlen, x5.scale, 0, x5.sink, x5.g))
-        torch.cuda.synchronize()
-        extra["prefill_large_heads"] = {
-            "fwd_us": t5.mean_us("f"), "bwd_us": t5.mean_us("b"),
-            "fwd_tflops": f5f / (t5.mean_us("f") * 1e-6) / 1e12,
-            "bwd_tflops": f5b / (t5.mean_us("b") * 1e-6) / 1e12}
-        out["extra_workloads"] = extra
-
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_oracle_baseline(x)
-        out["decode"]["cpu_oracle"] = cpu_oracle_decode_baseline(d)
+        out["cpu_baseline"] = cpu_prefill(x2, 10.0, label="8-sequence window-1024 prefill")
+        workloads["prefill_8seq_window1024"]["cpu_oracle"] = out["cpu_baseline"]
+        workloads["prefill_4x8192_large_heads"]["cpu_oracle"] = cpu_prefill(
+            x5, 8.0, slice_len=4096, label="4x8192 large-head prefill")
+        workloads["decode_64req_fp8"]["cpu_oracle"] = cpu_decode(d3, 6.0, label="64-request decode")
+        workloads["verify_3x4_227k"]["cpu_oracle_fp8"] = cpu_decode(d4f, 4.0, clip=32768,
+                                                                    label="227K fp8 verify")
+        workloads["verify_3x4_227k"]["cpu_oracle_bf16"] = cpu_decode(d4b, 4.0, clip=32768,
+                                                                     label="227K bf16 verify")
     print(json.dumps(out), flush=True)
 
 
