@@ -34,8 +34,8 @@ COMMON_FLAGS = [
 # Per-file extra flags.  decode.hip, fwd.hip and bwd2.hip: keep MFMA
 # accumulators in VGPRs; the default AGPR form makes the compiler copy
 # accumulators between register files around branches inside the loops (and
-# spills in the widest backward kernels).  The wide-head forward kernels
-# (fwd_wide.hip) need the AGPRs for capacity.
+# spills in the widest backward kernels).  The large-head forward kernel
+# (fwd_wide.hip) keeps its O accumulators in AGPRs.
 FILE_FLAGS = {
     "decode.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
     "fwd.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],

@@ -1,6 +1,6 @@
 // Forward entry points: the gate prefix and the head-dim 64 and 128 forward
 // kernels (the kernel itself is in fwd_pipe.h; head dims 256 and 512 use the
-// kernel in fwd_kernel.h, instantiated in fwd_wide.hip, which is built with
+// kernel in fwd_large.h, instantiated in fwd_wide.hip, which is built with
 // different register allocation options).
 #include "fwd_pipe.h"
 

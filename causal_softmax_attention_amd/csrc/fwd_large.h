@@ -1,0 +1,304 @@
+// Packed variable-length causal attention forward for large value heads
+// (d_v 256 or 512) on gfx950.
+//
+// Method (fla issue #1322, Description): the same definition as the other
+// forward kernels (GQA, gate bias G_i - G_j, sliding window, sink logit,
+// unequal query/key and value head dims up to 512); fp32 scores from bf16
+// operands, bf16 P in the PV product, O rounded to bf16, lse in fp32.
+//
+// gfx950 mapping: the O tile of a 512-wide value head does not fit one
+// wave's registers for more than 16 query rows, and with 16 rows per wave
+// every K and V operand read from LDS would feed a single MFMA, which makes
+// such a layout LDS-bound.  Here the work of a workgroup is split two ways:
+//  * 8 wavefronts, 128 (query head, row) slots: HPW heads of one KV head
+//    (GQA-packed) x 128 / HPW rows.  Wave w owns slots 16 w .. 16 w + 15:
+//    it computes S = Q K^T for them (v_mfma_f32_16x16x32_bf16, Q in
+//    registers), the online softmax (max, lazy rescale, exp, row sum) and
+//    writes P (bf16) and its rescale factors to LDS.
+//  * then every wave computes O for all 128 slots over its eighth of d_v:
+//    O^T += V^T P^T with v_mfma_f32_32x32x16_bf16 (V^T from
+//    ds_read_b64_tr_b16, P^T rows from the padded P tile), so each V
+//    fragment feeds four MFMAs and each P fragment feeds one per 32 columns.
+//    Before accumulating it applies the rescale factors the owners wrote.
+// Two barriers per 32-key tile: K/V of the tile in LDS, then P written.
+// K and V tiles arrive by direct global->LDS copies into a two-stage ring;
+// K uses the row-read swizzle of tile_swz, V a swizzle that keeps the four
+// rows of a transposed read on different 64-byte bank segments; P rows are
+// padded to 80 bytes, so the 32 rows of a P read fall on different banks.
+#pragma once
+#include "common.h"
+#include "kernels.h"
+
+namespace attn {
+
+template <int DQK, int DV, bool GATED, int HPW>
+__global__ __launch_bounds__(512) void fwd_large_kernel(FwdParams p) {
+  constexpr int NW = 8;                 // wavefronts
+  constexpr int SLOTS = 16 * NW;        // (head, row) slots of the workgroup
+  constexpr int BMH = SLOTS / HPW;      // rows per head
+  constexpr int BN = 32;                // keys per tile
+  constexpr int KB = BN / 16;           // 16-key blocks of S
+  constexpr int KS = DQK / 32;          // QK k-steps
+  constexpr int DVW = DV / NW;          // value columns per wave in PV
+  constexpr int NDB = DVW / 32;         // 32-wide column blocks per wave
+  constexpr int NRB = SLOTS / 32;       // 32-slot row blocks
+  constexpr int PS = BN / 16;           // PV k-steps
+  constexpr int KRB = DQK * 2, VRB = DV * 2;
+  constexpr int PRB = BN * 2 + 16;      // P row bytes, padded (80: rows land on distinct banks)
+  constexpr int KBLK = BN * KRB / 1024, VBLK = BN * VRB / 1024;   // 1 KB copy blocks per tile
+  static_assert(NDB >= 1 && DVW % 32 == 0, "value columns per wave");
+  static_assert(KBLK >= 1 && VBLK % NW == 0, "copy blocks");
+  static_assert(HPW == 1 || HPW == 2 || HPW == 4, "heads per workgroup");
+  constexpr int GH = HPW < 2 ? 2 : HPW;  // gate rows held (one copy fills two heads)
+  __shared__ __attribute__((aligned(1024))) uint8_t k_lds[2][BN * KRB];
+  __shared__ __attribute__((aligned(1024))) uint8_t v_lds[2][BN * VRB];
+  __shared__ __attribute__((aligned(16))) uint8_t p_lds[SLOTS * PRB];
+  __shared__ __attribute__((aligned(16))) float alpha_lds[SLOTS];
+  __shared__ __attribute__((aligned(16))) float l_lds[SLOTS];
+  __shared__ __attribute__((aligned(16))) float gk_lds[2][GH][BN];
+
+  const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
+  const int li = lane & 15, g = lane >> 4;
+  const int grp = p.Hq / p.Hkv;
+  const int nchunk = p.Hq / HPW;
+  const int hx = (nchunk % 8 == 0) ? (blockIdx.x % 8) * (nchunk / 8) + blockIdx.x / 8 : blockIdx.x;
+  const int h0 = hx * HPW;              // first head of the workgroup
+  const int kvh = h0 / grp;
+  const int n = blockIdx.z;
+  const int tile = gridDim.y - 1 - blockIdx.y;
+  const int seq0 = p.cu[n];
+  const int L = p.cu[n + 1] - seq0;
+  const int i0 = tile * BMH;
+  if (i0 >= L) return;
+  const int W = p.window;
+  const float c = p.scale_log2;
+
+  // ---- this wave's own slots: head hw, rows r0 .. r0 + 15 ----
+  const int hw = h0 + wave % HPW;
+  const int r0 = i0 + 16 * (wave / HPW);
+  const int r_last = min(r0 + 16, L) - 1;
+  const int row = r0 + li;
+  bf16x8 qop[KS];
+  float gq = 0.f;
+  if (row < L) {
+    const bf16* qp = reinterpret_cast<const bf16*>(p.q) + ((long)(seq0 + row) * p.Hq + hw) * DQK + 8 * g;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) qop[ks] = *reinterpret_cast<const bf16x8*>(qp + 32 * ks);
+    if constexpr (GATED) gq = p.G2[(long)hw * p.T + seq0 + row];
+  } else {
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) qop[ks] = bf16x8{};
+  }
+  const float sink2 = p.sink ? p.sink[hw] * kLog2e : kNegBig;
+  float m_run = p.sink ? sink2 - gq : kNegBig;   // kept without the row's gate term gq
+  float l_run = p.sink ? 1.f : 0.f;
+
+  // ---- O of all slots over this wave's value columns ----
+  f32x16 oacc[NDB][NRB];
+#pragma unroll
+  for (int db = 0; db < NDB; ++db)
+#pragma unroll
+    for (int rb = 0; rb < NRB; ++rb) oacc[db][rb] = f32x16{};
+
+  // ---- key range of the workgroup ----
+  const int kv_lo = W > 0 ? max(0, i0 - W + 1) : 0;
+  const int kv_hi = min(L, i0 + BMH);
+  const int t_begin = kv_lo / BN, t_end = (kv_hi + BN - 1) / BN;
+
+  // ---- tile copies: wave w copies the 1 KB blocks w, w + 8, ... ----
+  const uint8_t* kbase = reinterpret_cast<const uint8_t*>(p.k) + ((long)seq0 * p.Hkv + kvh) * KRB;
+  const uint8_t* vbase = reinterpret_cast<const uint8_t*>(p.v) + ((long)seq0 * p.Hkv + kvh) * VRB;
+  const int kstride = p.Hkv * KRB, vstride = p.Hkv * VRB;
+  auto v_swz = [](int r) { return (r & 3) << 2; };   // chunk bits 2-3: a read's 4 rows on 4 segments
+  auto fetch = [&](int t) {
+    const int j0 = t * BN, st = (t - t_begin) & 1;
+    const bool tail = j0 + BN > L;
+    const uint8_t* kb = kbase + (long)j0 * kstride;
+    const uint8_t* vb = vbase + (long)j0 * vstride;
+#pragma unroll
+    for (int jj = 0; jj < (KBLK + NW - 1) / NW; ++jj) {
+      const int j = wave + NW * jj;
+      if (KBLK % NW != 0 && j >= KBLK) break;         // uniform
+      const int o = j * 1024 + lane * 16;
+      const int r = o / KRB;
+      const int rr = tail ? min(r, L - 1 - j0) : r;   // rows past the end re-read the last row
+      const uint32_t off = (uint32_t)(rr * kstride + ((((o % KRB) >> 4) ^ tile_swz<KRB>(r)) << 4));
+      dma16(kb, off, __builtin_amdgcn_readfirstlane(lds_addr(k_lds[st]) + j * 1024));
+    }
+#pragma unroll
+    for (int jj = 0; jj < VBLK / NW; ++jj) {
+      const int j = wave + NW * jj;
+      const int o = j * 1024 + lane * 16;
+      const int r = o / VRB;
+      const int rr = tail ? min(r, L - 1 - j0) : r;
+      const uint32_t off = (uint32_t)(rr * vstride + ((((o % VRB) >> 4) ^ v_swz(r)) << 4));
+      dma16(vb, off, __builtin_amdgcn_readfirstlane(lds_addr(v_lds[st]) + j * 1024));
+    }
+    if constexpr (GATED) {
+      // gate terms of two heads per copy: lane l -> head 2 w + l / 32, key l % 32
+      if (2 * wave < HPW) {
+        const float* gb = p.G2 + (long)(h0 + 2 * wave) * p.T + seq0;   // wave-uniform base
+        const int hsel = min(2 * wave + (lane >> 5), HPW - 1) - 2 * wave;
+        const uint32_t go = (uint32_t)((hsel * p.T + min(j0 + (lane & 31), L - 1)) * 4);
+        dma4(gb, go, __builtin_amdgcn_readfirstlane(lds_addr(&gk_lds[st][2 * wave][0])));
+      }
+    }
+  };
+
+  // ---- per-lane LDS offsets ----
+  // K fragment (16-key block kb, k-step ks): row kb*16 + li, chunk 4 ks + g
+  uint32_t k_lane[KS];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) k_lane[ks] = (uint32_t)tile_off<KRB>(li, 64 * ks + 16 * g);
+  // P write: slot 16 w + li, keys kb*16 + 4g .. + 3 (8 bytes)
+  const uint32_t p_wr = (uint32_t)((16 * wave + li) * PRB + 8 * g);
+  // P^T fragment (row block rb, k-step s): slot rb*32 + l%32, keys 16 s + 8 h .. + 7
+  const int hh2 = lane >> 5;
+  const uint32_t p_rd = (uint32_t)((lane & 31) * PRB + 16 * hh2);
+  // V^T fragment (k-step s, column block db, read jr): row 16 s + 8 h + 4 jr + j,
+  // column wave*DVW + db*32 + 16 half + 4 cc (j = (l%16)/4, cc = l%4, half = (l/16)%2)
+  const int vj = (lane & 15) >> 2, vcc = lane & 3, vhalf = (lane >> 4) & 1;
+  uint32_t v_lane[NDB];
+#pragma unroll
+  for (int db = 0; db < NDB; ++db) {
+    const int r = 8 * hh2 + vj;   // row within the 16-key step (r & 3 = vj)
+    const int col = wave * DVW + db * 32 + 16 * vhalf + 4 * vcc;
+    const int ch = (col * 2) >> 4;
+    v_lane[db] = (uint32_t)(r * VRB + ((ch ^ v_swz(r)) << 4) + ((col * 2) & 15));
+  }
+
+  fetch(t_begin);
+  for (int t = t_begin; t < t_end; ++t) {
+    const int j0 = t * BN, st = (t - t_begin) & 1;
+    // ---- K/V of tile t in LDS; P of tile t-1 consumed by every wave ----
+    wait_vm<0>();
+    lds_barrier();
+    if (t + 1 < t_end) fetch(t + 1);
+
+    // ---- S = Q K^T for this wave's 16 slots (C lane: row li, keys 4g + i) ----
+    f32x4 s[KB];
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) {
+      s[kb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        const bf16x8 a = *reinterpret_cast<const bf16x8*>(k_lds[st] + k_lane[ks] + kb * 16 * KRB);
+        s[kb] = mfma16x16x32(a, qop[ks], s[kb]);
+      }
+    }
+    // ---- bias, mask, online softmax ----
+    const bool need_mask = (j0 + BN - 1 > r0) || (W > 0 && r_last - j0 >= W) || (j0 + BN > L) || (r_last < r0 + 15);
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) {
+      f32x4 gk = {0.f, 0.f, 0.f, 0.f};
+      if constexpr (GATED) gk = *reinterpret_cast<const f32x4*>(&gk_lds[st][wave % HPW][kb * 16 + 4 * g]);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) s[kb][i] = GATED ? __builtin_fmaf(s[kb][i], c, -gk[i]) : s[kb][i] * c;
+    }
+    if (need_mask) {
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int key = j0 + kb * 16 + 4 * g + i;
+          const bool vis = key <= row && key < L && (W <= 0 || row - key < W);
+          s[kb][i] = vis ? s[kb][i] : -INFINITY;
+        }
+    }
+    float mx = fmaxf(fmaxf(s[0][0], s[0][1]), fmaxf(s[0][2], s[0][3]));
+#pragma unroll
+    for (int kb = 1; kb < KB; ++kb) mx = fmaxf(mx, fmaxf(fmaxf(s[kb][0], s[kb][1]), fmaxf(s[kb][2], s[kb][3])));
+    mx = xgroup_max(mx);
+    float alpha = 1.f;
+    if (__builtin_expect(__any(mx > m_run + kRescaleSlack), 0)) {
+      const float m_new = fmaxf(m_run, mx);
+      alpha = fast_exp2(m_run - m_new);
+      l_run *= alpha;
+      m_run = m_new;
+    }
+    float rs = 0.f;
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) {
+      f32x4 e;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) e[i] = fast_exp2(s[kb][i] - m_run);
+      rs += (e[0] + e[1]) + (e[2] + e[3]);
+      *reinterpret_cast<bf16x4*>(p_lds + p_wr + kb * 32) = to_bf16x4(e);
+    }
+    l_run += xgroup_sum(rs);
+    if (g == 0) alpha_lds[16 * wave + li] = alpha;
+    lds_barrier();   // P and the rescale factors of tile t visible to every wave
+
+    // ---- O^T += V^T P^T over this wave's columns, for all slots ----
+#pragma unroll
+    for (int rb = 0; rb < NRB; ++rb) {
+      const float a = alpha_lds[rb * 32 + (lane & 31)];
+      if (__builtin_expect(__any(a != 1.f), 0)) {
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) oacc[db][rb] *= a;
+      }
+    }
+#pragma unroll
+    for (int ps = 0; ps < PS; ++ps) {
+      bf16x8 pf[NRB];
+#pragma unroll
+      for (int rb = 0; rb < NRB; ++rb)
+        pf[rb] = *reinterpret_cast<const bf16x8*>(p_lds + p_rd + rb * 32 * PRB + ps * 32);
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) {
+        const uint8_t* vb = v_lds[st] + v_lane[db] + 16 * ps * VRB;
+        const bf16x8 vf = concat(lds_read_tr16(reinterpret_cast<const bf16*>(vb)),
+                                 lds_read_tr16(reinterpret_cast<const bf16*>(vb + 4 * VRB)));
+#pragma unroll
+        for (int rb = 0; rb < NRB; ++rb)
+          oacc[db][rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[rb], oacc[db][rb], 0, 0, 0);
+      }
+    }
+  }
+
+  // ---- finalize: row sums of every slot from their owners; O = acc / l ----
+  lds_barrier();
+  if (g == 0) l_lds[16 * wave + li] = l_run;
+  if (g == 0 && row < L) p.lse[(long)(seq0 + row) * p.Hq + hw] = (m_run + gq + fast_log2(l_run)) * kLn2;
+  lds_barrier();
+#pragma unroll
+  for (int rb = 0; rb < NRB; ++rb) {
+    const int slot = rb * 32 + (lane & 31);
+    const int ws = slot >> 4;                      // owner wave of the slot
+    const int sh = h0 + ws % HPW;
+    const int srow = i0 + 16 * (ws / HPW) + (slot & 15);
+    if (srow >= L) continue;
+    const float inv = 1.0f / l_lds[slot];
+    bf16* op = reinterpret_cast<bf16*>(p.o) + ((long)(seq0 + srow) * p.Hq + sh) * DV + wave * DVW + 4 * hh2;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const f32x4 x = f32x4{oacc[db][rb][4 * q], oacc[db][rb][4 * q + 1], oacc[db][rb][4 * q + 2],
+                              oacc[db][rb][4 * q + 3]} * inv;
+        *reinterpret_cast<bf16x4*>(op + db * 32 + 8 * q) = to_bf16x4(x);
+      }
+  }
+}
+
+template <int DQK, int DV, int HPW>
+static hipError_t launch_large_hpw(const FwdParams& p, hipStream_t st) {
+  constexpr int BMH = 128 / HPW;
+  const int tiles = (p.max_seqlen + BMH - 1) / BMH;
+  const dim3 grid(p.Hq / HPW, tiles, p.num_seqs);
+  if (p.G2 != nullptr)
+    fwd_large_kernel<DQK, DV, true, HPW><<<grid, 512, 0, st>>>(p);
+  else
+    fwd_large_kernel<DQK, DV, false, HPW><<<grid, 512, 0, st>>>(p);
+  return hipGetLastError();
+}
+
+template <int DQK, int DV>
+static hipError_t launch_large(const FwdParams& p, hipStream_t st) {
+  const int grp = p.Hq / p.Hkv;
+  if (grp % 4 == 0) return launch_large_hpw<DQK, DV, 4>(p, st);
+  if (grp % 2 == 0) return launch_large_hpw<DQK, DV, 2>(p, st);
+  return launch_large_hpw<DQK, DV, 1>(p, st);
+}
+
+}  // namespace attn
