@@ -31,15 +31,18 @@ COMMON_FLAGS = [
     "-Wno-unused-result",
 ]
 
-# Per-file extra flags.  decode.hip, fwd.hip and bwd2.hip: keep MFMA
+# Per-file extra flags.  decode.hip, fwd.hip and bwd2*.hip: keep MFMA
 # accumulators in VGPRs; the default AGPR form makes the compiler copy
 # accumulators between register files around branches inside the loops (and
 # spills in the widest backward kernels).  The large-head forward kernel
-# (fwd_wide.hip) keeps its O accumulators in AGPRs.
+# (fwd_wide.hip, fwd_large_qk*.hip) keeps its O accumulators in AGPRs.
+VGPR_FORM = ["-mllvm", "-amdgpu-mfma-vgpr-form"]
 FILE_FLAGS = {
-    "decode.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
-    "fwd.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
-    "bwd2.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+    "decode.hip": VGPR_FORM,
+    "fwd.hip": VGPR_FORM,
+    "bwd2.hip": VGPR_FORM,
+    "bwd2_qk128.hip": VGPR_FORM,
+    "bwd2_qk256.hip": VGPR_FORM,
 }
 
 

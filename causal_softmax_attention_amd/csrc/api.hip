@@ -49,8 +49,7 @@ size_t round_up(size_t x) { return (x + 255) & ~size_t(255); }
   } while (0)
 
 bool fwd_dims_supported(int dqk, int dv) {
-  return (dqk == 64 && dv == 64) || (dqk == 128 && dv == 128) || (dqk == 256 && dv == 256) ||
-         (dqk == 256 && dv == 512);
+  return (dqk == 64 || dqk == 128 || dqk == 256) && (dv == 64 || dv == 128 || dv == 256 || dv == 512);
 }
 
 int check_prefill_common(const void* q, const void* k, const void* v, const int32_t* cu, int num_seqs,
@@ -60,7 +59,7 @@ int check_prefill_common(const void* q, const void* k, const void* v, const int3
   REQUIRE(Hq >= 1 && Hkv >= 1, ATTN_ERR_INVALID, "head counts must be positive (Hq=%d Hkv=%d)", Hq, Hkv);
   REQUIRE(Hq % Hkv == 0, ATTN_ERR_INVALID, "num_q_heads (%d) must be a multiple of num_kv_heads (%d)", Hq, Hkv);
   REQUIRE(fwd_dims_supported(dqk, dv), ATTN_ERR_UNSUPPORTED,
-          "head dims (d_qk=%d, d_v=%d) not supported; supported: (64,64) (128,128) (256,256) (256,512)",
+          "head dims (d_qk=%d, d_v=%d) not supported; supported: d_qk in {64, 128, 256}, d_v in {64, 128, 256, 512}",
           dqk, dv);
   REQUIRE(std::isfinite(scale) && scale > 0.f, ATTN_ERR_INVALID,
           "softmax_scale must be finite and positive (got %g)", (double)scale);
@@ -372,7 +371,6 @@ int paged_attention(bool prefill, const void* q, const int32_t* cu_seqlens_q, in
           "scales are only read with an fp8 KV cache");
   REQUIRE(head_dim == 64 || head_dim == 128, ATTN_ERR_UNSUPPORTED, "head_dim %d not supported (64, 128)",
           head_dim);
-  REQUIRE(!fp8 || head_dim == 128, ATTN_ERR_UNSUPPORTED, "the fp8 KV cache is supported with head_dim 128");
   REQUIRE(block_size == 16 || block_size == 32 || block_size == 64 || block_size == 128,
           ATTN_ERR_UNSUPPORTED, "block_size %d not supported (16, 32, 64, 128)", block_size);
   REQUIRE(num_q_heads >= 1 && num_kv_heads >= 1, ATTN_ERR_INVALID, "head counts must be positive");

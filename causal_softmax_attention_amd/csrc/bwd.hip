@@ -327,27 +327,33 @@ hipError_t launch_fill_zero(float* x, long n, hipStream_t st) {
 }
 
 template <int DQK, int DV>
+static hipError_t launch_fused_t(const BwdParams& p, hipStream_t st) {
+  const long rows = (long)p.T * p.Hq;
+  const int ktiles = (p.max_seqlen + 63) / 64;
+  bwd_fused_kernel<DQK, DV><<<dim3(p.Hkv, ktiles, p.num_seqs), 256, 0, st>>>(p);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const long n4 = rows * DQK / 4;
+  bwd_dq_convert_kernel<DQK><<<dim3((unsigned)((n4 + 255) / 256)), 256, 0, st>>>(
+      p.dq_acc, reinterpret_cast<bf16*>(p.dq), n4);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  if (p.dg != nullptr) {
+    gate_grad_kernel<<<dim3(p.Hq, p.num_seqs), 256, 0, st>>>(p.dG, nullptr, p.cu, p.dg, p.Hq, p.Hq, 1);
+    e = hipGetLastError();
+  }
+  return e;
+}
+
+template <int DQK, int DV>
 static hipError_t launch_bwd_t(const BwdParams& p, bool fused, hipStream_t st) {
   const long rows = (long)p.T * p.Hq;
   constexpr int RPB = 256 / (DV / 8);
   bwd_pre_kernel<DQK, DV><<<dim3((unsigned)((rows + RPB - 1) / RPB)), 256, 0, st>>>(p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  if (fused) {
-    const int ktiles = (p.max_seqlen + 63) / 64;
-    bwd_fused_kernel<DQK, DV><<<dim3(p.Hkv, ktiles, p.num_seqs), 256, 0, st>>>(p);
-    e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    const long n4 = rows * DQK / 4;
-    bwd_dq_convert_kernel<DQK><<<dim3((unsigned)((n4 + 255) / 256)), 256, 0, st>>>(
-        p.dq_acc, reinterpret_cast<bf16*>(p.dq), n4);
-    e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    if (p.dg != nullptr) {
-      gate_grad_kernel<<<dim3(p.Hq, p.num_seqs), 256, 0, st>>>(p.dG, nullptr, p.cu, p.dg, p.Hq, p.Hq, 1);
-      e = hipGetLastError();
-    }
-    return e;
+  if constexpr (DQK <= 128) {   // the fused-dQ path covers query/key head dims up to 128
+    if (fused) return launch_fused_t<DQK, DV>(p, st);
   }
   e = launch_bwd_two_pass(p, DQK, DV, st);
   if (e != hipSuccess) return e;
@@ -362,11 +368,21 @@ hipError_t launch_bwd(const BwdParams& p, int dqk, int dv, bool fused, hipStream
   if (p.num_seqs == 0 || p.T == 0 || p.max_seqlen == 0) {
     return hipSuccess;
   }
-  if (dqk == 64 && dv == 64) return launch_bwd_t<64, 64>(p, fused, st);
-  if (dqk == 128 && dv == 128) return launch_bwd_t<128, 128>(p, fused, st);
-  if (dqk == 256 && dv == 256) return launch_bwd_t<256, 256>(p, fused, st);
-  if (dqk == 256 && dv == 512) return launch_bwd_t<256, 512>(p, fused, st);
-  return hipErrorInvalidValue;
+  switch (dqk * 1000 + dv) {
+    case 64064: return launch_bwd_t<64, 64>(p, fused, st);
+    case 64128: return launch_bwd_t<64, 128>(p, fused, st);
+    case 64256: return launch_bwd_t<64, 256>(p, fused, st);
+    case 64512: return launch_bwd_t<64, 512>(p, fused, st);
+    case 128064: return launch_bwd_t<128, 64>(p, fused, st);
+    case 128128: return launch_bwd_t<128, 128>(p, fused, st);
+    case 128256: return launch_bwd_t<128, 256>(p, fused, st);
+    case 128512: return launch_bwd_t<128, 512>(p, fused, st);
+    case 256064: return launch_bwd_t<256, 64>(p, fused, st);
+    case 256128: return launch_bwd_t<256, 128>(p, fused, st);
+    case 256256: return launch_bwd_t<256, 256>(p, fused, st);
+    case 256512: return launch_bwd_t<256, 512>(p, fused, st);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 }  // namespace attn

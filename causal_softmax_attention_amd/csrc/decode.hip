@@ -38,9 +38,10 @@
 //   * page ids come through scalar loads, issued at the end of the step
 //     before the one that uses them.
 // K and V tiles are stored as 32 rows of D * elem bytes with 16-byte chunks
-// permuted per row so that the two read patterns are free of bank conflicts:
-// MFMA operand rows for K (ds_read_b128) and transposed reads for V
-// (ds_read_b64_tr_b8 for fp8, ds_read_b64_tr_b16 for bf16).
+// permuted per row so that the two read patterns are free of bank conflicts
+// under the bank model stated with the permutations below: MFMA operand rows
+// for K (ds_read_b128) and transposed reads for V (ds_read_b64_tr_b8 for
+// fp8, ds_read_b64_tr_b16 for bf16).
 //   fp8 cache: K bytes become bf16 with v_cvt_scalef32_pk_bf16_fp8 (exact:
 //     every e4m3 value is a bf16 value; two bytes per instruction) and
 //     S^T = K Q^T runs on v_mfma_f32_16x16x32_bf16 with the bf16 query as
@@ -88,22 +89,35 @@ __device__ __forceinline__ bf16x8 fp8x8_to_bf16x8(i32x2 w) {
   return bf16x8{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
 }
 
-// Chunk permutations of the K and V tiles (ROWB bytes per row).
-//   K, read as MFMA rows: 16 lanes read the same logical chunk of 16
-//   consecutive rows.  128-byte rows: rows of equal parity share banks, so
-//   the 8 even (odd) rows must land on 8 different chunk positions.
-//   256-byte rows: all rows share banks, 16 different positions.
+// Chunk permutations of the K and V tiles (ROWB bytes per row; 16-byte
+// chunk c of row r sits at chunk position c ^ swz(r)).  Bank model (measured
+// on gfx950 with the bank-conflict counter): ds_read_b128 serves 32 lanes
+// at a time over 512 bytes of banks, the transposed reads 32 lanes over
+// 256 bytes; a read is conflict-free when those lanes hit distinct bytes
+// modulo that span.
+//   K, read as MFMA rows: lanes (row li of 16, group g) read logical chunk
+//   g KCH + c of their row, so one instruction covers two chunks (g = 0, 1,
+//   KCH apart) of 16 rows.  Rows 512 / ROWB apart share banks, and the
+//   chunk pairs of those rows must land on distinct positions:
+//     256-byte rows (8 rows per parity, chunks c and c + 4): bits 0, 1
+//       and 3 of swz(r) distinct over the 8 rows;
+//     128-byte rows (4 rows per class mod 4, chunks c and c + 2): bits 0
+//       and 2 distinct over the 4 rows;
+//     64-byte rows (2 rows per class mod 8, chunks 0 and 1): bit 1.
 template <int ROWB>
 __device__ __forceinline__ int swz_k(int r) {
-  if constexpr (ROWB == 256) return r & 15;
-  else return (r >> 1) & 7;
+  if constexpr (ROWB == 256) return ((r >> 1) & 3) | (((r >> 3) & 1) << 3);
+  else if constexpr (ROWB == 128) return ((r >> 2) & 1) | (((r >> 3) & 1) << 2);
+  else return ((r >> 3) & 1) << 1;
 }
 //   V, read transposed: fp8 lane groups read one chunk of rows
 //   {4g..4g+3, 16+4g..16+4g+3}; bf16 groups read two adjacent chunks of
-//   rows 4g..4g+3 (and 16+4g..).
+//   rows 4g..4g+3 (and 16+4g..).  The rows a read covers that share banks
+//   (256 / ROWB apart) land on distinct positions.
 template <int ROWB, bool FP8>
 __device__ __forceinline__ int swz_v(int r) {
-  if constexpr (FP8) return ((r >> 1) & 3) | ((r >> 2) & 4);
+  if constexpr (FP8 && ROWB == 64) return ((r >> 2) & 1) | (((r >> 4) & 1) << 1);
+  else if constexpr (FP8) return ((r >> 1) & 3) | ((r >> 2) & 4);
   else if constexpr (ROWB == 256) return (r & 7) << 1;
   else return ((r >> 1) & 3) << 1;
 }
@@ -120,7 +134,7 @@ __global__ __launch_bounds__(64 * W) void decode_splitk_kernel(DecodeParams p) {
   constexpr int RPI = 1024 / ROWB;     // rows per copy instruction (64 lanes x 16 B)
   constexpr int NT = 32 * ROWB / 1024; // copy instructions per 32-row tile
   constexpr int NTW = NT / W;          // ... issued by each wave
-  static_assert(NT % W == 0 && (ROWB == 128 || ROWB == 256), "tile split");
+  static_assert(NT % W == 0 && (ROWB == 64 || ROWB == 128 || ROWB == 256), "tile split");
   constexpr int KS = D / 32;           // bf16 k-steps of 32 over the head dim
   constexpr int DPG = 8 * KS;          // head-dim elements per 16-lane group
   constexpr int KCH = DPG * ES / 16;   // 16-byte K chunks per lane and key block
@@ -644,7 +658,13 @@ struct DecodeShape {
 };
 template <int D, bool FP8, typename F>
 static auto with_shape(int row_blocks, F f) {
-  if (row_blocks > 4) return f(DecodeShape<D, FP8, 4, 2, kDecNstPrefill>{});
+  // 64-byte rows (fp8, D = 64): a 32-key tile is two copies, so at most two
+  // waves share it; the prefill block keeps 128 rows as two waves of four
+  if constexpr (D * (FP8 ? 1 : 2) < 128) {
+    if (row_blocks > 4) return f(DecodeShape<D, FP8, 2, 4, kDecNstPrefill>{});
+  } else {
+    if (row_blocks > 4) return f(DecodeShape<D, FP8, 4, 2, kDecNstPrefill>{});
+  }
   if (row_blocks <= 1) return f(DecodeShape<D, FP8, 1, 1, kDecNst1>{});
   if (row_blocks == 2) return f(DecodeShape<D, FP8, 1, 2, kDecNst2>{});
   return f(DecodeShape<D, FP8, 2, 2, FP8 ? kDecNst4Fp8 : kDecNst4Bf16>{});
@@ -661,7 +681,7 @@ static hipError_t launch_w(DecodeParams& p, hipStream_t st) {
 hipError_t launch_decode_splitk(DecodeParams& p, int head_dim, bool fp8, hipStream_t st) {
   if (p.row_blocks < 1) return hipErrorInvalidValue;
   if (head_dim == 128) return fp8 ? launch_w<128, true>(p, st) : launch_w<128, false>(p, st);
-  if (head_dim == 64 && !fp8) return launch_w<64, false>(p, st);
+  if (head_dim == 64) return fp8 ? launch_w<64, true>(p, st) : launch_w<64, false>(p, st);
   return hipErrorInvalidValue;
 }
 
@@ -677,7 +697,12 @@ int decode_balanced_groups(const DecodeParams& p, int head_dim, bool fp8) {
       using S = decltype(sh);
       return balanced_groups_t<128, false, S::W, S::RBW, S::NST>(p);
     });
-  if (head_dim == 64 && !fp8)
+  if (head_dim == 64 && fp8)
+    return with_shape<64, true>(p.row_blocks, [&](auto sh) {
+      using S = decltype(sh);
+      return balanced_groups_t<64, true, S::W, S::RBW, S::NST>(p);
+    });
+  if (head_dim == 64)
     return with_shape<64, false>(p.row_blocks, [&](auto sh) {
       using S = decltype(sh);
       return balanced_groups_t<64, false, S::W, S::RBW, S::NST>(p);

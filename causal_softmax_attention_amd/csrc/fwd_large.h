@@ -1,5 +1,6 @@
-// Packed variable-length causal attention forward for large value heads
-// (d_v 256 or 512) on gfx950.
+// Packed variable-length causal attention forward for large heads on
+// gfx950: value heads of 256 or 512 (any query/key head dim), and query/key
+// heads of 256 with value heads of 64 or 128.
 //
 // Method (fla issue #1322, Description): the same definition as the other
 // forward kernels (GQA, gate bias G_i - G_j, sliding window, sink logit,
@@ -10,20 +11,21 @@
 // wave's registers for more than 16 query rows, and with 16 rows per wave
 // every K and V operand read from LDS would feed a single MFMA, which makes
 // such a layout LDS-bound.  Here the work of a workgroup is split two ways:
-//  * 8 wavefronts, 128 (query head, row) slots: HPW heads of one KV head
-//    (GQA-packed) x 128 / HPW rows.  Wave w owns slots 16 w .. 16 w + 15:
-//    it computes S = Q K^T for them (v_mfma_f32_16x16x32_bf16, Q in
-//    registers), the online softmax (max, lazy rescale, exp, row sum) and
-//    writes P (bf16) and its rescale factors to LDS.
-//  * then every wave computes O for all 128 slots over its eighth of d_v:
+//  * NW wavefronts (8 for d_v >= 256, d_v / 32 below), 16 NW (query head,
+//    row) slots: HPW heads of one KV head (GQA-packed) x 16 NW / HPW rows.
+//    Wave w owns slots 16 w .. 16 w + 15: it computes S = Q K^T for them
+//    (v_mfma_f32_16x16x32_bf16, Q in registers), the online softmax (max,
+//    lazy rescale, exp, row sum) and writes P (bf16) and its rescale factors
+//    to LDS.
+//  * then every wave computes O for all slots over its 1 / NW of d_v:
 //    O^T += V^T P^T with v_mfma_f32_32x32x16_bf16 (V^T from
 //    ds_read_b64_tr_b16, P^T rows from the padded P tile), so each V
-//    fragment feeds four MFMAs and each P fragment feeds one per 32 columns.
+//    fragment feeds 16 NW / 32 MFMAs and each P fragment one per 32 columns.
 //    Before accumulating it applies the rescale factors the owners wrote.
 // Two barriers per 32-key tile: K/V of the tile in LDS, then P written.
 // K and V tiles arrive by direct global->LDS copies into a two-stage ring;
-// K uses the row-read swizzle of tile_swz, V a swizzle that keeps the four
-// rows of a transposed read on different 64-byte bank segments; P rows are
+// K uses the row-read swizzle of tile_swz, V a swizzle that keeps the rows
+// of a transposed read on different bank segments; P rows are
 // padded to 80 bytes, so the 32 rows of a P read fall on different banks.
 #pragma once
 #include "common.h"
@@ -31,9 +33,13 @@
 
 namespace attn {
 
+// Wavefronts per workgroup: one per 32 value columns, at most 8.
+template <int DV>
+constexpr int large_waves() { return DV >= 256 ? 8 : DV / 32; }
+
 template <int DQK, int DV, bool GATED, int HPW>
-__global__ __launch_bounds__(512) void fwd_large_kernel(FwdParams p) {
-  constexpr int NW = 8;                 // wavefronts
+__global__ __launch_bounds__(64 * large_waves<DV>()) void fwd_large_kernel(FwdParams p) {
+  constexpr int NW = large_waves<DV>(); // wavefronts
   constexpr int SLOTS = 16 * NW;        // (head, row) slots of the workgroup
   constexpr int BMH = SLOTS / HPW;      // rows per head
   constexpr int BN = 32;                // keys per tile
@@ -48,7 +54,8 @@ __global__ __launch_bounds__(512) void fwd_large_kernel(FwdParams p) {
   constexpr int KBLK = BN * KRB / 1024, VBLK = BN * VRB / 1024;   // 1 KB copy blocks per tile
   static_assert(NDB >= 1 && DVW % 32 == 0, "value columns per wave");
   static_assert(KBLK >= 1 && VBLK % NW == 0, "copy blocks");
-  static_assert(HPW == 1 || HPW == 2 || HPW == 4, "heads per workgroup");
+  static_assert((HPW == 1 || HPW == 2 || HPW == 4) && HPW <= NW, "heads per workgroup");
+  static_assert(NW >= 2 && NRB >= 1, "workgroup shape");
   constexpr int GH = HPW < 2 ? 2 : HPW;  // gate rows held (one copy fills two heads)
   __shared__ __attribute__((aligned(1024))) uint8_t k_lds[2][BN * KRB];
   __shared__ __attribute__((aligned(1024))) uint8_t v_lds[2][BN * VRB];
@@ -109,7 +116,13 @@ __global__ __launch_bounds__(512) void fwd_large_kernel(FwdParams p) {
   const uint8_t* kbase = reinterpret_cast<const uint8_t*>(p.k) + ((long)seq0 * p.Hkv + kvh) * KRB;
   const uint8_t* vbase = reinterpret_cast<const uint8_t*>(p.v) + ((long)seq0 * p.Hkv + kvh) * VRB;
   const int kstride = p.Hkv * KRB, vstride = p.Hkv * VRB;
-  auto v_swz = [](int r) { return (r & 3) << 2; };   // chunk bits 2-3: a read's 4 rows on 4 segments
+  // V chunk swizzle: a transposed read covers 64 bytes of 4 consecutive
+  // rows, served over 256 bytes of banks.  Rows of 256 bytes or more: chunk
+  // bits 2-3 from r % 4 put the 4 rows on 4 different 64-byte segments.
+  // 128-byte rows (8 chunks): only rows 2 apart share banks, so bit 2 from
+  // (r / 2) % 2 separates them.  Both depend only on r % 4, which the
+  // per-lane offsets below rely on.
+  auto v_swz = [](int r) { return VRB >= 256 ? (r & 3) << 2 : ((r >> 1) & 1) << 2; };
   auto fetch = [&](int t) {
     const int j0 = t * BN, st = (t - t_begin) & 1;
     const bool tail = j0 + BN > L;
@@ -161,7 +174,7 @@ __global__ __launch_bounds__(512) void fwd_large_kernel(FwdParams p) {
   uint32_t v_lane[NDB];
 #pragma unroll
   for (int db = 0; db < NDB; ++db) {
-    const int r = 8 * hh2 + vj;   // row within the 16-key step (r & 3 = vj)
+    const int r = 8 * hh2 + vj;   // row within the 16-key step (r % 4 = vj)
     const int col = wave * DVW + db * 32 + 16 * vhalf + 4 * vcc;
     const int ch = (col * 2) >> 4;
     v_lane[db] = (uint32_t)(r * VRB + ((ch ^ v_swz(r)) << 4) + ((col * 2) & 15));
@@ -283,20 +296,24 @@ __global__ __launch_bounds__(512) void fwd_large_kernel(FwdParams p) {
 
 template <int DQK, int DV, int HPW>
 static hipError_t launch_large_hpw(const FwdParams& p, hipStream_t st) {
-  constexpr int BMH = 128 / HPW;
+  constexpr int NW = large_waves<DV>();
+  constexpr int BMH = 16 * NW / HPW;
   const int tiles = (p.max_seqlen + BMH - 1) / BMH;
   const dim3 grid(p.Hq / HPW, tiles, p.num_seqs);
   if (p.G2 != nullptr)
-    fwd_large_kernel<DQK, DV, true, HPW><<<grid, 512, 0, st>>>(p);
+    fwd_large_kernel<DQK, DV, true, HPW><<<grid, 64 * NW, 0, st>>>(p);
   else
-    fwd_large_kernel<DQK, DV, false, HPW><<<grid, 512, 0, st>>>(p);
+    fwd_large_kernel<DQK, DV, false, HPW><<<grid, 64 * NW, 0, st>>>(p);
   return hipGetLastError();
 }
 
 template <int DQK, int DV>
 static hipError_t launch_large(const FwdParams& p, hipStream_t st) {
+  constexpr int NW = large_waves<DV>();
   const int grp = p.Hq / p.Hkv;
-  if (grp % 4 == 0) return launch_large_hpw<DQK, DV, 4>(p, st);
+  if constexpr (NW >= 4) {
+    if (grp % 4 == 0) return launch_large_hpw<DQK, DV, 4>(p, st);
+  }
   if (grp % 2 == 0) return launch_large_hpw<DQK, DV, 2>(p, st);
   return launch_large_hpw<DQK, DV, 1>(p, st);
 }

@@ -1,0 +1,13 @@
+// Forward for query/key head dim 64 with value head dim 256 or 512; the
+// kernel is in fwd_large.h.
+#include "fwd_large.h"
+
+namespace attn {
+
+hipError_t launch_fwd_large_qk64(const FwdParams& p, int dv, hipStream_t st) {
+  if (dv == 256) return launch_large<64, 256>(p, st);
+  if (dv == 512) return launch_large<64, 512>(p, st);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace attn

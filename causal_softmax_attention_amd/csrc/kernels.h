@@ -189,6 +189,8 @@ hipError_t launch_gate_prefix(const float* g, const int32_t* cu, float* G2,
                               int num_seqs, int T, int Hq, hipStream_t st);
 hipError_t launch_fwd(const FwdParams& p, int dqk, int dv, hipStream_t st);
 hipError_t launch_fwd_wide(const FwdParams& p, int dqk, int dv, hipStream_t st);
+hipError_t launch_fwd_large_qk64(const FwdParams& p, int dv, hipStream_t st);
+hipError_t launch_fwd_large_qk128(const FwdParams& p, int dv, hipStream_t st);
 
 struct BwdParams {
   const void* q;
@@ -220,6 +222,10 @@ struct BwdParams {
 // shared pre/post kernels.
 hipError_t launch_bwd(const BwdParams& p, int dqk, int dv, bool fused, hipStream_t st);
 hipError_t launch_bwd_two_pass(const BwdParams& p, int dqk, int dv, hipStream_t st);
+hipError_t launch_bwd_two_pass_qk64(const BwdParams& p, int dv, hipStream_t st);
+hipError_t launch_bwd_two_pass_qk128(const BwdParams& p, int dv, hipStream_t st);
+hipError_t launch_bwd_two_pass_qk256(const BwdParams& p, int dv, hipStream_t st);
+hipError_t launch_sink_reduce(const BwdParams& p, hipStream_t st);
 // Zero n floats with a kernel (no memset node, so it is safe under capture).
 hipError_t launch_fill_zero(float* x, long n, hipStream_t st);
 

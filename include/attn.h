@@ -109,8 +109,8 @@ const char* attn_version(void);
  *   sink fp32 [Hq] or NULL;  g fp32 [total_tokens, Hq] (log gates) or NULL
  *   o    bf16 [total_tokens, Hq, head_dim_v]   (output, round-to-nearest-even)
  *   lse  fp32 [total_tokens, Hq]               (output, natural log)
- * Supported (head_dim_qk, head_dim_v): (64,64), (128,128), (256,256),
- * (256,512).  workspace: attn_fwd_workspace_size() bytes (may be 0 / NULL
+ * Supported: head_dim_qk 64, 128 or 256 with head_dim_v 64, 128, 256 or
+ * 512 (every pair; other values ATTN_ERR_UNSUPPORTED).  workspace: attn_fwd_workspace_size() bytes (may be 0 / NULL
  * when that size is 0).
  * ---------------------------------------------------------------------- */
 size_t attn_fwd_workspace_size(int total_tokens, int num_q_heads, int has_gate);
@@ -213,7 +213,7 @@ int attn_bwd_varlen(const void* q, const void* k, const void* v,
  *            and at most 8192
  *   out      bf16 [Tq, Hq, head_dim] (output)
  *   lse      fp32 [Tq, Hq] (output, natural log) or NULL
- * Supported: head_dim 128 (bf16 or fp8 cache) or 64 (bf16 cache);
+ * Supported: head_dim 64 or 128, with a bf16 or an fp8 cache;
  * block_size 16, 32, 64 or 128; max_seqlen_q * (Hq / Hkv) <= 64.
  * workspace: attn_decode_workspace_size() bytes (same arguments); with a
  * single segment (kv_split_len >= max_seq_len) the kernel writes out and lse

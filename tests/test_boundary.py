@@ -59,7 +59,7 @@ def _decode(**kw):
     (dict(kvd=A.ATTN_DTYPE_BF16), UNSUPPORTED, "only read with an fp8"),
     (dict(kvd=7), UNSUPPORTED, "kv_dtype"),
     (dict(D=96), UNSUPPORTED, "head_dim"),
-    (dict(D=64), UNSUPPORTED, "fp8 KV cache is supported with head_dim 128"),
+    (dict(D=256), UNSUPPORTED, "head_dim"),
     (dict(B=24), UNSUPPORTED, "block_size"),
     (dict(Hq=60, Hkv=8), INVALID, "multiple"),
     (dict(Hq=128, Hkv=2, maxq=4), UNSUPPORTED, "exceeds 64"),
@@ -82,6 +82,15 @@ def test_decode_empty_batch_is_a_no_op():
     assert _decode(R=0) == OK
 
 
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("kvd", [A.ATTN_DTYPE_BF16, A.ATTN_DTYPE_FP8_E4M3FN])
+def test_decode_accepts_head_dims_64_and_128_for_both_caches(D, kvd):
+    # past the head-dim and cache-dtype checks, stopped by a NULL output
+    sc = P if kvd == A.ATTN_DTYPE_FP8_E4M3FN else NULL
+    assert _decode(D=D, kvd=kvd, ks=sc, vs=sc, out=NULL) == INVALID
+    assert "out is NULL" in L.attn_last_error().decode()
+
+
 def _fwd(**kw):
     a = dict(q=P, k=P, v=P, cu=P, N=2, maxs=64, T=100, Hq=8, Hkv=2, dqk=128, dv=128, scale=0.1, W=0,
              sink=NULL, g=NULL, o=P, lse=P, ws=NULL, wsb=0)
@@ -93,7 +102,10 @@ def _fwd(**kw):
 
 @pytest.mark.parametrize("kw,code,msg", [
     (dict(dqk=96, dv=96), UNSUPPORTED, "head dims"),
-    (dict(dqk=128, dv=256), UNSUPPORTED, "head dims"),
+    (dict(dqk=512, dv=512), UNSUPPORTED, "head dims"),
+    (dict(dqk=32, dv=64), UNSUPPORTED, "head dims"),
+    (dict(dqk=128, dv=1024), UNSUPPORTED, "head dims"),
+    (dict(dqk=256, dv=96), UNSUPPORTED, "head dims"),
     (dict(Hq=6, Hkv=4), INVALID, "multiple"),
     (dict(Hkv=0), INVALID, "positive"),
     (dict(maxs=0), INVALID, "max_seqlen"),
@@ -110,6 +122,18 @@ def _fwd(**kw):
 def test_forward_validation(kw, code, msg):
     assert _fwd(**kw) == code
     assert msg in L.attn_last_error().decode()
+
+
+# Every (d_qk, d_v) pair with d_qk in {64, 128, 256} and d_v in {64, 128,
+# 256, 512} passes the head-dim check: each call is then stopped by a check
+# that runs after it (a NULL output), never by the head dims.
+HEAD_DIM_PAIRS = [(a, b) for a in (64, 128, 256) for b in (64, 128, 256, 512)]
+
+
+@pytest.mark.parametrize("dqk,dv", HEAD_DIM_PAIRS)
+def test_forward_accepts_every_head_dim_pair(dqk, dv):
+    assert _fwd(dqk=dqk, dv=dv, o=NULL) == INVALID
+    assert "o is NULL" in L.attn_last_error().decode()
 
 
 def test_forward_empty_is_a_no_op():
@@ -136,11 +160,24 @@ def _bwd(**kw):
     (dict(flags=2, dqk=256, dv=512), UNSUPPORTED, "fused-dQ"),
     (dict(do=NULL), INVALID, "dO is NULL"),
     (dict(wsb=64), INVALID, "workspace too small"),
-    (dict(dqk=64, dv=128), UNSUPPORTED, "head dims"),
+    (dict(dqk=64, dv=96), UNSUPPORTED, "head dims"),
+    (dict(dqk=512, dv=128), UNSUPPORTED, "head dims"),
+    (dict(flags=2, dqk=256, dv=64), UNSUPPORTED, "fused-dQ"),
 ])
 def test_backward_validation(kw, code, msg):
     assert _bwd(**kw) == code
     assert msg in L.attn_last_error().decode()
+
+
+@pytest.mark.parametrize("dqk,dv", HEAD_DIM_PAIRS)
+@pytest.mark.parametrize("flags", [0, 1, 2])
+def test_backward_accepts_every_head_dim_pair(dqk, dv, flags):
+    # the fused-dQ path (flag 2) covers d_qk <= 128; the two-pass path all pairs
+    rc = _bwd(dqk=dqk, dv=dv, flags=flags, do=NULL)
+    if flags == 2 and dqk > 128:
+        assert rc == UNSUPPORTED and "fused-dQ" in L.attn_last_error().decode()
+    else:
+        assert rc == INVALID and "dO is NULL" in L.attn_last_error().decode()
 
 
 @pytest.mark.parametrize("kw,code,msg", [
@@ -254,7 +291,7 @@ def _prefill(**kw):
     (dict(maxq=0), INVALID, "max_seqlen_q"),
     (dict(ks=NULL), UNSUPPORTED, "per-token"),
     (dict(kvd=A.ATTN_DTYPE_BF16), UNSUPPORTED, "only read with an fp8"),
-    (dict(D=64), UNSUPPORTED, "fp8 KV cache is supported with head_dim 128"),
+    (dict(D=256), UNSUPPORTED, "head_dim"),
     (dict(B=24), UNSUPPORTED, "block_size"),
     (dict(Hq=60, Hkv=8), INVALID, "multiple"),
     (dict(split=48), INVALID, "multiple of"),

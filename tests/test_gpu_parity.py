@@ -90,6 +90,8 @@ DECODE_CASES = [
     ([17, 700, 2500], [1, 1, 1], 16, 2, 128, 16, synth.KV_FP8_E4M3FN),      # GQA 8
     ([17, 700, 2500], [2, 4, 1], 8, 8, 64, 32, synth.KV_BF16),              # MHA, D 64
     ([64, 65537], [4, 4], 32, 2, 128, 64, synth.KV_BF16),             # the aiter PR's Test plan context
+    ([1, 37, 300, 1029, 4096], [1, 1, 1, 1, 1], 32, 4, 64, 16, synth.KV_FP8_E4M3FN),   # fp8, D 64
+    ([5, 130, 2051], [4, 2, 3], 16, 4, 64, 64, synth.KV_FP8_E4M3FN),   # fp8, D 64, short queries
 ]
 
 
@@ -126,6 +128,7 @@ BALANCED_CASES = [
     ([3000, 17, 64, 2049, 4], [4, 3, 1, 2, 4], 64, 4, 128, 16, synth.KV_FP8_E4M3FN, True, True, False),
     ([129, 4100, 1, 600], [2, 1, 1, 4], 16, 2, 64, 32, synth.KV_BF16, True, False, False),
     ([6000, 6000, 5], [1, 4, 1], 64, 4, 128, 128, synth.KV_FP8_E4M3FN, False, True, True),
+    ([2, 900, 3100, 45], [1, 1, 4, 2], 32, 4, 64, 16, synth.KV_FP8_E4M3FN, True, True, False),
 ]
 
 
@@ -205,6 +208,16 @@ PREFILL_CASES = [
     ([300, 190], 4, 2, 256, 256, 0, True, True),
     ([257, 130], 4, 1, 256, 512, 0, True, True),
     ([257, 130], 4, 2, 256, 512, 64, True, False),
+    # unequal query/key and value head dims: every pair of d_qk in {64, 128, 256}
+    # and d_v in {64, 128, 256, 512} not covered above
+    ([3, 190, 77], 8, 2, 64, 128, 0, True, True),
+    ([150, 61], 4, 4, 128, 64, 50, True, False),
+    ([1, 140, 97], 4, 1, 64, 256, 0, True, True),
+    ([129, 70], 4, 2, 64, 512, 40, False, True),
+    ([200, 33], 8, 2, 128, 256, 0, True, True),
+    ([97, 160], 4, 1, 128, 512, 0, True, False),
+    ([180, 45], 4, 2, 256, 64, 0, True, True),
+    ([77, 150], 8, 2, 256, 128, 60, False, True),
 ]
 
 

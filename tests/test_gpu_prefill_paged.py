@@ -50,6 +50,7 @@ CASES = [
     ([513, 2000], [513, 300], 8, 2, 64, 32, BF16, 0, True, False, False, 256),
     ([1, 4000], [1, 9], 64, 4, 128, 16, FP8, 0, False, True, True, 0),
     ([2500], [2500], 16, 16, 128, 64, FP8, 700, True, True, False, 0),
+    ([600, 1500], [600, 200], 16, 4, 64, 32, FP8, 0, True, True, False, 0),      # fp8, D 64
 ]
 
 
