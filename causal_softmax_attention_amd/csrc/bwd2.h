@@ -573,17 +573,26 @@ struct BwdTiles {
 template <int DQK, int DV>
 hipError_t launch_bwd_two_pass_t(const BwdParams& p, hipStream_t st) {
   constexpr int KW = BwdTiles<DQK, DV>::KW, RW = BwdTiles<DQK, DV>::RW, BN = BwdTiles<DQK, DV>::BN;
-  const int ktiles = (p.max_seqlen + 4 * KW - 1) / (4 * KW);
-  const dim3 gk(p.Hkv, ktiles, p.num_seqs);   // sequence-major: a sequence's tiles share L2
-  if (p.G2) bwd_dkdv_kernel<DQK, DV, KW, true><<<gk, 256, 0, st>>>(p);
-  else bwd_dkdv_kernel<DQK, DV, KW, false><<<gk, 256, 0, st>>>(p);
-  hipError_t e = hipGetLastError();
+  hipError_t e;
+  if constexpr (DQK == 256 && DV >= 256) {
+    e = launch_dkdv_large(p, DQK, DV, st);   // bwd_large.hip
+  } else {
+    const int ktiles = (p.max_seqlen + 4 * KW - 1) / (4 * KW);
+    const dim3 gk(p.Hkv, ktiles, p.num_seqs);   // sequence-major: a sequence's tiles share L2
+    if (p.G2) bwd_dkdv_kernel<DQK, DV, KW, true><<<gk, 256, 0, st>>>(p);
+    else bwd_dkdv_kernel<DQK, DV, KW, false><<<gk, 256, 0, st>>>(p);
+    e = hipGetLastError();
+  }
   if (e != hipSuccess) return e;
-  const int qtiles = (p.max_seqlen + 4 * RW - 1) / (4 * RW);
-  const dim3 gq(p.Hq, qtiles, p.num_seqs);
-  if (p.G2) bwd_dq_kernel<DQK, DV, RW, BN, true><<<gq, 256, 0, st>>>(p);
-  else bwd_dq_kernel<DQK, DV, RW, BN, false><<<gq, 256, 0, st>>>(p);
-  e = hipGetLastError();
+  if constexpr (DQK == 256 && DV >= 256) {
+    e = launch_dq_large(p, DQK, DV, st);   // bwd_large.hip
+  } else {
+    const int qtiles = (p.max_seqlen + 4 * RW - 1) / (4 * RW);
+    const dim3 gq(p.Hq, qtiles, p.num_seqs);
+    if (p.G2) bwd_dq_kernel<DQK, DV, RW, BN, true><<<gq, 256, 0, st>>>(p);
+    else bwd_dq_kernel<DQK, DV, RW, BN, false><<<gq, 256, 0, st>>>(p);
+    e = hipGetLastError();
+  }
   if (e != hipSuccess) return e;
   return p.sink ? launch_sink_reduce(p, st) : hipSuccess;
 }

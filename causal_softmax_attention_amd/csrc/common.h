@@ -147,6 +147,15 @@ __device__ __forceinline__ f32x2 fp8x2_to_f32(int word) {
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return (uint32_t)(uintptr_t)(const LDS_AS void*)p;
 }
+// A wave-uniform pointer pinned to scalar registers (for the copy bases above
+// when the compiler has computed a uniform value in vector registers).
+template <typename T>
+__device__ __forceinline__ const T* sgpr_ptr(const T* p) {
+  const uint64_t u = (uint64_t)(uintptr_t)p;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)u);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(u >> 32));
+  return (const T*)(uintptr_t)(((uint64_t)hi << 32) | lo);
+}
 __device__ __forceinline__ void dma16(const void* sbase, uint32_t voff, uint32_t m0) {
   asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1"
                :: "v"(voff), "s"(sbase), "s"(m0) : "memory");

@@ -226,6 +226,8 @@ hipError_t launch_bwd_two_pass_qk64(const BwdParams& p, int dv, hipStream_t st);
 hipError_t launch_bwd_two_pass_qk128(const BwdParams& p, int dv, hipStream_t st);
 hipError_t launch_bwd_two_pass_qk256(const BwdParams& p, int dv, hipStream_t st);
 hipError_t launch_sink_reduce(const BwdParams& p, hipStream_t st);
+hipError_t launch_dkdv_large(const BwdParams& p, int dqk, int dv, hipStream_t st);
+hipError_t launch_dq_large(const BwdParams& p, int dqk, int dv, hipStream_t st);
 // Zero n floats with a kernel (no memset node, so it is safe under capture).
 hipError_t launch_fill_zero(float* x, long n, hipStream_t st);
 
