@@ -157,6 +157,7 @@ BwdLayout bwd_layout(int T, int Hq, int dqk, int has_gate, int has_sink, int fla
   size_t off = 0;
   L.delta = off; off += r4;
   L.G2 = off; if (has_gate) off += r4;
+  L.rowt = off; off += r4;
   if (L.fused) {
     L.dq_acc = off; off += round_up(rows * (size_t)(dqk > 0 ? dqk : 0) * sizeof(float));
     L.dG = off; if (has_gate) off += r4;
@@ -164,7 +165,6 @@ BwdLayout bwd_layout(int T, int Hq, int dqk, int has_gate, int has_sink, int fla
     L.dGrow = off; if (has_gate) off += r4;
     L.dGcol = off; if (has_gate) off += r4;
     L.sink_rows = off; if (has_sink) off += r4;
-    L.rowt = off; off += r4;
   }
   L.total = off;
   return L;
@@ -231,8 +231,8 @@ int attn_bwd_varlen(const void* q, const void* k, const void* v, const void* o, 
     p.dGrow = g ? reinterpret_cast<float*>(ws + lay.dGrow) : nullptr;
     p.dGcol = g ? reinterpret_cast<float*>(ws + lay.dGcol) : nullptr;
     p.sink_rows = sink ? reinterpret_cast<float*>(ws + lay.sink_rows) : nullptr;
-    p.rowt = reinterpret_cast<float*>(ws + lay.rowt);
   }
+  p.rowt = reinterpret_cast<float*>(ws + lay.rowt);
   p.dsink_acc = dsink;
   p.dq = dq; p.dk = dk; p.dv = dv; p.dg = dg;
   p.num_seqs = num_seqs; p.max_seqlen = max_seqlen; p.T = total_tokens;

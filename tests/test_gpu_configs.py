@@ -5,7 +5,8 @@ it checks sampled outputs, each computed from the definition on its own:
   1. dense 128 tokens, GQA 4, d 64, sink: everything.
   2. packed varlen, 32/8 heads, d 128, window 1024, sink, gates: the whole
      forward; backward for two KV-head groups (dq, dk, dv, dg of their heads)
-     and dsink of their query heads.
+     and dsink of their query heads, through the two-pass and the fused-dQ
+     paths.
   3. paged single-query decode, 64 requests up to 32K context, fp8 per-token
      scales, page 16: eight sampled requests (all their query rows).
   4. 3 x 4-token verify over ~227K contexts, page 128, bf16 and fp8: all rows.
@@ -65,18 +66,22 @@ def test_dense_128_full(A):
     assert np.max(np.abs(_np(lse) - rl)) < 1e-3
 
 
-def test_varlen_8seq_window_full_forward_sampled_backward(A):
-    _say("[case] varlen 8 seqs window 1024 sink gate")
-    x = synth.varlen_8seq_window1024(device=DEV)
-    o, lse, (dq, dk, dv, ds, dg) = _run_prefill(A, x)
-    ro, rl = oracle.forward(x.q, x.k, x.v, x.cu_seqlens, x.scale, x.window, x.sink, x.g)
-    e_o = rel_rms(_np(o), ro)
-    _say(f"    o={e_o:.3e} lse max abs={np.max(np.abs(_np(lse) - rl)):.2e}")
-    assert e_o <= TOL
-    assert np.max(np.abs(_np(lse) - rl)) < 1e-3
-    kvs = [0, 5]
-    rq, rk, rv, rs, rg = oracle.backward(x.q, x.k, x.v, x.do, x.cu_seqlens, x.scale, x.window, x.sink,
-                                         x.g, kv_heads=kvs)
+_CFG2_KVS = [0, 5]
+_cfg2_ref_cache = {}
+
+
+def _cfg2_backward_ref(x):
+    # the oracle's backward for two KV-head groups, shared by the two paths
+    if "ref" not in _cfg2_ref_cache:
+        _cfg2_ref_cache["ref"] = oracle.backward(x.q, x.k, x.v, x.do, x.cu_seqlens, x.scale, x.window,
+                                                 x.sink, x.g, kv_heads=_CFG2_KVS)
+    return _cfg2_ref_cache["ref"]
+
+
+def _cfg2_check_backward(x, grads):
+    dq, dk, dv, ds, dg = grads
+    rq, rk, rv, rs, rg = _cfg2_backward_ref(x)
+    kvs = _CFG2_KVS
     heads = [h for kv in kvs for h in range(kv * 4, kv * 4 + 4)]
     errs = dict(dq=rel_rms(_np(dq)[:, heads], rq[:, heads]),
                 dk=rel_rms(_np(dk)[:, kvs], rk[:, kvs]),
@@ -85,6 +90,29 @@ def test_varlen_8seq_window_full_forward_sampled_backward(A):
                 dg=rel_rms(_np(dg)[:, heads], rg[:, heads]))
     _say("   ", {k: f"{v:.3e}" for k, v in errs.items()})
     assert max(errs.values()) <= TOL
+
+
+def test_varlen_8seq_window_full_forward_sampled_backward(A):
+    _say("[case] varlen 8 seqs window 1024 sink gate")
+    x = synth.varlen_8seq_window1024(device=DEV)
+    o, lse, grads = _run_prefill(A, x)
+    ro, rl = oracle.forward(x.q, x.k, x.v, x.cu_seqlens, x.scale, x.window, x.sink, x.g)
+    e_o = rel_rms(_np(o), ro)
+    _say(f"    o={e_o:.3e} lse max abs={np.max(np.abs(_np(lse) - rl)):.2e}")
+    assert e_o <= TOL
+    assert np.max(np.abs(_np(lse) - rl)) < 1e-3
+    _cfg2_check_backward(x, grads)
+
+
+def test_varlen_8seq_window_fused_dq_sampled_backward(A):
+    # the same workload through the fused-dQ backward (fp32 atomics)
+    _say("[case] varlen 8 seqs window 1024 sink gate, fused dQ")
+    x = synth.varlen_8seq_window1024(device=DEV)
+    o, lse = A.attn_fwd_varlen(x.q, x.k, x.v, x.cu_seqlens, x.max_seqlen, x.scale, x.window, x.sink, x.g)
+    grads = A.attn_bwd_varlen(x.q, x.k, x.v, o, x.do, lse, x.cu_seqlens, x.max_seqlen, x.scale,
+                              x.window, x.sink, x.g, flags=A.ATTN_BWD_FUSED_DQ)
+    torch.cuda.synchronize()
+    _cfg2_check_backward(x, grads)
 
 
 def test_decode_64req_sampled_requests(A):
