@@ -219,23 +219,43 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdParams p) {
         // ---- S = Q K^T, dP = dO V^T: C lane (key li, rows rb*16+4g+i) ----
         f32x4 s[KBW][2], dp[KBW][2];
 #pragma unroll
-        for (int rb = 0; rb < 2; ++rb) {
+        for (int rb = 0; rb < 2; ++rb)
 #pragma unroll
           for (int kb = 0; kb < KBW; ++kb) {
             s[kb][rb] = f32x4{0.f, 0.f, 0.f, 0.f};
             dp[kb][rb] = f32x4{0.f, 0.f, 0.f, 0.f};
           }
+        {
+          // operand reads j = 0 .. NJ-1 (row block j / NR; then Q k-steps,
+          // then dO k-steps), issued one chunk of PC reads ahead of their
+          // MFMAs (the compiler otherwise waits for each read right away)
+          constexpr int NR = KSQ + KSV, NJ = 2 * NR, PC = 2, NC = NJ / PC;
+          static_assert(NJ % PC == 0, "chunks");
+          bf16x8 a[2][PC];
+          auto rd = [&](int j) -> bf16x8 {
+            const int rb = j / NR, r = j % NR;
+            return r < KSQ ? *reinterpret_cast<const bf16x8*>(ql + tile_off<QRB>(rb * 16 + li, 64 * r + 16 * g))
+                           : *reinterpret_cast<const bf16x8*>(ol + tile_off<ORB>(rb * 16 + li, 64 * (r - KSQ) + 16 * g));
+          };
 #pragma unroll
-          for (int ks = 0; ks < KSQ; ++ks) {
-            const bf16x8 a = *reinterpret_cast<const bf16x8*>(ql + tile_off<QRB>(rb * 16 + li, 64 * ks + 16 * g));
+          for (int j = 0; j < PC; ++j) a[0][j] = rd(j);
 #pragma unroll
-            for (int kb = 0; kb < KBW; ++kb) s[kb][rb] = mfma16x16x32(a, kop[kb][ks], s[kb][rb]);
-          }
+          for (int c = 0; c < NC; ++c) {
+            if (c + 1 < NC) {
 #pragma unroll
-          for (int ks = 0; ks < KSV; ++ks) {
-            const bf16x8 a = *reinterpret_cast<const bf16x8*>(ol + tile_off<ORB>(rb * 16 + li, 64 * ks + 16 * g));
+              for (int j = 0; j < PC; ++j) a[(c + 1) & 1][j] = rd((c + 1) * PC + j);
+            }
+            __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-            for (int kb = 0; kb < KBW; ++kb) dp[kb][rb] = mfma16x16x32(a, vop[kb][ks], dp[kb][rb]);
+            for (int j = 0; j < PC; ++j) {
+              const int jj = c * PC + j, rb = jj / NR, r = jj % NR;
+#pragma unroll
+              for (int kb = 0; kb < KBW; ++kb) {
+                if (r < KSQ) s[kb][rb] = mfma16x16x32(a[c & 1][j], kop[kb][r], s[kb][rb]);
+                else dp[kb][rb] = mfma16x16x32(a[c & 1][j], vop[kb][r - KSQ], dp[kb][rb]);
+              }
+            }
+            __builtin_amdgcn_sched_barrier(0);
           }
         }
         // ---- P (masked only on tiles that need it) and dS ----
@@ -459,23 +479,42 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(BwdParams p) {
       const uint8_t* vl = v_lds[buf];
       f32x4 s[KB][RBW], dp[KB][RBW];
 #pragma unroll
-      for (int kb = 0; kb < KB; ++kb) {
+      for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
         for (int rb = 0; rb < RBW; ++rb) {
           s[kb][rb] = f32x4{0.f, 0.f, 0.f, 0.f};
           dp[kb][rb] = f32x4{0.f, 0.f, 0.f, 0.f};
         }
+      {
+        // operand reads j = 0 .. NJ-1 (key block j / NR; then K k-steps,
+        // then V k-steps), issued one chunk of PC reads ahead of their MFMAs
+        constexpr int NR = KSQ + KSV, NJ = KB * NR, PC = 2, NC = NJ / PC;
+        static_assert(NJ % PC == 0, "chunks");
+        bf16x8 a[2][PC];
+        auto rd = [&](int j) -> bf16x8 {
+          const int kb = j / NR, r = j % NR;
+          return r < KSQ ? *reinterpret_cast<const bf16x8*>(kl + tile_off<KRB>(kb * 16 + li, 64 * r + 16 * g))
+                         : *reinterpret_cast<const bf16x8*>(vl + tile_off<VRB>(kb * 16 + li, 64 * (r - KSQ) + 16 * g));
+        };
 #pragma unroll
-        for (int ks = 0; ks < KSQ; ++ks) {
-          const bf16x8 a = *reinterpret_cast<const bf16x8*>(kl + tile_off<KRB>(kb * 16 + li, 64 * ks + 16 * g));
+        for (int j = 0; j < PC; ++j) a[0][j] = rd(j);
 #pragma unroll
-          for (int rb = 0; rb < RBW; ++rb) s[kb][rb] = mfma16x16x32(a, qop[rb][ks], s[kb][rb]);
-        }
+        for (int c = 0; c < NC; ++c) {
+          if (c + 1 < NC) {
 #pragma unroll
-        for (int ks = 0; ks < KSV; ++ks) {
-          const bf16x8 a = *reinterpret_cast<const bf16x8*>(vl + tile_off<VRB>(kb * 16 + li, 64 * ks + 16 * g));
+            for (int j = 0; j < PC; ++j) a[(c + 1) & 1][j] = rd((c + 1) * PC + j);
+          }
+          __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-          for (int rb = 0; rb < RBW; ++rb) dp[kb][rb] = mfma16x16x32(a, doop[rb][ks], dp[kb][rb]);
+          for (int j = 0; j < PC; ++j) {
+            const int jj = c * PC + j, kb = jj / NR, r = jj % NR;
+#pragma unroll
+            for (int rb = 0; rb < RBW; ++rb) {
+              if (r < KSQ) s[kb][rb] = mfma16x16x32(a[c & 1][j], qop[rb][r], s[kb][rb]);
+              else dp[kb][rb] = mfma16x16x32(a[c & 1][j], doop[rb][r - KSQ], dp[kb][rb]);
+            }
+          }
+          __builtin_amdgcn_sched_barrier(0);
         }
       }
       // ---- P (masked only on tiles that need it), dS, row sums ----
