@@ -226,8 +226,29 @@ __global__ __launch_bounds__(512) void bwd_dkdv_large_kernel(BwdParams p) {
 
       // ---- phase 1: S (S-waves) or dP (dP-waves): C lane = key li, rows rb*16 + 4g + i ----
       f32x4 acc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+      f32x4 pv[2];
       if (is_s) {
         phase1<KSQ, QRB>(lds_addr(ql) + q_rd, op, acc);
+        // P (masked only on tiles that need it) needs only S: formed and
+        // stored key-major while the dP-waves finish their longer product
+        const bool need_mask = (i0 < j0 + BN - 1) || (W > 0 && i0 + RQ - 1 - j0 >= W) || (i0 + RQ > L) ||
+                               (j0 + BN > L);
+        const float gk = GATED ? gk_lds[st][16 * kg + li] : 0.f;
+#pragma unroll
+        for (int rb = 0; rb < 2; ++rb) {
+          const f32x4 rowt = *reinterpret_cast<const f32x4*>(&row_lds[st][0][rb * 16 + 4 * g]);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) pv[rb][i] = fast_exp2(__builtin_fmaf(acc[rb][i], p.scale_log2, rowt[i] - gk));
+          if (need_mask) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const int row = i0 + rb * 16 + 4 * g + i;
+              const bool vis = key < L && row < L && key <= row && (W <= 0 || row - key < W);
+              pv[rb][i] = vis ? pv[rb][i] : 0.f;
+            }
+          }
+          *reinterpret_cast<bf16x4*>(pt_lds + pw + rb * 32) = to_bf16x4(pv[rb]);
+        }
       } else {
         phase1<KSV, ORB>(lds_addr(ol) + o_rd, op, acc);
         x_lds[kg][0][lane] = acc[0];
@@ -235,33 +256,18 @@ __global__ __launch_bounds__(512) void bwd_dkdv_large_kernel(BwdParams p) {
       }
       lds_barrier();   // dP of every key group visible
 
-      // ---- S-waves: P, dS (masked only on tiles that need it), key-major bf16 ----
+      // ---- S-waves: dS = P (dP - delta), key-major bf16 ----
       if (is_s) {
-        const bool need_mask = (i0 < j0 + BN - 1) || (W > 0 && i0 + RQ - 1 - j0 >= W) || (i0 + RQ > L) ||
-                               (j0 + BN > L);
-        const float gk = GATED ? gk_lds[st][16 * kg + li] : 0.f;
 #pragma unroll
         for (int rb = 0; rb < 2; ++rb) {
           const f32x4 dp = x_lds[kg][rb][lane];
-          const f32x4 rowt = *reinterpret_cast<const f32x4*>(&row_lds[st][0][rb * 16 + 4 * g]);
           const f32x4 del = *reinterpret_cast<const f32x4*>(&row_lds[st][1][rb * 16 + 4 * g]);
-          f32x4 pv, ds;
-#pragma unroll
-          for (int i = 0; i < 4; ++i) pv[i] = fast_exp2(__builtin_fmaf(acc[rb][i], p.scale_log2, rowt[i] - gk));
-          if (need_mask) {
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              const int row = i0 + rb * 16 + 4 * g + i;
-              const bool vis = key < L && row < L && key <= row && (W <= 0 || row - key < W);
-              pv[i] = vis ? pv[i] : 0.f;
-            }
-          }
+          f32x4 ds;
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
-            ds[i] = pv[i] * (dp[i] - del[i]);
+            ds[i] = pv[rb][i] * (dp[i] - del[i]);
             colsum += ds[i];
           }
-          *reinterpret_cast<bf16x4*>(pt_lds + pw + rb * 32) = to_bf16x4(pv);
           *reinterpret_cast<bf16x4*>(dst_lds + pw + rb * 32) = to_bf16x4(ds);
         }
       }
@@ -478,8 +484,27 @@ __global__ __launch_bounds__(512) void bwd_dq_large_kernel(BwdParams p) {
 
     // ---- phase 1: C lane = slot li, keys kb*16 + 4g + i ----
     f32x4 acc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+    f32x4 pv[2];
     if (is_s) {
       phase1<KSQ, KRB>(lds_addr(k_lds[st]) + k_rd, op, acc);
+      // P needs only S: formed while the dP-waves finish their longer product
+      const bool need_mask = (j0 + BN - 1 > r0) || (W > 0 && r_last - j0 >= W) || (j0 + BN > L) ||
+                             (r_last < r0 + 15);
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        f32x4 gk = {0.f, 0.f, 0.f, 0.f};
+        if constexpr (GATED) gk = *reinterpret_cast<const f32x4*>(&gk_lds[st][kg % HPW][kb * 16 + 4 * g]);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) pv[kb][i] = fast_exp2(__builtin_fmaf(acc[kb][i], c, rowt - gk[i]));
+        if (need_mask) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int key = j0 + kb * 16 + 4 * g + i;
+            const bool vis = key <= row && key < L && row < L && (W <= 0 || row - key < W);
+            pv[kb][i] = vis ? pv[kb][i] : 0.f;
+          }
+        }
+      }
     } else {
       phase1<KSV, VRB>(lds_addr(v_lds[st]) + v_rd, op, acc);
       x_lds[kg][0][lane] = acc[0];
@@ -488,29 +513,15 @@ __global__ __launch_bounds__(512) void bwd_dq_large_kernel(BwdParams p) {
     lds_barrier();
 
     if (is_s) {
-      const bool need_mask = (j0 + BN - 1 > r0) || (W > 0 && r_last - j0 >= W) || (j0 + BN > L) ||
-                             (r_last < r0 + 15);
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
         const f32x4 dp = x_lds[kg][kb][lane];
-        f32x4 gk = {0.f, 0.f, 0.f, 0.f};
-        if constexpr (GATED) gk = *reinterpret_cast<const f32x4*>(&gk_lds[st][kg % HPW][kb * 16 + 4 * g]);
-        f32x4 pv, ds;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) pv[i] = fast_exp2(__builtin_fmaf(acc[kb][i], c, rowt - gk[i]));
-        if (need_mask) {
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int key = j0 + kb * 16 + 4 * g + i;
-            const bool vis = key <= row && key < L && row < L && (W <= 0 || row - key < W);
-            pv[i] = vis ? pv[i] : 0.f;
-          }
-        }
+        f32x4 ds;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          ds[i] = pv[i] * (dp[i] - dlt);
+          ds[i] = pv[kb][i] * (dp[i] - dlt);
           rowsum += ds[i];
-          pdp += pv[i] * dp[i];
+          pdp += pv[kb][i] * dp[i];
         }
         *reinterpret_cast<bf16x4*>(ds_lds + dsw + kb * 32) = to_bf16x4(ds);
       }
