@@ -283,6 +283,43 @@ def cpu_decode(d, budget_s, clip=None, label="decode"):
                       f"{clip_txt} ({nbytes / 1e6:.0f} MB of algorithmic bytes) in {spent:.1f} s"}
 
 
+def cpu_prefill_paged(d, budget_s, new_clip, label):
+    """The paged-prefill oracle on the requests of the workload in order until
+    ~budget_s, each cut to its first `new_clip` new tokens (the context ends
+    at the last kept token, so every kept row sees exactly the keys it sees
+    in the full call); TFLOP/s by the same flop count as the GPU figure."""
+    import oracle
+    import synth
+    fp8 = d.kv_dtype == 1
+    q, cu = d.q.cpu(), d.cu_seqlens_q.cpu()
+    bt, sl = d.block_table.cpu(), d.seq_lens.cpu()
+    B, D, Hq = d.k_cache.shape[2], d.k_cache.shape[3], q.shape[1]
+    spent, done, flops = 0.0, [], 0.0
+    for r in range(len(d.q_lens)):
+        n = min(d.q_lens[r], new_clip)
+        L = int(sl[r]) - d.q_lens[r] + n
+        pages = bt[r, :(L + B - 1) // B].to(d.k_cache.device)
+        kc = d.k_cache.index_select(0, pages).cpu()
+        vc = d.v_cache.index_select(0, pages).cpu()
+        kc, vc = (c.numpy() if fp8 else c.double().numpy() for c in (kc, vc))
+        ks = d.k_scale.index_select(0, pages).cpu().numpy() if fp8 else None
+        vs = d.v_scale.index_select(0, pages).cpu().numpy() if fp8 else None
+        qr = q[int(cu[r]):int(cu[r]) + n]
+        one_bt = torch.arange(len(pages), dtype=torch.int32)[None, :]
+        t0 = time.perf_counter()
+        oracle.prefill_paged(qr, torch.tensor([0, n], dtype=torch.int32), kc, vc, one_bt,
+                             torch.tensor([L], dtype=torch.int32), d.scale, fp8, ks, vs)
+        spent += time.perf_counter() - t0
+        flops += synth.paged_attention_flops([L], [n], Hq, D)
+        done.append(r)
+        if spent >= budget_s:
+            break
+    return {"value": flops / spent / 1e12, "unit": "TFLOP/s", "cores": int(_blas_threads()), "kind": "oracle",
+            "sample": f"float64 paged-prefill oracle on requests {done[0]}..{done[-1]} of the {label} "
+                      f"workload, each cut to its first {new_clip} new tokens ({flops / 1e9:.1f} GFLOP) "
+                      f"in {spent:.1f} s"}
+
+
 def machine_info():
     info = {"torch": torch.__version__, "hip": getattr(torch.version, "hip", None),
             "python": platform.python_version(), "os_cpu_count": os.cpu_count(),
@@ -341,9 +378,11 @@ def main():
     d3 = synth.decode_64req_fp8(device=dev)
     d4f = synth.verify_3x4_227k(kv_dtype=synth.KV_FP8_E4M3FN, device=dev)
     d4b = synth.verify_3x4_227k(kv_dtype=synth.KV_BF16, device=dev)
+    d6 = synth.prefill_paged_bench(device=dev)
     f2f, f2b, pairs2 = prefill_flops(x2)
     f5f, f5b, pairs5 = prefill_flops(x5)
     b3, b4f, b4b = _dec_bytes(d3), _dec_bytes(d4f), _dec_bytes(d4b)
+    f6 = synth.paged_attention_flops(d6.seq_lens.tolist(), d6.q_lens, d6.q.shape[1], d6.q.shape[2])
     print(f"[bench] prefill T={x2.total_tokens} pairs={pairs2}; large heads T={x5.total_tokens} "
           f"pairs={pairs5}; decode bytes={b3:.3e}; verify bytes fp8={b4f:.3e} bf16={b4b:.3e}",
           file=sys.stderr, flush=True)
@@ -364,10 +403,16 @@ def main():
         return lambda: A.attn_decode_paged(d.q, d.cu_seqlens_q, mq, d.k_cache, d.v_cache, d.kv_dtype,
                                            d.k_scale, d.v_scale, d.block_table, d.seq_lens, ml, d.scale)
 
+    def paged(d):
+        mq, ml = d.max_seqlen_q, d.max_seq_len
+        return lambda: A.attn_prefill_paged(d.q, d.cu_seqlens_q, mq, d.k_cache, d.v_cache, d.kv_dtype,
+                                            d.k_scale, d.v_scale, d.block_table, d.seq_lens, ml, d.scale)
+
     calls = {
         "prefill_fwd": fwd(x2), "prefill_bwd": bwd(x2, o2, l2),
         "large_heads_fwd": fwd(x5), "large_heads_bwd": bwd(x5, o5, l5),
         "decode": dec(d3), "verify_fp8": dec(d4f), "verify_bf16": dec(d4b),
+        "prefill_paged": paged(d6),
     }
 
     def step(tm=None):
@@ -403,6 +448,7 @@ def main():
         "prefill_fwd": ("mfma", f2f), "prefill_bwd": ("mfma", f2b),
         "large_heads_fwd": ("mfma", f5f), "large_heads_bwd": ("mfma", f5b),
         "decode": ("hbm", b3), "verify_fp8": ("hbm", b4f), "verify_bf16": ("hbm", b4b),
+        "prefill_paged": ("mfma", f6),
     }
     figures = {}
     for k, (bound, w) in work.items():
@@ -418,7 +464,8 @@ def main():
     value = tf(f2f + f2b, us["prefill_fwd"] + us["prefill_bwd"])
     api = {"prefill_fwd": "attn_fwd_varlen", "prefill_bwd": "attn_bwd_varlen",
            "large_heads_fwd": "attn_fwd_varlen", "large_heads_bwd": "attn_bwd_varlen",
-           "decode": "attn_decode_paged", "verify_fp8": "attn_decode_paged", "verify_bf16": "attn_decode_paged"}
+           "decode": "attn_decode_paged", "verify_fp8": "attn_decode_paged", "verify_bf16": "attn_decode_paged",
+           "prefill_paged": "attn_prefill_paged"}
     dom = max(us, key=us.get)
     bound, w = work[dom]
     roof = {"bound": bound, "call": f"{api[dom]} ({dom})",
@@ -453,6 +500,11 @@ def main():
             "fp8": {**figures["verify_fp8"], "target": ">= 70% of HBM peak (<= 128.5 us)"},
             "bf16": {**figures["verify_bf16"], "target": ">= 70% of HBM peak (<= 249.1 us)"},
             "pages_context_other_gpu": PAGES_VERIFY_CONTEXT},
+        "prefill_paged_4x2048new": {
+            "config": "chunked prefill over the paged cache: 4 requests x 2048 new tokens, total contexts "
+                      "%s, 64q/4kv heads, d 128, page 16, per-token fp8 e4m3fn KV, shuffled page table"
+                      % d6.seq_lens.tolist(),
+            **figures["prefill_paged"], "target": "reported"},
     }
 
     out = {
@@ -472,7 +524,8 @@ def main():
             "workload": "value: prefill forward+backward TFLOP/s on 8 packed seqs (lengths U[256,4096], "
                         "seed 2, T=%d), 32q/8kv heads, d 128, window 1024, sink, log gates; the step also "
                         "runs the 4x8192 d_qk 256 / d_v 512 prefill fwd+bwd, the 64-request per-token fp8 "
-                        "decode layer and the 3x4-token 227K verify (bf16 and fp8)" % x2.total_tokens,
+                        "decode layer, the 3x4-token 227K verify (bf16 and fp8) and the 4x2048-new-token paged fp8 "
+                        "chunked prefill" % x2.total_tokens,
             "global_batch": len(x2.seqlens), "seq_len": x2.max_seqlen, "parallelism": "single-gpu",
         },
         "timing_method": f"per call: median of {args.repeats} repeats of the mean over "
@@ -492,6 +545,8 @@ def main():
                                                                     label="227K fp8 verify")
         workloads["verify_3x4_227k"]["cpu_oracle_bf16"] = cpu_decode(d4b, 4.0, clip=32768,
                                                                      label="227K bf16 verify")
+        workloads["prefill_paged_4x2048new"]["cpu_oracle"] = cpu_prefill_paged(d6, 5.0, new_clip=128,
+                                                                               label="paged chunked prefill")
     print(json.dumps(out), flush=True)
 
 
