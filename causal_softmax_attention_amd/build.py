@@ -39,6 +39,7 @@ COMMON_FLAGS = [
 VGPR_FORM = ["-mllvm", "-amdgpu-mfma-vgpr-form"]
 FILE_FLAGS = {
     "decode.hip": VGPR_FORM,
+    "prefill_paged.hip": VGPR_FORM,
     "fwd.hip": VGPR_FORM,
     "bwd2.hip": VGPR_FORM,
     "bwd2_qk128.hip": VGPR_FORM,

@@ -6,7 +6,8 @@ the rest of the path; lse max abs <= 1e-3; output bias below 1e-3) and span
 several 128-row query blocks, ragged last blocks, single-segment (direct
 output) and split-K launches, mixed batches with decode rows, GQA 16 / 4 / 1,
 head dim 64 and 128, and the sink / window / gate / per-tensor-scale
-features.  The chunked-prefill workload the benchmark times is checked on
+features, on both kernels (the split-K kernel and, for single-segment calls
+on an fp8 cache without a gate, the pipelined tile kernel).  The chunked-prefill workload the benchmark times is checked on
 sampled rows against the prefill oracle's rows of the whole sequence.
 """
 import sys
@@ -51,6 +52,14 @@ CASES = [
     ([1, 4000], [1, 9], 64, 4, 128, 16, FP8, 0, False, True, True, 0),
     ([2500], [2500], 16, 16, 128, 64, FP8, 700, True, True, False, 0),
     ([600, 1500], [600, 200], 16, 4, 64, 32, FP8, 0, True, True, False, 0),      # fp8, D 64
+    # one segment per query tile on an fp8 cache without a gate: the
+    # pipelined tile kernel (GQA 16 / 8 / 2 / 1, ragged tiles, window, sink,
+    # per-tensor scales, pages of 16 / 32 / 64 keys, D 64 and 128)
+    ([1200, 700], [1200, 300], 64, 4, 128, 16, FP8, 0, False, False, False, 65536),
+    ([900, 2000], [900, 129], 16, 8, 128, 32, FP8, 300, True, False, False, 65536),
+    ([1000, 50], [100, 50], 32, 4, 128, 64, FP8, 0, True, False, True, 65536),
+    ([600], [400], 4, 4, 64, 16, FP8, 0, True, False, True, 65536),
+    ([700, 333], [700, 333], 16, 4, 64, 16, FP8, 200, False, False, False, 65536),
 ]
 
 
