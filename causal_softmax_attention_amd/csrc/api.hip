@@ -476,7 +476,7 @@ int paged_attention(bool prefill, const void* q, const int32_t* cu_seqlens_q, in
   p.rpu = max_seqlen_q * (num_q_heads / num_kv_heads);
   p.unit_info = reinterpret_cast<int32_t*>(ws + lay.units);
   hipError_t e = prefill && attn::paged_pipe_supported(p, head_dim, fp8, softmax_scale)
-                    ? attn::launch_paged_pipe(p, head_dim, max_seqlen_q, s)
+                    ? attn::launch_paged_pipe(p, head_dim, fp8, max_seqlen_q, s)
                     : attn::launch_decode_splitk(p, head_dim, fp8, s);
   if (e != hipSuccess) return hip_fail(e, prefill ? "paged prefill launch" : "decode launch");
   if (lay.num_splits == 1) return ok();

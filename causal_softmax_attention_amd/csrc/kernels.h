@@ -72,11 +72,11 @@ struct DecodeParams {
 };
 // Sets p.nqb and, for a balanced launch, p.sk_G.
 hipError_t launch_decode_splitk(DecodeParams& p, int head_dim, bool fp8, hipStream_t st);
-// Paged prefill as a pipelined 64-key tile loop (prefill_paged.hip): per-token
-// or per-tensor fp8 cache, one segment per query tile (output written
-// directly), no gate cache, softmax_scale > 0.
+// Paged prefill as a pipelined 64-key tile loop (prefill_paged.hip): bf16 or
+// fp8 cache (per-token or per-tensor scales), sink, window and gate; one
+// segment per query tile (output written directly), softmax_scale > 0.
 bool paged_pipe_supported(const DecodeParams& p, int head_dim, bool fp8, float softmax_scale);
-hipError_t launch_paged_pipe(const DecodeParams& p, int head_dim, int max_q, hipStream_t st);
+hipError_t launch_paged_pipe(const DecodeParams& p, int head_dim, bool fp8, int max_q, hipStream_t st);
 // The workgroup count (p.sk_G) a balanced launch with these parameters
 // would use (host side; 0 on a runtime error).
 int decode_balanced_groups(const DecodeParams& p, int head_dim, bool fp8);

@@ -1,6 +1,6 @@
-// Paged prefill over the per-token fp8 cache as a pipelined tile loop:
-// whole 64-key tiles of the paged cache, converted once per workgroup into
-// the bf16 tile that the forward's 32x32x16 MFMA body reads.
+// Paged prefill as a pipelined tile loop: whole 64-key tiles of the paged
+// cache in the bf16 tile that the forward's 32x32x16 MFMA body reads (an
+// fp8 cache converted into it once per workgroup).
 //
 // Method (ROCm/aiter PR #6660, "Technical details" and commit messages 2
 // and 3; fla issue #1322, Description, for the causal online softmax): the
@@ -11,18 +11,22 @@
 // the value product, that product carried as a bf16 high part plus a bf16
 // low part (so the fp8 path keeps the precision of its fp32 P).  Per-tensor
 // scales fold the K scale into the score factor and apply the V scale to
-// the output.  The sink logit joins the softmax denominator without a value.
+// the output; a bf16 cache has no scales and its P enters PV as one bf16.
+// The sink logit joins the softmax denominator without a value; the log-gate
+// bias G(query position) - G(key) comes from the paged cumulative-gate cache
+// [pages, query heads, page size].
 //
 // gfx950 mapping (the tile body of fwd_pipe.h, adapted):
 //  * One workgroup of four waves per (HPW query heads of one KV group,
 //    query tile, request); wave w takes head w % HPW and 32 tokens.
-//  * Per 64-key tile every wave copies its quarter of the fp8 K and V rows
-//    from their pages into a raw LDS ring (global_load_lds from the page
-//    base in SGPRs, one tile ahead), then converts exactly the bytes it
-//    copied into the swizzled bf16 tile (v_cvt_scalef32_pk_bf16_fp8: exact,
-//    scale 1); rows past the sequence end are written as zeros (their cache
-//    bytes may be NaN).  The workgroup synchronises twice per tile: before
-//    the conversion (the bf16 tile is free) and after it.
+//  * Per 64-key tile every wave copies its quarter of the K and V rows from
+//    their pages (global_load_lds from the page base in SGPRs, one tile
+//    ahead).  fp8: into a raw LDS ring, then the wave converts exactly the
+//    bytes it copied into the swizzled bf16 tile (v_cvt_scalef32_pk_bf16_fp8:
+//    exact, scale 1), and the workgroup synchronises twice per tile (before
+//    the conversion, the bf16 tile being free, and after it).  bf16: straight
+//    into a two-stage ring of swizzled tiles, one barrier per tile.  V rows
+//    past the sequence end are zeroed (their cache bytes may be NaN).
 //  * Sᵀ = K Qᵀ and Oᵀ += Vᵀ Pᵀ on v_mfma_f32_32x32x16_bf16 with the
 //    exponentials of the previous tile between the QK MFMAs and the V-scaled
 //    high / low parts of its probabilities formed between the PV MFMAs.
@@ -41,8 +45,14 @@ __device__ __forceinline__ bf16x8 fp8x8_bf16(i32x2 w) {
   return bf16x8{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
 }
 
-template <int D, int HPW, bool PT>
+// Cache modes: fp8 with per-token scales, fp8 with per-tensor scales, bf16.
+constexpr int kPagedFp8Token = 0, kPagedFp8Tensor = 1, kPagedBf16 = 2;
+
+template <int D, int HPW, int MODE, bool GATED>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void paged_pipe_kernel(DecodeParams p) {
+  constexpr bool FP8 = MODE != kPagedBf16;
+  constexpr bool PT = MODE == kPagedFp8Tensor;
+  constexpr bool SCALES = MODE == kPagedFp8Token;   // per-key K / V scales, P' as high + low parts
   constexpr int RW = 32;                 // tokens per wave
   constexpr int WPH = 4 / HPW;           // row groups per head
   constexpr int BM = RW * WPH;           // tokens per workgroup
@@ -51,7 +61,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
   constexpr int DB = D / 32;             // 32-wide output column blocks
   constexpr int PS = BN / 16;            // PV k-steps
   constexpr int RB = D * 2;              // bytes per bf16 tile row
-  constexpr int CROW = D;                // bytes per fp8 cache row
+  constexpr int CROW = FP8 ? D : 2 * D;  // bytes per cache row
   constexpr int KPC = 1024 / CROW;       // keys per 1 KB copy
   constexpr int NCP = BN / KPC;          // copies per tile and tensor
   constexpr int CPW = NCP / 4;           // ... per wave
@@ -59,12 +69,17 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
   static_assert(CPW * 4 == NCP && CPW >= 1, "tile copies split over four waves");
   static_assert(D == 64 || D == 128, "head dim 64 or 128");
   constexpr int NQK = KB * KS, NPV = PS * DB, NE = KB * 16;
-  __shared__ __attribute__((aligned(1024))) uint8_t k_lds[BN * RB];
-  __shared__ __attribute__((aligned(1024))) uint8_t v_lds[BN * RB];
-  __shared__ __attribute__((aligned(1024))) uint8_t kr_lds[2][BN * CROW];
-  __shared__ __attribute__((aligned(1024))) uint8_t vr_lds[2][BN * CROW];
-  __shared__ __attribute__((aligned(16))) float ks_lds[2][BN];   // K scale * score factor per key
-  __shared__ __attribute__((aligned(16))) float vs_lds[2][BN];   // V scale per key
+  constexpr int NSTB = FP8 ? 1 : 2;      // bf16 tile stages
+  constexpr int RAW = FP8 ? BN * CROW : 16;
+  constexpr int NSC = SCALES ? BN : 4;
+  constexpr int NGK = GATED ? BN : 4;
+  __shared__ __attribute__((aligned(1024))) uint8_t k_lds[NSTB][BN * RB];
+  __shared__ __attribute__((aligned(1024))) uint8_t v_lds[NSTB][BN * RB];
+  __shared__ __attribute__((aligned(1024))) uint8_t kr_lds[2][RAW];   // fp8: raw tiles
+  __shared__ __attribute__((aligned(1024))) uint8_t vr_lds[2][RAW];
+  __shared__ __attribute__((aligned(16))) float ks_lds[2][NSC];       // K scale * score factor per key
+  __shared__ __attribute__((aligned(16))) float vs_lds[2][NSC];       // V scale per key
+  __shared__ __attribute__((aligned(16))) float gk_lds[2][4][NGK];    // per wave: -log2(e) G of its head's keys
 
   const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int lr = lane & 31, hh = lane >> 5;
@@ -80,6 +95,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
   if (i0 >= n) return;
   const int P0 = L - n;                  // position of the request's first new token
   const int W = p.window;
+  const int bsh = p.B_shift, bmask = p.B - 1;
+  const int32_t* bt = p.block_table + (long)r * p.max_pages;
   // score factor (log2 units); per-tensor K scale folded in
   const float c = PT ? p.scale_log2 * p.k_scale[0] : p.scale_log2;
   const float v_mul = PT ? p.v_scale[0] : 1.f;
@@ -100,7 +117,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) qop[ks] = bf16x8{};
   }
-  float m_run = p.sink ? p.sink[h] * kLog2e : kNegBig;
+  // gate of the row's own position (the query side of G_query - G_key);
+  // the running max is kept without it
+  float gq = 0.f;
+  if constexpr (GATED) {
+    const int pr = min(pos, L - 1);
+    const int pq = bt[pr >> bsh];
+    gq = p.g_cache[((((long)pq * p.Hq + h) << bsh) + (pr & bmask))] * kLog2e;
+  }
+  float m_run = p.sink ? p.sink[h] * kLog2e - gq : kNegBig;
   float l_run = p.sink ? 1.f : 0.f;
   f32x16 oacc[DB];
 #pragma unroll
@@ -121,8 +146,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
   // holds them: pages are whole multiples of KPC keys); wave w issues copies
   // w, w + 4, ...  Groups past the last key re-read the group of the last
   // key (in range; those rows are zeroed at conversion). ----
-  const int32_t* bt = p.block_table + (long)r * p.max_pages;
-  const int bsh = p.B_shift, bmask = p.B - 1;
   const int last_group = ((L - 1) / KPC) * KPC;
   const uint8_t* kcache = reinterpret_cast<const uint8_t*>(p.k_cache);
   const uint8_t* vcache = reinterpret_cast<const uint8_t*>(p.v_cache);
@@ -131,9 +154,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
     const int page = bt[kc >> bsh];   // wave-uniform: a scalar load
     return sgpr_ptr(cache + (((long)page * p.Hkv + kvh) * p.B + (kc & bmask)) * CROW);
   };
-  // one scale per key of the tile, lane l -> key min(j0 + l, L - 1), from
-  // the (at most four) pages the tile spans
-  auto scale_off = [&](int j0) {
+  // one value per key of the tile, lane l -> key min(j0 + l, L - 1), from
+  // the (at most four) pages the tile spans: the element offset of slot
+  // (page, head hd of nh, key) in a [pages, nh, page size] array
+  auto slot_off = [&](int j0, int nh, int hd) {
     const int key = min(j0 + lane, L - 1);
     const int pi0 = j0 >> bsh;
     const int last_pi = (L - 1) >> bsh;
@@ -141,25 +165,44 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
     const int pa = bt[min(pi0, last_pi)], pb = bt[min(pi0 + 1, last_pi)];
     const int pc = bt[min(pi0 + 2, last_pi)], pd = bt[min(pi0 + 3, last_pi)];
     const int page = q == 0 ? pa : q == 1 ? pb : q == 2 ? pc : pd;
-    return ((((uint32_t)page * (uint32_t)p.Hkv + (uint32_t)kvh) << bsh) + (uint32_t)(key & bmask)) * 4u;
+    return ((((uint32_t)page * (uint32_t)nh + (uint32_t)hd) << bsh) + (uint32_t)(key & bmask)) * 4u;
   };
-  auto fetch_k = [&](int t) {   // raw K of tile t (and its K scales) -> stage t & 1
+  // bf16 copies land in the swizzled tile directly: lane l fills bytes
+  // 16 l .. 16 l + 15 of its 1 KB block, tile row KPC cb + l / (RB / 16) at
+  // chunk position l % (RB / 16), which holds logical chunk position ^ swz
+  auto src_off = [&](int cb, bool is_v) -> uint32_t {
+    if constexpr (FP8) return (uint32_t)(lane * 16);
+    const int rr = lane / (RB / 16), pc = lane % (RB / 16);
+    const int row = KPC * cb + rr;
+    const int sw = is_v ? swz_v32<RB>(row) : swz_k32<RB>(row);
+    return (uint32_t)(rr * CROW + ((pc ^ sw) << 4));
+  };
+  // K of tile t (with its K scales and this wave's gate terms) -> stage t & 1
+  auto fetch_k = [&](int t) {
     const int j0 = t * BN, st = t & 1;
+    uint8_t* dst = FP8 ? kr_lds[st] : k_lds[st & (NSTB - 1)];
 #pragma unroll
     for (int j = 0; j < CPW; ++j) {
       const int cb = wave + 4 * j;
-      dma16(group_base(kcache, j0 + KPC * cb), (uint32_t)(lane * 16), lds_addr(&kr_lds[st][cb * 1024]));
+      dma16(group_base(kcache, j0 + KPC * cb), src_off(cb, false), lds_addr(dst + cb * 1024));
     }
-    if (!PT && wave == 0) dma4(p.k_scale, scale_off(j0), lds_addr(&ks_lds[st][0]));
+    if constexpr (SCALES) {
+      if (wave == 0) dma4(p.k_scale, slot_off(j0, p.Hkv, kvh), lds_addr(&ks_lds[st][0]));
+    }
+    if constexpr (GATED) dma4(p.g_cache, slot_off(j0, p.Hq, h), lds_addr(&gk_lds[st][wave][0]));
   };
-  auto fetch_v = [&](int t) {   // raw V of tile t (and its V scales) -> stage t & 1
+  // V of tile t (with its V scales) -> stage t & 1
+  auto fetch_v = [&](int t) {
     const int j0 = t * BN, st = t & 1;
+    uint8_t* dst = FP8 ? vr_lds[st] : v_lds[st & (NSTB - 1)];
 #pragma unroll
     for (int j = 0; j < CPW; ++j) {
       const int cb = wave + 4 * j;
-      dma16(group_base(vcache, j0 + KPC * cb), (uint32_t)(lane * 16), lds_addr(&vr_lds[st][cb * 1024]));
+      dma16(group_base(vcache, j0 + KPC * cb), src_off(cb, true), lds_addr(dst + cb * 1024));
     }
-    if (!PT && wave == 1) dma4(p.v_scale, scale_off(j0), lds_addr(&vs_lds[st][0]));
+    if constexpr (SCALES) {
+      if (wave == 1) dma4(p.v_scale, slot_off(j0, p.Hkv, kvh), lds_addr(&vs_lds[st][0]));
+    }
   };
 
   // ---- conversion of the bytes this wave copied: lane l of copy cb holds
@@ -187,9 +230,29 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
   // the element its own lane copied); clamped away from 0 so that a masked
   // score (-inf) stays -inf
   auto scale_k = [&](int t) {
-    if (!PT && wave == 0) {
-      float* s = &ks_lds[t & 1][lane];
-      *s = fmaxf(*s * c, 1e-30f);
+    if constexpr (SCALES) {
+      if (wave == 0) {
+        float* s = &ks_lds[t & 1][lane];
+        *s = fmaxf(*s * c, 1e-30f);
+      }
+    }
+    if constexpr (GATED) {   // the wave's own gate terms, times -log2(e)
+      float* g = &gk_lds[t & 1][wave][lane];
+      *g = *g * -kLog2e;
+    }
+  };
+  // bf16: V rows past the sequence end that this wave copied (stage of tile t)
+  auto zero_tail_v = [&](int t) {
+    if constexpr (!FP8) {
+      const int j0 = t * BN;
+      if (j0 + BN > L) {
+#pragma unroll
+        for (int j = 0; j < CPW; ++j) {
+          const int cb = wave + 4 * j;
+          const int row = KPC * cb + lane / (RB / 16);
+          if (j0 + row >= L) *reinterpret_cast<i32x4*>(v_lds[t & (NSTB - 1)] + cb * 1024 + lane * 16) = i32x4{0, 0, 0, 0};
+        }
+      }
     }
   };
 
@@ -199,13 +262,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
   const int vrow = 4 * hh + vj;
   const uint32_t v_lane0 =
       (uint32_t)(vrow * RB + (((2 * vhalf + (vc >> 1)) ^ swz_v32<RB>(vrow)) << 4) + 8 * (vc & 1));
-  auto k_addr = [&](int ks) {
-    uint32_t a = (lds_addr(k_lds) + k_lane0) ^ (uint32_t)(32 * ks);
+  auto k_addr = [&](int t, int ks) {
+    uint32_t a = (lds_addr(k_lds[t & (NSTB - 1)]) + k_lane0) ^ (uint32_t)(32 * ks);
     asm volatile("" : "+v"(a));
     return (const LDS_AS uint8_t*)a;
   };
-  auto v_addr = [&](int db) {
-    uint32_t a = (lds_addr(v_lds) + v_lane0) ^ (uint32_t)(64 * db);
+  auto v_addr = [&](int t, int db) {
+    uint32_t a = (lds_addr(v_lds[t & (NSTB - 1)]) + v_lane0) ^ (uint32_t)(64 * db);
     asm volatile("" : "+v"(a));
     return (const LDS_AS uint8_t*)a;
   };
@@ -215,15 +278,23 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
   fetch_k(t_begin);
   auto sync = [&](int t) {
     wait_vm<0>();
-    lds_barrier();   // everyone past iteration t-1: the bf16 tiles are free
-    if (t < t_end) {
-      convert(kr_lds[t & 1], k_lds, t * BN, false);
-      scale_k(t);
+    if constexpr (FP8) {
+      lds_barrier();   // everyone past iteration t-1: the bf16 tiles are free
+      if (t < t_end) {
+        convert(kr_lds[t & 1], k_lds[0], t * BN, false);
+        scale_k(t);
+      }
+      if (t > t_begin) convert(vr_lds[(t - 1) & 1], v_lds[0], (t - 1) * BN, true);
+      if (t + 1 < t_end) fetch_k(t + 1);
+      if (t < t_end) fetch_v(t);
+      lds_barrier();   // converted tiles and scales visible
+    } else {
+      if (t < t_end) scale_k(t);
+      if (t > t_begin) zero_tail_v(t - 1);
+      lds_barrier();   // tiles K(t), V(t-1) landed everywhere; the stages of K(t-1), V(t-2) are free
+      if (t + 1 < t_end) fetch_k(t + 1);
+      if (t < t_end) fetch_v(t);
     }
-    if (t > t_begin) convert(vr_lds[(t - 1) & 1], v_lds, (t - 1) * BN, true);
-    if (t + 1 < t_end) fetch_k(t + 1);
-    if (t < t_end) fetch_v(t);
-    lds_barrier();   // converted tiles and scales visible
   };
 
   auto mask = [&](int t, f32x16 (&s)[KB]) {
@@ -294,7 +365,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
   auto p_operand = [&](f32x16 (&y)[KB], int ps, int t_v) {
     const int kb = ps / 2, o = 8 * (ps % 2);
     float a[8];
-    if constexpr (PT) {
+    if constexpr (!SCALES) {
 #pragma unroll
       for (int e = 0; e < 8; ++e) a[e] = y[kb][o + e];
     } else {
@@ -313,7 +384,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
       const bf16x2 hp = __builtin_convertvector(f32x2{a[e], a[e + 1]}, bf16x2);
       hv[e] = hp[0];
       hv[e + 1] = hp[1];
-      if constexpr (!PT) {
+      if constexpr (SCALES) {
         const unsigned hb = __builtin_bit_cast(unsigned, hp);
         const bf16x2 lp = __builtin_convertvector(
             f32x2{a[e] - __uint_as_float(hb << 16), a[e + 1] - __uint_as_float(hb & 0xffff0000u)}, bf16x2);
@@ -322,7 +393,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
       }
     }
     phi[ps & 1] = hv;
-    if constexpr (!PT) plo[ps & 1] = lv;
+    if constexpr (SCALES) plo[ps & 1] = lv;
   };
 
   // Bias work (block B) on the fresh scores s: s * (K scale * factor), in
@@ -331,16 +402,22 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
   const float* ksl = nullptr;
   float mrow = -INFINITY;
   auto ks_read = [&](int gi) {
-    if constexpr (!PT) ks4[gi & 1] = *reinterpret_cast<const f32x4*>(ksl + 8 * gi + 4 * hh);
+    if constexpr (SCALES) ks4[gi & 1] = *reinterpret_cast<const f32x4*>(ksl + 8 * gi + 4 * hh);
+  };
+  f32x4 gk4[2];
+  const float* gkl = nullptr;
+  auto gk_read = [&](int gi) {
+    if constexpr (GATED) gk4[gi & 1] = *reinterpret_cast<const f32x4*>(gkl + 8 * gi + 4 * hh);
   };
   auto bias_elem = [&](f32x16 (&s)[KB], int e) {
     const int kb = e / 16, i = e % 16, gi = e / 4;
-    if constexpr (PT) {
-      s[kb][i] = s[kb][i] * c;
-    } else {
-      if (i % 4 == 0 && gi + 1 < NE / 4) ks_read(gi + 1);
-      s[kb][i] = s[kb][i] * ks4[gi & 1][i % 4];
+    if (i % 4 == 0 && gi + 1 < NE / 4) {
+      ks_read(gi + 1);
+      gk_read(gi + 1);
     }
+    const float f = SCALES ? ks4[gi & 1][i % 4] : c;
+    if constexpr (GATED) s[kb][i] = __builtin_fmaf(s[kb][i], f, gk4[gi & 1][i % 4]);
+    else s[kb][i] = s[kb][i] * f;
   };
   auto bias_slot = [&](f32x16 (&s)[KB], int j, auto ns) {
     constexpr int per = NE / decltype(ns)::value;
@@ -361,19 +438,23 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
     mx = max_nq(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
   };
   auto bias_begin = [&](int t) {
-    if constexpr (!PT) {
+    if constexpr (SCALES) {
       ksl = &ks_lds[t & 1][0];
       ks_read(0);
+    }
+    if constexpr (GATED) {
+      gkl = &gk_lds[t & 1][wave][0];
+      gk_read(0);
     }
     mrow = -INFINITY;
   };
 
   // Block A: S(t) = K(t) Q^T, with the exponent work of yold between the MFMAs.
-  constexpr int FA_LEAD = PT ? 3 : 2, FA_NB = FA_LEAD + 1;   // per-token scales hold two P' operands
-  auto block_a = [&](f32x16 (&snew)[KB], f32x16 (&yold)[KB], bool ex) {
+  constexpr int FA_LEAD = SCALES ? 2 : 3, FA_NB = FA_LEAD + 1;   // per-token scales hold two P' operands
+  auto block_a = [&](int t, f32x16 (&snew)[KB], f32x16 (&yold)[KB], bool ex) {
     const LDS_AS uint8_t* ka[KS];
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) ka[ks] = k_addr(ks);
+    for (int ks = 0; ks < KS; ++ks) ka[ks] = k_addr(t, ks);
     bf16x8 kf[FA_NB];
     auto kread = [&](int f) { kf[f % FA_NB] = *reinterpret_cast<const LDS_AS bf16x8*>(ka[f % KS] + (f / KS) * 32 * RB); };
 #pragma unroll
@@ -391,10 +472,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
   // Block B: O^T += V^T(t-1) P'^T (high and low parts) slot by slot, with the
   // next k-step's P' operand and the bias and max work of s between the
   // MFMAs; V^T fragments are read FB_LEAD slots ahead.
-  constexpr int FB_LEAD = PT ? 2 : 1, FB_NB = FB_LEAD + 1;
+  constexpr int FB_LEAD = SCALES ? 1 : 2, FB_NB = FB_LEAD + 1;
   auto pv_mfma = [&](const bf16x8& a, int ps, int db) {
     oacc[db] = mfma32x32x16(a, phi[ps & 1], oacc[db]);
-    if constexpr (!PT) oacc[db] = mfma32x32x16(a, plo[ps & 1], oacc[db]);
+    if constexpr (SCALES) oacc[db] = mfma32x32x16(a, plo[ps & 1], oacc[db]);
   };
   auto block_b = [&](int t, f32x16 (&s)[KB], f32x16 (&yold)[KB], bool pvon) {
     bias_begin(t);
@@ -406,7 +487,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
     }
     const LDS_AS uint8_t* va[DB];
 #pragma unroll
-    for (int db = 0; db < DB; ++db) va[db] = v_addr(db);
+    for (int db = 0; db < DB; ++db) va[db] = v_addr(t - 1, db);
     bf16x8 vf[FB_NB];
     auto vread = [&](int f) {
       const int ps = f / DB, db = f % DB;
@@ -430,7 +511,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
   auto pv_only = [&](int t, f32x16 (&yold)[KB]) {
     const LDS_AS uint8_t* va[DB];
 #pragma unroll
-    for (int db = 0; db < DB; ++db) va[db] = v_addr(db);
+    for (int db = 0; db < DB; ++db) va[db] = v_addr(t - 1, db);
 #pragma unroll
     for (int ps = 0; ps < PS; ++ps) {
       p_operand(yold, ps, t - 1);
@@ -445,14 +526,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
   f32x16 sA[KB], sB[KB];
   auto first = [&](int t, f32x16 (&s)[KB]) {
     sync(t);
-    block_a(s, sB, false);
+    block_a(t, s, sB, false);
     if (need_mask(t)) mask(t, s);
     block_b(t, s, sB, false);
     rescale();
   };
   auto full = [&](int t, f32x16 (&snew)[KB], f32x16 (&yold)[KB]) {
     sync(t);
-    block_a(snew, yold, true);
+    block_a(t, snew, yold, true);
     if (need_mask(t)) mask(t, snew);
     block_b(t, snew, yold, true);
     rescale();
@@ -497,39 +578,48 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
         const f32x4 x = f32x4{oacc[db][4 * q], oacc[db][4 * q + 1], oacc[db][4 * q + 2], oacc[db][4 * q + 3]} * inv;
         *reinterpret_cast<bf16x4*>(op + 32 * db + 8 * q) = to_bf16x4(x);
       }
-    if (hh == 0 && p.lse != nullptr) p.lse[grow] = empty ? -INFINITY : (m_run + fast_log2(l_run)) * kLn2;
+    if (hh == 0 && p.lse != nullptr) p.lse[grow] = empty ? -INFINITY : (m_run + gq + fast_log2(l_run)) * kLn2;
   }
 }
 
-template <int D, int HPW>
-hipError_t launch_paged_hpw(const DecodeParams& p, int max_q, hipStream_t st) {
+template <int D, int HPW, int MODE>
+hipError_t launch_paged_mode(const DecodeParams& p, int max_q, hipStream_t st) {
   constexpr int BM = 32 * (4 / HPW);
   const dim3 grid(p.Hq / HPW, (max_q + BM - 1) / BM, p.R);
-  if (p.per_tensor)
-    paged_pipe_kernel<D, HPW, true><<<grid, 256, 0, st>>>(p);
+  if (p.g_cache != nullptr)
+    paged_pipe_kernel<D, HPW, MODE, true><<<grid, 256, 0, st>>>(p);
   else
-    paged_pipe_kernel<D, HPW, false><<<grid, 256, 0, st>>>(p);
+    paged_pipe_kernel<D, HPW, MODE, false><<<grid, 256, 0, st>>>(p);
   return hipGetLastError();
 }
 
+template <int D, int HPW>
+hipError_t launch_paged_hpw(const DecodeParams& p, bool fp8, int max_q, hipStream_t st) {
+  if (!fp8) return launch_paged_mode<D, HPW, kPagedBf16>(p, max_q, st);
+  if (p.per_tensor) return launch_paged_mode<D, HPW, kPagedFp8Tensor>(p, max_q, st);
+  return launch_paged_mode<D, HPW, kPagedFp8Token>(p, max_q, st);
+}
+
 template <int D>
-hipError_t launch_paged_d(const DecodeParams& p, int max_q, hipStream_t st) {
+hipError_t launch_paged_d(const DecodeParams& p, bool fp8, int max_q, hipStream_t st) {
   const int grp = p.Hq / p.Hkv;
-  if (grp % 4 == 0) return launch_paged_hpw<D, 4>(p, max_q, st);
-  if (grp % 2 == 0) return launch_paged_hpw<D, 2>(p, max_q, st);
-  return launch_paged_hpw<D, 1>(p, max_q, st);
+  if (grp % 4 == 0) return launch_paged_hpw<D, 4>(p, fp8, max_q, st);
+  if (grp % 2 == 0) return launch_paged_hpw<D, 2>(p, fp8, max_q, st);
+  return launch_paged_hpw<D, 1>(p, fp8, max_q, st);
 }
 
 }  // namespace
 
 bool paged_pipe_supported(const DecodeParams& p, int head_dim, bool fp8, float softmax_scale) {
-  return fp8 && (head_dim == 64 || head_dim == 128) && p.num_splits == 1 && p.g_cache == nullptr &&
-         softmax_scale > 0.f && p.B >= 1024 / head_dim && p.out != nullptr;
+  // one copy holds 1024 bytes of consecutive keys of one page
+  const int keys_per_copy = 1024 / (head_dim * (fp8 ? 1 : 2));
+  return (head_dim == 64 || head_dim == 128) && p.num_splits == 1 && softmax_scale > 0.f &&
+         p.B >= keys_per_copy && p.out != nullptr;
 }
 
-hipError_t launch_paged_pipe(const DecodeParams& p, int head_dim, int max_q, hipStream_t st) {
-  if (head_dim == 128) return launch_paged_d<128>(p, max_q, st);
-  if (head_dim == 64) return launch_paged_d<64>(p, max_q, st);
+hipError_t launch_paged_pipe(const DecodeParams& p, int head_dim, bool fp8, int max_q, hipStream_t st) {
+  if (head_dim == 128) return launch_paged_d<128>(p, fp8, max_q, st);
+  if (head_dim == 64) return launch_paged_d<64>(p, fp8, max_q, st);
   return hipErrorInvalidValue;
 }
 

@@ -6,8 +6,8 @@ the rest of the path; lse max abs <= 1e-3; output bias below 1e-3) and span
 several 128-row query blocks, ragged last blocks, single-segment (direct
 output) and split-K launches, mixed batches with decode rows, GQA 16 / 4 / 1,
 head dim 64 and 128, and the sink / window / gate / per-tensor-scale
-features, on both kernels (the split-K kernel and, for single-segment calls
-on an fp8 cache without a gate, the pipelined tile kernel).  The chunked-prefill workload the benchmark times is checked on
+features, on both kernels (the split-K kernel and, for single-segment
+calls, the pipelined tile kernel).  The chunked-prefill workload the benchmark times is checked on
 sampled rows against the prefill oracle's rows of the whole sequence.
 """
 import sys
@@ -60,6 +60,12 @@ CASES = [
     ([1000, 50], [100, 50], 32, 4, 128, 64, FP8, 0, True, False, True, 65536),
     ([600], [400], 4, 4, 64, 16, FP8, 0, True, False, True, 65536),
     ([700, 333], [700, 333], 16, 4, 64, 16, FP8, 200, False, False, False, 65536),
+    # the same kernel on a bf16 cache and with the gate cache
+    ([800, 1600], [800, 300], 32, 4, 128, 16, BF16, 200, True, False, False, 65536),
+    ([700], [700], 8, 4, 64, 32, BF16, 0, False, True, False, 65536),
+    ([900, 400], [600, 400], 64, 4, 128, 16, FP8, 0, True, True, False, 65536),
+    ([1000], [513], 16, 4, 128, 64, FP8, 300, False, True, True, 65536),
+    ([2500], [2500], 16, 16, 128, 64, FP8, 700, True, True, False, 65536),
 ]
 
 
