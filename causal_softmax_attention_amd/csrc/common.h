@@ -125,6 +125,28 @@ __device__ __forceinline__ float xgroup_sum(float x) {
   return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
+// Coefficient pairs for split_lo, (-1, 0) and (0, -1) as bf16 pairs.  They
+// must reach v_dot2_f32_bf16 from registers: as an inline constant the
+// compiler encodes (-1, 0) as the f32 constant -1.0, whose bf16 halves the
+// hardware reads as (0, -1).  Made once per kernel; the empty asm keeps the
+// compiler from folding them back into constants.
+struct SplitCoef {
+  bf16x2 c0, c1;
+};
+__device__ __forceinline__ SplitCoef split_coef() {
+  unsigned c0, c1;
+  asm("s_mov_b32 %0, 0x0000bf80" : "=s"(c0));
+  asm("s_mov_b32 %0, 0xbf800000" : "=s"(c1));
+  return SplitCoef{__builtin_bit_cast(bf16x2, c0), __builtin_bit_cast(bf16x2, c1)};
+}
+
+// x - h[0] and y - h[1] for h = (x, y) rounded to bf16: one v_dot2_f32_bf16
+// each (h . (-1, 0) + x); the difference of a float and its bf16 rounding is
+// exact in fp32.
+__device__ __forceinline__ f32x2 split_lo(bf16x2 h, float x, float y, SplitCoef k) {
+  return f32x2{__builtin_amdgcn_fdot2_f32_bf16(h, k.c0, x, false), __builtin_amdgcn_fdot2_f32_bf16(h, k.c1, y, false)};
+}
+
 // Two OCP e4m3fn bytes (low or high half of a 32-bit word) -> two floats.
 template <bool HI>
 __device__ __forceinline__ f32x2 fp8x2_to_f32(int word) {

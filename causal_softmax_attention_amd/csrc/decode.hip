@@ -296,6 +296,19 @@ __global__ __launch_bounds__(64 * W) void decode_splitk_kernel(DecodeParams p) {
   // per-tensor scales: K folded into the score factor, V applied at the end
   const float qk_mul = per_tensor ? p.scale_log2 * p.k_scale[0] : p.scale_log2;
   const float v_mul = per_tensor ? p.v_scale[0] : 1.f;
+  const SplitCoef coef = split_coef();
+  if constexpr (FP8) {
+    if (per_tensor) {
+      // no scale copies: the wave's scale slots of every stage hold 1.0 (the
+      // wave reads only its own slots, in order after these writes)
+#pragma unroll
+      for (int j = 0; j < NST; ++j) {
+        float* sl = reinterpret_cast<float*>(smem + j * STAGE + 2 * TILE + wave * 2 * SCB);
+        sl[lane] = 1.f;
+        sl[64 + lane] = 1.f;
+      }
+    }
+  }
 
   f32x4 oacc[RBW][DB];
   float m_run[RBW], l_run[RBW];
@@ -350,11 +363,9 @@ __global__ __launch_bounds__(64 * W) void decode_splitk_kernel(DecodeParams p) {
     for (int kb = 0; kb < 2; ++kb) {
       ks4[kb] = f32x4{1.f, 1.f, 1.f, 1.f};
       vs4[kb] = f32x4{1.f, 1.f, 1.f, 1.f};
-      if constexpr (FP8) {
-        if (!per_tensor) {
-          ks4[kb] = *reinterpret_cast<const f32x4*>(Sc + kb * 16 + 4 * g);
-          vs4[kb] = *reinterpret_cast<const f32x4*>(Sc + 64 + kb * 16 + 4 * g);
-        }
+      if constexpr (FP8) {   // per-tensor scales: the slots hold 1.0
+        ks4[kb] = *reinterpret_cast<const f32x4*>(Sc + kb * 16 + 4 * g);
+        vs4[kb] = *reinterpret_cast<const f32x4*>(Sc + 64 + kb * 16 + 4 * g);
       }
 #pragma unroll
       for (int i = 0; i < 4; ++i) ks4[kb][i] *= qk_mul;
@@ -411,12 +422,11 @@ __global__ __launch_bounds__(64 * W) void decode_splitk_kernel(DecodeParams p) {
           const float p1 = fast_exp2(x[kb][i + 1] - m_run[rb]);
           rs += p0 + p1;
           if constexpr (FP8) {
-            // hi = RNE(P'), lo = RNE(P' - hi), two columns per conversion
+            // hi = RNE(P'), lo = RNE(P' - hi), two columns per conversion;
+            // P' - hi (exact in fp32) from one dot2 per column
             const float a = p0 * vs4[kb][i], b = p1 * vs4[kb][i + 1];
             const bf16x2 h = __builtin_convertvector(f32x2{a, b}, bf16x2);
-            const unsigned hb = __builtin_bit_cast(unsigned, h);
-            const bf16x2 lo = __builtin_convertvector(
-                f32x2{a - __uint_as_float(hb << 16), b - __uint_as_float(hb & 0xffff0000u)}, bf16x2);
+            const bf16x2 lo = __builtin_convertvector(split_lo(h, a, b, coef), bf16x2);
             phi[rb][kb * 4 + i] = h[0];
             phi[rb][kb * 4 + i + 1] = h[1];
             plo[rb][kb * 4 + i] = lo[0];

@@ -362,6 +362,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
   // probabilities times their V scales as bf16 high and low parts (one
   // rounding each: hi = RNE(P'), lo = RNE(P' - hi)); per-tensor scales: P.
   bf16x8 phi[2], plo[2];
+  const SplitCoef coef = split_coef();
   auto p_operand = [&](f32x16 (&y)[KB], int ps, int t_v) {
     const int kb = ps / 2, o = 8 * (ps % 2);
     float a[8];
@@ -385,9 +386,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
       hv[e] = hp[0];
       hv[e + 1] = hp[1];
       if constexpr (SCALES) {
-        const unsigned hb = __builtin_bit_cast(unsigned, hp);
-        const bf16x2 lp = __builtin_convertvector(
-            f32x2{a[e] - __uint_as_float(hb << 16), a[e + 1] - __uint_as_float(hb & 0xffff0000u)}, bf16x2);
+        const bf16x2 lp = __builtin_convertvector(split_lo(hp, a[e], a[e + 1], coef), bf16x2);
         lv[e] = lp[0];
         lv[e + 1] = lp[1];
       }
