@@ -29,12 +29,12 @@ __all__ = ["attn_fwd_varlen", "attn_bwd_varlen", "attn_decode_paged", "attn_deco
            "attn_bwd_workspace_size", "attn_decode_workspace_size",
            "attn_prefill_paged_workspace_size",
            "ATTN_DTYPE_BF16", "ATTN_DTYPE_FP8_E4M3FN", "ATTN_DTYPE_FP32",
-           "ATTN_BWD_DETERMINISTIC", "ATTN_BWD_FUSED_DQ",
+           "ATTN_BWD_DETERMINISTIC", "ATTN_BWD_FUSED_DQ", "ATTN_BWD_RECOMPUTE_DQ",
            "AttnError", "lib_path", "library"]
 
 ATTN_OK, ATTN_ERR_INVALID, ATTN_ERR_UNSUPPORTED, ATTN_ERR_HIP = 0, -1, -2, -3
 ATTN_DTYPE_BF16, ATTN_DTYPE_FP8_E4M3FN, ATTN_DTYPE_FP32 = 0, 1, 2
-ATTN_BWD_DETERMINISTIC, ATTN_BWD_FUSED_DQ = 1, 2
+ATTN_BWD_DETERMINISTIC, ATTN_BWD_FUSED_DQ, ATTN_BWD_RECOMPUTE_DQ = 1, 2, 4
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 
@@ -57,7 +57,7 @@ _SIGNATURES = {
     "attn_fwd_workspace_size": ([_c_int, _c_int, _c_int], _c_size),
     "attn_fwd_varlen": ([_vp, _vp, _vp, _vp, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int,
                          _c_int, _c_float, _c_int, _vp, _vp, _vp, _vp, _vp, _c_size, _vp], _c_int),
-    "attn_bwd_workspace_size": ([_c_int] * 6, _c_size),
+    "attn_bwd_workspace_size": ([_c_int] * 10, _c_size),
     "attn_bwd_varlen": ([_vp, _vp, _vp, _vp, _vp, _vp, _vp, _c_int, _c_int, _c_int, _c_int,
                          _c_int, _c_int, _c_int, _c_float, _c_int, _vp, _vp, _vp, _vp, _vp,
                          _vp, _vp, _c_int, _vp, _c_size, _vp], _c_int),
@@ -138,11 +138,11 @@ def attn_fwd_workspace_size(total_tokens, num_q_heads, has_gate) -> int:
     return int(library.attn_fwd_workspace_size(total_tokens, num_q_heads, int(bool(has_gate))))
 
 
-def attn_bwd_workspace_size(total_tokens, num_q_heads, head_dim_qk, has_gate, has_sink,
-                            flags=0) -> int:
-    return int(library.attn_bwd_workspace_size(total_tokens, num_q_heads, head_dim_qk,
-                                               int(bool(has_gate)), int(bool(has_sink)),
-                                               int(flags)))
+def attn_bwd_workspace_size(total_tokens, num_seqs, max_seqlen, num_q_heads, head_dim_qk, head_dim_v,
+                            window, has_gate, has_sink, flags=0) -> int:
+    return int(library.attn_bwd_workspace_size(total_tokens, num_seqs, max_seqlen, num_q_heads,
+                                               head_dim_qk, head_dim_v, window, int(bool(has_gate)),
+                                               int(bool(has_sink)), int(flags)))
 
 
 def attn_decode_workspace_size(num_requests, max_seqlen_q, max_seq_len, num_q_heads,
@@ -207,8 +207,9 @@ def attn_fwd_varlen(q, k, v, cu_seqlens, max_seqlen, softmax_scale=None, window=
 def attn_bwd_varlen(q, k, v, o, do, lse, cu_seqlens, max_seqlen, softmax_scale=None,
                     window=0, sink=None, g=None, flags=0):
     """Gradients of attn_fwd_varlen given dO.  flags: 0 / ATTN_BWD_DETERMINISTIC
-    (two-pass, no atomics) or ATTN_BWD_FUSED_DQ (dQ fused into the dK/dV pass
-    with fp32 atomics, d_qk <= 128).  Returns (dq, dk, dv bf16, dsink fp32
+    (two-pass, no atomics; for d_v 512, and d_qk 256 with d_v 128 / 256, dS
+    is stored between the passes unless ATTN_BWD_RECOMPUTE_DQ is added) or ATTN_BWD_FUSED_DQ (dQ fused into the
+    dK/dV pass with fp32 atomics, d_qk <= 128).  Returns (dq, dk, dv bf16, dsink fp32
     [Hq] or None, dg fp32 [T, Hq] or None)."""
     dev = q.device
     _need(q, "q", torch.bfloat16, None, 3)
@@ -233,7 +234,8 @@ def attn_bwd_varlen(q, k, v, o, do, lse, cu_seqlens, max_seqlen, softmax_scale=N
     dvv = torch.empty_like(v)
     dsink = torch.empty((Hq,), dtype=torch.float32, device=dev) if sink is not None else None
     dg = torch.empty((T, Hq), dtype=torch.float32, device=dev) if g is not None else None
-    ws_n = attn_bwd_workspace_size(T, Hq, dqk, g is not None, sink is not None, flags)
+    ws_n = attn_bwd_workspace_size(T, cu_seqlens.numel() - 1, int(max_seqlen), Hq, dqk, dv, int(window),
+                                   g is not None, sink is not None, flags)
     ws = _workspace(ws_n, dev)
     st = library.attn_bwd_varlen(
         _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(do), _ptr(lse), _ptr(cu_seqlens),

@@ -9,6 +9,7 @@
 #include <cstring>
 
 #include "../../include/attn.h"
+#include "bwd_ds.h"
 #include "common.h"
 #include "kernels.h"
 
@@ -140,20 +141,42 @@ int attn_fwd_varlen(const void* q, const void* k, const void* v, const int32_t* 
 // ---------------------------------------------------------------------------
 namespace {
 struct BwdLayout {
-  size_t delta, G2, dq_acc, dG, dGrow, dGcol, sink_rows, rowt, total;
-  bool fused;
+  size_t delta, G2, dq_acc, dG, dGrow, dGcol, sink_rows, rowt, ds, ds_rows, psink, total;
+  bool fused, store_ds;
+  long ds_nrt;
+  int ds_nslot;
 };
+// Largest dS store the two-pass backward takes by itself (bf16 tiles plus
+// the gate's row partials); beyond it the dQ pass recomputes S and dP.
+constexpr size_t kBwdDsMaxBytes = size_t(32) << 30;
+// The dS store pays where recomputing S and dP in the dQ pass costs more than
+// writing and reading 2 bytes per pair.  Measured on one MI355X (whole
+// backward, causal, with or without it): d 256 x 512 on 4 x 8192 tokens
+// 13.9 -> 10.5 ms; 2 x 4096 tokens: 128 x 512 2.04 -> 1.78 ms, 64 x 512
+// 1.72 -> 1.67 ms, 256 x 128 1.19 -> 1.17 ms, 128 x 256 unchanged; 8
+// sequences, window 1024, 128 x 128: 0.87 -> 0.93 ms (slower).  Pairs not
+// measured recompute.
+bool bwd_ds_pays(int dqk, int dv) { return dv == 512 || (dqk == 256 && dv >= 128); }
 // Which backward runs: the fused-dQ kernel (fp32 atomics; the pages keep it
 // to head dims up to 128) only when asked for, the two-pass kernels
 // otherwise (faster on this GPU, and deterministic).
 bool bwd_uses_fused(int dqk, int flags) {
   return (flags & ATTN_BWD_FUSED_DQ) && !(flags & ATTN_BWD_DETERMINISTIC) && dqk <= 128;
 }
-BwdLayout bwd_layout(int T, int Hq, int dqk, int has_gate, int has_sink, int flags) {
+BwdLayout bwd_layout(int T, int num_seqs, int max_seqlen, int Hq, int dqk, int dv, int window, int has_gate,
+                     int has_sink, int flags) {
   BwdLayout L{};
   const size_t rows = (size_t)(T > 0 ? T : 0) * (Hq > 0 ? Hq : 0);
   const size_t r4 = round_up(rows * sizeof(float));
   L.fused = bwd_uses_fused(dqk, flags);
+  if (!L.fused && !(flags & ATTN_BWD_RECOMPUTE_DQ) && bwd_ds_pays(dqk, dv) && T > 0 && Hq > 0 && num_seqs > 0 &&
+      max_seqlen > 0) {
+    L.ds_nrt = attn::ds_row_tiles(T, num_seqs);
+    L.ds_nslot = attn::ds_slots(max_seqlen, window);
+    const size_t tiles = (size_t)Hq * (size_t)L.ds_nrt * (size_t)L.ds_nslot;
+    const size_t bytes = tiles * attn::kDsTileBytes + (has_gate ? tiles * attn::kDsRows * sizeof(float) : 0);
+    L.store_ds = bytes <= kBwdDsMaxBytes;
+  }
   size_t off = 0;
   L.delta = off; off += r4;
   L.G2 = off; if (has_gate) off += r4;
@@ -165,16 +188,25 @@ BwdLayout bwd_layout(int T, int Hq, int dqk, int has_gate, int has_sink, int fla
     L.dGrow = off; if (has_gate) off += r4;
     L.dGcol = off; if (has_gate) off += r4;
     L.sink_rows = off; if (has_sink) off += r4;
+    if (L.store_ds) {
+      const size_t tiles = (size_t)Hq * (size_t)L.ds_nrt * (size_t)L.ds_nslot;
+      L.ds = off; off += round_up(tiles * attn::kDsTileBytes);
+      L.ds_rows = off; if (has_gate) off += round_up(tiles * attn::kDsRows * sizeof(float));
+      L.psink = off; if (has_sink) off += r4;
+    }
   }
   L.total = off;
   return L;
 }
 }  // namespace
 
-size_t attn_bwd_workspace_size(int total_tokens, int num_q_heads, int head_dim_qk, int has_gate,
-                               int has_sink, int flags) {
+size_t attn_bwd_workspace_size(int total_tokens, int num_seqs, int max_seqlen, int num_q_heads,
+                               int head_dim_qk, int head_dim_v, int window, int has_gate, int has_sink,
+                               int flags) {
   if (total_tokens <= 0 || num_q_heads <= 0) return 0;
-  return bwd_layout(total_tokens, num_q_heads, head_dim_qk, has_gate, has_sink, flags).total;
+  return bwd_layout(total_tokens, num_seqs, max_seqlen, num_q_heads, head_dim_qk, head_dim_v, window, has_gate,
+                    has_sink, flags)
+      .total;
 }
 
 int attn_bwd_varlen(const void* q, const void* k, const void* v, const void* o, const void* dO,
@@ -189,8 +221,10 @@ int attn_bwd_varlen(const void* q, const void* k, const void* v, const void* o, 
   REQUIRE((sink == nullptr) == (dsink == nullptr), ATTN_ERR_INVALID,
           "dsink must be given exactly when sink is given");
   REQUIRE((g == nullptr) == (dg == nullptr), ATTN_ERR_INVALID, "dg must be given exactly when g is given");
-  REQUIRE((flags & ~(ATTN_BWD_DETERMINISTIC | ATTN_BWD_FUSED_DQ)) == 0, ATTN_ERR_INVALID,
+  REQUIRE((flags & ~(ATTN_BWD_DETERMINISTIC | ATTN_BWD_FUSED_DQ | ATTN_BWD_RECOMPUTE_DQ)) == 0, ATTN_ERR_INVALID,
           "unknown flags 0x%x", flags);
+  REQUIRE(!((flags & ATTN_BWD_FUSED_DQ) && (flags & ATTN_BWD_RECOMPUTE_DQ)), ATTN_ERR_INVALID,
+          "ATTN_BWD_RECOMPUTE_DQ belongs to the two-pass backward, not ATTN_BWD_FUSED_DQ");
   REQUIRE(!((flags & ATTN_BWD_FUSED_DQ) && (flags & ATTN_BWD_DETERMINISTIC)), ATTN_ERR_INVALID,
           "ATTN_BWD_FUSED_DQ and ATTN_BWD_DETERMINISTIC exclude each other");
   REQUIRE(!((flags & ATTN_BWD_FUSED_DQ) && head_dim_qk > 128), ATTN_ERR_UNSUPPORTED,
@@ -212,7 +246,8 @@ int attn_bwd_varlen(const void* q, const void* k, const void* v, const void* o, 
   REQ_PTR(dv, 16);
   if (sink) { REQ_PTR(sink, 4); REQ_PTR(dsink, 4); }
   if (g) { REQ_PTR(g, 4); REQ_PTR(dg, 4); }
-  const BwdLayout lay = bwd_layout(total_tokens, num_q_heads, head_dim_qk, g != nullptr, sink != nullptr, flags);
+  const BwdLayout lay = bwd_layout(total_tokens, num_seqs, max_seqlen, num_q_heads, head_dim_qk, head_dim_v,
+                                   window, g != nullptr, sink != nullptr, flags);
   REQUIRE(workspace_bytes >= lay.total, ATTN_ERR_INVALID, "workspace too small: %zu < %zu bytes",
           workspace_bytes, lay.total);
   REQ_PTR(workspace, 256);
@@ -231,6 +266,13 @@ int attn_bwd_varlen(const void* q, const void* k, const void* v, const void* o, 
     p.dGrow = g ? reinterpret_cast<float*>(ws + lay.dGrow) : nullptr;
     p.dGcol = g ? reinterpret_cast<float*>(ws + lay.dGcol) : nullptr;
     p.sink_rows = sink ? reinterpret_cast<float*>(ws + lay.sink_rows) : nullptr;
+    if (lay.store_ds) {
+      p.ds = ws + lay.ds;
+      p.ds_rows = g ? reinterpret_cast<float*>(ws + lay.ds_rows) : nullptr;
+      p.psink = sink ? reinterpret_cast<float*>(ws + lay.psink) : nullptr;
+      p.ds_nrt = lay.ds_nrt;
+      p.ds_nslot = lay.ds_nslot;
+    }
   }
   p.rowt = reinterpret_cast<float*>(ws + lay.rowt);
   p.dsink_acc = dsink;

@@ -10,7 +10,8 @@
 //
 // Launches (plus the gate prefix scan shared with the forward):
 //   bwd_pre   delta_i = sum_d fp32(O) fp32(dO) and the row term G2 - lse
-//             log2(e), head-major; zero dq_acc, dG, dsink
+//             log2(e), head-major (with a dS store also psink_i); zero
+//             dq_acc, dG, dsink
 //   then either the deterministic two-pass kernels (bwd2.h, bwd_large.h),
 //   or bwd_fused (bwd_fused.h: dQ through fp32 atomics, pre-reduced over
 //   the workgroup's keys) followed by
@@ -51,6 +52,7 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(BwdParams p) {
     const long hm = (row - tok * p.Hq) * p.T + tok;   // head-major index
     p.delta[hm] = s;
     if (p.rowt != nullptr) p.rowt[hm] = (p.G2 != nullptr ? p.G2[hm] : 0.f) - p.lse[row] * kLog2e;
+    if (p.psink != nullptr) p.psink[hm] = fast_exp2((p.sink[row - tok * p.Hq] - p.lse[row]) * kLog2e);
     if (p.dG != nullptr) p.dG[row] = 0.f;
   }
   if (p.dq_acc != nullptr) {

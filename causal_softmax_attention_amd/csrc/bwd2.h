@@ -19,7 +19,15 @@
 //             complete per row and stored.
 // Both recompute S = QK^T and dP = dO V^T; dQ costs those two products
 // again instead of fp32 atomics.
+//
+// With a dS store (STORE; layout in bwd_ds.h) the dK/dV pass also writes dS
+// and, for the gate, its fp32 row sums per 16-key block, and accumulates the
+// sink gradient per key (sum_i psink_i P_ij dP_ij, a column sum like the
+// gate's); the dQ pass is then bwd_dq_ds (bwd_dq_ds.h), which reads dS
+// instead of forming S and dP again.
 #pragma once
+#include "bwd_dq_ds.h"
+#include "bwd_ds.h"
 #include "common.h"
 #include "kernels.h"
 
@@ -30,11 +38,6 @@ namespace attn {
 // per dQ wave; a two-stage Q/dO ring, three stages measured slower).
 constexpr int kBwdKwSmall = 16, kBwdRwSmall = 32, kBwdNstDkdv = 2;
 
-__device__ __forceinline__ int xcd_remap(int x, int n) {
-  // consecutive logical indices -> same XCD (blocks go round-robin over 8)
-  if (n % 8 != 0) return x;
-  return (x % 8) * (n / 8) + x / 8;
-}
 
 // ---------------------------------------------------------------------------
 // dK/dV pass.  Each wave keeps KW keys of K and V in registers and walks the
@@ -42,8 +45,11 @@ __device__ __forceinline__ int xcd_remap(int x, int n) {
 // tiles (and the per-row lse, delta and gate terms) reach LDS by direct
 // copies into a two-stage ring of swizzled tiles, one tile ahead of the
 // math; rows past the end re-read the last row (finite) and are masked.
-template <int DQK, int DV, int KW, bool GATED>
-__global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdParams p) {
+// (three waves per SIMD for the head dims that fit them: the dS store's
+// extra registers would otherwise tip the 128/128 kernel over 168)
+template <int DQK, int DV, int KW, bool GATED, bool STORE>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(DQK + DV <= 256 ? 3 : 1)))
+void bwd_dkdv_kernel(BwdParams p) {
   constexpr int RQ = 32;              // query rows per tile
   constexpr int KBW = KW / 16;        // 16-key blocks per wave
   constexpr int BNW = 4 * KW;         // keys per workgroup
@@ -59,7 +65,9 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdParams p) {
   constexpr int LPT = QPW + OPW + (GATED ? 1 : 0);
   __shared__ __attribute__((aligned(1024))) uint8_t q_lds[NSQ][RQ * QRB];
   __shared__ __attribute__((aligned(1024))) uint8_t do_lds[NSQ][RQ * ORB];
-  __shared__ __attribute__((aligned(16))) float row_lds[NSQ][2][64];   // row term, delta (lanes >= RQ repeat)
+  static_assert(!STORE || KW == kDsKeys, "a wave's keys are one dS key block");
+  // row term, delta (and psink with a dS store); lanes >= RQ repeat
+  __shared__ __attribute__((aligned(16))) float row_lds[NSQ][STORE ? 3 : 2][64];
   __shared__ __attribute__((aligned(16))) float gk_lds[NSQ][4][64];    // per wave: its keys' gate terms
 
   const int kvh = xcd_remap(blockIdx.x, p.Hkv), n = blockIdx.z, ktile = blockIdx.y;
@@ -144,6 +152,9 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdParams p) {
       const long hr = (long)hh * p.T + seq0 + i0;
       dma4(p.rowt + hr, ro, lds_addr(&row_lds[st][0][0]));
       dma4(p.delta + hr, ro, lds_addr(&row_lds[st][1][0]));
+      if constexpr (STORE) {
+        if (p.psink != nullptr) dma4(p.psink + hr, ro, lds_addr(&row_lds[st][STORE ? 2 : 0][0]));
+      }
     }
     if constexpr (GATED) {
       // this wave's keys for the tile's head, lane l -> key jw + l % KW
@@ -169,9 +180,13 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdParams p) {
       fetch(f_hg, f_qt, s0);
       advance(f_hg, f_qt);
     }
-  float colsum[KBW];
+  float colsum[KBW], sinkcol[KBW];
 #pragma unroll
-  for (int kb = 0; kb < KBW; ++kb) colsum[kb] = 0.f;
+  for (int kb = 0; kb < KBW; ++kb) colsum[kb] = sinkcol[kb] = 0.f;
+  // dS store: the lane-dependent selections of the row-sum reduction (lane
+  // bits 3, 2, 1 pick the half kept at each step) and the sink switch
+  const bool b3 = (li >> 3) & 1, b2 = (li >> 2) & 1, b1 = (li >> 1) & 1;
+  const bool has_psink = STORE && p.psink != nullptr;
   // Every wave takes part in every tile's wait, barrier and copies (tile
   // `it` of the flattened (head, query tile) order lives in stage it % NSQ),
   // but computes only the query tiles its keys can see: per head, rows from
@@ -300,6 +315,49 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdParams p) {
           }
           pop[kb] = concat(to_bf16x4(pv[kb][0]), to_bf16x4(pv[kb][1]));
           dsop[kb] = concat(to_bf16x4(dsv[0]), to_bf16x4(dsv[1]));
+          if constexpr (STORE) {
+            if (has_psink) {
+              // sink gradient, key side: sum over rows of psink_i P_ij dP_ij
+              const float* psl = row_lds[buf][STORE ? 2 : 0];
+#pragma unroll
+              for (int rb = 0; rb < 2; ++rb) {
+                const f32x4 ps4 = *reinterpret_cast<const f32x4*>(psl + rb * 16 + 4 * g);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) sinkcol[kb] = __builtin_fmaf(pv[kb][rb][i] * ps4[i], dp[kb][rb][i], sinkcol[kb]);
+              }
+            }
+            // dS tile of (head h, row tile i0 / 32, this wave's key block)
+            const int rt = i0 / kDsRows;
+            const int slot = jw / kDsKeys - ds_kb_lo(rt, W);
+            if (slot >= 0 && slot < p.ds_nslot) {   // always, for the tiles a wave computes
+              const long t = ds_tile(h, ds_grt(seq0, n, rt), slot, p.ds_nrt, p.ds_nslot);
+              uint8_t* tb = reinterpret_cast<uint8_t*>(p.ds) + t * kDsTileBytes;
+              *reinterpret_cast<bf16x4*>(tb + ds_off(li, 4 * g)) = to_bf16x4(dsv[0]);
+              *reinterpret_cast<bf16x4*>(tb + ds_off(li, 16 + 4 * g)) = to_bf16x4(dsv[1]);
+              if constexpr (GATED) {
+                // fp32 row sums over the block's 16 keys (lanes li): a
+                // reduce-scatter over lane bits 3, 2, 1, then a pair sum;
+                // lane li ends with the row 16 b3 + 4 g + 2 b2 + b1
+                float a[4];
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                  const float keep = b3 ? dsv[1][j] : dsv[0][j], send = b3 ? dsv[0][j] : dsv[1][j];
+                  a[j] = keep + dpp_f32<0x140>(send);   // row_mirror: partner 15 - li
+                }
+                float c[2];
+#pragma unroll
+                for (int j = 0; j < 2; ++j) {
+                  const float keep = b2 ? a[2 + j] : a[j], send = b2 ? a[j] : a[2 + j];
+                  c[j] = keep + dpp_f32<0x141>(send);   // row_half_mirror: partner flips bits 2..0
+                }
+                const float keep = b1 ? c[1] : c[0], send = b1 ? c[0] : c[1];
+                float r = keep + dpp_f32<0x4e>(send);   // quad_perm [2,3,0,1]: partner li ^ 2
+                r += dpp_f32<0xb1>(r);                   // quad_perm [1,0,3,2]: partner li ^ 1
+                if ((li & 1) == 0)
+                  p.ds_rows[t * kDsRows + 16 * b3 + 4 * g + 2 * b2 + b1] = r;
+              }
+            }
+          }
         }
         // ---- dV^T += dO^T P, dK^T += Q^T dS (32 rows per MFMA) ----
         const int mm = li >> 2, c4 = li & 3;
@@ -331,6 +389,16 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdParams p) {
         const int key = jw + kb * 16 + li;
         if (g == 0 && key < L) p.dGcol[(long)h * p.T + seq0 + key] = cs;   // head-major
         colsum[kb] = 0.f;
+      }
+    }
+    if (has_psink) {
+      const int h = kvh * grp + hg;
+#pragma unroll
+      for (int kb = 0; kb < KBW; ++kb) {
+        const float sc = xgroup_sum(sinkcol[kb]);
+        const int key = jw + kb * 16 + li;
+        if (g == 0 && key < L) p.sink_rows[(long)h * p.T + seq0 + key] = sc;   // per key, head-major
+        sinkcol[kb] = 0.f;
       }
     }
   }
@@ -618,12 +686,22 @@ hipError_t launch_bwd_two_pass_t(const BwdParams& p, hipStream_t st) {
   } else {
     const int ktiles = (p.max_seqlen + 4 * KW - 1) / (4 * KW);
     const dim3 gk(p.Hkv, ktiles, p.num_seqs);   // sequence-major: a sequence's tiles share L2
-    if (p.G2) bwd_dkdv_kernel<DQK, DV, KW, true><<<gk, 256, 0, st>>>(p);
-    else bwd_dkdv_kernel<DQK, DV, KW, false><<<gk, 256, 0, st>>>(p);
+    if (p.ds != nullptr) {
+      if (p.G2) bwd_dkdv_kernel<DQK, DV, KW, true, true><<<gk, 256, 0, st>>>(p);
+      else bwd_dkdv_kernel<DQK, DV, KW, false, true><<<gk, 256, 0, st>>>(p);
+    } else {
+      if (p.G2) bwd_dkdv_kernel<DQK, DV, KW, true, false><<<gk, 256, 0, st>>>(p);
+      else bwd_dkdv_kernel<DQK, DV, KW, false, false><<<gk, 256, 0, st>>>(p);
+    }
     e = hipGetLastError();
   }
   if (e != hipSuccess) return e;
-  if constexpr (DQK == 256 && DV >= 256) {
+  if (p.ds != nullptr) {
+    // dQ from the stored dS: 128 rows per workgroup
+    const dim3 gq(p.Hq, (p.max_seqlen + 4 * kDsRows - 1) / (4 * kDsRows), p.num_seqs);
+    bwd_dq_ds_kernel<DQK><<<gq, 256, 0, st>>>(p);
+    e = hipGetLastError();
+  } else if constexpr (DQK == 256 && DV >= 256) {
     e = launch_dq_large(p, DQK, DV, st);   // bwd_large.hip
   } else {
     const int qtiles = (p.max_seqlen + 4 * RW - 1) / (4 * RW);

@@ -23,7 +23,12 @@
 //    ds_read_b64_tr_b16, P and dS from the key-major tiles).
 // Q and dO tiles (with the per-row terms and the keys' gate terms) arrive by
 // direct global->LDS copies into a two-stage ring, one tile ahead.
+// With a dS store (STORE; layout in bwd_ds.h) the S-waves also write dS of
+// the band's tiles, the gate's fp32 row sums per 16-key block and the sink
+// gradient's per-key sums (sum_i psink_i P_ij dP_ij); the dQ pass is then
+// bwd_dq_ds instead of the recomputing kernel below.
 #pragma once
+#include "bwd_ds.h"
 #include "common.h"
 #include "kernels.h"
 
@@ -71,7 +76,7 @@ __device__ __forceinline__ void phase1(uint32_t base, const bf16x8* op, f32x4 (&
   }
 }
 
-template <int DQK, int DV, bool GATED>
+template <int DQK, int DV, bool GATED, bool STORE>
 __global__ __launch_bounds__(512) void bwd_dkdv_large_kernel(BwdParams p) {
   constexpr int NW = 8;
   constexpr int BN = 64;              // keys per workgroup
@@ -89,7 +94,7 @@ __global__ __launch_bounds__(512) void bwd_dkdv_large_kernel(BwdParams p) {
   __shared__ __attribute__((aligned(16))) uint8_t pt_lds[BN * PRB];
   __shared__ __attribute__((aligned(16))) uint8_t dst_lds[BN * PRB];
   __shared__ __attribute__((aligned(16))) f32x4 x_lds[4][2][64];        // dP, S-wave partner's
-  __shared__ __attribute__((aligned(16))) float row_lds[2][2][64];       // row term, delta
+  __shared__ __attribute__((aligned(16))) float row_lds[2][STORE ? 3 : 2][64];   // row term, delta (, psink)
   __shared__ __attribute__((aligned(16))) float gk_lds[2][64];           // keys' gate terms
 
   const int kvh = blockIdx.x, n = blockIdx.z, ktile = blockIdx.y;
@@ -169,6 +174,9 @@ __global__ __launch_bounds__(512) void bwd_dkdv_large_kernel(BwdParams p) {
       const long hr = (long)hh * p.T + seq0 + i0;
       dma4(p.rowt + hr, ro, lds_addr(&row_lds[st][0][0]));
       dma4(p.delta + hr, ro, lds_addr(&row_lds[st][1][0]));
+      if constexpr (STORE) {
+        if (p.psink != nullptr) dma4(p.psink + hr, ro, lds_addr(&row_lds[st][STORE ? 2 : 0][0]));
+      }
     }
     if constexpr (GATED) {
       if (wave == 1) {
@@ -207,6 +215,9 @@ __global__ __launch_bounds__(512) void bwd_dkdv_large_kernel(BwdParams p) {
   }
 
   float colsum = 0.f;                  // S-waves: dS column sum of the lane's key (its 4 rows)
+  float sinkcol = 0.f;                 // S-waves, dS store: sum of psink_i P_ij dP_ij over the lane's rows
+  const bool has_psink = STORE && p.psink != nullptr;
+  const bool b3 = (li >> 3) & 1, b2 = (li >> 2) & 1, b1 = (li >> 1) & 1;
   int f_hg = 0, f_qt = 0;
   fetch(0, 0, 0);
   if (++f_qt == nqt) { f_qt = 0; ++f_hg; }
@@ -258,6 +269,7 @@ __global__ __launch_bounds__(512) void bwd_dkdv_large_kernel(BwdParams p) {
 
       // ---- S-waves: dS = P (dP - delta), key-major bf16 ----
       if (is_s) {
+        f32x4 dsv[2];
 #pragma unroll
         for (int rb = 0; rb < 2; ++rb) {
           const f32x4 dp = x_lds[kg][rb][lane];
@@ -269,6 +281,47 @@ __global__ __launch_bounds__(512) void bwd_dkdv_large_kernel(BwdParams p) {
             colsum += ds[i];
           }
           *reinterpret_cast<bf16x4*>(dst_lds + pw + rb * 32) = to_bf16x4(ds);
+          dsv[rb] = ds;
+          if constexpr (STORE) {
+            if (has_psink) {
+              const f32x4 ps4 = *reinterpret_cast<const f32x4*>(&row_lds[st][STORE ? 2 : 0][rb * 16 + 4 * g]);
+#pragma unroll
+              for (int i = 0; i < 4; ++i) sinkcol = __builtin_fmaf(pv[rb][i] * ps4[i], dp[i], sinkcol);
+            }
+          }
+        }
+        if constexpr (STORE) {
+          // dS tile of (head, row tile i0 / 32, this group's key block), for
+          // the band's tiles only (the others hold no visible pair)
+          const int rt = i0 / kDsRows, kb = (j0 + 16 * kg) / kDsKeys;
+          const int slot = kb - ds_kb_lo(rt, W);
+          if (slot >= 0 && slot < p.ds_nslot && kb <= ds_kb_hi(rt, L)) {
+            const long t = ds_tile(kvh * grp + hg, ds_grt(seq0, n, rt), slot, p.ds_nrt, p.ds_nslot);
+            uint8_t* tb = reinterpret_cast<uint8_t*>(p.ds) + t * kDsTileBytes;
+            *reinterpret_cast<bf16x4*>(tb + ds_off(li, 4 * g)) = to_bf16x4(dsv[0]);
+            *reinterpret_cast<bf16x4*>(tb + ds_off(li, 16 + 4 * g)) = to_bf16x4(dsv[1]);
+            if constexpr (GATED) {
+              // fp32 row sums over the block's 16 keys (lanes li): reduce-scatter
+              // over lane bits 3, 2, 1, then a pair sum; lane li ends with row
+              // 16 b3 + 4 g + 2 b2 + b1
+              float a[4];
+#pragma unroll
+              for (int j = 0; j < 4; ++j) {
+                const float keep = b3 ? dsv[1][j] : dsv[0][j], send = b3 ? dsv[0][j] : dsv[1][j];
+                a[j] = keep + dpp_f32<0x140>(send);
+              }
+              float c[2];
+#pragma unroll
+              for (int j = 0; j < 2; ++j) {
+                const float keep = b2 ? a[2 + j] : a[j], send = b2 ? a[j] : a[2 + j];
+                c[j] = keep + dpp_f32<0x141>(send);
+              }
+              const float keep = b1 ? c[1] : c[0], send = b1 ? c[0] : c[1];
+              float r = keep + dpp_f32<0x4e>(send);
+              r += dpp_f32<0xb1>(r);
+              if ((li & 1) == 0) p.ds_rows[t * kDsRows + 16 * b3 + 4 * g + 2 * b2 + b1] = r;
+            }
+          }
         }
       }
       lds_barrier();   // P and dS of the tile visible
@@ -306,6 +359,11 @@ __global__ __launch_bounds__(512) void bwd_dkdv_large_kernel(BwdParams p) {
       const float cs = xgroup_sum(colsum);
       if (g == 0 && key < L) p.dGcol[(long)(kvh * grp + hg) * p.T + seq0 + key] = cs;
       colsum = 0.f;
+    }
+    if (has_psink && is_s) {
+      const float sc = xgroup_sum(sinkcol);
+      if (g == 0 && key < L) p.sink_rows[(long)(kvh * grp + hg) * p.T + seq0 + key] = sc;   // per key
+      sinkcol = 0.f;
     }
   }
 
@@ -589,8 +647,13 @@ hipError_t launch_dq_large_t(const BwdParams& p, hipStream_t st) {
 template <int DQK, int DV>
 hipError_t launch_dkdv_large_t(const BwdParams& p, hipStream_t st) {
   const dim3 grid(p.Hkv, (p.max_seqlen + 63) / 64, p.num_seqs);
-  if (p.G2) bwd_dkdv_large_kernel<DQK, DV, true><<<grid, 512, 0, st>>>(p);
-  else bwd_dkdv_large_kernel<DQK, DV, false><<<grid, 512, 0, st>>>(p);
+  if (p.ds != nullptr) {
+    if (p.G2) bwd_dkdv_large_kernel<DQK, DV, true, true><<<grid, 512, 0, st>>>(p);
+    else bwd_dkdv_large_kernel<DQK, DV, false, true><<<grid, 512, 0, st>>>(p);
+  } else {
+    if (p.G2) bwd_dkdv_large_kernel<DQK, DV, true, false><<<grid, 512, 0, st>>>(p);
+    else bwd_dkdv_large_kernel<DQK, DV, false, false><<<grid, 512, 0, st>>>(p);
+  }
   return hipGetLastError();
 }
 

@@ -125,6 +125,21 @@ __device__ __forceinline__ float xgroup_sum(float x) {
   return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
+// Workgroup index x of n -> logical index: consecutive logical indices land on
+// the same XCD (workgroups are dealt round-robin over the 8 XCDs).
+__device__ __forceinline__ int xcd_remap(int x, int n) {
+  if (n % 8 != 0) return x;
+  return (x % 8) * (n / 8) + x / 8;
+}
+
+// x of another lane of the same 16-lane row through a DPP move (CTRL: a
+// quad_perm, row_mirror 0x140 or row_half_mirror 0x141; every lane has a
+// source in these patterns).
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xf, 0xf, false));
+}
+
 // Coefficient pairs for split_lo, (-1, 0) and (0, -1) as bf16 pairs.  They
 // must reach v_dot2_f32_bf16 from registers: as an inline constant the
 // compiler encodes (-1, 0) as the f32 constant -1.0, whose bf16 halves the

@@ -215,6 +215,12 @@ struct BwdParams {
   float* dGcol;             // [Hq, T] fp32 (two-pass: column sums of dS, stored; head-major)
   float* sink_rows;         // [Hq, T] fp32 (two-pass: psink_i * sum_j P_ij dP_ij; head-major)
   float* dsink_acc;         // [Hq] fp32 (the dsink output itself)
+  // two-pass with a dS store (layout in bwd_ds.h); ds == nullptr: dQ pass recomputes S, dP
+  void* ds;                 // bf16 dS tiles
+  float* ds_rows;           // fp32 row sums of dS per tile (gate) or nullptr
+  float* psink;             // [Hq, T] psink_i = e^(sink_h - lse_i) (with a sink) or nullptr
+  long ds_nrt;              // row tiles of the layout
+  int ds_nslot;             // key-block slots per row tile
   void* dq;
   void* dk;
   void* dv;

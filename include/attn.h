@@ -139,14 +139,23 @@ int attn_fwd_varlen(const void* q, const void* k, const void* v,
  *            (sum_j dS_ij - sum_i' dS_i'i)         (gate bias G_i - G_j)
  * Two implementations (Oct 5 comment), chosen by `flags`:
  *   0 or ATTN_BWD_DETERMINISTIC: two passes (dK/dV KV-major, then dQ
- *     Q-major, S and dP recomputed in each); every sum is complete inside
- *     one wavefront and stored, so results are bitwise reproducible.
+ *     Q-major); every sum is complete inside one wavefront or added in a
+ *     fixed order, so results are bitwise reproducible.  For head_dim_v
+ *     512, and head_dim_qk 256 with head_dim_v 128 or 256, the dK/dV pass
+ *     stores dS (bf16, the rounding the dQ product uses) and the gate's fp32
+ *     row sums of dS per 16-key block in the workspace, and the dQ pass reads
+ *     them instead of forming S and dP again; the sink gradient is then
+ *     summed per key (sum_i psink_i P_ij dP_ij) and over keys.  Other head
+ *     dims, a store that would pass 32 GiB, and ATTN_BWD_RECOMPUTE_DQ: the
+ *     dQ pass recomputes S and dP and sums the rows itself.
  *   ATTN_BWD_FUSED_DQ: dQ fused into the dK/dV pass, each S and dP tile
  *     computed once, dQ partials added with fp32 atomics into a zeroed fp32
  *     workspace and converted to bf16 after the kernel; gate and sink
  *     partials also through fp32 atomics, so dq, dsink and dg are not
  *     bitwise reproducible.  head_dim_qk <= 128 only (as on the page).
- * Any other flag bit, or both bits, is ATTN_ERR_INVALID.
+ * ATTN_BWD_RECOMPUTE_DQ may be added to 0 or ATTN_BWD_DETERMINISTIC.  Any
+ * other flag bit, FUSED_DQ with DETERMINISTIC or RECOMPUTE_DQ, is
+ * ATTN_ERR_INVALID.
  *
  *   q, k, v, cu_seqlens, sink, g, sizes: exactly as passed to the forward
  *   o    bf16 [T, Hq, head_dim_v]   the forward's output
@@ -157,18 +166,25 @@ int attn_fwd_varlen(const void* q, const void* k, const void* v,
  *   dv   bf16 [T, Hkv, head_dim_v]   (output)
  *   dsink fp32 [Hq]       output; must be NULL iff sink is NULL
  *   dg    fp32 [T, Hq]    output; must be NULL iff g is NULL
- * workspace: attn_bwd_workspace_size() bytes for the same gate, sink and
- * flags.
+ * workspace: attn_bwd_workspace_size() bytes for the same sizes, window,
+ * gate, sink and flags (the dS store needs O(Hq * T * min(window,
+ * max_seqlen)) bytes: 2 per visible pair, up to twice that near the causal
+ * diagonal, plus 1/8 of it for the gate's row sums).
  * ---------------------------------------------------------------------- */
 enum attn_bwd_flags {
   ATTN_BWD_DETERMINISTIC = 1,  /* two-pass kernels, no atomics: bitwise
                                   reproducible (also the default path) */
-  ATTN_BWD_FUSED_DQ = 2        /* dQ fused into the dK/dV pass through fp32
+  ATTN_BWD_FUSED_DQ = 2,       /* dQ fused into the dK/dV pass through fp32
                                   atomics (head_dim_qk <= 128 only) */
+  ATTN_BWD_RECOMPUTE_DQ = 4     /* two-pass without the dS store: the dQ pass
+                                  recomputes S and dP (less workspace) */
 };
 
-size_t attn_bwd_workspace_size(int total_tokens, int num_q_heads,
-                               int head_dim_qk, int has_gate, int has_sink,
+/* Workspace bytes of attn_bwd_varlen for these arguments (0 when
+ * total_tokens or num_q_heads is 0). */
+size_t attn_bwd_workspace_size(int total_tokens, int num_seqs, int max_seqlen,
+                               int num_q_heads, int head_dim_qk, int head_dim_v,
+                               int window, int has_gate, int has_sink,
                                int flags);
 
 int attn_bwd_varlen(const void* q, const void* k, const void* v,

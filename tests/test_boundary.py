@@ -157,6 +157,7 @@ def _bwd(**kw):
     (dict(g=P), INVALID, "dg must be given"),
     (dict(flags=3), INVALID, "exclude each other"),
     (dict(flags=8), INVALID, "unknown flags"),
+    (dict(flags=6), INVALID, "ATTN_BWD_RECOMPUTE_DQ belongs"),
     (dict(flags=2, dqk=256, dv=512), UNSUPPORTED, "fused-dQ"),
     (dict(do=NULL), INVALID, "dO is NULL"),
     (dict(wsb=64), INVALID, "workspace too small"),
@@ -170,7 +171,7 @@ def test_backward_validation(kw, code, msg):
 
 
 @pytest.mark.parametrize("dqk,dv", HEAD_DIM_PAIRS)
-@pytest.mark.parametrize("flags", [0, 1, 2])
+@pytest.mark.parametrize("flags", [0, 1, 2, 4, 5])
 def test_backward_accepts_every_head_dim_pair(dqk, dv, flags):
     # the fused-dQ path (flag 2) covers d_qk <= 128; the two-pass path all pairs
     rc = _bwd(dqk=dqk, dv=dv, flags=flags, do=NULL)
@@ -200,10 +201,29 @@ def test_workspace_sizes():
     # forward: gate prefix only
     assert A.attn_fwd_workspace_size(1000, 8, False) == 0
     assert A.attn_fwd_workspace_size(1000, 8, True) >= 1000 * 8 * 4
-    # backward: the fused path holds an fp32 dQ accumulator, the two-pass one does not
-    two = A.attn_bwd_workspace_size(1000, 8, 128, True, True, 0)
-    fused = A.attn_bwd_workspace_size(1000, 8, 128, True, True, A.ATTN_BWD_FUSED_DQ)
-    assert fused >= 1000 * 8 * 128 * 4 > two
+    # backward: the fused path holds an fp32 dQ accumulator; the two-pass one,
+    # for d_v 512 and for d_qk 256 with d_v 128 / 256, stores dS (bf16 tiles
+    # of 32 rows x 16 keys for every (row tile, key block) in the band, plus
+    # fp32 row sums with a gate) unless told to recompute; other head dims
+    # recompute
+    rec = A.attn_bwd_workspace_size(1000, 2, 600, 8, 128, 128, 0, True, True, 0)
+    fused = A.attn_bwd_workspace_size(1000, 2, 600, 8, 128, 128, 0, True, True, A.ATTN_BWD_FUSED_DQ)
+    assert fused >= 1000 * 8 * 128 * 4 > rec
+    for dqk, dv in ((128, 256), (256, 64), (64, 64)):
+        assert A.attn_bwd_workspace_size(1000, 2, 600, 8, dqk, dv, 0, True, True, 0) == rec
+    for dqk, dv in ((64, 512), (128, 512), (256, 128), (256, 256)):
+        assert A.attn_bwd_workspace_size(1000, 2, 600, 8, dqk, dv, 0, True, True, 0) > rec
+    assert A.attn_bwd_workspace_size(1000, 2, 600, 8, 256, 512, 0, True, True, A.ATTN_BWD_RECOMPUTE_DQ) == rec
+    stored = A.attn_bwd_workspace_size(1000, 2, 600, 8, 256, 512, 0, True, True, 0)
+    # 1000 // 32 + 2 + 1 row tiles, 2 * ceil(600 / 32) slots, 1 KB + 128 B each
+    assert stored >= rec + 8 * (1000 // 32 + 3) * 38 * (1024 + 128)
+    assert A.attn_bwd_workspace_size(1000, 2, 600, 8, 256, 256, 0, True, True,
+                                     A.ATTN_BWD_DETERMINISTIC) == stored
+    # a window bounds the slots per row tile: 2 + (W + 14) // 16
+    win = A.attn_bwd_workspace_size(1000, 2, 600, 8, 256, 512, 64, True, True, 0)
+    assert rec + 8 * 34 * 6 * 1024 <= win < stored
+    # without a gate, no row sums
+    assert A.attn_bwd_workspace_size(1000, 2, 600, 8, 256, 512, 0, False, True, 0) < stored
     # decode: partials for every (query row, split)
     ws = A.attn_decode_workspace_size(64, 1, 32768, 64, 4, 128, 16, 1024)
     assert ws >= 64 * 64 * 32 * 128 * 4

@@ -246,15 +246,17 @@ def test_forward_matches_oracle(A, case):
     assert np.max(np.abs(_np(lse) - rl)) <= 2e-3
 
 
-# the fused-dQ backward covers d_qk <= 128 (larger heads are rejected, see
-# test_fused_dq_rejects_large_heads)
-BACKWARD_CASES = [(c, m) for c in PREFILL_CASES for m in ("two-pass", "fused-dq")
+# two-pass with the dS store (the default), two-pass recomputing S and dP in
+# the dQ pass, fused dQ; the fused-dQ backward covers d_qk <= 128 (larger
+# heads are rejected, see test_fused_dq_rejects_large_heads)
+BACKWARD_CASES = [(c, m) for c in PREFILL_CASES for m in ("two-pass", "recompute-dq", "fused-dq")
                   if not (m == "fused-dq" and c[3] > 128)]
+BWD_FLAGS = {"two-pass": 0, "recompute-dq": 4, "fused-dq": 2}
 
 
 @pytest.mark.parametrize("case,mode", BACKWARD_CASES, ids=lambda v: v if isinstance(v, str) else _pf_id(v))
 def test_backward_matches_oracle(A, case, mode):
-    flags = A.ATTN_BWD_FUSED_DQ if mode == "fused-dq" else 0
+    flags = BWD_FLAGS[mode]
     _say(f"[case] backward {mode} {_pf_id(case)}")
     x = _prefill(case, seed=321)
     o, lse = A.attn_fwd_varlen(x.q, x.k, x.v, x.cu_seqlens, x.max_seqlen, x.scale, x.window,
@@ -275,12 +277,15 @@ def test_backward_matches_oracle(A, case, mode):
         assert e <= TOL, nm
 
 
-def test_backward_two_pass_is_bitwise_deterministic(A):
-    _say("[case] backward determinism")
-    x = _prefill(PREFILL_CASES[2], seed=9)
+# flags 1 stores dS between the passes for the large heads (case 5: d 256 x
+# 256) and recomputes for the others (case 2: d 128); flags 5 always recomputes
+@pytest.mark.parametrize("ci,flags", [(2, 1), (5, 1), (5, 5)], ids=["d128", "d256-ds-store", "d256-recompute"])
+def test_backward_two_pass_is_bitwise_deterministic(A, ci, flags):
+    _say(f"[case] backward determinism case {ci} flags={flags}")
+    x = _prefill(PREFILL_CASES[ci], seed=9)
     o, lse = A.attn_fwd_varlen(x.q, x.k, x.v, x.cu_seqlens, x.max_seqlen, x.scale, x.window, x.sink, x.g)
     runs = [A.attn_bwd_varlen(x.q, x.k, x.v, o, x.do, lse, x.cu_seqlens, x.max_seqlen, x.scale, x.window,
-                              x.sink, x.g, flags=A.ATTN_BWD_DETERMINISTIC) for _ in range(3)]
+                              x.sink, x.g, flags=flags) for _ in range(3)]
     torch.cuda.synchronize()
     for r in runs[1:]:
         for a, b in zip(runs[0], r):
