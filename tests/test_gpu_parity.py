@@ -309,6 +309,21 @@ def test_forward_empty_and_zero_length_sequences(A):
     assert rel_rms(_np(o), ro) <= TOL
 
 
+# zero-length sequences around short ones, through both backward paths: the
+# dS store (d 128 x 512, d 256 x 512) and the recomputing dQ pass (d 64 x 64)
+@pytest.mark.parametrize("dqk,dv,W", [(64, 64, 0), (128, 512, 0), (256, 512, 20)])
+def test_backward_zero_length_sequences(A, dqk, dv, W):
+    _say(f"[case] backward with zero-length sequences d{dqk}x{dv} w{W}")
+    x = synth.prefill_inputs([0, 40, 0, 3, 70, 0], 4, 2, dqk, dv, seed=6, window=W, device=DEV)
+    o, lse = A.attn_fwd_varlen(x.q, x.k, x.v, x.cu_seqlens, x.max_seqlen, x.scale, W, x.sink, x.g)
+    got = A.attn_bwd_varlen(x.q, x.k, x.v, o, x.do, lse, x.cu_seqlens, x.max_seqlen, x.scale, W, x.sink, x.g)
+    torch.cuda.synchronize()
+    ref = oracle.backward(x.q, x.k, x.v, x.do, x.cu_seqlens, x.scale, W, x.sink, x.g)
+    errs = {nm: rel_rms(_np(gt), want) for nm, gt, want in zip(["dq", "dk", "dv", "dsink", "dg"], got, ref)}
+    _say("    " + " ".join(f"{k}={v:.3e}" for k, v in errs.items()))
+    assert max(errs.values()) <= TOL
+
+
 # ----------------------------------------------------------------------------
 # decode with sink / sliding window / log gate / per-tensor scales
 # ----------------------------------------------------------------------------
