@@ -481,13 +481,14 @@ def main():
                       "sink, log gates" % x2.total_tokens,
             "fwd": figures["prefill_fwd"], "bwd": figures["prefill_bwd"],
             "fwdbwd_tflops": value, "fwdbwd_frac_of_bf16_mfma_peak": value / MFMA_BF16_PEAK_TFLOPS,
-            "bwd_path": "two-pass (deterministic)",
+            "bwd_path": "two-pass (deterministic), dQ pass recomputes S and dP",
             "bwd_fused_dq": {"us": fused["median_us"], "tflops": tf(f2b, fused["median_us"]), "timing": fused},
             "target": "forward >= 50% of bf16 MFMA peak (<= 142.5 us)"},
         "prefill_4x8192_large_heads": {
             "config": "4 x 8192 tokens, 16q/4kv heads, d_qk 256, d_v 512, sink, log gates, no window",
             "fwd": figures["large_heads_fwd"], "bwd": figures["large_heads_bwd"],
             "fwdbwd_tflops": tf(f5f + f5b, us["large_heads_fwd"] + us["large_heads_bwd"]),
+            "bwd_path": "two-pass (deterministic), dS stored between the passes",
             "target": "forward >= 50% of bf16 MFMA peak (<= 2.62 ms); backward reported"},
         "decode_64req_fp8": {
             "config": "64 requests, contexts U[1,32768] (seed 3), 64q/4kv heads, d 128, page 16, "
