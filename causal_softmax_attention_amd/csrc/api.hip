@@ -173,9 +173,9 @@ BwdLayout bwd_layout(int T, int num_seqs, int max_seqlen, int Hq, int dqk, int d
       max_seqlen > 0) {
     L.ds_nrt = attn::ds_row_tiles(T, num_seqs);
     L.ds_nslot = attn::ds_slots(max_seqlen, window);
-    const size_t tiles = (size_t)Hq * (size_t)L.ds_nrt * (size_t)L.ds_nslot;
-    const size_t bytes = tiles * attn::kDsTileBytes + (has_gate ? tiles * attn::kDsRows * sizeof(float) : 0);
-    L.store_ds = bytes <= kBwdDsMaxBytes;
+    // in floating point first: the exact product can pass 2^64 for extreme sizes
+    const double per_tile = attn::kDsTileBytes + (has_gate ? attn::kDsRows * sizeof(float) : 0);
+    L.store_ds = (double)Hq * (double)L.ds_nrt * (double)L.ds_nslot * per_tile <= (double)kBwdDsMaxBytes;
   }
   size_t off = 0;
   L.delta = off; off += r4;

@@ -37,11 +37,12 @@ constexpr int kDsTileBytes = kDsRows * kDsKeys * 2;
 __host__ __device__ inline long ds_row_tiles(long T, int num_seqs) { return T / kDsRows + num_seqs + 1; }
 
 __host__ __device__ inline int ds_slots(int max_seqlen, int window) {
-  const int rt = (max_seqlen + kDsRows - 1) / kDsRows;
-  const int full = 2 * rt;
-  if (window <= 0) return full;
-  const int w = 2 + (window + 14) / 16;
-  return w < full ? w : full;
+  // in 64-bit: max_seqlen + 31 and window + 14 overflow int near INT_MAX
+  const long rt = ((long)max_seqlen + kDsRows - 1) / kDsRows;
+  const long full = 2 * rt;
+  if (window <= 0) return (int)full;
+  const long w = 2 + ((long)window + 14) / 16;
+  return (int)(w < full ? w : full);
 }
 
 __host__ __device__ inline int ds_kb_lo(int rt, int window) {

@@ -224,6 +224,15 @@ def test_workspace_sizes():
     assert rec + 8 * 34 * 6 * 1024 <= win < stored
     # without a gate, no row sums
     assert A.attn_bwd_workspace_size(1000, 2, 600, 8, 256, 512, 0, False, True, 0) < stored
+    # past 32 GiB of store the dQ pass recomputes: the size falls back to the
+    # recomputing layout, also where the exact byte count would pass 2^64
+    big = A.attn_bwd_workspace_size(2**31 - 1, 1, 2**31 - 1, 64, 256, 512, 0, True, True, 0)
+    big_rec = A.attn_bwd_workspace_size(2**31 - 1, 1, 2**31 - 1, 64, 256, 512, 0, True, True,
+                                        A.ATTN_BWD_RECOMPUTE_DQ)
+    assert big == big_rec > 0
+    mid = A.attn_bwd_workspace_size(131072, 1, 131072, 16, 256, 512, 0, True, True, 0)
+    assert mid == A.attn_bwd_workspace_size(131072, 1, 131072, 16, 256, 512, 0, True, True,
+                                            A.ATTN_BWD_RECOMPUTE_DQ)
     # decode: partials for every (query row, split)
     ws = A.attn_decode_workspace_size(64, 1, 32768, 64, 4, 128, 16, 1024)
     assert ws >= 64 * 64 * 32 * 128 * 4
