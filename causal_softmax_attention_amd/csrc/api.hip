@@ -340,11 +340,19 @@ DecLayout dec_layout(int R, int max_q, int max_seq_len, int Hq, int Hkv, int D, 
   L.split_len = split_len > 0 ? split_len
                 : prefill ? choose_split_len_prefill(R, Hkv, query_blocks(max_q, Hq, Hkv), max_seq_len, B)
                           : choose_split_len(R, Hkv, max_seq_len, B);
-  L.num_splits = (max_seq_len + L.split_len - 1) / L.split_len;
+  L.num_splits = (int)(((long)max_seq_len + L.split_len - 1) / L.split_len);
   if (L.num_splits == 1) return L;     // single segment: the kernel writes the output
   // partial slots: rows x splits (fixed-length split), and for a decode with
   // the library's split also pieces x rows-per-unit (balanced split, used
   // when there is no window); room for the larger
+  // (sizes past 2^60 bytes, where the exact products could wrap, are
+  // reported as SIZE_MAX: no workspace can hold them)
+  const double est = ((double)R * max_q * Hq * std::max(L.num_splits, 1) + attn::kDecodeMaxBalancedWG * 64.0) *
+                     ((double)D + 2) * sizeof(float);
+  if (est > 1.1529215e18) {
+    L.total = SIZE_MAX;
+    return L;
+  }
   size_t slots = balanced_groups > 0 ? 0 : (size_t)R * max_q * Hq * L.num_splits;
   if (!prefill && split_len == 0) {
     const size_t groups = balanced_groups > 0 ? (size_t)balanced_groups : (size_t)attn::kDecodeMaxBalancedWG;
@@ -432,6 +440,7 @@ int paged_attention(bool prefill, const void* q, const int32_t* cu_seqlens_q, in
   }
   if (num_requests == 0) return ok();
   REQUIRE(max_seq_len >= 1, ATTN_ERR_INVALID, "max_seq_len %d must be >= 1", max_seq_len);
+  REQUIRE(max_seq_len <= (1 << 30), ATTN_ERR_UNSUPPORTED, "max_seq_len %d exceeds 2^30 tokens", max_seq_len);
   REQUIRE(num_blocks >= 1, ATTN_ERR_INVALID, "num_blocks %d must be >= 1", num_blocks);
   REQUIRE((long)max_pages * block_size >= max_seq_len, ATTN_ERR_INVALID,
           "max_pages %d * block_size %d cannot hold max_seq_len %d", max_pages, block_size, max_seq_len);
@@ -460,6 +469,7 @@ int paged_attention(bool prefill, const void* q, const int32_t* cu_seqlens_q, in
   if (lse) REQ_PTR(lse, 4);
   DecLayout lay = dec_layout(num_requests, max_seqlen_q, max_seq_len, num_q_heads, num_kv_heads,
                              head_dim, block_size, kv_split_len, prefill);
+  REQUIRE(lay.total != SIZE_MAX, ATTN_ERR_UNSUPPORTED, "partials of this call would pass 2^60 bytes");
   if (noalloc) {
     // allocation-free path: size the partials for the grid that will run
     // (the balanced split's exact piece count needs the occupancy of its

@@ -224,14 +224,16 @@ int attn_bwd_varlen(const void* q, const void* k, const void* v,
  *   k_scale, v_scale fp32 [num_blocks, Hkv, block_size]: required for fp8,
  *            must be NULL for bf16
  *   block_table int32 [num_requests, max_pages]; seq_lens int32 [num_requests]
- *   max_seq_len >= every seq_lens[r] (sizes the split grid)
+ *   max_seq_len >= every seq_lens[r] (sizes the split grid); at most 2^30,
+ *                else ATTN_ERR_UNSUPPORTED
  *   kv_split_len 0 = library's choice, else a multiple of max(block_size, 32)
  *            and at most 8192
  *   out      bf16 [Tq, Hq, head_dim] (output)
  *   lse      fp32 [Tq, Hq] (output, natural log) or NULL
  * Supported: head_dim 64 or 128, with a bf16 or an fp8 cache;
  * block_size 16, 32, 64 or 128; max_seqlen_q * (Hq / Hkv) <= 64.
- * workspace: attn_decode_workspace_size() bytes (same arguments); with a
+ * workspace: attn_decode_workspace_size() bytes (same arguments; SIZE_MAX
+ * when the partials would pass 2^60 bytes: such calls are UNSUPPORTED); with a
  * single segment (kv_split_len >= max_seq_len) the kernel writes out and lse
  * itself, needs no workspace (size 0, workspace may be NULL) and no reduce.
  * ---------------------------------------------------------------------- */

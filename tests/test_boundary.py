@@ -69,6 +69,7 @@ def _decode(**kw):
     (dict(q=NULL), INVALID, "q is NULL"),
     (dict(kc=P_ODD), INVALID, "aligned"),
     (dict(wsb=16, maxsl=4096, maxp=256), INVALID, "workspace too small"),
+    (dict(maxsl=(1 << 30) + 1, maxp=(1 << 26) + 1), UNSUPPORTED, "exceeds 2^30"),
     (dict(R=-1), INVALID, "negative"),
     (dict(scale=float("nan")), INVALID, "finite"),
 ])
@@ -233,6 +234,11 @@ def test_workspace_sizes():
     mid = A.attn_bwd_workspace_size(131072, 1, 131072, 16, 256, 512, 0, True, True, 0)
     assert mid == A.attn_bwd_workspace_size(131072, 1, 131072, 16, 256, 512, 0, True, True,
                                             A.ATTN_BWD_RECOMPUTE_DQ)
+    # sizes whose partials would pass 2^60 bytes (where exact products could
+    # wrap) are reported as SIZE_MAX, which no workspace matches
+    M = 2**31 - 1
+    assert A.attn_decode_workspace_size(M, 4, M, 64, 4, 128, 16, 0) == 2**64 - 1
+    assert A.attn_prefill_paged_workspace_size(M, M, M, 64, 4, 128, 16, 0) == 2**64 - 1
     # decode: partials for every (query row, split)
     ws = A.attn_decode_workspace_size(64, 1, 32768, 64, 4, 128, 16, 1024)
     assert ws >= 64 * 64 * 32 * 128 * 4
