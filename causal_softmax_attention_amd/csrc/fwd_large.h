@@ -22,7 +22,13 @@
 //    ds_read_b64_tr_b16, P^T rows from the padded P tile), so each V
 //    fragment feeds 16 NW / 32 MFMAs and each P fragment one per 32 columns.
 //    Before accumulating it applies the rescale factors the owners wrote.
-// Two barriers per 32-key tile: K/V of the tile in LDS, then P written.
+// The tile loop is software pipelined: iteration u forms S, the softmax and
+// P of tile u + 1 (P and its rescale factors into one of two LDS buffers)
+// and accumulates the PV of tile u from the other buffer, half of it before
+// the softmax and half between its exponentials.  One barrier per 32-key
+// tile publishes P(u + 1), the K of tile u + 1 and the V of tile u; K and V
+// have rings of their own, so tile u + 2's K and tile u + 1's V can be copied
+// as soon as the barrier has retired the reads of K(u) and V(u - 1).
 // K and V tiles arrive by direct global->LDS copies into a two-stage ring;
 // K uses the row-read swizzle of tile_swz, V a swizzle that keeps the rows
 // of a transposed read on different bank segments; P rows are
@@ -59,8 +65,8 @@ __global__ __launch_bounds__(64 * large_waves<DV>()) void fwd_large_kernel(FwdPa
   constexpr int GH = HPW < 2 ? 2 : HPW;  // gate rows held (one copy fills two heads)
   __shared__ __attribute__((aligned(1024))) uint8_t k_lds[2][BN * KRB];
   __shared__ __attribute__((aligned(1024))) uint8_t v_lds[2][BN * VRB];
-  __shared__ __attribute__((aligned(16))) uint8_t p_lds[SLOTS * PRB];
-  __shared__ __attribute__((aligned(16))) float alpha_lds[SLOTS];
+  __shared__ __attribute__((aligned(16))) uint8_t p_lds[2][SLOTS * PRB];
+  __shared__ __attribute__((aligned(16))) float alpha_lds[2][SLOTS];
   __shared__ __attribute__((aligned(16))) float l_lds[SLOTS];
   __shared__ __attribute__((aligned(16))) float gk_lds[2][GH][BN];
 
@@ -98,7 +104,7 @@ __global__ __launch_bounds__(64 * large_waves<DV>()) void fwd_large_kernel(FwdPa
   }
   const float sink2 = p.sink ? p.sink[hw] * kLog2e : kNegBig;
   float m_run = p.sink ? sink2 - gq : kNegBig;   // kept without the row's gate term gq
-  float l_run = p.sink ? 1.f : 0.f;
+  float l_run = p.sink && g == 0 ? 1.f : 0.f;   // per-lane parts of the row sum
 
   // ---- O of all slots over this wave's value columns ----
   f32x16 oacc[NDB][NRB];
@@ -123,11 +129,12 @@ __global__ __launch_bounds__(64 * large_waves<DV>()) void fwd_large_kernel(FwdPa
   // (r / 2) % 2 separates them.  Both depend only on r % 4, which the
   // per-lane offsets below rely on.
   auto v_swz = [](int r) { return VRB >= 256 ? (r & 3) << 2 : ((r >> 1) & 1) << 2; };
-  auto fetch = [&](int t) {
-    const int j0 = t * BN, st = (t - t_begin) & 1;
+  // copies of tile t_begin + u: K (and the keys' gate terms) into K stage
+  // u & 1, V into V stage u & 1
+  auto fetch_k = [&](int u) {
+    const int j0 = (t_begin + u) * BN, st = u & 1;
     const bool tail = j0 + BN > L;
     const uint8_t* kb = kbase + (long)j0 * kstride;
-    const uint8_t* vb = vbase + (long)j0 * vstride;
 #pragma unroll
     for (int jj = 0; jj < (KBLK + NW - 1) / NW; ++jj) {
       const int j = wave + NW * jj;
@@ -138,15 +145,6 @@ __global__ __launch_bounds__(64 * large_waves<DV>()) void fwd_large_kernel(FwdPa
       const uint32_t off = (uint32_t)(rr * kstride + ((((o % KRB) >> 4) ^ tile_swz<KRB>(r)) << 4));
       dma16(kb, off, __builtin_amdgcn_readfirstlane(lds_addr(k_lds[st]) + j * 1024));
     }
-#pragma unroll
-    for (int jj = 0; jj < VBLK / NW; ++jj) {
-      const int j = wave + NW * jj;
-      const int o = j * 1024 + lane * 16;
-      const int r = o / VRB;
-      const int rr = tail ? min(r, L - 1 - j0) : r;
-      const uint32_t off = (uint32_t)(rr * vstride + ((((o % VRB) >> 4) ^ v_swz(r)) << 4));
-      dma16(vb, off, __builtin_amdgcn_readfirstlane(lds_addr(v_lds[st]) + j * 1024));
-    }
     if constexpr (GATED) {
       // gate terms of two heads per copy: lane l -> head 2 w + l / 32, key l % 32
       if (2 * wave < HPW) {
@@ -155,6 +153,20 @@ __global__ __launch_bounds__(64 * large_waves<DV>()) void fwd_large_kernel(FwdPa
         const uint32_t go = (uint32_t)((hsel * p.T + min(j0 + (lane & 31), L - 1)) * 4);
         dma4(gb, go, __builtin_amdgcn_readfirstlane(lds_addr(&gk_lds[st][2 * wave][0])));
       }
+    }
+  };
+  auto fetch_v = [&](int u) {
+    const int j0 = (t_begin + u) * BN, st = u & 1;
+    const bool tail = j0 + BN > L;
+    const uint8_t* vb = vbase + (long)j0 * vstride;
+#pragma unroll
+    for (int jj = 0; jj < VBLK / NW; ++jj) {
+      const int j = wave + NW * jj;
+      const int o = j * 1024 + lane * 16;
+      const int r = o / VRB;
+      const int rr = tail ? min(r, L - 1 - j0) : r;
+      const uint32_t off = (uint32_t)(rr * vstride + ((((o % VRB) >> 4) ^ v_swz(r)) << 4));
+      dma16(vb, off, __builtin_amdgcn_readfirstlane(lds_addr(v_lds[st]) + j * 1024));
     }
   };
 
@@ -180,26 +192,22 @@ __global__ __launch_bounds__(64 * large_waves<DV>()) void fwd_large_kernel(FwdPa
     v_lane[db] = (uint32_t)(r * VRB + ((ch ^ v_swz(r)) << 4) + ((col * 2) & 15));
   }
 
-  fetch(t_begin);
-  for (int t = t_begin; t < t_end; ++t) {
-    const int j0 = t * BN, st = (t - t_begin) & 1;
-    // ---- K/V of tile t in LDS; P of tile t-1 consumed by every wave ----
-    wait_vm<0>();
-    lds_barrier();
-    if (t + 1 < t_end) fetch(t + 1);
-
-    // ---- S = Q K^T for this wave's 16 slots (C lane: row li, keys 4g + i) ----
-    f32x4 s[KB];
+  // ---- S of tile t_begin + u for this wave's 16 slots (C lane: row li, keys 4g + i) ----
+  auto s_tile = [&](int u, f32x4 (&s)[KB]) {
+    const uint8_t* kt = k_lds[u & 1];
 #pragma unroll
-    for (int kb = 0; kb < KB; ++kb) {
-      s[kb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int kb = 0; kb < KB; ++kb) s[kb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        const bf16x8 a = *reinterpret_cast<const bf16x8*>(k_lds[st] + k_lane[ks] + kb * 16 * KRB);
+    for (int ks = 0; ks < KS; ++ks)   // the key blocks' chains alternate
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) {
+        const bf16x8 a = *reinterpret_cast<const bf16x8*>(kt + k_lane[ks] + kb * 16 * KRB);
         s[kb] = mfma16x16x32(a, qop[ks], s[kb]);
       }
-    }
-    // ---- bias, mask, online softmax ----
+  };
+  // ---- bias, mask, online softmax; P and the rescale factor into buffer u & 1 ----
+  auto softmax_tile = [&](int u, f32x4 (&s)[KB], auto&& between) {
+    const int j0 = (t_begin + u) * BN, st = u & 1;
     const bool need_mask = (j0 + BN - 1 > r0) || (W > 0 && r_last - j0 >= W) || (j0 + BN > L) || (r_last < r0 + 15);
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb) {
@@ -221,14 +229,16 @@ __global__ __launch_bounds__(64 * large_waves<DV>()) void fwd_large_kernel(FwdPa
     float mx = fmaxf(fmaxf(s[0][0], s[0][1]), fmaxf(s[0][2], s[0][3]));
 #pragma unroll
     for (int kb = 1; kb < KB; ++kb) mx = fmaxf(mx, fmaxf(fmaxf(s[kb][0], s[kb][1]), fmaxf(s[kb][2], s[kb][3])));
-    mx = xgroup_max(mx);
-    float alpha = 1.f;
-    if (__builtin_expect(__any(mx > m_run + kRescaleSlack), 0)) {
-      const float m_new = fmaxf(m_run, mx);
-      alpha = fast_exp2(m_run - m_new);
-      l_run *= alpha;
-      m_run = m_new;
-    }
+    // lazy rescale, without a branch (so that the exponentials can be
+    // scheduled between the MFMAs of the other tile's PV): the running max
+    // moves only when some lane's own max passes it by more than the slack,
+    // which is when the row max does
+    between();   // the other tile's MFMAs that the exponentials can hide behind
+    const float mg = xgroup_max(mx);
+    const float m_new = __any(mx > m_run + kRescaleSlack) ? fmaxf(m_run, mg) : m_run;
+    const float alpha = m_new != m_run ? fast_exp2(m_run - m_new) : 1.f;
+    l_run *= alpha;
+    m_run = m_new;
     float rs = 0.f;
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb) {
@@ -236,30 +246,34 @@ __global__ __launch_bounds__(64 * large_waves<DV>()) void fwd_large_kernel(FwdPa
 #pragma unroll
       for (int i = 0; i < 4; ++i) e[i] = fast_exp2(s[kb][i] - m_run);
       rs += (e[0] + e[1]) + (e[2] + e[3]);
-      *reinterpret_cast<bf16x4*>(p_lds + p_wr + kb * 32) = to_bf16x4(e);
+      *reinterpret_cast<bf16x4*>(p_lds[st] + p_wr + kb * 32) = to_bf16x4(e);
     }
-    l_run += xgroup_sum(rs);
-    if (g == 0) alpha_lds[16 * wave + li] = alpha;
-    lds_barrier();   // P and the rescale factors of tile t visible to every wave
-
-    // ---- O^T += V^T P^T over this wave's columns, for all slots ----
+    l_run += rs;   // the lane groups' parts are added after the loop
+    if (g == 0) alpha_lds[st][16 * wave + li] = alpha;
+  };
+  // ---- O^T += V^T P^T of tile t_begin + u over this wave's columns, for all slots ----
+  auto o_rescale = [&](int u) {
 #pragma unroll
     for (int rb = 0; rb < NRB; ++rb) {
-      const float a = alpha_lds[rb * 32 + (lane & 31)];
+      const float a = alpha_lds[u & 1][rb * 32 + (lane & 31)];
       if (__builtin_expect(__any(a != 1.f), 0)) {
 #pragma unroll
         for (int db = 0; db < NDB; ++db) oacc[db][rb] *= a;
       }
     }
+  };
+  auto pv_tile = [&](int u, int ps_lo, int ps_hi) {   // k-steps ps_lo .. ps_hi - 1
+    const uint8_t* pt = p_lds[u & 1];
+    const uint8_t* vt = v_lds[u & 1];
 #pragma unroll
-    for (int ps = 0; ps < PS; ++ps) {
+    for (int ps = ps_lo; ps < ps_hi; ++ps) {
       bf16x8 pf[NRB];
 #pragma unroll
       for (int rb = 0; rb < NRB; ++rb)
-        pf[rb] = *reinterpret_cast<const bf16x8*>(p_lds + p_rd + rb * 32 * PRB + ps * 32);
+        pf[rb] = *reinterpret_cast<const bf16x8*>(pt + p_rd + rb * 32 * PRB + ps * 32);
 #pragma unroll
       for (int db = 0; db < NDB; ++db) {
-        const uint8_t* vb = v_lds[st] + v_lane[db] + 16 * ps * VRB;
+        const uint8_t* vb = vt + v_lane[db] + 16 * ps * VRB;
         const bf16x8 vf = concat(lds_read_tr16(reinterpret_cast<const bf16*>(vb)),
                                  lds_read_tr16(reinterpret_cast<const bf16*>(vb + 4 * VRB)));
 #pragma unroll
@@ -267,9 +281,40 @@ __global__ __launch_bounds__(64 * large_waves<DV>()) void fwd_large_kernel(FwdPa
           oacc[db][rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[rb], oacc[db][rb], 0, 0, 0);
       }
     }
+  };
+
+  // ---- tile loop, software pipelined across waves and tiles: iteration u
+  // computes S and P of tile u + 1 and the PV of tile u, so one barrier per
+  // tile publishes P(u + 1) and retires the reads of tiles u (K) and u - 1 (V) ----
+  const int NT = t_end - t_begin;
+  fetch_k(0);
+  fetch_v(0);
+  if (NT > 1) fetch_k(1);
+  wait_vm<0>();
+  lds_barrier();
+  {
+    f32x4 s[KB];
+    s_tile(0, s);
+    softmax_tile(0, s, [] {});
   }
+  for (int u = 0; u + 1 < NT; ++u) {
+    wait_vm<0>();
+    lds_barrier();   // K(u + 1) and V(u) landed, P(u) visible; tile u - 1 fully read
+    if (u + 2 < NT) fetch_k(u + 2);   // into the stage of K(u), read in the last iteration
+    fetch_v(u + 1);                   // into the stage of V(u - 1), likewise
+    o_rescale(u);
+    f32x4 s[KB];
+    s_tile(u + 1, s);
+    pv_tile(u, 0, PS / 2);
+    softmax_tile(u + 1, s, [&] { pv_tile(u, PS / 2, PS); });
+  }
+  wait_vm<0>();
+  lds_barrier();   // P of the last tile visible
+  o_rescale(NT - 1);
+  pv_tile(NT - 1, 0, PS);
 
   // ---- finalize: row sums of every slot from their owners; O = acc / l ----
+  l_run = xgroup_sum(l_run);
   lds_barrier();
   if (g == 0) l_lds[16 * wave + li] = l_run;
   if (g == 0 && row < L) p.lse[(long)(seq0 + row) * p.Hq + hw] = (m_run + gq + fast_log2(l_run)) * kLn2;
