@@ -92,6 +92,7 @@ DECODE_CASES = [
     ([64, 65537], [4, 4], 32, 2, 128, 64, synth.KV_BF16),             # the aiter PR's Test plan context
     ([1, 37, 300, 1029, 4096], [1, 1, 1, 1, 1], 32, 4, 64, 16, synth.KV_FP8_E4M3FN),   # fp8, D 64
     ([5, 130, 2051], [4, 2, 3], 16, 4, 64, 64, synth.KV_FP8_E4M3FN),   # fp8, D 64, short queries
+    ([5, 130, 2051], [4, 2, 3], 64, 4, 64, 64, synth.KV_FP8_E4M3FN),   # fp8, D 64, two-wave verify shape
 ]
 
 
