@@ -219,6 +219,10 @@ PREFILL_CASES = [
     ([97, 160], 4, 1, 128, 512, 0, True, False),
     ([180, 45], 4, 2, 256, 64, 0, True, True),
     ([77, 150], 8, 2, 256, 128, 60, False, True),
+    # one query head per workgroup in the large-head kernels: MHA, and a KV
+    # group of three heads
+    ([200, 37], 4, 4, 256, 512, 0, True, True),
+    ([150, 90], 6, 2, 128, 256, 50, True, True),
     # the backward's dS store over many row tiles and key-block slots: a
     # window band of 300 keys, and an unwindowed causal triangle
     ([1500, 700], 4, 2, 256, 512, 300, True, True),
