@@ -248,7 +248,7 @@ void bwd_dkdv_kernel(BwdParams p) {
           static_assert(NJ % PC == 0, "chunks");
           bf16x8 a[2][PC];
           auto rd = [&](int j) -> bf16x8 {
-            const int rb = j / NR, r = j % NR;
+            const int rb = j % 2, r = j / 2;   // the two row blocks' chains alternate
             return r < KSQ ? *reinterpret_cast<const bf16x8*>(ql + tile_off<QRB>(rb * 16 + li, 64 * r + 16 * g))
                            : *reinterpret_cast<const bf16x8*>(ol + tile_off<ORB>(rb * 16 + li, 64 * (r - KSQ) + 16 * g));
           };
@@ -263,7 +263,7 @@ void bwd_dkdv_kernel(BwdParams p) {
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int j = 0; j < PC; ++j) {
-              const int jj = c * PC + j, rb = jj / NR, r = jj % NR;
+              const int jj = c * PC + j, rb = jj % 2, r = jj / 2;
 #pragma unroll
               for (int kb = 0; kb < KBW; ++kb) {
                 if (r < KSQ) s[kb][rb] = mfma16x16x32(a[c & 1][j], kop[kb][r], s[kb][rb]);

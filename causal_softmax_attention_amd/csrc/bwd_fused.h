@@ -226,15 +226,20 @@ __global__ __launch_bounds__(64 * fused_waves<DV>()) void bwd_fused_kernel(BwdPa
         for (int rb = 0; rb < 2; ++rb) {
           s[rb] = f32x4{0.f, 0.f, 0.f, 0.f};
           dp[rb] = f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+        // the two row blocks' chains alternate
 #pragma unroll
-          for (int ks = 0; ks < KSQ; ++ks)
+        for (int ks = 0; ks < KSQ; ++ks)
+#pragma unroll
+          for (int rb = 0; rb < 2; ++rb)
             s[rb] = mfma16x16x32(*reinterpret_cast<const bf16x8*>(ql + tile_off<QRB>(rb * 16 + li, 64 * ks + 16 * g)),
                                  kop[ks], s[rb]);
 #pragma unroll
-          for (int ks = 0; ks < KSV; ++ks)
+        for (int ks = 0; ks < KSV; ++ks)
+#pragma unroll
+          for (int rb = 0; rb < 2; ++rb)
             dp[rb] = mfma16x16x32(*reinterpret_cast<const bf16x8*>(ol + tile_off<ORB>(rb * 16 + li, 64 * ks + 16 * g)),
                                   vop[ks], dp[rb]);
-        }
         // ---- P, dS, partial sums ----
         f32x4 pv[2], dsv[2];
 #pragma unroll
